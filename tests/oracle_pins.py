@@ -1,0 +1,231 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees with
+an independent source: a library routine (stable argsort, scipy softmax and
+expit, numpy/torch matmul), exact integer arithmetic, a structurally different
+dense formulation, or an algebraic identity of the method (the merged-weight
+identity x(W + AB) = xW + (xA)B, B = 0 reducing to the base MoE, invariance
+under token permutation).  The checks are run against the real oracle by
+tests/test_oracle.py and against deliberately broken copies of it by
+tests/test_oracle_mutants.py.
+
+The layer definition being pinned is the one of the vLLM blog page
+"Multi-LoRA" (vllm.com.cn/blog/multi-lora), section "Implementing Multi-LoRA
+inference for MoE models in vLLM": top-k routing, y = xW + (xA)B for both
+projections, SiLU(gate) * up in between, weighted combination of the experts.
+"""
+from __future__ import annotations
+
+import numpy as np
+import scipy.special
+
+import oracle
+from moe_lora_layer_amd import synth
+
+REL = 1e-12
+
+
+def _rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / scale) if a.size else 0.0
+
+
+def tiny_cfg(T=6, h=16, I=8, E=4, k=2, L=3, r=2, dtype="f32", seed=7, requests=None):
+    return synth.LayerConfig("pin", T, h, I, E, k, L, r, dtype,
+                             requests=requests if requests is not None else T, seed=seed)
+
+
+def _f64_inputs(inp, dtype):
+    return {n: synth.to_float(inp[n], dtype).astype(np.float64)
+            for n in ["x", "w_gate_up", "w_down", "a_gate_up", "b_gate_up", "a_down", "b_down"]}
+
+
+def dense_reference(inp, cfg):
+    """Every expert for every token, then a dense [T][E] gate matrix that is zero off the top-k.
+    Routing from a library softmax and a stable argsort; products from numpy einsum."""
+    f = _f64_inputs(inp, cfg.dtype)
+    T, I, E, k = cfg.tokens, cfg.intermediate, cfg.experts, cfg.top_k
+    logits = inp["logits"].astype(np.float64)
+    order = np.argsort(-inp["logits"], axis=1, kind="stable")[:, :k]
+    probs = scipy.special.softmax(logits, axis=1)
+    kept = np.take_along_axis(probs, order, axis=1)
+    gates = np.zeros((T, E))
+    np.put_along_axis(gates, order, kept / kept.sum(axis=1, keepdims=True), axis=1)
+    ad = inp["adapter_ids"]
+    X = f["x"]
+    A1, B1, A2, B2 = f["a_gate_up"][ad], f["b_gate_up"][ad], f["a_down"][ad], f["b_down"][ad]
+    G = np.einsum("th,enh->ten", X, f["w_gate_up"])
+    Z1 = np.einsum("th,terh->ter", X, A1)
+    G = G + np.einsum("ter,tenr->ten", Z1, B1)
+    act = G[..., :I] * scipy.special.expit(G[..., :I]) * G[..., I:]
+    D = np.einsum("tei,ehi->teh", act, f["w_down"])
+    Z2 = np.einsum("tei,teri->ter", act, A2)
+    D = D + np.einsum("ter,tehr->teh", Z2, B2)
+    return np.einsum("te,teh->th", gates, D)
+
+
+# ----------------------------------------------------------------------------- routing
+
+def check_route_ids_stable_argsort():
+    rng = np.random.default_rng(1)
+    for T, E, k in [(50, 8, 2), (40, 16, 4), (30, 5, 5), (10, 1, 1), (64, 32, 8)]:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        # inject ties: copy some logits onto neighbours
+        logits[::3, E // 2] = logits[::3, 0]
+        logits[1::4, -1] = logits[1::4, E // 3]
+        ids, _ = oracle.route(logits, k)
+        ref = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref), (T, E, k)
+    ids, _ = oracle.route(np.array([[1.0, 3.0, 3.0, 2.0]], np.float32), 2)
+    assert ids.tolist() == [[1, 2]]
+
+
+def check_route_weights_softmax():
+    rng = np.random.default_rng(2)
+    for T, E in [(40, 8), (20, 16), (5, 3)]:
+        logits = (3 * rng.standard_normal((T, E))).astype(np.float32)
+        _, w = oracle.route(logits, E)       # k = E: the full softmax in logit order
+        order = np.argsort(-logits, axis=1, kind="stable")
+        ref = np.take_along_axis(scipy.special.softmax(logits.astype(np.float64), axis=1), order, axis=1)
+        assert _rel_err(w, ref) <= REL
+        for k in range(1, E):
+            ids, w = oracle.route(logits, k)
+            kept = np.take_along_axis(logits.astype(np.float64), ids, axis=1)
+            ref = scipy.special.softmax(kept, axis=1)   # renormalised over the kept experts
+            assert _rel_err(w, ref) <= REL, k
+            assert np.max(np.abs(w.sum(axis=1) - 1.0)) <= 1e-12
+        _, w1 = oracle.route(logits, 1)
+        assert np.all(w1 == 1.0)
+
+
+# ----------------------------------------------------------------------------- permutation
+
+def check_align_stable_argsort():
+    rng = np.random.default_rng(3)
+    for T, k, E, L in [(100, 2, 8, 4), (37, 4, 32, 64), (64, 1, 1, 16), (5, 3, 3, 1), (0, 2, 4, 2),
+                       (200, 2, 2, 2)]:
+        ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+        ad = rng.integers(0, L, size=T).astype(np.int32)
+        ss, off = oracle.align(ids, ad, E, L)
+        keys = (ids.astype(np.int64) * L + ad[:, None]).reshape(-1)
+        assert np.array_equal(ss, np.argsort(keys, kind="stable").astype(np.int32)), (T, k, E, L)
+        ref_off = np.concatenate([[0], np.cumsum(np.bincount(keys, minlength=E * L))])
+        assert np.array_equal(off, ref_off), (T, k, E, L)
+    # every slot in one bucket keeps slot order
+    ids = np.full((9, 2), 1, np.int32)
+    ss, off = oracle.align(ids, np.zeros(9, np.int32), 3, 2)
+    assert ss.tolist() == list(range(18)) and off.tolist() == [0, 0, 0, 18, 18, 18, 18]
+
+
+# ----------------------------------------------------------------------------- forward
+
+def check_forward_dense_formulation():
+    shapes = [dict(T=6, h=16, I=8, E=4, k=2, L=3, r=2),
+              dict(T=8, h=8, I=16, E=3, k=3, L=2, r=4),
+              dict(T=5, h=16, I=16, E=4, k=1, L=3, r=1),
+              dict(T=7, h=8, I=8, E=2, k=2, L=1, r=2)]
+    for i, s in enumerate(shapes):
+        for dtype in ("f32", "bf16"):
+            cfg = tiny_cfg(dtype=dtype, seed=20 + i, **s)
+            inp = synth.make_inputs(cfg)
+            *_, out = oracle.layer(inp, cfg, threads=2)
+            ref = dense_reference(inp, cfg)
+            assert _rel_err(out, ref) <= REL, (s, dtype, _rel_err(out, ref))
+
+
+def check_gate_up_integer_exact():
+    rng = np.random.default_rng(4)
+    h, I, E, L, r = 64, 32, 3, 2, 4
+    inp = {"x": rng.integers(-2, 3, (3, h)), "w_gate_up": rng.integers(-2, 3, (E, 2 * I, h)),
+           "w_down": rng.integers(-2, 3, (E, h, I)), "a_gate_up": rng.integers(-2, 3, (L, E, r, h)),
+           "b_gate_up": rng.integers(-2, 3, (L, E, 2 * I, r)), "a_down": rng.integers(-2, 3, (L, E, r, I)),
+           "b_down": rng.integers(-2, 3, (L, E, h, r))}
+    dims = {"hidden": h, "intermediate": I, "experts": E, "adapters": L, "rank": r, "dtype": "f32"}
+    fin = {n: v.astype(np.float32) for n, v in inp.items()}
+    for t, e, l in [(0, 0, 0), (1, 2, 1), (2, 1, 0)]:
+        got = oracle.slot(fin, dims, t, e, l)
+        x = inp["x"][t].astype(np.int64)
+        z1 = inp["a_gate_up"][l, e].astype(np.int64) @ x
+        g = inp["w_gate_up"][e].astype(np.int64) @ x + inp["b_gate_up"][l, e].astype(np.int64) @ z1
+        assert np.array_equal(got["z1"], z1.astype(np.float64))
+        assert np.array_equal(got["g"], g.astype(np.float64)), (t, e, l)
+        # the activation and the down projection against library routines on the same values
+        gg = got["g"]
+        assert _rel_err(got["a"], gg[:I] * scipy.special.expit(gg[:I]) * gg[I:]) <= REL
+        a = got["a"]
+        z2 = inp["a_down"][l, e].astype(np.float64) @ a
+        d = inp["w_down"][e].astype(np.float64) @ a + inp["b_down"][l, e].astype(np.float64) @ z2
+        assert _rel_err(got["z2"], z2) <= REL
+        assert _rel_err(got["d"], d) <= REL
+
+
+def check_lora_zero_is_base_moe():
+    cfg = tiny_cfg(T=8, h=16, I=8, E=4, k=2, L=3, r=2, dtype="bf16", seed=31)
+    inp = synth.make_inputs(cfg)
+    zero_b = dict(inp, b_gate_up=np.zeros_like(inp["b_gate_up"]), b_down=np.zeros_like(inp["b_down"]))
+    zero_ab = dict(zero_b, a_gate_up=np.zeros_like(inp["a_gate_up"]), a_down=np.zeros_like(inp["a_down"]))
+    *_, out_b0 = oracle.layer(zero_b, cfg, threads=1)
+    *_, out_ab0 = oracle.layer(zero_ab, cfg, threads=1)
+    assert np.array_equal(out_b0, out_ab0)           # LoRA term exactly 0.0
+    *_, out_lora = oracle.layer(inp, cfg, threads=1)
+    assert _rel_err(out_lora, out_b0) > 1e-3            # and it does matter when B != 0
+    assert _rel_err(out_b0, dense_reference(zero_b, cfg)) <= REL
+
+
+def check_merged_weight_identity():
+    cfg = tiny_cfg(T=9, h=16, I=8, E=3, k=2, L=3, r=2, dtype="f32", seed=41)
+    inp = synth.make_inputs(cfg)
+    *_, out = oracle.layer(inp, cfg, threads=2)
+    ids, w = oracle.route(inp["logits"], cfg.top_k)
+    f = _f64_inputs(inp, "f32")
+    for l in range(cfg.adapters):
+        toks = np.nonzero(inp["adapter_ids"] == l)[0]
+        if toks.size == 0:
+            continue
+        # merged weights, transposed storage: (W + A B)^T = W^T + B^T A^T
+        wgu = f["w_gate_up"] + f["b_gate_up"][l] @ f["a_gate_up"][l]
+        wdn = f["w_down"] + f["b_down"][l] @ f["a_down"][l]
+        E = cfg.experts
+        merged = {"x": f["x"], "w_gate_up": wgu, "w_down": wdn,
+                  "a_gate_up": np.zeros((1, E, 1, cfg.hidden)), "b_gate_up": np.zeros((1, E, 2 * cfg.intermediate, 1)),
+                  "a_down": np.zeros((1, E, 1, cfg.intermediate)), "b_down": np.zeros((1, E, cfg.hidden, 1)),
+                  "adapter_ids": np.zeros(cfg.tokens, np.int32)}
+        dims = {"hidden": cfg.hidden, "intermediate": cfg.intermediate, "experts": E, "adapters": 1,
+                "rank": 1, "dtype": "f64"}
+        base = oracle.forward(merged, dims, ids, w, tokens=toks, threads=2)
+        assert _rel_err(base, out[toks]) <= 1e-12, l
+
+
+def check_dense_case_torch():
+    import torch
+    cfg = tiny_cfg(T=10, h=16, I=24, E=1, k=1, L=4, r=4, dtype="bf16", seed=51)
+    inp = synth.make_inputs(cfg)
+    ids, w, _, _, out = oracle.layer(inp, cfg, threads=2)
+    assert np.all(ids == 0) and np.all(w == 1.0)
+    f = {n: torch.from_numpy(v) for n, v in _f64_inputs(inp, "bf16").items()}
+    ad = torch.from_numpy(inp["adapter_ids"].astype(np.int64))
+    x = f["x"]
+    I = cfg.intermediate
+    g = x @ f["w_gate_up"][0].T + torch.einsum("tr,tnr->tn", torch.einsum("th,trh->tr", x, f["a_gate_up"][ad, 0]),
+                                               f["b_gate_up"][ad, 0])
+    a = torch.nn.functional.silu(g[:, :I]) * g[:, I:]
+    d = a @ f["w_down"][0].T + torch.einsum("tr,tnr->tn", torch.einsum("ti,tri->tr", a, f["a_down"][ad, 0]),
+                                            f["b_down"][ad, 0])
+    assert _rel_err(out, d.numpy()) <= REL
+
+
+def check_token_permutation_invariance():
+    cfg = tiny_cfg(T=12, h=16, I=8, E=4, k=2, L=3, r=2, dtype="bf16", seed=61)
+    inp = synth.make_inputs(cfg)
+    *_, out = oracle.layer(inp, cfg, threads=3)
+    perm = np.random.default_rng(5).permutation(cfg.tokens)
+    sh = dict(inp, x=inp["x"][perm], logits=inp["logits"][perm], adapter_ids=inp["adapter_ids"][perm])
+    *_, out_p = oracle.layer(sh, cfg, threads=3)
+    assert np.array_equal(out_p, out[perm])
+
+
+ALL_CHECKS = [check_route_ids_stable_argsort, check_route_weights_softmax, check_align_stable_argsort,
+              check_forward_dense_formulation, check_gate_up_integer_exact, check_lora_zero_is_base_moe,
+              check_merged_weight_identity, check_dense_case_torch, check_token_permutation_invariance]

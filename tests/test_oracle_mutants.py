@@ -1,0 +1,47 @@
+"""Plant plausible mistakes in copies of the oracle source (on the CPU) and
+show that the pins catch every one of them: a dropped term, a wrong sign, a
+swapped operand, a wrong stride or index, a wrong tie rule, a missing
+normalisation or weight."""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "lora_term_dropped": ("y[n] = base + lora;", "y[n] = base;"),
+    "silu_sign": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
+    "gate_up_swapped": ("a[i] = silu(g[i]) * g[I + i];", "a[i] = silu(g[I + i]) * g[i];"),
+    "tie_to_higher_id": ("lg[e] > lg[best]", "lg[e] >= lg[best]"),
+    "b_stride": ("b_off + n * r", "b_off + n"),
+    "w_stride": ("w_off + n * K", "w_off + n"),
+    "adapter_expert_index": ("int64_t le = (int64_t)l * E + e;", "int64_t le = (int64_t)e * L + l;"),
+    "no_renormalisation": ("topk_w[t * k + j] = ex[j] / sum;", "topk_w[t * k + j] = ex[j];"),
+    "adapter_major_keys": ("(int64_t)topk_ids[s] * L + adapter_ids[s / k]", "(int64_t)adapter_ids[s / k] * E + topk_ids[s]"),
+    "combine_weight_dropped": ("o[n] += w * d[n];", "o[n] += d[n];"),
+    "x_transposed": ("xin[i] = elem(x, t * h + i, dtype);", "xin[i] = elem(x, i * T + t, dtype);"),
+    "down_uses_up_half": ("lora_projection(a, I, h, r, w_dn,", "lora_projection(g + I, I, h, r, w_dn,"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(oracle._SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = oracle.load_library(oracle.compile_source(path, os.path.join(d, "libmutant.so")))
+        monkeypatch.setattr(oracle, "_lib", lib)
+        caught = []
+        for check in oracle_pins.ALL_CHECKS:
+            try:
+                check()
+            except (AssertionError, ValueError):
+                caught.append(check.__name__)
+                break
+        assert caught, f"no pin caught mutant {name}"
