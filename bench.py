@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE multi-LoRA layer on one MI355X.
+
+A step is one pass of the whole layer over one batch of synthetic input:
+moelora_align (routing + bucketed permutation) followed by moelora_forward
+(base grouped GEMMs, LoRA shrink/expand, SiLU-mul, top-k combination), with
+every input already resident in HBM.  Prints one JSON line on stdout; details
+go to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: decode_h4096 (64 tokens, h 4096, I 11008, 16 experts top-2,
+8 adapters rank 32, bf16).  Per-kernel durations come from HIP events that the
+library records on the launch stream between its kernels
+(moelora_forward_profiled).  The CPU baseline times the plain C oracle on the
+host's cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-LoRA layer tokens/s; shrink/expand HBM GB/s and GEMM MFMA % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA bf16; fp32 (vector/MFMA)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_work(cfg, offsets):
+    """Algorithmic bytes and flops per stage of one forward launch, from the active
+    experts and (expert, adapter) buckets of this batch."""
+    import numpy as np
+    T, h, I, E, k, L, r = (cfg.tokens, cfg.hidden, cfg.intermediate, cfg.experts, cfg.top_k,
+                           cfg.adapters, cfg.rank)
+    S = T * k
+    b = 2 if cfg.dtype == "bf16" else 4
+    counts = np.diff(offsets)
+    P = int(np.count_nonzero(counts))                            # active buckets
+    Eact = int(np.count_nonzero(counts.reshape(E, L).sum(axis=1)))  # active experts
+    w = {
+        "prep": (S * 4 * 3 + (E * L + 1) * 4, 0),
+        "zero": (2 * S * r * 4, 0),
+        "gemm_gate_up": (Eact * 2 * I * h * b + S * h * b + S * 2 * I * 4, 2 * S * h * 2 * I),
+        "shrink_gate_up": (P * h * r * b + S * h * b + S * r * 4, 2 * S * h * r),
+        "expand_gate_up": (P * r * 2 * I * b + S * r * 4 + S * 2 * I * 4 + S * I * b, 2 * S * r * 2 * I),
+        "gemm_down": (Eact * h * I * b + S * I * b + S * h * 4, 2 * S * I * h),
+        "shrink_down": (P * I * r * b + S * I * b + S * r * 4, 2 * S * I * r),
+        "expand_down": (P * r * h * b + S * r * 4 + 2 * S * h * 4, 2 * S * r * h),
+        "combine": (S * h * 4 + T * h * b + S * 8, 2 * S * h),
+    }
+    return w, Eact, P
+
+
+def main() -> int:
+    from moe_lora_layer_amd import synth
+
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_h4096", choices=synth.WORKLOAD_ORDER)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=64,
+                    help="tokens in the oracle's timed sample (default 64)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py: --gpus {args.gpus} is not supported: this layer is built and measured on "
+            "one GPU only (no collectives); run with --gpus 1")
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        log("bench.py: --steps must be >= 1 and --warmup >= 0")
+        return 2
+
+    import numpy as np
+    import torch
+    from moe_lora_layer_amd import ops
+
+    cfg = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg)
+    log(f"[bench] {cfg.name}: inputs generated in {time.time() - t0:.1f}s")
+
+    def dev_t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    names = ["w_gate_up", "w_down", "a_gate_up", "b_gate_up", "a_down", "b_down"]
+    W = {n: dev_t(inp[n]) for n in names}
+    x = dev_t(inp["x"])
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    adapter_ids = torch.from_numpy(inp["adapter_ids"]).to(dev)
+    d = ops.dims_for(cfg)
+    layer = ops.MoELoRALayer(d, W, dev)
+    nst = len(ops.STAGES)
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+        for e in evs:
+            e.record()          # creates the underlying HIP event
+        return evs
+
+    events = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        ids, w, ss, off, _ = ops.align(d, logits, adapter_ids, out=layer.routing,
+                                       workspace_buf=layer.ws_align, status=layer.status)
+        return ops.forward(d, x, *[W[n] for n in names], w, ss, off, out=layer.out,
+                           workspace_buf=layer.ws_fwd, stage_events=evs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(layer.status[0].item()) != 0:
+        log("[bench] align reported a bad adapter id")
+        return 1
+
+    # ---- timed region: exactly K steps ---------------------------------------
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    # --------------------------------------------------------------------------
+
+    stage_ms = np.array([[events[i][s].elapsed_time(events[i][s + 1]) for s in range(nst)]
+                         for i in range(args.steps)])
+    mean_ms = stage_ms.mean(axis=0)
+    offsets = layer.routing[3].cpu().numpy()
+    work, Eact, P = stage_work(cfg, offsets)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = cfg.tokens * args.steps / elapsed
+
+    stages = {}
+    for sname, ms in zip(ops.STAGES, mean_ms):
+        by, fl = work[sname]
+        stages[sname] = {"us": round(ms * 1e3, 2), "GB/s": round(by / (ms * 1e-3) / 1e9, 1),
+                         "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2)}
+        log(f"[bench] {sname:15s} {ms * 1e3:9.2f} us  {stages[sname]['GB/s']:8.1f} GB/s "
+            f"({100 * stages[sname]['GB/s'] / HBM_PEAK_GBS:5.1f}% HBM)  "
+            f"{stages[sname]['TFLOP/s']:8.2f} TFLOP/s")
+    dom = ops.STAGES[int(np.argmax(mean_ms))]
+    by, fl = work[dom]
+    dom_s = mean_ms[ops.STAGES.index(dom)] * 1e-3
+    peak_f = MFMA_PEAK_TFLOPS[cfg.dtype]
+    if fl / (peak_f * 1e12) > by / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(fl / dom_s / 1e12, 2), "peak": peak_f,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(by / dom_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["kernel_us"] = round(dom_s * 1e6, 2)
+    log(f"[bench] {cfg.name}: {value:.1f} tokens/s, {ms_per_step:.3f} ms/step, "
+        f"sum of stages {mean_ms.sum():.3f} ms, active experts {Eact}, active buckets {P}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(cfg.tokens, args.cpu_tokens)
+        sel = np.linspace(0, cfg.tokens - 1, n).round().astype(np.int64)
+        threads = oracle.max_threads()
+        tc = time.perf_counter()
+        ids, wts = oracle.route(inp["logits"], cfg.top_k)
+        oracle.align(ids, inp["adapter_ids"], cfg.experts, cfg.adapters)
+        oracle.forward(inp, oracle.dims_of(cfg), ids, wts, tokens=sel, threads=threads)
+        tcpu = time.perf_counter() - tc
+        cpu = {"value": round(n / tcpu, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n} of {cfg.tokens} tokens (routing and permutation of all {cfg.tokens}), "
+                         f"fp64 C oracle, {tcpu:.1f} s wall"}
+        log(f"[bench] cpu oracle: {n} tokens in {tcpu:.1f}s on {threads} threads")
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded normal inputs, random-init weights)",
+        "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden,
+                   "intermediate": cfg.intermediate, "experts": cfg.experts, "top_k": cfg.top_k,
+                   "adapters": cfg.adapters, "rank": cfg.rank, "requests": cfg.requests,
+                   "adapter_dist": cfg.adapter_dist, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stages": stages,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,206 @@
+/*
+ * moelora.h -- C ABI of the fused MoE multi-LoRA layer for AMD MI355X (gfx950).
+ *
+ * The layer is the one described on the vLLM blog page "Multi-LoRA"
+ * (vllm.com.cn/blog/multi-lora), section "Implementing Multi-LoRA inference for
+ * MoE models in vLLM" and Fig. 1:
+ *   - a router sends each token to its top-k experts and the expert outputs are
+ *     combined with the routing weights;
+ *   - each expert runs a gate_up projection (h -> 2I) and a down projection
+ *     (I -> h) with SiLU(gate) * up in between;
+ *   - every projection with frozen weight W (h_in x h_out) carries the LoRA
+ *     adapter of the token's request, A (h_in x r) and B (r x h_out), and
+ *     computes y = xW + (xA)B: a shrink z = xA and an expand zB;
+ *   - LoRA weights exist per (adapter, expert), so each expert runs four LoRA
+ *     ops and two sparsities compound: expert routing and adapter choice.
+ *
+ * Two calls make one layer step:
+ *   moelora_align   routing + the (expert, adapter)-bucketed slot permutation
+ *   moelora_forward base grouped GEMMs, LoRA shrink/expand, SiLU-mul, combine
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers (hipMalloc / torch allocations on the
+ *     current device), row-major, contiguous, 16-byte aligned.
+ *   - Weights are K-contiguous: each array holds its matrix TRANSPOSED, i.e.
+ *     row n of the array is column n of the page's h_in x h_out matrix.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it: no host synchronisation, no allocation, no host reads of
+ *     device memory.  The caller keeps every buffer alive until the stream has
+ *     executed the work.  Calls are reentrant; concurrent calls need distinct
+ *     outputs and workspaces.
+ *   - Inputs are never written.  The library keeps no state between calls.
+ *   - Errors are returned as a moelora_status code before anything is
+ *     enqueued (argument errors) or right after the launches (MOELORA_ERR_HIP).
+ *     No C++ exception crosses this boundary.
+ */
+#ifndef MOELORA_H
+#define MOELORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOELORA_ABI_VERSION 1
+
+typedef enum moelora_status {
+  MOELORA_OK = 0,
+  MOELORA_ERR_NULL = 1,         /* a required pointer is NULL                            */
+  MOELORA_ERR_DIMS = 2,         /* a dimension is out of range                           */
+  MOELORA_ERR_UNSUPPORTED = 3,  /* dtype or rank not supported                           */
+  MOELORA_ERR_ALIGNMENT = 4,    /* a tensor pointer is not 16-byte aligned               */
+  MOELORA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than *_workspace_size       */
+  MOELORA_ERR_HIP = 6           /* the HIP runtime reported an error at launch           */
+} moelora_status;
+
+typedef enum moelora_dtype {
+  MOELORA_F32 = 0,   /* x, weights and out in float32                                    */
+  MOELORA_BF16 = 1   /* x, weights and out in bfloat16; accumulation is always float32   */
+} moelora_dtype;
+
+/*
+ * Layer dimensions.  Limits (checked, MOELORA_ERR_DIMS / _UNSUPPORTED otherwise):
+ *   tokens T >= 0 (T == 0 is a no-op), T * top_k < 2^31
+ *   hidden h and intermediate I: positive multiples of 64
+ *   experts E >= 1, 1 <= top_k <= min(E, 8), adapters L >= 1, E * L <= 8192
+ *   rank r in {16, 32, 64}
+ */
+typedef struct moelora_dims {
+  int64_t tokens;        /* T                                                       */
+  int64_t hidden;        /* h: gate_up input width, down output width               */
+  int64_t intermediate;  /* I: gate_up produces 2I columns, [gate | up]             */
+  int32_t experts;       /* E                                                       */
+  int32_t top_k;         /* k                                                       */
+  int32_t adapters;      /* L: adapters resident at once                            */
+  int32_t rank;          /* r                                                       */
+  int32_t dtype;         /* moelora_dtype                                           */
+} moelora_dims;
+
+int moelora_abi_version(void);
+
+/* Static string for a status code (never NULL). */
+const char* moelora_status_string(int status);
+
+/* Bytes of device workspace moelora_align needs for these dimensions. */
+int moelora_align_workspace_size(const moelora_dims* dims, size_t* bytes);
+
+/*
+ * moelora_align -- routing and the (expert, adapter)-bucketed permutation.
+ *
+ * Routing (same page, section "Implementing Multi-LoRA inference for MoE
+ * models in vLLM": the router picks the most relevant experts per token): for
+ * each token t, the k experts with the largest logits in descending logit order
+ * (exact float comparison, ties to the lower expert id), and weights equal to
+ * the softmax over all E logits restricted to those k and renormalised to sum
+ * to one (computed as exp(l_j - l_max) / sum over the kept j, in float32).
+ *
+ * Permutation (the compound sparsity of expert routing and adapter choice,
+ * same section): slot s = t*k + j has key topk_ids[s] * L + adapter_ids[t].
+ * sorted_slots is the stable sort of all slots by key; bucket_offsets[b] is the
+ * number of slots with key < b.  Both are deterministic and bit-exact.
+ *
+ *   router_logits  in  float [T][E]
+ *   adapter_ids    in  int32 [T], each in [0, L)
+ *   topk_ids       out int32 [T][k]
+ *   topk_weights   out float [T][k]
+ *   sorted_slots   out int32 [T*k]
+ *   bucket_offsets out int32 [E*L + 1]   (bucket_offsets[E*L] = T*k)
+ *   device_status  out int32 [1] or NULL: 0 = ok, 1 = an adapter id was outside
+ *                  [0, L) (it was treated as 0; the outputs are then unspecified).
+ *                  Read it after the stream has executed the call.
+ *   workspace      device scratch of at least moelora_align_workspace_size bytes
+ */
+int moelora_align(const moelora_dims* dims, const float* router_logits,
+                  const int32_t* adapter_ids, int32_t* topk_ids, float* topk_weights,
+                  int32_t* sorted_slots, int32_t* bucket_offsets, int32_t* device_status,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace moelora_forward needs for these dimensions. */
+int moelora_forward_workspace_size(const moelora_dims* dims, size_t* bytes);
+
+/*
+ * moelora_forward -- the layer for every slot, then the weighted combination.
+ *
+ * For each slot s (token t, expert e = its bucket's expert, adapter l = its
+ * bucket's adapter), following the page's section "Implementing Multi-LoRA
+ * inference for MoE models in vLLM" (the expert MLP, y = xW + xAB, shrink and
+ * expand, four LoRA ops per expert) and section "Kernel optimisation" (split-K
+ * shrink with relaxed atomics, the LoRA add fused with the base add):
+ *   g = x_t W_gu[e] + (x_t A_gu[l][e]) B_gu[l][e]          (2I columns)
+ *   a = SiLU(g[0:I]) * g[I:2I],  SiLU(v) = v / (1 + exp(-v))
+ *   d = a W_dn[e] + (a A_dn[l][e]) B_dn[l][e]              (h columns)
+ *   out[t] = sum_{j<k} topk_weights[t][j] * d(slot t*k+j), summed in j order
+ * The activation a is rounded to the layer dtype before the down projection;
+ * every sum is accumulated in float32.  Split-K atomics make the low bits of
+ * out vary from run to run.
+ *
+ *   x          in  [T][h]
+ *   w_gate_up  in  [E][2I][h]      (W_gu^T; rows [0,I) gate, [I,2I) up)
+ *   w_down     in  [E][h][I]       (W_dn^T)
+ *   a_gate_up  in  [L][E][r][h]    (A_gu^T)
+ *   b_gate_up  in  [L][E][2I][r]   (B_gu^T)
+ *   a_down     in  [L][E][r][I]    (A_dn^T)
+ *   b_down     in  [L][E][h][r]    (B_dn^T)
+ *   topk_weights, sorted_slots, bucket_offsets: as produced by moelora_align
+ *              (any stable bucketed permutation of the same keys is valid)
+ *   out        out [T][h], fully overwritten
+ *   workspace  device scratch of at least moelora_forward_workspace_size bytes;
+ *              its contents after the call are the intermediates described by
+ *              moelora_forward_workspace_layout.
+ */
+int moelora_forward(const moelora_dims* dims, const void* x, const void* w_gate_up,
+                    const void* w_down, const void* a_gate_up, const void* b_gate_up,
+                    const void* a_down, const void* b_down, const float* topk_weights,
+                    const int32_t* sorted_slots, const int32_t* bucket_offsets, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stages of moelora_forward, in launch order (one kernel each).
+ */
+enum moelora_stage {
+  MOELORA_STAGE_PREP = 0,        /* inverse permutation and tile lists              */
+  MOELORA_STAGE_ZERO = 1,        /* clear the shrink accumulators                    */
+  MOELORA_STAGE_GEMM_GATE_UP = 2,
+  MOELORA_STAGE_SHRINK_GATE_UP = 3,
+  MOELORA_STAGE_EXPAND_GATE_UP = 4,  /* + base add + SiLU-mul                        */
+  MOELORA_STAGE_GEMM_DOWN = 5,
+  MOELORA_STAGE_SHRINK_DOWN = 6,
+  MOELORA_STAGE_EXPAND_DOWN = 7,
+  MOELORA_STAGE_COMBINE = 8,
+  MOELORA_NUM_STAGES = 9
+};
+
+/*
+ * moelora_forward with per-stage timing for profilers and benchmarks.
+ * stage_events: NULL, or MOELORA_NUM_STAGES + 1 hipEvent_t handles created by
+ * the caller; event i is recorded on `stream` before stage i is launched and
+ * event MOELORA_NUM_STAGES after the last stage, so the elapsed time between
+ * events i and i+1 is the duration of stage i.  Everything else is identical to
+ * moelora_forward (which is this call with stage_events == NULL).
+ */
+int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void* w_gate_up,
+                             const void* w_down, const void* a_gate_up, const void* b_gate_up,
+                             const void* a_down, const void* b_down, const float* topk_weights,
+                             const int32_t* sorted_slots, const int32_t* bucket_offsets,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* stage_events);
+
+/*
+ * Debug aid for layer-by-layer reconciliation: byte offsets, inside the forward
+ * workspace, of the intermediates left there by moelora_forward, all indexed by
+ * sorted position p (row p belongs to slot sorted_slots[p]):
+ *   offsets[0]  G   float [T*k][2I]  gate_up base output xW (before the LoRA add)
+ *   offsets[1]  Z1  float [T*k][r]   gate_up shrink xA
+ *   offsets[2]  ACT dtype [T*k][I]   SiLU(gate) * up, including both LoRA terms
+ *   offsets[3]  Z2  float [T*k][r]   down shrink a A
+ *   offsets[4]  D   float [T*k][h]   down output including its LoRA term
+ */
+int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOELORA_H */

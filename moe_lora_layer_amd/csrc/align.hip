@@ -1,0 +1,186 @@
+// Routing and the (expert, adapter)-bucketed slot permutation, one workgroup.
+//
+// Follows the vLLM blog page "Multi-LoRA" (vllm.com.cn/blog/multi-lora),
+// section "Implementing Multi-LoRA inference for MoE models in vLLM": each
+// token goes to its most relevant experts, and expert routing compounds with
+// the per-request adapter choice, so slots are grouped by (expert, adapter).
+//
+// One workgroup of 1024 threads runs four phases separated by barriers:
+//   1. route: per token, a k-deep insertion list over the E logits (ties keep
+//      the lower id), softmax weights renormalised over the kept k; the slot
+//      keys e*L + l go to the workspace;
+//   2. chunk ranks: the S slots are cut into C contiguous chunks, one per wave.
+//      A wave walks its chunk 64 slots at a time; lanes with equal keys find
+//      each other with ballots, so every slot gets its rank among equal keys of
+//      lower index inside the chunk, and the chunk's per-bucket counts live in
+//      LDS (cnt[c][b]);
+//   3. scan: bucket totals, a wavefront-level exclusive prefix scan over the
+//      buckets gives bucket_offsets, and cnt[c][b] becomes the first output
+//      position of chunk c's slots in bucket b;
+//   4. scatter: sorted_slots[cnt[c][key] + rank] = s.
+// device_status: 0 ok, 1 an adapter id outside [0, L), 2 internal inconsistency.
+// No step depends on atomic ordering, so the result is bit-exact and stable.
+#include "device_common.h"
+#include "launch.h"
+
+namespace moelora {
+
+constexpr int kAlignThreads = 1024;
+constexpr int kMaxTopK = 8;
+
+__global__ void __launch_bounds__(kAlignThreads)
+k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_ids, int T, int E,
+        int k, int L, int chunks, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+        int32_t* __restrict__ sorted_slots, int32_t* __restrict__ offsets,
+        int32_t* __restrict__ status, int32_t* __restrict__ ws_key, int32_t* __restrict__ ws_rank) {
+  extern __shared__ int cnt[];  // [chunks][nb]
+  __shared__ int wave_tmp[16];
+  __shared__ int bad;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int nb = E * L;
+  const int S = T * k;
+
+  for (int i = tid; i < chunks * nb; i += kAlignThreads) cnt[i] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+
+  // ---- 1. route --------------------------------------------------------------
+  for (int t = tid; t < T; t += kAlignThreads) {
+    int l = adapter_ids[t];
+    if (l < 0 || l >= L) {
+      bad = 1;
+      l = 0;
+    }
+    float val[kMaxTopK];
+    int id[kMaxTopK];
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q) {
+      val[q] = -INFINITY;
+      id[q] = 0x7fffffff;
+    }
+    const float* lg = logits + static_cast<int64_t>(t) * E;
+    for (int e = 0; e < E; ++e) {
+      float cv = lg[e];
+      int ci = e;
+      // carry the candidate down the list: it passes every entry it beats
+#pragma unroll
+      for (int q = 0; q < kMaxTopK; ++q) {
+        if (q < k) {
+          bool before = cv > val[q] || (cv == val[q] && ci < id[q]);
+          if (before) {
+            float tv = val[q];
+            int ti = id[q];
+            val[q] = cv;
+            id[q] = ci;
+            cv = tv;
+            ci = ti;
+          }
+        }
+      }
+    }
+    float ex[kMaxTopK];
+    float sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q) {
+      if (q < k) {
+        ex[q] = expf(val[q] - val[0]);
+        sum += ex[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q) {
+      if (q < k) {
+        int s = t * k + q;
+        topk_ids[s] = id[q];
+        topk_w[s] = ex[q] / sum;
+        ws_key[s] = id[q] * L + l;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. ranks inside each chunk -------------------------------------------
+  const int chunk_len = (S + chunks - 1) / chunks;
+  if (wave < chunks) {
+    const int c0 = wave * chunk_len;
+    const int c1 = min(S, c0 + chunk_len);
+    int* my_cnt = cnt + wave * nb;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    for (int base = c0; base < c1; base += kWave) {
+      const int s = base + lane;
+      const bool valid = s < c1;
+      const int key = valid ? ws_key[s] : -1;
+      uint64_t remaining = __ballot(valid);
+      uint64_t peers = 0;
+      while (remaining) {
+        const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+        const int lk = __shfl(key, leader, kWave);
+        const uint64_t m = __ballot(valid && key == lk);
+        if (valid && key == lk) peers = m;
+        remaining &= ~m;
+      }
+      const int rank = __popcll(peers & lt_mask);
+      if (valid) ws_rank[s] = my_cnt[key] + rank;
+      __builtin_amdgcn_wave_barrier();
+      if (valid && rank == 0) my_cnt[key] += __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. bucket offsets (block-wide exclusive scan) -------------------------
+  const int per = (nb + kAlignThreads - 1) / kAlignThreads;
+  const int b0 = min(nb, tid * per);
+  const int b1 = min(nb, b0 + per);
+  int local = 0;
+  for (int b = b0; b < b1; ++b)
+    for (int c = 0; c < chunks; ++c) local += cnt[c * nb + b];
+  int total = 0;
+  int run = block_exclusive_scan(local, wave_tmp, &total);
+  for (int b = b0; b < b1; ++b) {
+    offsets[b] = run;
+    for (int c = 0; c < chunks; ++c) {
+      int v = cnt[c * nb + b];
+      cnt[c * nb + b] = run;
+      run += v;
+    }
+  }
+  if (tid == 0) offsets[nb] = total;
+  __syncthreads();
+
+  // ---- 4. scatter --------------------------------------------------------------
+  for (int s = tid; s < S; s += kAlignThreads) {
+    const int c = s / chunk_len;
+    const int dst = cnt[c * nb + ws_key[s]] + ws_rank[s];
+    if (dst >= 0 && dst < S)
+      sorted_slots[dst] = s;
+    else
+      bad = 2;  // cannot happen for consistent counts; never write out of bounds
+  }
+  __syncthreads();
+  if (tid == 0 && status != nullptr) *status = bad;
+}
+
+int align_chunks(int nb) {
+  int c = kAlignLdsInts / nb;
+  if (c > 16) c = 16;
+  if (c < 1) c = 1;
+  return c;
+}
+
+hipError_t launch_align(const float* logits, const int32_t* adapter_ids, int T, int E, int k,
+                        int L, int32_t* topk_ids, float* topk_w, int32_t* sorted_slots,
+                        int32_t* offsets, int32_t* status, int32_t* ws_key, int32_t* ws_rank,
+                        hipStream_t stream) {
+  const int nb = E * L;
+  const int chunks = align_chunks(nb);
+  const size_t lds = static_cast<size_t>(chunks) * nb * sizeof(int);
+  hipLaunchKernelGGL(k_align, dim3(1), dim3(kAlignThreads), lds, stream, logits, adapter_ids, T, E,
+                     k, L, chunks, topk_ids, topk_w, sorted_slots, offsets, status, ws_key, ws_rank);
+  return hipGetLastError();
+}
+
+}  // namespace moelora

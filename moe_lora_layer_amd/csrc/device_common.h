@@ -1,0 +1,124 @@
+// Device-side helpers shared by the gfx950 kernels: element types, MFMA
+// wrappers and fragment layouts, bf16 rounding, wave/block scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moelora {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// bfloat16 is stored as its raw 16-bit pattern.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even.  Inputs are finite here.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32 tiles.
+//
+// For both element types one instruction computes a 32x32 fp32 block
+// D += A (32 x KSTEP) * B (KSTEP x 32).  Lane l = 32*h + c supplies
+//   A fragment: row c of A, k-elements [h*KPACK, (h+1)*KPACK) of the step
+//   B fragment: column c of B, the same k-elements
+// and receives D element (row 8*(i/4) + 4*h + i%4, column c) in acc[i].
+//   bf16: v_mfma_f32_32x32x16_bf16, KSTEP 16, KPACK 8 (16 bytes per lane)
+//   f32 : v_mfma_f32_32x32x2_f32,    KSTEP 2,  KPACK 1 (4 bytes per lane)
+// Any mapping of the real k indices onto the step's k positions is valid as
+// long as A and B fragments use the same one.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16_t> {
+  static constexpr int KSTEP = 16;
+  static constexpr int KPACK = 8;
+  typedef bf16x8_t frag_t;
+  __device__ __forceinline__ static void run(f32x16_t& acc, frag_t a, frag_t b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag_t load(const bf16_t* p) {
+    return __builtin_bit_cast(frag_t, *reinterpret_cast<const uint4*>(p));
+  }
+  __device__ __forceinline__ static frag_t zero() { return __builtin_bit_cast(frag_t, make_uint4(0, 0, 0, 0)); }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KSTEP = 2;
+  static constexpr int KPACK = 1;
+  typedef float frag_t;
+  __device__ __forceinline__ static void run(f32x16_t& acc, frag_t a, frag_t b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag_t load(const float* p) { return *p; }
+  __device__ __forceinline__ static frag_t zero() { return 0.0f; }
+};
+
+// Row (within the 32x32 block) of accumulator element i held by a lane of half h.
+__device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+__device__ __forceinline__ f32x16_t zero_acc() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+// Relaxed, device-scope fp32 atomic add (hardware global_atomic_add_f32, no return).
+__device__ __forceinline__ void atomic_add_relaxed(float* p, float v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Inclusive scan of one int across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan of one int per thread across the whole block (blockDim.x a
+// multiple of 64, at most 1024).  wave_tmp must hold 16 ints of LDS.  Every
+// thread of the block must call it.  *total receives the block-wide sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tmp, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  int x = wave_inclusive_scan(v);
+  if (lane == kWave - 1) wave_tmp[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < nw ? wave_tmp[lane] : 0;
+    s = wave_inclusive_scan(s);
+    if (lane < nw) wave_tmp[lane] = s;
+  }
+  __syncthreads();
+  int prefix = w > 0 ? wave_tmp[w - 1] : 0;
+  *total = wave_tmp[nw - 1];
+  __syncthreads();
+  return prefix + x - v;
+}
+
+}  // namespace moelora

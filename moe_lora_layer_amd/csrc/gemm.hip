@@ -1,0 +1,276 @@
+// Base grouped GEMM of the MoE experts on the MFMA units, plus the tile
+// planner that turns bucket_offsets into per-expert M-tiles.
+//
+// The vLLM blog page "Multi-LoRA" (vllm.com.cn/blog/multi-lora), section
+// "Implementing Multi-LoRA inference for MoE models in vLLM", runs the expert
+// projections as a grouped GEMM: one GEMM per expert over the tokens routed to
+// it.  Here the rows of every expert are contiguous in the sorted order, so the
+// grid is a flat list of (M-tile, N-tile) pairs with the M-tiles computed on
+// the device; surplus workgroups exit at once.
+//
+// Tile: BM x BN outputs, K stepped by 128 bytes (64 bf16 / 32 fp32).  Both
+// operands are K-contiguous in memory (x rows and W^T rows), staged from
+// registers into LDS with a 16-byte-chunk XOR swizzle (chunk ^ (row & 7)) so
+// that the MFMA fragment reads (32 rows, same chunk) hit all banks, double
+// buffered: the next K-step's global loads are in flight while the MFMAs of
+// the current one run.
+#include "device_common.h"
+#include "launch.h"
+
+namespace moelora {
+
+// ------------------------------------------------------------------------- prep
+constexpr int kPrepThreads = 1024;
+
+// Writes tiles for items [i0, i1) whose lengths come from offsets at stride
+// `step`; `first` is the index of the first tile of item i0.
+// Tiles are only emitted below max_tiles and only for rows inside [0, S), so a
+// malformed offsets array cannot make any later kernel read out of bounds.
+__device__ void emit_tiles(const int32_t* offsets, int i0, int i1, int step, int rows, int first,
+                           int S, int max_tiles, int4* tiles) {
+  int t = first;
+  for (int i = i0; i < i1; ++i) {
+    const int r0 = max(0, offsets[i * step]);
+    const int r1 = min(S, offsets[(i + 1) * step]);
+    for (int r = r0; r < r1 && t < max_tiles; r += rows) tiles[t++] = make_int4(i, r, min(r1, r + rows), 0);
+  }
+}
+
+__device__ int count_tiles(const int32_t* offsets, int i0, int i1, int step, int rows, int S) {
+  int n = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int r0 = max(0, offsets[i * step]);
+    const int r1 = min(S, offsets[(i + 1) * step]);
+    if (r1 > r0) n += (r1 - r0 + rows - 1) / rows;
+  }
+  return n;
+}
+
+__global__ void __launch_bounds__(kPrepThreads)
+k_prep(const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ offsets, int S,
+       int E, int L, int bm, int bml, int max_mt, int max_lt, int32_t* __restrict__ pos,
+       int4* __restrict__ mtiles, int4* __restrict__ ltiles, int32_t* __restrict__ counts) {
+  __shared__ int wave_tmp[16];
+  const int tid = threadIdx.x;
+  for (int p = tid; p < S; p += kPrepThreads) {
+    const int s = sorted_slots[p];
+    if (s >= 0 && s < S) pos[s] = p;
+  }
+
+  // M-tiles: one item per expert, rows [offsets[e*L], offsets[(e+1)*L]).
+  {
+    const int per = (E + kPrepThreads - 1) / kPrepThreads;
+    const int i0 = min(E, tid * per), i1 = min(E, i0 + per);
+    int total = 0;
+    const int first =
+        block_exclusive_scan(count_tiles(offsets, i0, i1, L, bm, S), wave_tmp, &total);
+    emit_tiles(offsets, i0, i1, L, bm, first, S, max_mt, mtiles);
+    if (tid == 0) counts[0] = min(total, max_mt);
+  }
+  // LoRA tiles: one item per (expert, adapter) bucket.
+  {
+    const int nb = E * L;
+    const int per = (nb + kPrepThreads - 1) / kPrepThreads;
+    const int i0 = min(nb, tid * per), i1 = min(nb, i0 + per);
+    int total = 0;
+    const int first =
+        block_exclusive_scan(count_tiles(offsets, i0, i1, 1, bml, S), wave_tmp, &total);
+    emit_tiles(offsets, i0, i1, 1, bml, first, S, max_lt, ltiles);
+    if (tid == 0) counts[1] = min(total, max_lt);
+  }
+}
+
+hipError_t launch_prep(const int32_t* sorted_slots, const int32_t* offsets, int S, int E, int L,
+                       const TilePlan& plan, int32_t* pos, int4* mtiles, int4* ltiles,
+                       int32_t* counts, hipStream_t stream) {
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, sorted_slots, offsets, S, E,
+                     L, plan.bm, plan.bml, plan.max_mt, plan.max_lt, pos, mtiles, ltiles, counts);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------- zero
+// A plain fill kernel (no hipMemsetAsync: the call must stay capture-friendly).
+__global__ void __launch_bounds__(256) k_zero(float4* __restrict__ p, int64_t n4) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += gridDim.x * 256ll)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+hipError_t launch_zero(float* p, int64_t n, hipStream_t stream) {
+  const int64_t n4 = n / 4;  // callers pass multiples of 4
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     reinterpret_cast<float4*>(p), n4);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------- gemm
+template <typename T, int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(WM * WN * kWave)
+k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
+       const T* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
+       const int4* __restrict__ mtiles, const int32_t* __restrict__ counts, int n_ntiles) {
+  typedef Mfma<T> M;
+  constexpr int NT = WM * WN * kWave;
+  constexpr int ROWB = 128;                    // bytes of K per LDS row
+  constexpr int BK = ROWB / sizeof(T);
+  constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
+  constexpr int A_CH = BM * 8 / NT;
+  constexpr int B_CH = BN * 8 / NT;
+  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(A_CH >= 1 && B_CH >= 1 && BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads");
+  static_assert(FM >= 1 && FN >= 1, "wave tile");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2][(BM + BN) * ROWB];
+
+  const int mt = blockIdx.x / n_ntiles;
+  const int nt = blockIdx.x % n_ntiles;
+  if (mt >= counts[0]) return;
+  const int4 tile = mtiles[mt];
+  const int e = tile.x, row0 = tile.y, row_end = tile.z;
+  const int64_t n0 = static_cast<int64_t>(nt) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave / WN, wn = wave % WN;
+  const int c32 = lane & 31, h = lane >> 5;
+
+  // global sources and LDS destinations of this thread's 16-byte chunks
+  const T* a_src[A_CH];
+  int a_dst[A_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int q = tid + i * NT, row = q >> 3, ch = q & 7;
+    const int p = row0 + row;
+    a_src[i] = nullptr;
+    if (p < row_end) {
+      const int r = gather_slots ? gather_slots[p] / gather_k : p;
+      a_src[i] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + ch * VEC;
+    }
+    a_dst[i] = row * ROWB + ((ch ^ (row & 7)) << 4);
+  }
+  const T* b_src[B_CH];
+  int b_dst[B_CH];
+  const T* We = Wt + static_cast<int64_t>(e) * N * K;
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int q = tid + i * NT, row = q >> 3, ch = q & 7;
+    const int64_t n = n0 + row;
+    b_src[i] = n < N ? We + n * K + ch * VEC : nullptr;
+    b_dst[i] = BM * ROWB + row * ROWB + ((ch ^ (row & 7)) << 4);
+  }
+
+  uint4 a_reg[A_CH], b_reg[B_CH];
+  auto gload = [&](int kt) {
+    const int64_t ko = static_cast<int64_t>(kt) * BK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i)
+      a_reg[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + ko) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i)
+      b_reg[i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + ko) : make_uint4(0, 0, 0, 0);
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<uint4*>(&smem[buf][a_dst[i]]) = a_reg[i];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) *reinterpret_cast<uint4*>(&smem[buf][b_dst[i]]) = b_reg[i];
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = zero_acc();
+
+  // byte offset of lane's fragment inside an LDS row, for K-step ks
+  auto frag_off = [&](int row, int ks) {
+    const int byte = (ks * M::KSTEP + h * M::KPACK) * static_cast<int>(sizeof(T));
+    return row * ROWB + ((((byte >> 4) ^ (row & 7))) << 4) + (byte & 15);
+  };
+
+  const int nk = static_cast<int>(K / BK);
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const unsigned char* As = smem[cur];
+    const unsigned char* Bs = smem[cur] + BM * ROWB;
+#pragma unroll
+    for (int ks = 0; ks < BK / M::KSTEP; ++ks) {
+      typename M::frag_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = M::load(reinterpret_cast<const T*>(As + frag_off(wm * WTM + i * 32 + c32, ks)));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = M::load(reinterpret_cast<const T*>(Bs + frag_off(wn * WTN + j * 32 + c32, ks)));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) M::run(acc[i][j], af[i], bfr[j]);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * WTN + j * 32 + c32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = row0 + wm * WTM + i * 32 + acc_row(r, h);
+        if (p < row_end && n < N) C[static_cast<int64_t>(p) * N + n] = acc[i][j][r];
+      }
+    }
+}
+
+template <typename T, int BM, int BN, int WM, int WN>
+static hipError_t gemm_launch(const TilePlan& plan, const void* X, int x_rows, const int32_t* gather_slots,
+                              int gather_k, const void* Wt, int64_t N, int64_t K, float* C,
+                              const int4* mtiles, const int32_t* counts, hipStream_t stream) {
+  const int n_ntiles = static_cast<int>((N + BN - 1) / BN);
+  const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles;
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN>), dim3(static_cast<unsigned>(grid)),
+                     dim3(WM * WN * kWave), 0, stream, static_cast<const T*>(X), x_rows, gather_slots,
+                     gather_k, static_cast<const T*>(Wt), N, K, C, mtiles, counts, n_ntiles);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t gemm_dispatch(const TilePlan& plan, const void* X, int x_rows, const int32_t* gather_slots,
+                                int gather_k, const void* Wt, int64_t N, int64_t K, float* C,
+                                const int4* mtiles, const int32_t* counts, hipStream_t stream) {
+  switch (plan.bm) {
+    case 32:
+      return gemm_launch<T, 32, 128, 1, 4>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles,
+                                           counts, stream);
+    case 64:
+      return gemm_launch<T, 64, 128, 2, 2>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles,
+                                           counts, stream);
+    case 128:
+      return gemm_launch<T, 128, 128, 2, 2>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles,
+                                            counts, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
+                       const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
+                       int64_t K, float* C, const int4* mtiles, const int32_t* counts,
+                       hipStream_t stream) {
+  if (dtype == DT_BF16)
+    return gemm_dispatch<bf16_t>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts,
+                                 stream);
+  return gemm_dispatch<float>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts,
+                              stream);
+}
+
+}  // namespace moelora

@@ -1,0 +1,67 @@
+// Internal launchers of the gfx950 kernels (host side).  Every launcher only
+// enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moelora {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// LDS ints available to the align kernel's per-chunk bucket counters.
+constexpr int kAlignLdsInts = 15360;
+int align_chunks(int nb);
+
+hipError_t launch_align(const float* logits, const int32_t* adapter_ids, int T, int E, int k,
+                        int L, int32_t* topk_ids, float* topk_w, int32_t* sorted_slots,
+                        int32_t* offsets, int32_t* status, int32_t* ws_key, int32_t* ws_rank,
+                        hipStream_t stream);
+
+// Tile descriptor: x = expert (M-tiles) or bucket (LoRA tiles), y = first
+// sorted row, z = end row (exclusive), w unused.
+struct TilePlan {
+  int bm;        // rows per M-tile of the base GEMMs
+  int bml;       // rows per LoRA tile
+  int max_mt;    // upper bound of M-tiles, known on the host
+  int max_lt;    // upper bound of LoRA tiles
+};
+
+hipError_t launch_prep(const int32_t* sorted_slots, const int32_t* offsets, int S, int E, int L,
+                       const TilePlan& plan, int32_t* pos, int4* mtiles, int4* ltiles,
+                       int32_t* counts, hipStream_t stream);
+
+hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
+
+// C[p][n] = sum_k X[row(p)][k] * Wt[e][n][k] over the M-tiles of `mtiles`;
+// row(p) = gather_slots[p] / gather_k when gather_slots != nullptr, else p,
+// clamped to [0, x_rows).
+hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
+                       const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
+                       int64_t K, float* C, const int4* mtiles, const int32_t* counts,
+                       hipStream_t stream);
+
+// Z[p][q] += sum_k X[row(p)][k] * At[l][e][q][k] over the LoRA tiles (split-K,
+// fp32 atomics).  Z must be zero beforehand.
+hipError_t launch_shrink(int dtype, int rank, const TilePlan& plan, const void* X, int x_rows,
+                         const int32_t* gather_slots, int gather_k, const void* At, int E, int L,
+                         int64_t K, float* Z, const int4* ltiles, const int32_t* counts,
+                         hipStream_t stream);
+
+// gate_up expand + base add + SiLU-mul:
+// ACT[p][i] = SiLU(G[p][i] + Z[p].Bt[i]) * (G[p][I+i] + Z[p].Bt[I+i]).
+hipError_t launch_expand_gate_up(int dtype, int rank, const TilePlan& plan, const float* Z,
+                                 const void* Bt, int E, int L, const float* G, void* ACT,
+                                 int64_t I, const int4* ltiles, const int32_t* counts,
+                                 hipStream_t stream);
+
+// down expand added in place: D[p][n] += Z[p].Bt[n].
+hipError_t launch_expand_down(int dtype, int rank, const TilePlan& plan, const float* Z,
+                              const void* Bt, int E, int L, float* D, int64_t h,
+                              const int4* ltiles, const int32_t* counts, hipStream_t stream);
+
+// out[t][n] = sum_{j<k} w[t][j] * D[pos[t*k+j]][n], in j order.
+hipError_t launch_combine(int dtype, const float* D, const int32_t* pos, const float* w, int T,
+                          int k, int64_t h, void* out, hipStream_t stream);
+
+}  // namespace moelora

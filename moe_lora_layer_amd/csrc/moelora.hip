@@ -1,0 +1,244 @@
+// C ABI of the fused MoE multi-LoRA layer: argument checks, workspace layout,
+// tile planning and the launch sequence.  Declarations and the meaning of
+// every argument are in include/moelora.h.
+#include <stdint.h>
+
+#include "launch.h"
+#include "moelora.h"
+
+using moelora::TilePlan;
+
+namespace {
+
+constexpr size_t kSectionAlign = 256;
+constexpr int64_t kMaxGrid = (1ll << 31) - 1;
+
+size_t round_up(size_t x) { return (x + kSectionAlign - 1) / kSectionAlign * kSectionAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(const moelora_dims* d) {
+  if (d == nullptr) return MOELORA_ERR_NULL;
+  if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
+  if (d->rank != 16 && d->rank != 32 && d->rank != 64) return MOELORA_ERR_UNSUPPORTED;
+  if (d->tokens < 0 || d->hidden <= 0 || d->intermediate <= 0) return MOELORA_ERR_DIMS;
+  if (d->hidden % 64 != 0 || d->intermediate % 64 != 0) return MOELORA_ERR_DIMS;
+  if (d->hidden > (1 << 20) || d->intermediate > (1 << 20)) return MOELORA_ERR_DIMS;
+  if (d->experts < 1 || d->adapters < 1 || d->top_k < 1 || d->top_k > 8 ||
+      d->top_k > d->experts)
+    return MOELORA_ERR_DIMS;
+  if (static_cast<int64_t>(d->experts) * d->adapters > 8192) return MOELORA_ERR_DIMS;
+  if (d->tokens * d->top_k >= (1ll << 31)) return MOELORA_ERR_DIMS;
+  return MOELORA_OK;
+}
+
+TilePlan make_plan(const moelora_dims* d) {
+  const int64_t S = d->tokens * d->top_k;
+  const int64_t E = d->experts, nb = E * d->adapters;
+  const int64_t avg = (S + E - 1) / E;  // mean rows per expert
+  TilePlan p;
+  p.bm = avg <= 24 ? 32 : (avg <= 48 ? 64 : 128);
+  p.bml = 64;
+  p.max_mt = static_cast<int>(S / p.bm + (E < S ? E : S) + 1);
+  p.max_lt = static_cast<int>(S / p.bml + (nb < S ? nb : S) + 1);
+  return p;
+}
+
+struct ForwardLayout {
+  size_t pos, counts, mtiles, ltiles, g, z1, z2, act, d, total;
+};
+
+ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
+  const size_t S = static_cast<size_t>(d->tokens * d->top_k);
+  const size_t h = static_cast<size_t>(d->hidden), I = static_cast<size_t>(d->intermediate);
+  const size_t r = static_cast<size_t>(d->rank);
+  const size_t esz = d->dtype == MOELORA_BF16 ? 2 : 4;
+  ForwardLayout L;
+  size_t off = 0;
+  L.pos = off;    off += round_up(S * 4);
+  L.counts = off; off += round_up(4 * 4);
+  L.mtiles = off; off += round_up(static_cast<size_t>(plan.max_mt) * 16);
+  L.ltiles = off; off += round_up(static_cast<size_t>(plan.max_lt) * 16);
+  L.g = off;      off += round_up(S * 2 * I * 4);
+  L.z1 = off;     // Z1 and Z2 are adjacent so one fill clears both
+  L.z2 = off + S * r * 4;
+  off += round_up(2 * S * r * 4);
+  L.act = off;    off += round_up(S * I * esz);
+  L.d = off;      off += round_up(S * h * 4);
+  L.total = off;
+  return L;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOELORA_OK : MOELORA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moelora_abi_version(void) { return MOELORA_ABI_VERSION; }
+
+const char* moelora_status_string(int status) {
+  switch (status) {
+    case MOELORA_OK: return "moelora: ok";
+    case MOELORA_ERR_NULL: return "moelora: a required pointer is NULL";
+    case MOELORA_ERR_DIMS: return "moelora: dimensions out of range";
+    case MOELORA_ERR_UNSUPPORTED: return "moelora: unsupported dtype or rank";
+    case MOELORA_ERR_ALIGNMENT: return "moelora: a tensor pointer is not 16-byte aligned";
+    case MOELORA_ERR_WORKSPACE: return "moelora: workspace missing or too small";
+    case MOELORA_ERR_HIP: return "moelora: HIP launch error";
+    default: return "moelora: unknown status";
+  }
+}
+
+int moelora_align_workspace_size(const moelora_dims* dims, size_t* bytes) {
+  const int rc = check_dims(dims);
+  if (rc != MOELORA_OK) return rc;
+  if (bytes == nullptr) return MOELORA_ERR_NULL;
+  const size_t S = static_cast<size_t>(dims->tokens * dims->top_k);
+  *bytes = 2 * round_up(S * 4);
+  return MOELORA_OK;
+}
+
+int moelora_align(const moelora_dims* dims, const float* router_logits,
+                  const int32_t* adapter_ids, int32_t* topk_ids, float* topk_weights,
+                  int32_t* sorted_slots, int32_t* bucket_offsets, int32_t* device_status,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != MOELORA_OK) return rc;
+  if (bucket_offsets == nullptr) return MOELORA_ERR_NULL;
+  const int64_t T = dims->tokens;
+  if (T > 0 && (router_logits == nullptr || adapter_ids == nullptr || topk_ids == nullptr ||
+                topk_weights == nullptr || sorted_slots == nullptr))
+    return MOELORA_ERR_NULL;
+  size_t need = 0;
+  moelora_align_workspace_size(dims, &need);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MOELORA_ERR_WORKSPACE;
+  const void* ptrs[] = {router_logits, adapter_ids, topk_ids, topk_weights, sorted_slots,
+                        bucket_offsets, workspace};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return MOELORA_ERR_ALIGNMENT;
+  const size_t S = static_cast<size_t>(T * dims->top_k);
+  int32_t* ws_key = static_cast<int32_t*>(workspace);
+  int32_t* ws_rank = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + round_up(S * 4));
+  return hip_status(moelora::launch_align(router_logits, adapter_ids, static_cast<int>(T),
+                                          dims->experts, dims->top_k, dims->adapters, topk_ids,
+                                          topk_weights, sorted_slots, bucket_offsets,
+                                          device_status, ws_key, ws_rank,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int moelora_forward_workspace_size(const moelora_dims* dims, size_t* bytes) {
+  const int rc = check_dims(dims);
+  if (rc != MOELORA_OK) return rc;
+  if (bytes == nullptr) return MOELORA_ERR_NULL;
+  *bytes = dims->tokens == 0 ? 0 : forward_layout(dims, make_plan(dims)).total;
+  return MOELORA_OK;
+}
+
+int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]) {
+  const int rc = check_dims(dims);
+  if (rc != MOELORA_OK) return rc;
+  if (offsets == nullptr) return MOELORA_ERR_NULL;
+  const ForwardLayout L = forward_layout(dims, make_plan(dims));
+  offsets[0] = L.g;
+  offsets[1] = L.z1;
+  offsets[2] = L.act;
+  offsets[3] = L.z2;
+  offsets[4] = L.d;
+  return MOELORA_OK;
+}
+
+int moelora_forward(const moelora_dims* dims, const void* x, const void* w_gate_up,
+                    const void* w_down, const void* a_gate_up, const void* b_gate_up,
+                    const void* a_down, const void* b_down, const float* topk_weights,
+                    const int32_t* sorted_slots, const int32_t* bucket_offsets, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return moelora_forward_profiled(dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down,
+                                  b_down, topk_weights, sorted_slots, bucket_offsets, out,
+                                  workspace, workspace_bytes, stream, nullptr);
+}
+
+int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void* w_gate_up,
+                             const void* w_down, const void* a_gate_up, const void* b_gate_up,
+                             const void* a_down, const void* b_down, const float* topk_weights,
+                             const int32_t* sorted_slots, const int32_t* bucket_offsets,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* stage_events) {
+  int rc = check_dims(dims);
+  if (rc != MOELORA_OK) return rc;
+  const int64_t T = dims->tokens;
+  if (T == 0) return MOELORA_OK;
+  const void* ptrs[] = {x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
+                        topk_weights, sorted_slots, bucket_offsets, out};
+  for (const void* p : ptrs)
+    if (p == nullptr) return MOELORA_ERR_NULL;
+  const TilePlan plan = make_plan(dims);
+  const ForwardLayout L = forward_layout(dims, plan);
+  if (workspace == nullptr || workspace_bytes < L.total) return MOELORA_ERR_WORKSPACE;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOELORA_ERR_ALIGNMENT;
+  if (!aligned16(workspace)) return MOELORA_ERR_ALIGNMENT;
+
+  const int k = dims->top_k, E = dims->experts, Lad = dims->adapters, r = dims->rank;
+  const int dt = dims->dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
+  const int64_t h = dims->hidden, I = dims->intermediate;
+  const int S = static_cast<int>(T * k);
+  // grid sizes must fit the launch limits
+  const int64_t ntiles_max = (2 * I + 127) / 128;
+  if (static_cast<int64_t>(plan.max_mt) * ntiles_max > kMaxGrid ||
+      static_cast<int64_t>(plan.max_lt) * 2048 > kMaxGrid)
+    return MOELORA_ERR_DIMS;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int4* mtiles = reinterpret_cast<int4*>(ws + L.mtiles);
+  int4* ltiles = reinterpret_cast<int4*>(ws + L.ltiles);
+  float* G = reinterpret_cast<float*>(ws + L.g);
+  float* Z1 = reinterpret_cast<float*>(ws + L.z1);
+  float* Z2 = reinterpret_cast<float*>(ws + L.z2);
+  void* ACT = ws + L.act;
+  float* D = reinterpret_cast<float*>(ws + L.d);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // event i is recorded right before stage i, the last one after the last stage
+  auto mark = [&](int i) -> hipError_t {
+    if (stage_events == nullptr) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st);
+  };
+  hipError_t e = mark(MOELORA_STAGE_PREP);
+  if (e == hipSuccess)
+    e = moelora::launch_prep(sorted_slots, bucket_offsets, S, E, Lad, plan, pos, mtiles, ltiles,
+                             counts, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_ZERO);
+  if (e == hipSuccess) e = moelora::launch_zero(Z1, 2ll * S * r, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);
+  if (e == hipSuccess)
+    e = moelora::launch_gemm(dt, plan, x, static_cast<int>(T), sorted_slots, k, w_gate_up, 2 * I,
+                             h, G, mtiles, counts, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_GATE_UP);
+  if (e == hipSuccess)
+    e = moelora::launch_shrink(dt, r, plan, x, static_cast<int>(T), sorted_slots, k, a_gate_up, E,
+                               Lad, h, Z1, ltiles, counts, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_EXPAND_GATE_UP);
+  if (e == hipSuccess)
+    e = moelora::launch_expand_gate_up(dt, r, plan, Z1, b_gate_up, E, Lad, G, ACT, I, ltiles,
+                                       counts, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
+  if (e == hipSuccess)
+    e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, mtiles, counts, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_DOWN);
+  if (e == hipSuccess)
+    e = moelora::launch_shrink(dt, r, plan, ACT, S, nullptr, 1, a_down, E, Lad, I, Z2, ltiles,
+                               counts, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_EXPAND_DOWN);
+  if (e == hipSuccess)
+    e = moelora::launch_expand_down(dt, r, plan, Z2, b_down, E, Lad, D, h, ltiles, counts, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_COMBINE);
+  if (e == hipSuccess)
+    e = moelora::launch_combine(dt, D, pos, topk_weights, static_cast<int>(T), k, h, out, st);
+  if (e == hipSuccess) e = mark(MOELORA_NUM_STAGES);
+  return hip_status(e);
+}
+
+}  // extern "C"

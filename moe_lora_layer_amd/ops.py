@@ -1,0 +1,230 @@
+"""Python binding of libmoelora.so: the C ABI of include/moelora.h via ctypes.
+
+Argument marshalling only.  Every step of the layer runs in the library's HIP
+kernels; torch supplies device memory and the current stream.  There is no
+fallback: if the library is missing, every call raises.
+
+torch must be imported before the library is loaded, so that the library
+binds to the HIP runtime torch already uses (one runtime per process).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoelora.so")
+
+MOELORA_F32, MOELORA_BF16 = 0, 1
+STAGES = ["prep", "zero", "gemm_gate_up", "shrink_gate_up", "expand_gate_up", "gemm_down",
+          "shrink_down", "expand_down", "combine"]
+_TORCH_DT = {MOELORA_F32: torch.float32, MOELORA_BF16: torch.bfloat16}
+_DT_NAME = {"f32": MOELORA_F32, "bf16": MOELORA_BF16}
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("intermediate", ctypes.c_int64), ("experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("adapters", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    def __repr__(self):
+        return ("Dims(T=%d, h=%d, I=%d, E=%d, k=%d, L=%d, r=%d, dtype=%d)" %
+                (self.tokens, self.hidden, self.intermediate, self.experts, self.top_k,
+                 self.adapters, self.rank, self.dtype))
+
+
+_lib = None
+
+
+def library():
+    """The loaded libmoelora.so (raises RuntimeError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m moe_lora_layer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        pd = ctypes.POINTER(Dims)
+        L.moelora_abi_version.restype = ctypes.c_int
+        L.moelora_status_string.argtypes = [ctypes.c_int]
+        L.moelora_status_string.restype = ctypes.c_char_p
+        L.moelora_align_workspace_size.argtypes = [pd, ctypes.POINTER(sz)]
+        L.moelora_forward_workspace_size.argtypes = [pd, ctypes.POINTER(sz)]
+        L.moelora_forward_workspace_layout.argtypes = [pd, ctypes.POINTER(sz)]
+        L.moelora_align.argtypes = [pd] + [vp] * 8 + [sz, vp]
+        L.moelora_forward.argtypes = [pd] + [vp] * 12 + [sz, vp]
+        L.moelora_forward_profiled.argtypes = [pd] + [vp] * 12 + [sz, vp, vp]
+        for f in (L.moelora_align_workspace_size, L.moelora_forward_workspace_size,
+                  L.moelora_forward_workspace_layout, L.moelora_align, L.moelora_forward,
+                  L.moelora_forward_profiled):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(rc: int) -> str:
+    return library().moelora_status_string(rc).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError(f"{what}: {status_string(rc)} (status {rc})")
+
+
+def make_dims(tokens, hidden, intermediate, experts, top_k, adapters, rank, dtype) -> Dims:
+    if isinstance(dtype, str):
+        dtype = _DT_NAME[dtype]
+    elif isinstance(dtype, torch.dtype):
+        dtype = MOELORA_BF16 if dtype == torch.bfloat16 else MOELORA_F32
+    return Dims(int(tokens), int(hidden), int(intermediate), int(experts), int(top_k),
+                int(adapters), int(rank), int(dtype))
+
+
+def dims_for(cfg, tokens=None) -> Dims:
+    """Dims of a workload config (moe_lora_layer_amd.synth.LayerConfig)."""
+    return make_dims(cfg.tokens if tokens is None else tokens, cfg.hidden, cfg.intermediate,
+                     cfg.experts, cfg.top_k, cfg.adapters, cfg.rank, cfg.dtype)
+
+
+def align_workspace_size(d: Dims) -> int:
+    n = ctypes.c_size_t()
+    _check(library().moelora_align_workspace_size(ctypes.byref(d), ctypes.byref(n)),
+           "moelora_align_workspace_size")
+    return n.value
+
+
+def forward_workspace_size(d: Dims) -> int:
+    n = ctypes.c_size_t()
+    _check(library().moelora_forward_workspace_size(ctypes.byref(d), ctypes.byref(n)),
+           "moelora_forward_workspace_size")
+    return n.value
+
+
+def forward_workspace_layout(d: Dims) -> dict:
+    offs = (ctypes.c_size_t * 5)()
+    _check(library().moelora_forward_workspace_layout(ctypes.byref(d), offs),
+           "moelora_forward_workspace_layout")
+    return dict(zip(["G", "Z1", "ACT", "Z2", "D"], list(offs)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A device byte buffer usable as a workspace (at least 256 bytes)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def align(d: Dims, logits: torch.Tensor, adapter_ids: torch.Tensor, *, out=None,
+          workspace_buf=None, status=None, stream=None):
+    """moelora_align.  Returns (topk_ids, topk_weights, sorted_slots, bucket_offsets, status)."""
+    dev = logits.device
+    T, E, k, L = d.tokens, d.experts, d.top_k, d.adapters
+    _expect(logits, "logits", (T, E), torch.float32, dev)
+    _expect(adapter_ids, "adapter_ids", (T,), torch.int32, dev)
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T * k,), dtype=torch.int32, device=dev),
+               torch.empty((E * L + 1,), dtype=torch.int32, device=dev))
+    topk_ids, topk_w, sorted_slots, offsets = out
+    if status is None:
+        status = torch.zeros((4,), dtype=torch.int32, device=dev)
+    if workspace_buf is None:
+        workspace_buf = workspace(align_workspace_size(d), dev)
+    _check(library().moelora_align(ctypes.byref(d), _ptr(logits), _ptr(adapter_ids), _ptr(topk_ids),
+                                   _ptr(topk_w), _ptr(sorted_slots), _ptr(offsets), _ptr(status),
+                                   _ptr(workspace_buf), workspace_buf.numel(), _stream(stream)),
+           "moelora_align")
+    return topk_ids, topk_w, sorted_slots, offsets, status
+
+
+def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down, topk_weights,
+            sorted_slots, bucket_offsets, *, out=None, workspace_buf=None, stream=None,
+            stage_events=None):
+    """moelora_forward (moelora_forward_profiled when stage_events, a list of
+    len(STAGES) + 1 recorded-once torch.cuda.Event(enable_timing=True), is given).
+    Returns out [T][h]."""
+    dev = x.device
+    T, h, I, E, k, L, r = d.tokens, d.hidden, d.intermediate, d.experts, d.top_k, d.adapters, d.rank
+    dt = _TORCH_DT[d.dtype]
+    _expect(x, "x", (T, h), dt, dev)
+    _expect(w_gate_up, "w_gate_up", (E, 2 * I, h), dt, dev)
+    _expect(w_down, "w_down", (E, h, I), dt, dev)
+    _expect(a_gate_up, "a_gate_up", (L, E, r, h), dt, dev)
+    _expect(b_gate_up, "b_gate_up", (L, E, 2 * I, r), dt, dev)
+    _expect(a_down, "a_down", (L, E, r, I), dt, dev)
+    _expect(b_down, "b_down", (L, E, h, r), dt, dev)
+    _expect(topk_weights, "topk_weights", (T, k), torch.float32, dev)
+    _expect(sorted_slots, "sorted_slots", (T * k,), torch.int32, dev)
+    _expect(bucket_offsets, "bucket_offsets", (E * L + 1,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((T, h), dtype=dt, device=dev)
+    _expect(out, "out", (T, h), dt, dev)
+    if workspace_buf is None:
+        workspace_buf = workspace(forward_workspace_size(d), dev)
+    args = [ctypes.byref(d), _ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(a_gate_up),
+            _ptr(b_gate_up), _ptr(a_down), _ptr(b_down), _ptr(topk_weights), _ptr(sorted_slots),
+            _ptr(bucket_offsets), _ptr(out), _ptr(workspace_buf), workspace_buf.numel(),
+            _stream(stream)]
+    if stage_events is None:
+        _check(library().moelora_forward(*args), "moelora_forward")
+    else:
+        if len(stage_events) != len(STAGES) + 1:
+            raise ValueError(f"need {len(STAGES) + 1} events")
+        handles = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
+        if any(not h for h in handles):
+            raise ValueError("record every event once before passing it (creates the handle)")
+        _check(library().moelora_forward_profiled(*args, handles), "moelora_forward_profiled")
+    return out
+
+
+class MoELoRALayer:
+    """One layer's weights plus preallocated outputs and workspaces for a fixed
+    token count; ``__call__`` runs moelora_align then moelora_forward with no
+    allocation."""
+
+    def __init__(self, d: Dims, weights: dict, device):
+        self.d = d
+        self.w = weights
+        T, E, k, L, h = d.tokens, d.experts, d.top_k, d.adapters, d.hidden
+        dt = _TORCH_DT[d.dtype]
+        self.routing = (torch.empty((T, k), dtype=torch.int32, device=device),
+                        torch.empty((T, k), dtype=torch.float32, device=device),
+                        torch.empty((T * k,), dtype=torch.int32, device=device),
+                        torch.empty((E * L + 1,), dtype=torch.int32, device=device))
+        self.status = torch.zeros((4,), dtype=torch.int32, device=device)
+        self.ws_align = workspace(align_workspace_size(d), device)
+        self.ws_fwd = workspace(forward_workspace_size(d), device)
+        self.out = torch.empty((T, h), dtype=dt, device=device)
+
+    def __call__(self, x, logits, adapter_ids, stream=None):
+        ids, w, ss, off, _ = align(self.d, logits, adapter_ids, out=self.routing,
+                                   workspace_buf=self.ws_align, status=self.status, stream=stream)
+        W = self.w
+        return forward(self.d, x, W["w_gate_up"], W["w_down"], W["a_gate_up"], W["b_gate_up"],
+                       W["a_down"], W["b_down"], w, ss, off, out=self.out,
+                       workspace_buf=self.ws_fwd, stream=stream)

@@ -1,0 +1,127 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/moelora.h declares, and rejects bad arguments before any HIP call.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (binds the library to torch's HIP runtime)
+
+from moe_lora_layer_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moelora.h")
+
+OK, ERR_NULL, ERR_DIMS, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_HIP = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moelora_\w+)\s*\(", text)))
+
+
+def good_dims(**kw):
+    base = dict(tokens=64, hidden=256, intermediate=512, experts=8, top_k=2, adapters=4, rank=16,
+                dtype="bf16")
+    base.update(kw)
+    return ops.make_dims(**base)
+
+
+def test_library_exports_every_declared_function():
+    lib = ops.library()
+    names = declared_functions()
+    assert {"moelora_align", "moelora_forward"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.moelora_abi_version() == 1
+
+
+def test_status_strings():
+    for rc in range(7):
+        s = ops.status_string(rc)
+        assert s.startswith("moelora:")
+    assert "unknown" in ops.status_string(99)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(dtype=7), ERR_UNSUPPORTED), (dict(rank=8), ERR_UNSUPPORTED), (dict(rank=128), ERR_UNSUPPORTED),
+    (dict(hidden=100), ERR_DIMS), (dict(intermediate=96), ERR_DIMS), (dict(tokens=-1), ERR_DIMS),
+    (dict(top_k=9, experts=16), ERR_DIMS), (dict(top_k=3, experts=2), ERR_DIMS), (dict(experts=0), ERR_DIMS),
+    (dict(adapters=0), ERR_DIMS), (dict(experts=128, adapters=65), ERR_DIMS),
+    (dict(tokens=1 << 30, top_k=2), ERR_DIMS),
+])
+def test_dims_validation(kw, rc):
+    d = good_dims(**kw)
+    n = ctypes.c_size_t()
+    lib = ops.library()
+    assert lib.moelora_forward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == rc
+    assert lib.moelora_align_workspace_size(ctypes.byref(d), ctypes.byref(n)) == rc
+
+
+def test_null_dims_and_outputs():
+    lib = ops.library()
+    n = ctypes.c_size_t()
+    assert lib.moelora_forward_workspace_size(None, ctypes.byref(n)) == ERR_NULL
+    assert lib.moelora_forward_workspace_size(ctypes.byref(good_dims()), None) == ERR_NULL
+    assert lib.moelora_forward_workspace_layout(ctypes.byref(good_dims()), None) == ERR_NULL
+
+
+def test_workspace_sizes_and_layout():
+    d = good_dims(tokens=100, hidden=320, intermediate=192, experts=5, top_k=2, adapters=3, rank=32)
+    size = ops.forward_workspace_size(d)
+    lay = ops.forward_workspace_layout(d)
+    S, I, h, r = 200, 192, 320, 32
+    order = ["G", "Z1", "Z2", "ACT", "D"]
+    offs = [lay["G"], lay["Z1"], lay["Z2"], lay["ACT"], lay["D"]]
+    assert all(o % 16 == 0 for o in offs)
+    assert lay["Z2"] == lay["Z1"] + S * r * 4
+    assert lay["G"] + S * 2 * I * 4 <= lay["Z1"]
+    assert lay["Z2"] + S * r * 4 <= lay["ACT"]
+    assert lay["ACT"] + S * I * 2 <= lay["D"]
+    assert lay["D"] + S * h * 4 <= size, order
+    assert ops.align_workspace_size(d) >= 2 * S * 4
+    assert ops.forward_workspace_size(good_dims(tokens=0)) == 0
+
+
+def _vp(v):
+    return ctypes.c_void_p(v)
+
+
+def test_align_argument_errors():
+    lib = ops.library()
+    d = good_dims()
+    fake = 1 << 20
+    ws = ops.align_workspace_size(d)
+    args = [_vp(fake)] * 7
+    # NULL output
+    a = list(args); a[4] = None
+    assert lib.moelora_align(ctypes.byref(d), *a[:6], None, _vp(fake), ws, None) == ERR_NULL
+    # workspace too small / missing
+    assert lib.moelora_align(ctypes.byref(d), *args[:6], None, _vp(fake), ws - 1, None) == ERR_WORKSPACE
+    assert lib.moelora_align(ctypes.byref(d), *args[:6], None, None, ws, None) == ERR_WORKSPACE
+    # misaligned pointer
+    a = list(args); a[1] = _vp(fake + 4)
+    assert lib.moelora_align(ctypes.byref(d), *a[:6], None, _vp(fake), ws, None) == ERR_ALIGNMENT
+    # bad dims first
+    bad = good_dims(rank=3)
+    assert lib.moelora_align(ctypes.byref(bad), *args[:6], None, _vp(fake), ws, None) == ERR_UNSUPPORTED
+
+
+def test_forward_argument_errors():
+    lib = ops.library()
+    d = good_dims()
+    fake = 1 << 20
+    ws = ops.forward_workspace_size(d)
+    ptrs = [_vp(fake)] * 11
+    p = list(ptrs); p[3] = None
+    assert lib.moelora_forward(ctypes.byref(d), *p, _vp(fake), ws, None) == ERR_NULL
+    assert lib.moelora_forward(ctypes.byref(d), *ptrs, _vp(fake), ws - 1, None) == ERR_WORKSPACE
+    assert lib.moelora_forward(ctypes.byref(d), *ptrs, None, ws, None) == ERR_WORKSPACE
+    p = list(ptrs); p[0] = _vp(fake + 2)
+    assert lib.moelora_forward(ctypes.byref(d), *p, _vp(fake), ws, None) == ERR_ALIGNMENT
+    assert lib.moelora_forward(ctypes.byref(d), *ptrs, _vp(fake + 8), ws, None) == ERR_ALIGNMENT
+    # T == 0 is a no-op that touches nothing
+    z = good_dims(tokens=0)
+    assert lib.moelora_forward(ctypes.byref(z), *([None] * 11), None, 0, None) == OK

@@ -1,0 +1,89 @@
+"""moelora_align on the GPU against the oracle: routing ids, the bucketed
+permutation and the bucket offsets must be bit-exact; routing weights within
+1e-6.  Runs through the C ABI (ops.align is ctypes marshalling only)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import device, run_align, say
+from moe_lora_layer_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(cfg, rinp, repeats=1):
+    dev = device()
+    logits = torch.from_numpy(rinp["logits"]).to(dev)
+    ad = torch.from_numpy(rinp["adapter_ids"]).to(dev)
+    ref_ids, ref_w = oracle.route(rinp["logits"], cfg.top_k)
+    ref_ss, ref_off = oracle.align(ref_ids, rinp["adapter_ids"], cfg.experts, cfg.adapters)
+    first = None
+    for rep in range(repeats):
+        ids, w, ss, off, st = run_align(cfg, {"logits": logits, "adapter_ids": ad})
+        got = (ids.cpu().numpy(), w.cpu().numpy(), ss.cpu().numpy(), off.cpu().numpy())
+        assert int(st[0].item()) == 0
+        assert np.array_equal(got[0], ref_ids), "topk ids"
+        assert np.array_equal(got[2], ref_ss), "sorted slots"
+        assert np.array_equal(got[3], ref_off), "bucket offsets"
+        assert np.max(np.abs(got[1].astype(np.float64) - ref_w)) <= 1e-6 if got[1].size else True
+        if first is None:
+            first = got
+        else:
+            for a, b in zip(first, got):
+                assert np.array_equal(a, b), "align is not deterministic"
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_align_workloads(name):
+    cfg = synth.WORKLOADS[name]
+    say(f"align {name}: T={cfg.tokens} E={cfg.experts} k={cfg.top_k} L={cfg.adapters}")
+    _check(cfg, synth.make_routing_inputs(cfg), repeats=3)
+
+
+def _cfg(T, E, k, L, seed=1, **kw):
+    return synth.LayerConfig("edge", T, 64, 64, E, k, L, 16, "bf16", requests=T if T else 1,
+                             seed=seed, **kw)
+
+
+@pytest.mark.parametrize("T,E,k,L", [(1, 8, 2, 4), (1, 1, 1, 1), (3, 4, 4, 2), (1000, 32, 8, 16),
+                                     (5000, 16, 2, 8), (257, 256, 8, 32), (70, 8192, 1, 1),
+                                     (4096, 64, 6, 128), (20000, 2, 2, 3)])
+def test_align_shapes(T, E, k, L):
+    cfg = _cfg(T, E, k, L)
+    say(f"align shape T={T} E={E} k={k} L={L}")
+    _check(cfg, synth.make_routing_inputs(cfg), repeats=2)
+
+
+def test_align_degenerate_routing():
+    # every token on the same experts and adapter; ties everywhere; empty experts
+    T, E, k, L = 700, 16, 3, 4
+    cfg = _cfg(T, E, k, L)
+    r = {"logits": np.zeros((T, E), np.float32), "adapter_ids": np.full(T, 2, np.int32)}
+    _check(cfg, r, repeats=3)
+    r = {"logits": np.tile(np.arange(E, dtype=np.float32)[::-1] // 4, (T, 1)).astype(np.float32),
+         "adapter_ids": (np.arange(T) % L).astype(np.int32)}
+    _check(cfg, r, repeats=2)
+
+
+def test_align_empty_tokens():
+    dev = device()
+    d = ops.make_dims(0, 64, 64, 4, 2, 3, 16, "bf16")
+    ids, w, ss, off, st = ops.align(d, torch.empty((0, 4), dtype=torch.float32, device=dev),
+                                    torch.empty((0,), dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert off.cpu().numpy().tolist() == [0] * 13
+    assert int(st[0].item()) == 0
+
+
+def test_align_reports_bad_adapter():
+    cfg = _cfg(50, 8, 2, 4)
+    r = synth.make_routing_inputs(cfg)
+    r["adapter_ids"][7] = 4        # out of range
+    dev = device()
+    _, _, ss, off, st = ops.align(ops.dims_for(cfg), torch.from_numpy(r["logits"]).to(dev),
+                                  torch.from_numpy(r["adapter_ids"]).to(dev))
+    torch.cuda.synchronize()
+    assert int(st[0].item()) == 1
+    # still a permutation of the slots, in bounds
+    assert sorted(ss.cpu().numpy().tolist()) == list(range(100))

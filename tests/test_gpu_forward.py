@@ -1,0 +1,187 @@
+"""moelora_forward on the GPU against the oracle, through the C ABI.
+
+Tolerance: max|gpu - oracle| <= 1e-2 * max|oracle| for bf16 layers and
+1e-4 * max|oracle| for fp32 layers, over every compared output.  Small shapes
+(several tiles and ragged tails in M, N and K) are compared in full; the five
+workloads at full size are compared on sampled tokens, in the same launch
+configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (WEIGHTS, assert_close, device, device_inputs, run_align, run_forward, say,
+                      sample_tokens, to_f64, workspace_view)
+from moe_lora_layer_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(cfg, inp):
+    dev = device()
+    dinp = device_inputs(inp, cfg, dev)
+    ids, w, ss, off, st = run_align(cfg, dinp)
+    assert int(st[0].item()) == 0
+    out, ws = run_forward(cfg, dinp, w, ss, off)
+    return dinp, (ids, w, ss, off), out, ws
+
+
+def _small(T, h, I, E, k, L, r, dtype, seed, requests=None, **kw):
+    return synth.LayerConfig("small", T, h, I, E, k, L, r, dtype,
+                             requests=requests if requests is not None else T, seed=seed, **kw)
+
+
+SMALL = [
+    # (T, h, I, E, k, L, r, dtype): rows/expert 16 (BM 32), 38 (BM 64), 67 (BM 128);
+    # N tails (2I, h not multiples of 128), K of 64..640, ranks 16/32/64
+    (64, 256, 512, 8, 2, 4, 16, "f32"),
+    (96, 192, 320, 5, 2, 3, 32, "f32"),
+    (200, 320, 192, 6, 2, 3, 64, "f32"),
+    (64, 256, 512, 8, 2, 4, 16, "bf16"),
+    (96, 192, 320, 5, 2, 3, 32, "bf16"),
+    (200, 320, 192, 6, 2, 3, 64, "bf16"),
+    (300, 640, 448, 4, 1, 7, 32, "bf16"),
+    (33, 128, 64, 3, 3, 2, 16, "bf16"),
+    (1, 64, 64, 4, 2, 2, 64, "bf16"),
+    (7, 64, 128, 1, 1, 3, 16, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
+def test_forward_small(shape):
+    cfg = _small(*shape, seed=sum(shape[:7]))
+    say(f"forward small {shape}")
+    inp = synth.make_inputs(cfg)
+    _, (ids, w, ss, off), out, _ = _layer(cfg, inp)
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
+    assert_close(to_f64(out), ref, cfg.dtype, "out")
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_forward_workload(name):
+    cfg = synth.WORKLOADS[name]
+    say(f"forward workload {name}: generating inputs")
+    inp = synth.make_inputs(cfg)
+    say(f"forward workload {name}: running on GPU")
+    _, (ids, w, ss, off), out, _ = _layer(cfg, inp)
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    toks = sample_tokens(cfg.tokens, 24 if cfg.tokens > 64 else cfg.tokens)
+    say(f"forward workload {name}: oracle on {len(toks)} tokens")
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w, tokens=toks)
+    assert_close(to_f64(out)[toks], ref, cfg.dtype, f"{name} out")
+
+
+def test_forward_intermediates():
+    """Layer-by-layer reconciliation: G, Z1, ACT, Z2, D read from the workspace
+    against the oracle's per-slot intermediates."""
+    cfg = _small(96, 192, 320, 5, 2, 3, 32, "f32", seed=5)
+    inp = synth.make_inputs(cfg)
+    _, (ids, w, ss, off), out, ws = _layer(cfg, inp)
+    d = ops.dims_for(cfg)
+    lay = ops.forward_workspace_layout(d)
+    S, I, h, r = cfg.slots, cfg.intermediate, cfg.hidden, cfg.rank
+    G = to_f64(workspace_view(ws, lay["G"], (S, 2 * I), torch.float32))
+    Z1 = to_f64(workspace_view(ws, lay["Z1"], (S, r), torch.float32))
+    ACT = to_f64(workspace_view(ws, lay["ACT"], (S, I), torch.float32))
+    Z2 = to_f64(workspace_view(ws, lay["Z2"], (S, r), torch.float32))
+    D = to_f64(workspace_view(ws, lay["D"], (S, h), torch.float32))
+    ss = ss.cpu().numpy()
+    ids = ids.cpu().numpy()
+    dims = oracle.dims_of(cfg)
+    base_inp = dict(inp, b_gate_up=np.zeros_like(inp["b_gate_up"]))
+    for p in sample_tokens(S, 20, seed=3):
+        s = int(ss[p])
+        t, j = divmod(s, cfg.top_k)
+        e, l = int(ids[t, j]), int(inp["adapter_ids"][t])
+        ref = oracle.slot(inp, dims, t, e, l)
+        base = oracle.slot(base_inp, dims, t, e, l)["g"]   # xW alone
+        assert_close(G[p], base, "f32", f"G p={p}")
+        assert_close(Z1[p], ref["z1"], "f32", f"Z1 p={p}")
+        assert_close(ACT[p], ref["a"], "f32", f"ACT p={p}")
+        assert_close(Z2[p], ref["z2"], "f32", f"Z2 p={p}")
+        assert_close(D[p], ref["d"], "f32", f"D p={p}")
+
+
+def test_integer_exact_gate_up():
+    """x, W, A, B in {-2..2} (exact in bf16); every partial sum of xW and xA stays
+    below 2^24, so the GPU's G = xW and Z1 = xA are exact in fp32 whatever the
+    summation order (split-K atomics included) and must equal the oracle's bit
+    for bit."""
+    cfg = _small(128, 4096, 256, 4, 2, 3, 32, "bf16", seed=9)
+    rng = np.random.default_rng(11)
+    inp = synth.make_inputs(cfg)
+    for n in ["x"] + WEIGHTS:
+        inp[n] = synth.from_float(rng.integers(-2, 3, inp[n].shape).astype(np.float32), "bf16")
+    _, (ids, w, ss, off), out, ws = _layer(cfg, inp)
+    lay = ops.forward_workspace_layout(ops.dims_for(cfg))
+    S, I, r = cfg.slots, cfg.intermediate, cfg.rank
+    G = to_f64(workspace_view(ws, lay["G"], (S, 2 * I), torch.float32))
+    Z1 = to_f64(workspace_view(ws, lay["Z1"], (S, r), torch.float32))
+    ss, ids = ss.cpu().numpy(), ids.cpu().numpy()
+    dims = oracle.dims_of(cfg)
+    base_inp = dict(inp, b_gate_up=np.zeros_like(inp["b_gate_up"]))
+    for p in range(0, S, 7):
+        t, j = divmod(int(ss[p]), cfg.top_k)
+        e, l = int(ids[t, j]), int(inp["adapter_ids"][t])
+        ref = oracle.slot(base_inp, dims, t, e, l)
+        assert np.array_equal(G[p], ref["g"]), p
+        assert np.array_equal(Z1[p], ref["z1"]), p
+
+
+def test_zero_lora_matches_between_a_and_b():
+    """A = 0 and B = 0 both make the LoRA term exactly zero: the two GPU runs
+    must agree bit for bit, and match the oracle's base MoE."""
+    cfg = _small(200, 320, 192, 6, 2, 3, 64, "bf16", seed=13)
+    inp = synth.make_inputs(cfg)
+    zb = dict(inp, b_gate_up=np.zeros_like(inp["b_gate_up"]), b_down=np.zeros_like(inp["b_down"]))
+    za = dict(inp, a_gate_up=np.zeros_like(inp["a_gate_up"]), a_down=np.zeros_like(inp["a_down"]))
+    _, _, out_b, _ = _layer(cfg, zb)
+    _, _, out_a, _ = _layer(cfg, za)
+    assert torch.equal(out_a, out_b)
+    ids, w = oracle.route(inp["logits"], cfg.top_k)
+    assert_close(to_f64(out_b), oracle.forward(zb, oracle.dims_of(cfg), ids, w), "bf16", "base")
+
+
+def test_forward_with_oracle_permutation():
+    """Forward fed with the oracle's routing and permutation (isolates align)."""
+    cfg = _small(150, 256, 320, 7, 3, 5, 32, "bf16", seed=17)
+    inp = synth.make_inputs(cfg)
+    dev = device()
+    dinp = device_inputs(inp, cfg, dev)
+    ids, w = oracle.route(inp["logits"], cfg.top_k)
+    ss, off = oracle.align(ids, inp["adapter_ids"], cfg.experts, cfg.adapters)
+    out, _ = run_forward(cfg, dinp, torch.from_numpy(w.astype(np.float32)).to(dev),
+                         torch.from_numpy(ss).to(dev), torch.from_numpy(off).to(dev))
+    assert_close(to_f64(out), oracle.forward(inp, oracle.dims_of(cfg), ids, w), "bf16", "out")
+
+
+def test_canaries_and_second_stream():
+    """Guard bytes around the output and the workspace stay untouched, and a run
+    on a second stream with its own workspace gives the same result."""
+    cfg = _small(96, 192, 320, 5, 2, 3, 32, "bf16", seed=19)
+    inp = synth.make_inputs(cfg)
+    dev = device()
+    dinp = device_inputs(inp, cfg, dev)
+    d = ops.dims_for(cfg)
+    ids, w, ss, off, _ = run_align(cfg, dinp)
+    G = 4096
+    wsz = ops.forward_workspace_size(d)
+    ws_full = torch.full((wsz + 2 * G,), 0xA5, dtype=torch.uint8, device=dev)
+    out_full = torch.full((cfg.tokens * cfg.hidden + 2 * G,), 7.0, dtype=torch.bfloat16, device=dev)
+    ws = ws_full[G:G + wsz]
+    out = out_full[G:G + cfg.tokens * cfg.hidden].view(cfg.tokens, cfg.hidden)
+    ops.forward(d, dinp["x"], *[dinp[n] for n in WEIGHTS], w, ss, off, out=out, workspace_buf=ws)
+    torch.cuda.synchronize()
+    assert torch.all(ws_full[:G] == 0xA5) and torch.all(ws_full[G + wsz:] == 0xA5)
+    assert torch.all(out_full[:G] == 7.0) and torch.all(out_full[G + cfg.tokens * cfg.hidden:] == 7.0)
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        out2 = ops.forward(d, dinp["x"], *[dinp[n] for n in WEIGHTS], w, ss, off)
+    s2.synchronize()
+    ids_ref, w_ref = oracle.route(inp["logits"], cfg.top_k)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ids_ref, w_ref)
+    assert_close(to_f64(out), ref, "bf16", "stream 1")
+    assert_close(to_f64(out2), ref, "bf16", "stream 2")
