@@ -73,6 +73,40 @@ template <> struct Mfma<float> {
   __device__ __forceinline__ static frag_t zero() { return 0.0f; }
 };
 
+// ---------------------------------------------------------------------------
+// MFMA 16x16 tiles (weight-streaming kernels).
+// Lane l = 16*g + c (g in 0..3) supplies A row c and B column c with the
+// k-elements [g*KPACK, (g+1)*KPACK) of the step, and receives D element
+// (row 4*g + i, column c) in acc[i], i in 0..3.
+//   bf16: v_mfma_f32_16x16x32_bf16, KSTEP 32, KPACK 8
+//   f32 : v_mfma_f32_16x16x4_f32,   KSTEP 4,  KPACK 1
+// ---------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Mfma16;
+
+template <> struct Mfma16<bf16_t> {
+  static constexpr int KSTEP = 32;
+  static constexpr int KPACK = 8;
+  typedef bf16x8_t frag_t;
+  __device__ __forceinline__ static void run(f32x4_t& acc, frag_t a, frag_t b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag_t load(const bf16_t* p) { return Mfma<bf16_t>::load(p); }
+  __device__ __forceinline__ static frag_t zero() { return Mfma<bf16_t>::zero(); }
+};
+
+template <> struct Mfma16<float> {
+  static constexpr int KSTEP = 4;
+  static constexpr int KPACK = 1;
+  typedef float frag_t;
+  __device__ __forceinline__ static void run(f32x4_t& acc, frag_t a, frag_t b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag_t load(const float* p) { return *p; }
+  __device__ __forceinline__ static frag_t zero() { return 0.0f; }
+};
+
 // Row (within the 32x32 block) of accumulator element i held by a lane of half h.
 __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 

@@ -105,23 +105,36 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------------- gemm
-template <typename T, int BM, int BN, int WM, int WN>
+// ------------------------------------------------------------------- LDS gemm
+// P = number of K-steps whose global loads are in flight ahead of the MFMAs
+// (register ring of P stages); NT = weights are loaded with the nontemporal
+// hint (each weight element is used by one M-tile only in decode batches).
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const void* p) {
+  if (NT) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false>
 __global__ void __launch_bounds__(WM * WN * kWave)
 k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
        const T* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
        const int4* __restrict__ mtiles, const int32_t* __restrict__ counts, int n_ntiles) {
   typedef Mfma<T> M;
-  constexpr int NT = WM * WN * kWave;
+  constexpr int NT_ = WM * WN * kWave;
   constexpr int ROWB = 128;                    // bytes of K per LDS row
   constexpr int BK = ROWB / sizeof(T);
   constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
-  constexpr int A_CH = BM * 8 / NT;
-  constexpr int B_CH = BN * 8 / NT;
+  constexpr int A_CH = BM * 8 / NT_;
+  constexpr int B_CH = BN * 8 / NT_;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  static_assert(A_CH >= 1 && B_CH >= 1 && BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads");
-  static_assert(FM >= 1 && FN >= 1, "wave tile");
+  static_assert(A_CH >= 1 && B_CH >= 1 && BM * 8 % NT_ == 0 && BN * 8 % NT_ == 0, "tile/threads");
+  static_assert(FM >= 1 && FN >= 1 && P >= 1, "wave tile");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2][(BM + BN) * ROWB];
 
   const int mt = blockIdx.x / n_ntiles;
@@ -142,11 +155,11 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   int a_dst[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int q = tid + i * NT, row = q >> 3, ch = q & 7;
+    const int q = tid + i * NT_, row = q >> 3, ch = q & 7;
     const int p = row0 + row;
     a_src[i] = nullptr;
     if (p < row_end) {
-      const int r = gather_slots ? gather_slots[p] / gather_k : p;
+      const int r = GATHER ? gather_slots[p] / gather_k : p;
       a_src[i] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + ch * VEC;
     }
     a_dst[i] = row * ROWB + ((ch ^ (row & 7)) << 4);
@@ -156,27 +169,33 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   const T* We = Wt + static_cast<int64_t>(e) * N * K;
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int q = tid + i * NT, row = q >> 3, ch = q & 7;
+    const int q = tid + i * NT_, row = q >> 3, ch = q & 7;
     const int64_t n = n0 + row;
     b_src[i] = n < N ? We + n * K + ch * VEC : nullptr;
     b_dst[i] = BM * ROWB + row * ROWB + ((ch ^ (row & 7)) << 4);
   }
 
-  uint4 a_reg[A_CH], b_reg[B_CH];
-  auto gload = [&](int kt) {
-    const int64_t ko = static_cast<int64_t>(kt) * BK;
+  // ROT: every workgroup starts its K walk at a different step, so that
+  // workgroups resident together do not all read the same K columns at once
+  const int nk = static_cast<int>(K / BK);
+  const int kstart = ROT ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk) : 0;
+  uint4 a_reg[P][A_CH], b_reg[P][B_CH];
+  auto gload = [&](int slot, int kt) {
+    int kk = kt + kstart;
+    if (ROT && kk >= nk) kk -= nk;
+    const int64_t ko = static_cast<int64_t>(kk) * BK;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i)
-      a_reg[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + ko) : make_uint4(0, 0, 0, 0);
+      a_reg[slot][i] = a_src[i] ? load16<false>(a_src[i] + ko) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_CH; ++i)
-      b_reg[i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + ko) : make_uint4(0, 0, 0, 0);
+      b_reg[slot][i] = b_src[i] ? load16<NT>(b_src[i] + ko) : make_uint4(0, 0, 0, 0);
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int slot, int buf) {
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<uint4*>(&smem[buf][a_dst[i]]) = a_reg[i];
+    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<uint4*>(&smem[buf][a_dst[i]]) = a_reg[slot][i];
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) *reinterpret_cast<uint4*>(&smem[buf][b_dst[i]]) = b_reg[i];
+    for (int i = 0; i < B_CH; ++i) *reinterpret_cast<uint4*>(&smem[buf][b_dst[i]]) = b_reg[slot][i];
   };
 
   f32x16_t acc[FM][FN];
@@ -190,16 +209,9 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     const int byte = (ks * M::KSTEP + h * M::KPACK) * static_cast<int>(sizeof(T));
     return row * ROWB + ((((byte >> 4) ^ (row & 7))) << 4) + (byte & 15);
   };
-
-  const int nk = static_cast<int>(K / BK);
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const unsigned char* As = smem[cur];
-    const unsigned char* Bs = smem[cur] + BM * ROWB;
+  auto compute = [&](int buf) {
+    const unsigned char* As = smem[buf];
+    const unsigned char* Bs = smem[buf] + BM * ROWB;
 #pragma unroll
     for (int ks = 0; ks < BK / M::KSTEP; ++ks) {
       typename M::frag_t af[FM], bfr[FN];
@@ -214,8 +226,26 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
 #pragma unroll
         for (int j = 0; j < FN; ++j) M::run(acc[i][j], af[i], bfr[j]);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+  };
+
+  // K-step kt lives in register slot kt % P until it is copied to LDS buffer kt % 2
+#pragma unroll
+  for (int s = 0; s < P; ++s)
+    if (s < nk) gload(s, s);
+  sstore(0, 0);
+  __syncthreads();
+  if (P < nk) gload(0, P);
+  for (int kt0 = 0; kt0 < nk; kt0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int kt = kt0 + u;
+      if (kt < nk) {
+        compute(kt & 1);
+        if (kt + 1 < nk) sstore((u + 1) % P, (kt + 1) & 1);
+        __syncthreads();
+        if (kt + 1 + P < nk) gload((u + 1) % P, kt + 1 + P);
+      }
+    }
   }
 
 #pragma unroll
@@ -231,34 +261,37 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     }
 }
 
-template <typename T, int BM, int BN, int WM, int WN>
-static hipError_t gemm_launch(const TilePlan& plan, const void* X, int x_rows, const int32_t* gather_slots,
-                              int gather_k, const void* Wt, int64_t N, int64_t K, float* C,
-                              const int4* mtiles, const int32_t* counts, hipStream_t stream) {
-  const int n_ntiles = static_cast<int>((N + BN - 1) / BN);
+struct GemmArgs {
+  const void* X;
+  int x_rows;
+  const int32_t* gather_slots;
+  int gather_k;
+  const void* Wt;
+  int64_t N, K;
+  float* C;
+  const int4* mtiles;
+  const int32_t* counts;
+};
+
+template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false>
+static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
+  const int n_ntiles = static_cast<int>((a.N + BN - 1) / BN);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles;
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN>), dim3(static_cast<unsigned>(grid)),
-                     dim3(WM * WN * kWave), 0, stream, static_cast<const T*>(X), x_rows, gather_slots,
-                     gather_k, static_cast<const T*>(Wt), N, K, C, mtiles, counts, n_ntiles);
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT>), dim3(static_cast<unsigned>(grid)),
+                     dim3(WM * WN * kWave), 0, stream, static_cast<const T*>(a.X), a.x_rows,
+                     a.gather_slots, a.gather_k, static_cast<const T*>(a.Wt), a.N, a.K, a.C,
+                     a.mtiles, a.counts, n_ntiles);
   return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t gemm_dispatch(const TilePlan& plan, const void* X, int x_rows, const int32_t* gather_slots,
-                                int gather_k, const void* Wt, int64_t N, int64_t K, float* C,
-                                const int4* mtiles, const int32_t* counts, hipStream_t stream) {
+template <typename T, bool GATHER>
+static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
+  // decode-sized M-tiles stream the weights: nontemporal loads, rotated K walk
   switch (plan.bm) {
-    case 32:
-      return gemm_launch<T, 32, 128, 1, 4>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles,
-                                           counts, stream);
-    case 64:
-      return gemm_launch<T, 64, 128, 2, 2>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles,
-                                           counts, stream);
-    case 128:
-      return gemm_launch<T, 128, 128, 2, 2>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles,
-                                            counts, stream);
-    default:
-      return hipErrorInvalidValue;
+    case 32: return lds_launch<T, 32, 128, 1, 4, 2, true, GATHER, true>(plan, a, stream);
+    case 64: return lds_launch<T, 64, 128, 2, 2, 2, true, GATHER, true>(plan, a, stream);
+    case 128: return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false>(plan, a, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -266,11 +299,13 @@ hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_row
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, const int4* mtiles, const int32_t* counts,
                        hipStream_t stream) {
+  const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts};
+  const bool gather = gather_slots != nullptr;
   if (dtype == DT_BF16)
-    return gemm_dispatch<bf16_t>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts,
-                                 stream);
-  return gemm_dispatch<float>(plan, X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts,
-                              stream);
+    return gather ? gemm_dispatch<bf16_t, true>(plan, a, stream)
+                  : gemm_dispatch<bf16_t, false>(plan, a, stream);
+  return gather ? gemm_dispatch<float, true>(plan, a, stream)
+                : gemm_dispatch<float, false>(plan, a, stream);
 }
 
 }  // namespace moelora

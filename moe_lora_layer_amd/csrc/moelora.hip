@@ -37,7 +37,9 @@ TilePlan make_plan(const moelora_dims* d) {
   const int64_t E = d->experts, nb = E * d->adapters;
   const int64_t avg = (S + E - 1) / E;  // mean rows per expert
   TilePlan p;
-  p.bm = avg <= 24 ? 32 : (avg <= 48 ? 64 : 128);
+  // one M-tile per expert in the common case: mean rows per expert plus 25%
+  const int64_t want = (avg * 5 + 3) / 4;
+  p.bm = want <= 32 ? 32 : (want <= 64 ? 64 : 128);
   p.bml = 64;
   p.max_mt = static_cast<int>(S / p.bm + (E < S ? E : S) + 1);
   p.max_lt = static_cast<int>(S / p.bml + (nb < S ? nb : S) + 1);
@@ -184,7 +186,7 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   const int64_t h = dims->hidden, I = dims->intermediate;
   const int S = static_cast<int>(T * k);
   // grid sizes must fit the launch limits
-  const int64_t ntiles_max = (2 * I + 127) / 128;
+  const int64_t ntiles_max = (2 * I + 31) / 32;
   if (static_cast<int64_t>(plan.max_mt) * ntiles_max > kMaxGrid ||
       static_cast<int64_t>(plan.max_lt) * 2048 > kMaxGrid)
     return MOELORA_ERR_DIMS;
