@@ -10,8 +10,8 @@
 //
 // Tile: BM x BN outputs, K stepped by 128 bytes (64 bf16 / 32 fp32).  Both
 // operands are K-contiguous in memory (x rows and W^T rows), staged from
-// registers into LDS with a 16-byte-chunk XOR swizzle (chunk ^ (row & 7)) so
-// that the MFMA fragment reads (32 rows, same chunk) hit all banks, double
+// registers into LDS with a 16-byte-chunk XOR swizzle so that the MFMA
+// fragment reads (consecutive rows, same chunk) hit all banks, double
 // buffered: the next K-step's global loads are in flight while the MFMAs of
 // the current one run.
 #include "device_common.h"
@@ -21,6 +21,7 @@ namespace moelora {
 
 // ------------------------------------------------------------------------- prep
 constexpr int kPrepThreads = 1024;
+constexpr int kXcds = 8;  // XCDs of an MI355X
 
 // Writes tiles for items [i0, i1) whose lengths come from offsets at stride
 // `step`; `first` is the index of the first tile of item i0.
@@ -49,7 +50,8 @@ __device__ int count_tiles(const int32_t* offsets, int i0, int i1, int step, int
 __global__ void __launch_bounds__(kPrepThreads)
 k_prep(const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ offsets, int S,
        int E, int L, int bm, int bml, int max_mt, int max_lt, int32_t* __restrict__ pos,
-       int4* __restrict__ mtiles, int4* __restrict__ ltiles, int32_t* __restrict__ counts) {
+       int4* __restrict__ mtiles, int4* __restrict__ ltiles, int32_t* __restrict__ counts,
+       int32_t* __restrict__ expert_tiles) {
   __shared__ int wave_tmp[16];
   const int tid = threadIdx.x;
   for (int p = tid; p < S; p += kPrepThreads) {
@@ -65,7 +67,16 @@ k_prep(const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ off
     const int first =
         block_exclusive_scan(count_tiles(offsets, i0, i1, L, bm, S), wave_tmp, &total);
     emit_tiles(offsets, i0, i1, L, bm, first, S, max_mt, mtiles);
-    if (tid == 0) counts[0] = min(total, max_mt);
+    // expert_tiles[e] = index of expert e's first M-tile; expert_tiles[E] = count
+    int t = first;
+    for (int i = i0; i < i1; ++i) {
+      expert_tiles[i] = min(t, max_mt);
+      t += count_tiles(offsets, i, i + 1, L, bm, S);
+    }
+    if (tid == 0) {
+      counts[0] = min(total, max_mt);
+      expert_tiles[E] = min(total, max_mt);
+    }
   }
   // LoRA tiles: one item per (expert, adapter) bucket.
   {
@@ -82,9 +93,10 @@ k_prep(const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ off
 
 hipError_t launch_prep(const int32_t* sorted_slots, const int32_t* offsets, int S, int E, int L,
                        const TilePlan& plan, int32_t* pos, int4* mtiles, int4* ltiles,
-                       int32_t* counts, hipStream_t stream) {
+                       int32_t* counts, int32_t* expert_tiles, hipStream_t stream) {
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, sorted_slots, offsets, S, E,
-                     L, plan.bm, plan.bml, plan.max_mt, plan.max_lt, pos, mtiles, ltiles, counts);
+                     L, plan.bm, plan.bml, plan.max_mt, plan.max_lt, pos, mtiles, ltiles, counts,
+                     expert_tiles);
   return hipGetLastError();
 }
 
@@ -119,11 +131,24 @@ __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false>
+// 16-byte chunk swizzle of the LDS tiles (rows of 128 bytes = 8 chunks).  A
+// fragment read has 16 consecutive rows read the same logical chunk; with 64
+// LDS banks those 16 x 16 bytes must cover all banks, i.e. rows r and r + 8 of
+// equal parity must land on different chunks: chunk ^ ((row >> 1) & 7).
+template <int SWZ>
+__device__ __forceinline__ int swz(int row) { return SWZ == 0 ? (row & 7) : ((row >> 1) & 7); }
+
+__device__ __forceinline__ uint4 masked(uint4 v, uint32_t m) {
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
+          bool SCHED = false, int SWZ = 1, bool XCDMAP = true>
 __global__ void __launch_bounds__(WM * WN * kWave)
 k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
        const T* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
-       const int4* __restrict__ mtiles, const int32_t* __restrict__ counts, int n_ntiles) {
+       const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
+       const int32_t* __restrict__ expert_tiles, int n_ntiles) {
   typedef Mfma<T> M;
   constexpr int NT_ = WM * WN * kWave;
   constexpr int ROWB = 128;                    // bytes of K per LDS row
@@ -137,9 +162,23 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   static_assert(FM >= 1 && FN >= 1 && P >= 1, "wave tile");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2][(BM + BN) * ROWB];
 
-  const int mt = blockIdx.x / n_ntiles;
-  const int nt = blockIdx.x % n_ntiles;
-  if (mt >= counts[0]) return;
+  // Workgroup order.  The grid is sized from a host-side bound; the first
+  // counts[0] * n_ntiles workgroups are the real ones.  Hardware hands
+  // consecutive workgroup ids to the 8 XCDs in turn; XCDMAP remaps the real
+  // ones so that consecutive logical ids run on the same XCD (each XCD gets
+  // an equal share), then each expert's tiles are walked N-tile by N-tile with
+  // its M-tiles innermost, so M-tiles sharing one weight tile run together on
+  // one XCD (one L2).
+  const int active = counts[0] * n_ntiles;
+  if (static_cast<int>(blockIdx.x) >= active) return;
+  const int xcd = blockIdx.x % kXcds, q = active / kXcds, rem = active % kXcds;
+  const int bid = XCDMAP ? xcd * q + min(xcd, rem) + blockIdx.x / kXcds : static_cast<int>(blockIdx.x);
+  const int t0 = bid / n_ntiles;
+  const int ex = mtiles[t0].x;
+  const int ta = expert_tiles[ex], tb = expert_tiles[ex + 1];
+  const int local = bid - ta * n_ntiles;
+  const int nt = local / (tb - ta);
+  const int mt = ta + local % (tb - ta);
   const int4 tile = mtiles[mt];
   const int e = tile.x, row0 = tile.y, row_end = tile.z;
   const int64_t n0 = static_cast<int64_t>(nt) * BN;
@@ -150,29 +189,33 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   const int wm = wave / WN, wn = wave % WN;
   const int c32 = lane & 31, h = lane >> 5;
 
-  // global sources and LDS destinations of this thread's 16-byte chunks
+  // global sources and LDS destinations of this thread's 16-byte chunks.
+  // Rows outside the tile read a clamped valid row and store zeros instead
+  // (a select, not a branch).
   const T* a_src[A_CH];
+  uint32_t a_mask[A_CH];
   int a_dst[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
     const int q = tid + i * NT_, row = q >> 3, ch = q & 7;
     const int p = row0 + row;
-    a_src[i] = nullptr;
-    if (p < row_end) {
-      const int r = GATHER ? gather_slots[p] / gather_k : p;
-      a_src[i] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + ch * VEC;
-    }
-    a_dst[i] = row * ROWB + ((ch ^ (row & 7)) << 4);
+    a_mask[i] = p < row_end ? 0xffffffffu : 0u;
+    const int pc = p < row_end ? p : row_end - 1;
+    const int r = GATHER ? gather_slots[pc] / gather_k : pc;
+    a_src[i] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + ch * VEC;
+    a_dst[i] = row * ROWB + ((ch ^ swz<SWZ>(row)) << 4);
   }
   const T* b_src[B_CH];
+  uint32_t b_mask[B_CH];
   int b_dst[B_CH];
   const T* We = Wt + static_cast<int64_t>(e) * N * K;
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     const int q = tid + i * NT_, row = q >> 3, ch = q & 7;
     const int64_t n = n0 + row;
-    b_src[i] = n < N ? We + n * K + ch * VEC : nullptr;
-    b_dst[i] = BM * ROWB + row * ROWB + ((ch ^ (row & 7)) << 4);
+    b_mask[i] = n < N ? 0xffffffffu : 0u;
+    b_src[i] = We + (n < N ? n : N - 1) * K + ch * VEC;
+    b_dst[i] = BM * ROWB + row * ROWB + ((ch ^ swz<SWZ>(row)) << 4);
   }
 
   // ROT: every workgroup starts its K walk at a different step, so that
@@ -185,17 +228,17 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     if (ROT && kk >= nk) kk -= nk;
     const int64_t ko = static_cast<int64_t>(kk) * BK;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i)
-      a_reg[slot][i] = a_src[i] ? load16<false>(a_src[i] + ko) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < A_CH; ++i) a_reg[slot][i] = load16<false>(a_src[i] + ko);
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      b_reg[slot][i] = b_src[i] ? load16<NT>(b_src[i] + ko) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < B_CH; ++i) b_reg[slot][i] = load16<NT>(b_src[i] + ko);
   };
   auto sstore = [&](int slot, int buf) {
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<uint4*>(&smem[buf][a_dst[i]]) = a_reg[slot][i];
+    for (int i = 0; i < A_CH; ++i)
+      *reinterpret_cast<uint4*>(&smem[buf][a_dst[i]]) = masked(a_reg[slot][i], a_mask[i]);
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) *reinterpret_cast<uint4*>(&smem[buf][b_dst[i]]) = b_reg[slot][i];
+    for (int i = 0; i < B_CH; ++i)
+      *reinterpret_cast<uint4*>(&smem[buf][b_dst[i]]) = masked(b_reg[slot][i], b_mask[i]);
   };
 
   f32x16_t acc[FM][FN];
@@ -207,24 +250,48 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   // byte offset of lane's fragment inside an LDS row, for K-step ks
   auto frag_off = [&](int row, int ks) {
     const int byte = (ks * M::KSTEP + h * M::KPACK) * static_cast<int>(sizeof(T));
-    return row * ROWB + ((((byte >> 4) ^ (row & 7))) << 4) + (byte & 15);
+    return row * ROWB + ((((byte >> 4) ^ swz<SWZ>(row))) << 4) + (byte & 15);
+  };
+  // Fragments of K-step ks+1 are read from LDS while the MFMAs of step ks
+  // run (two fragment sets); the scheduling hints interleave one LDS read with
+  // every MFMA_PER_READ MFMAs of the step.
+  constexpr int KSN = BK / M::KSTEP;
+  constexpr int READS = FM + FN;
+  constexpr int MFMAS = FM * FN;
+  typedef typename M::frag_t frag_t;
+  auto read = [&](frag_t (&af)[FM], frag_t (&bfr)[FN], const unsigned char* As,
+                  const unsigned char* Bs, int ks) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[i] = M::load(reinterpret_cast<const T*>(As + frag_off(wm * WTM + i * 32 + c32, ks)));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bfr[j] = M::load(reinterpret_cast<const T*>(Bs + frag_off(wn * WTN + j * 32 + c32, ks)));
+  };
+  auto mma = [&](const frag_t (&af)[FM], const frag_t (&bfr)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) M::run(acc[i][j], af[i], bfr[j]);
+    if (SCHED) {
+#pragma unroll
+      for (int r = 0; r < READS; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, (MFMAS + READS - 1) / READS, 0);  // MFMAs
+      }
+    }
   };
   auto compute = [&](int buf) {
     const unsigned char* As = smem[buf];
     const unsigned char* Bs = smem[buf] + BM * ROWB;
+    frag_t a0[FM], b0[FN], a1[FM], b1[FN];
+    read(a0, b0, As, Bs, 0);
 #pragma unroll
-    for (int ks = 0; ks < BK / M::KSTEP; ++ks) {
-      typename M::frag_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = M::load(reinterpret_cast<const T*>(As + frag_off(wm * WTM + i * 32 + c32, ks)));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = M::load(reinterpret_cast<const T*>(Bs + frag_off(wn * WTN + j * 32 + c32, ks)));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) M::run(acc[i][j], af[i], bfr[j]);
+    for (int ks = 0; ks < KSN; ks += 2) {
+      if (ks + 1 < KSN) read(a1, b1, As, Bs, ks + 1);
+      mma(a0, b0);
+      if (ks + 2 < KSN) read(a0, b0, As, Bs, ks + 2);
+      if (ks + 1 < KSN) mma(a1, b1);
     }
   };
 
@@ -271,16 +338,18 @@ struct GemmArgs {
   float* C;
   const int4* mtiles;
   const int32_t* counts;
+  const int32_t* expert_tiles;
 };
 
-template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false>
+template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
+          bool SCHED = false, int SWZ = 1, bool XCDMAP = true>
 static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
   const int n_ntiles = static_cast<int>((a.N + BN - 1) / BN);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles;
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP>), dim3(static_cast<unsigned>(grid)),
                      dim3(WM * WN * kWave), 0, stream, static_cast<const T*>(a.X), a.x_rows,
                      a.gather_slots, a.gather_k, static_cast<const T*>(a.Wt), a.N, a.K, a.C,
-                     a.mtiles, a.counts, n_ntiles);
+                     a.mtiles, a.counts, a.expert_tiles, n_ntiles);
   return hipGetLastError();
 }
 
@@ -288,9 +357,9 @@ template <typename T, bool GATHER>
 static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
   // decode-sized M-tiles stream the weights: nontemporal loads, rotated K walk
   switch (plan.bm) {
-    case 32: return lds_launch<T, 32, 128, 1, 4, 2, true, GATHER, true>(plan, a, stream);
-    case 64: return lds_launch<T, 64, 128, 2, 2, 2, true, GATHER, true>(plan, a, stream);
-    case 128: return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false>(plan, a, stream);
+    case 32: return lds_launch<T, 32, 128, 1, 4, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
+    case 64: return lds_launch<T, 64, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
+    case 128: return lds_launch<T, 128, 128, 2, 2, 2, false, GATHER, false>(plan, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -298,8 +367,8 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStre
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, const int4* mtiles, const int32_t* counts,
-                       hipStream_t stream) {
-  const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts};
+                       const int32_t* expert_tiles, hipStream_t stream) {
+  const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts, expert_tiles};
   const bool gather = gather_slots != nullptr;
   if (dtype == DT_BF16)
     return gather ? gemm_dispatch<bf16_t, true>(plan, a, stream)

@@ -27,9 +27,12 @@ struct TilePlan {
   int max_lt;    // upper bound of LoRA tiles
 };
 
+// Inverse permutation pos[slot] = sorted position, the M-tile list (tiles of
+// plan.bm rows per expert, in expert order) with expert_tiles[e] = first tile
+// of expert e (expert_tiles[E] = tile count), and the LoRA tile list.
 hipError_t launch_prep(const int32_t* sorted_slots, const int32_t* offsets, int S, int E, int L,
                        const TilePlan& plan, int32_t* pos, int4* mtiles, int4* ltiles,
-                       int32_t* counts, hipStream_t stream);
+                       int32_t* counts, int32_t* expert_tiles, hipStream_t stream);
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 
@@ -39,7 +42,7 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, const int4* mtiles, const int32_t* counts,
-                       hipStream_t stream);
+                       const int32_t* expert_tiles, hipStream_t stream);
 
 // Z[p][q] += sum_k X[row(p)][k] * At[l][e][q][k] over the LoRA tiles (split-K,
 // fp32 atomics).  Z must be zero beforehand.

@@ -47,7 +47,7 @@ TilePlan make_plan(const moelora_dims* d) {
 }
 
 struct ForwardLayout {
-  size_t pos, counts, mtiles, ltiles, g, z1, z2, act, d, total;
+  size_t pos, counts, etiles, mtiles, ltiles, g, z1, z2, act, d, total;
 };
 
 ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
@@ -59,6 +59,7 @@ ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
   size_t off = 0;
   L.pos = off;    off += round_up(S * 4);
   L.counts = off; off += round_up(4 * 4);
+  L.etiles = off; off += round_up((static_cast<size_t>(d->experts) + 1) * 4);
   L.mtiles = off; off += round_up(static_cast<size_t>(plan.max_mt) * 16);
   L.ltiles = off; off += round_up(static_cast<size_t>(plan.max_lt) * 16);
   L.g = off;      off += round_up(S * 2 * I * 4);
@@ -194,6 +195,7 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   char* ws = static_cast<char*>(workspace);
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* etiles = reinterpret_cast<int32_t*>(ws + L.etiles);
   int4* mtiles = reinterpret_cast<int4*>(ws + L.mtiles);
   int4* ltiles = reinterpret_cast<int4*>(ws + L.ltiles);
   float* G = reinterpret_cast<float*>(ws + L.g);
@@ -211,13 +213,13 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   hipError_t e = mark(MOELORA_STAGE_PREP);
   if (e == hipSuccess)
     e = moelora::launch_prep(sorted_slots, bucket_offsets, S, E, Lad, plan, pos, mtiles, ltiles,
-                             counts, st);
+                             counts, etiles, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_ZERO);
   if (e == hipSuccess) e = moelora::launch_zero(Z1, 2ll * S * r, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);
   if (e == hipSuccess)
     e = moelora::launch_gemm(dt, plan, x, static_cast<int>(T), sorted_slots, k, w_gate_up, 2 * I,
-                             h, G, mtiles, counts, st);
+                             h, G, mtiles, counts, etiles, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_GATE_UP);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, x, static_cast<int>(T), sorted_slots, k, a_gate_up, E,
@@ -228,7 +230,8 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
                                        counts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
   if (e == hipSuccess)
-    e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, mtiles, counts, st);
+    e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, mtiles, counts, etiles,
+                             st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_DOWN);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, ACT, S, nullptr, 1, a_down, E, Lad, I, Z2, ltiles,
