@@ -142,13 +142,15 @@ __device__ __forceinline__ uint4 masked(uint4 v, uint32_t m) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
+// ksplit > 1: workgroup (tile, s) covers the s-th of ksplit K ranges and adds
+// its partial tile to C with relaxed fp32 atomics (C must be zero before).
 template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
           bool SCHED = false, int SWZ = 1, bool XCDMAP = true>
 __global__ void __launch_bounds__(WM * WN * kWave)
 k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
        const T* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
        const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
-       const int32_t* __restrict__ expert_tiles, int n_ntiles) {
+       const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit) {
   typedef Mfma<T> M;
   constexpr int NT_ = WM * WN * kWave;
   constexpr int ROWB = 128;                    // bytes of K per LDS row
@@ -169,10 +171,12 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   // an equal share), then each expert's tiles are walked N-tile by N-tile with
   // its M-tiles innermost, so M-tiles sharing one weight tile run together on
   // one XCD (one L2).
+  const int ks = static_cast<int>(blockIdx.x) % ksplit;
+  const int pid = static_cast<int>(blockIdx.x) / ksplit;
   const int active = counts[0] * n_ntiles;
-  if (static_cast<int>(blockIdx.x) >= active) return;
-  const int xcd = blockIdx.x % kXcds, q = active / kXcds, rem = active % kXcds;
-  const int bid = XCDMAP ? xcd * q + min(xcd, rem) + blockIdx.x / kXcds : static_cast<int>(blockIdx.x);
+  if (pid >= active) return;
+  const int xcd = pid % kXcds, q = active / kXcds, rem = active % kXcds;
+  const int bid = XCDMAP ? xcd * q + min(xcd, rem) + pid / kXcds : pid;
   const int t0 = bid / n_ntiles;
   const int ex = mtiles[t0].x;
   const int ta = expert_tiles[ex], tb = expert_tiles[ex + 1];
@@ -220,13 +224,16 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
 
   // ROT: every workgroup starts its K walk at a different step, so that
   // workgroups resident together do not all read the same K columns at once
-  const int nk = static_cast<int>(K / BK);
-  const int kstart = ROT ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk) : 0;
+  const int nk_all = static_cast<int>(K / BK);
+  const int nk_per = (nk_all + ksplit - 1) / ksplit;
+  const int kbeg = min(nk_all, ks * nk_per);
+  const int nk = min(nk_all, kbeg + nk_per) - kbeg;  // K-steps of this workgroup
+  const int kstart = (ROT && nk > 0) ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk) : 0;
   uint4 a_reg[P][A_CH], b_reg[P][B_CH];
   auto gload = [&](int slot, int kt) {
     int kk = kt + kstart;
     if (ROT && kk >= nk) kk -= nk;
-    const int64_t ko = static_cast<int64_t>(kk) * BK;
+    const int64_t ko = static_cast<int64_t>(kbeg + kk) * BK;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) a_reg[slot][i] = load16<false>(a_src[i] + ko);
 #pragma unroll
@@ -296,6 +303,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   };
 
   // K-step kt lives in register slot kt % P until it is copied to LDS buffer kt % 2
+  if (nk <= 0) return;  // uniform: an empty K split (only for tiny K)
 #pragma unroll
   for (int s = 0; s < P; ++s)
     if (s < nk) gload(s, s);
@@ -323,7 +331,13 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int p = row0 + wm * WTM + i * 32 + acc_row(r, h);
-        if (p < row_end && n < N) C[static_cast<int64_t>(p) * N + n] = acc[i][j][r];
+        if (p < row_end && n < N) {
+          float* dst = C + static_cast<int64_t>(p) * N + n;
+          if (ksplit > 1)
+            atomic_add_relaxed(dst, acc[i][j][r]);
+          else
+            *dst = acc[i][j][r];
+        }
       }
     }
 }
@@ -339,17 +353,18 @@ struct GemmArgs {
   const int4* mtiles;
   const int32_t* counts;
   const int32_t* expert_tiles;
+  int ksplit;
 };
 
 template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
           bool SCHED = false, int SWZ = 1, bool XCDMAP = true>
 static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
   const int n_ntiles = static_cast<int>((a.N + BN - 1) / BN);
-  const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles;
+  const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
   hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP>), dim3(static_cast<unsigned>(grid)),
                      dim3(WM * WN * kWave), 0, stream, static_cast<const T*>(a.X), a.x_rows,
                      a.gather_slots, a.gather_k, static_cast<const T*>(a.Wt), a.N, a.K, a.C,
-                     a.mtiles, a.counts, a.expert_tiles, n_ntiles);
+                     a.mtiles, a.counts, a.expert_tiles, n_ntiles, a.ksplit);
   return hipGetLastError();
 }
 
@@ -359,7 +374,10 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStre
   switch (plan.bm) {
     case 32: return lds_launch<T, 32, 128, 1, 4, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
     case 64: return lds_launch<T, 64, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
-    case 128: return lds_launch<T, 128, 128, 2, 2, 2, false, GATHER, false>(plan, a, stream);
+    case 128:
+      if (plan.stream)
+        return lds_launch<T, 128, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
+      return lds_launch<T, 128, 128, 2, 2, 2, false, GATHER, false>(plan, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -367,8 +385,9 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStre
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, const int4* mtiles, const int32_t* counts,
-                       const int32_t* expert_tiles, hipStream_t stream) {
-  const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts, expert_tiles};
+                       const int32_t* expert_tiles, int ksplit, hipStream_t stream) {
+  const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts, expert_tiles,
+                   ksplit < 1 ? 1 : ksplit};
   const bool gather = gather_slots != nullptr;
   if (dtype == DT_BF16)
     return gather ? gemm_dispatch<bf16_t, true>(plan, a, stream)

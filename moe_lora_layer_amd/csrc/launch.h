@@ -25,6 +25,9 @@ struct TilePlan {
   int bml;       // rows per LoRA tile
   int max_mt;    // upper bound of M-tiles, known on the host
   int max_lt;    // upper bound of LoRA tiles
+  bool stream;   // weight tiles are used by one M-tile only: stream them
+  int ksplit_gu; // K splits of the gate_up GEMM (1 = none)
+  int ksplit_dn; // K splits of the down GEMM (1 = none)
 };
 
 // Inverse permutation pos[slot] = sorted position, the M-tile list (tiles of
@@ -38,11 +41,12 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 
 // C[p][n] = sum_k X[row(p)][k] * Wt[e][n][k] over the M-tiles of `mtiles`;
 // row(p) = gather_slots[p] / gather_k when gather_slots != nullptr, else p,
-// clamped to [0, x_rows).
+// clamped to [0, x_rows).  ksplit > 1 splits K over workgroups that add into
+// C with fp32 atomics (C must be zero beforehand).
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, const int4* mtiles, const int32_t* counts,
-                       const int32_t* expert_tiles, hipStream_t stream);
+                       const int32_t* expert_tiles, int ksplit, hipStream_t stream);
 
 // Z[p][q] += sum_k X[row(p)][k] * At[l][e][q][k] over the LoRA tiles (split-K,
 // fp32 atomics).  Z must be zero beforehand.

@@ -3,6 +3,8 @@
 // every argument are in include/moelora.h.
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "launch.h"
 #include "moelora.h"
 
@@ -40,9 +42,24 @@ TilePlan make_plan(const moelora_dims* d) {
   // one M-tile per expert in the common case: mean rows per expert plus 25%
   const int64_t want = (avg * 5 + 3) / 4;
   p.bm = want <= 32 ? 32 : (want <= 64 ? 64 : 128);
+  // at most one 128-row M-tile per expert: nothing reuses a weight tile, so the
+  // weights are streamed (nontemporal loads, rotated K walk)
+  p.stream = p.bm < 128 || want <= 160;
   p.bml = 64;
   p.max_mt = static_cast<int>(S / p.bm + (E < S ? E : S) + 1);
   p.max_lt = static_cast<int>(S / p.bml + (nb < S ? nb : S) + 1);
+  // Split K only when the real M x N tiles cannot give every CU a workgroup
+  // (e.g. one expert and a narrow output): ~1024 workgroups, >= 8 K-steps
+  // per split.
+  const int64_t est_tiles = std::max<int64_t>((S + p.bm - 1) / p.bm, std::min<int64_t>(E, S));
+  auto splits = [&](int64_t N, int64_t K) {
+    const int64_t wgs = std::max<int64_t>(1, est_tiles * ((N + 127) / 128));
+    const int64_t steps = K / (d->dtype == MOELORA_BF16 ? 64 : 32);
+    if (wgs >= 256) return 1;
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((1024 + wgs - 1) / wgs, steps / 8)));
+  };
+  p.ksplit_gu = splits(2 * d->intermediate, d->hidden);
+  p.ksplit_dn = splits(d->hidden, d->intermediate);
   return p;
 }
 
@@ -63,11 +80,11 @@ ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
   L.mtiles = off; off += round_up(static_cast<size_t>(plan.max_mt) * 16);
   L.ltiles = off; off += round_up(static_cast<size_t>(plan.max_lt) * 16);
   L.g = off;      off += round_up(S * 2 * I * 4);
-  L.z1 = off;     // Z1 and Z2 are adjacent so one fill clears both
-  L.z2 = off + S * r * 4;
-  off += round_up(2 * S * r * 4);
   L.act = off;    off += round_up(S * I * esz);
-  L.d = off;      off += round_up(S * h * 4);
+  L.z1 = off;     // Z1, Z2 and D are adjacent: one fill clears Z1 and Z2, and D
+  L.z2 = off + S * r * 4;  // too when the down GEMM accumulates with atomics
+  L.d = off + 2 * S * r * 4;
+  off += round_up(2 * S * r * 4 + S * h * 4);
   L.total = off;
   return L;
 }
@@ -188,7 +205,8 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   const int S = static_cast<int>(T * k);
   // grid sizes must fit the launch limits
   const int64_t ntiles_max = (2 * I + 31) / 32;
-  if (static_cast<int64_t>(plan.max_mt) * ntiles_max > kMaxGrid ||
+  if (static_cast<int64_t>(plan.max_mt) * ntiles_max * std::max(plan.ksplit_gu, plan.ksplit_dn) >
+          kMaxGrid ||
       static_cast<int64_t>(plan.max_lt) * 2048 > kMaxGrid)
     return MOELORA_ERR_DIMS;
 
@@ -215,11 +233,14 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
     e = moelora::launch_prep(sorted_slots, bucket_offsets, S, E, Lad, plan, pos, mtiles, ltiles,
                              counts, etiles, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_ZERO);
-  if (e == hipSuccess) e = moelora::launch_zero(Z1, 2ll * S * r, st);
+  const int64_t nzero = 2ll * S * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * h : 0);
+  if (e == hipSuccess) e = moelora::launch_zero(Z1, nzero, st);
+  if (e == hipSuccess && plan.ksplit_gu > 1)
+    e = moelora::launch_zero(G, static_cast<int64_t>(S) * 2 * I, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);
   if (e == hipSuccess)
     e = moelora::launch_gemm(dt, plan, x, static_cast<int>(T), sorted_slots, k, w_gate_up, 2 * I,
-                             h, G, mtiles, counts, etiles, st);
+                             h, G, mtiles, counts, etiles, plan.ksplit_gu, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_GATE_UP);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, x, static_cast<int>(T), sorted_slots, k, a_gate_up, E,
@@ -231,7 +252,7 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
   if (e == hipSuccess)
     e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, mtiles, counts, etiles,
-                             st);
+                             plan.ksplit_dn, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_DOWN);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, ACT, S, nullptr, 1, a_down, E, Lad, I, Z2, ltiles,

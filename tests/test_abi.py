@@ -73,14 +73,13 @@ def test_workspace_sizes_and_layout():
     size = ops.forward_workspace_size(d)
     lay = ops.forward_workspace_layout(d)
     S, I, h, r = 200, 192, 320, 32
-    order = ["G", "Z1", "Z2", "ACT", "D"]
-    offs = [lay["G"], lay["Z1"], lay["Z2"], lay["ACT"], lay["D"]]
-    assert all(o % 16 == 0 for o in offs)
-    assert lay["Z2"] == lay["Z1"] + S * r * 4
-    assert lay["G"] + S * 2 * I * 4 <= lay["Z1"]
-    assert lay["Z2"] + S * r * 4 <= lay["ACT"]
-    assert lay["ACT"] + S * I * 2 <= lay["D"]
-    assert lay["D"] + S * h * 4 <= size, order
+    extent = {"G": S * 2 * I * 4, "Z1": S * r * 4, "ACT": S * I * 2, "Z2": S * r * 4, "D": S * h * 4}
+    assert all(o % 16 == 0 for o in lay.values())
+    spans = sorted((lay[n], lay[n] + extent[n], n) for n in extent)
+    for (a0, a1, na), (b0, b1, nb) in zip(spans, spans[1:]):
+        assert a1 <= b0, (na, nb)          # no two intermediates overlap
+    assert spans[-1][1] <= size
+    assert lay["Z2"] == lay["Z1"] + S * r * 4 and lay["D"] == lay["Z2"] + S * r * 4
     assert ops.align_workspace_size(d) >= 2 * S * 4
     assert ops.forward_workspace_size(good_dims(tokens=0)) == 0
 
