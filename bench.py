@@ -164,7 +164,11 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": round(by / dom_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    # HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (scaled by a
+    # device-copy calibration), kept under profiles/; None once the kernels changed
+    from moe_lora_layer_amd import profiling
+    roof["traffic"] = profiling.load_traffic(cfg.name, dom)
+    roof["algorithmic_bytes"] = by
     roof["kernel"] = dom
     roof["kernel_us"] = round(dom_s * 1e6, 2)
     log(f"[bench] {cfg.name}: {value:.1f} tokens/s, {ms_per_step:.3f} ms/step, "

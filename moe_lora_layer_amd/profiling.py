@@ -1,0 +1,122 @@
+"""Turn rocprofv3 output into the short summaries kept under profiles/.
+
+  python -m moe_lora_layer_amd.profiling trace  <csv_dir> <out.md> <title> <command...>
+  python -m moe_lora_layer_amd.profiling traffic <out.json> <out.md> <kernel-substring>
+        <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> <copy_bytes> <algo_bytes>
+
+`trace` reads <csv_dir>/run_kernel_stats.csv (rocprofv3 --kernel-trace --stats
+--output-format csv).  `traffic` reads per-dispatch FETCH_SIZE and WRITE_SIZE
+(KiB) of the named kernel from two --pmc runs, and the same counters for a
+device copy of known size; the counters are scaled by known/counted of the
+copy.  The traffic record carries a digest of the kernel sources: bench.py
+reports the traffic only while the sources are unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(_HERE)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources and the public header (kernel identity)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(_HERE, "csrc", "*"))) + [os.path.join(ROOT, "include", "moelora.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str, kernel: str):
+    """Bytes per launch of `kernel` at `workload` from profiles/, or None when the
+    record is missing or was taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"{workload}_{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_digest():
+        return None
+    return rec.get("traffic_bytes")
+
+
+def _pmc(dirname: str):
+    rows = list(csv.DictReader(open(os.path.join(dirname, "run_counter_collection.csv"))))
+    out = {}
+    for r in rows:
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _pick(d: dict, sub: str):
+    keys = [k for k in d if sub in k]
+    if len(keys) != 1:
+        raise SystemExit(f"kernel '{sub}' matches {len(keys)} names: {keys}")
+    return keys[0], d[keys[0]]
+
+
+def trace(csv_dir: str, out_md: str, title: str, command: str) -> None:
+    rows = list(csv.DictReader(open(os.path.join(csv_dir, "run_kernel_stats.csv"))))
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", command, "```", "",
+             "| kernel | calls | average us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:120]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def traffic(out_json: str, out_md: str, kernel: str, fetch_dir: str, write_dir: str,
+            copy_fetch_dir: str, copy_write_dir: str, copy_bytes: float, algo_bytes: float,
+            commands: list[str]) -> None:
+    name, fetch = _pick(_pmc(fetch_dir), kernel)
+    _, write = _pick(_pmc(write_dir), kernel)
+    _, cf = _pick(_pmc(copy_fetch_dir), "copyBuffer")
+    _, cw = _pick(_pmc(copy_write_dir), "copyBuffer")
+    fscale = copy_bytes / (statistics.mean(cf) * 1024.0)
+    wscale = copy_bytes / (statistics.mean(cw) * 1024.0)
+    fb = statistics.mean(fetch) * 1024.0 * fscale
+    wb = statistics.mean(write) * 1024.0 * wscale
+    rec = {"kernel": name, "dispatches": len(fetch), "fetch_kib_per_dispatch": statistics.mean(fetch),
+           "write_kib_per_dispatch": statistics.mean(write), "copy_bytes": copy_bytes,
+           "copy_fetch_kib": statistics.mean(cf), "copy_write_kib": statistics.mean(cw),
+           "fetch_scale": fscale, "write_scale": wscale, "traffic_bytes": fb + wb,
+           "algorithmic_bytes": algo_bytes, "traffic_over_algorithmic": (fb + wb) / algo_bytes,
+           "source_sha256": source_digest(), "commands": commands}
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# HBM traffic of `{name[:100]}`", "",
+             "Commands (from the repository root on one MI355X):", "", "```", *commands, "```", "",
+             f"- dispatches averaged: {len(fetch)}",
+             f"- FETCH_SIZE per dispatch: {statistics.mean(fetch):.6g} KiB; WRITE_SIZE: {statistics.mean(write):.6g} KiB",
+             f"- copy calibration ({copy_bytes / 2**30:.3g} GiB device copy): FETCH_SIZE "
+             f"{statistics.mean(cf):.6g} KiB -> scale {fscale:.4g}; WRITE_SIZE {statistics.mean(cw):.6g} KiB "
+             f"-> scale {wscale:.4g}",
+             f"- scaled traffic per launch: {fb / 1e9:.4g} GB read + {wb / 1e9:.4g} GB written = {(fb + wb) / 1e9:.4g} GB",
+             f"- algorithmic bytes per launch: {algo_bytes / 1e9:.4g} GB (ratio {(fb + wb) / algo_bytes:.3f})",
+             f"- kernel sources sha256: {rec['source_sha256']}"]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "trace":
+        trace(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
+    elif sys.argv[1] == "traffic":
+        a = sys.argv
+        traffic(a[2], a[3], a[4], a[5], a[6], a[7], a[8], float(a[9]), float(a[10]), a[11:])
+    else:
+        raise SystemExit(__doc__)
