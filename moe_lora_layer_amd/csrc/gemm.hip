@@ -144,8 +144,10 @@ __device__ __forceinline__ uint4 masked(uint4 v, uint32_t m) {
 
 // ksplit > 1: workgroup (tile, s) covers the s-th of ksplit K ranges and adds
 // its partial tile to C with relaxed fp32 atomics (C must be zero before).
+// PIPE: the LDS writes of K-step kt+1 and the global loads of K-step kt+2 are
+// issued between the MFMAs of K-step kt (one barrier per K-step); requires P = 1.
 template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
-          bool SCHED = false, int SWZ = 1, bool XCDMAP = true>
+          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false>
 __global__ void __launch_bounds__(WM * WN * kWave)
 k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
        const T* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
@@ -288,7 +290,8 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
       }
     }
   };
-  auto compute = [&](int buf) {
+  // hook(step) runs between the MFMAs of K-steps step and step+1
+  auto compute_h = [&](int buf, auto&& hook) {
     const unsigned char* As = smem[buf];
     const unsigned char* Bs = smem[buf] + BM * ROWB;
     frag_t a0[FM], b0[FN], a1[FM], b1[FN];
@@ -297,10 +300,15 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     for (int ks = 0; ks < KSN; ks += 2) {
       if (ks + 1 < KSN) read(a1, b1, As, Bs, ks + 1);
       mma(a0, b0);
+      hook(ks);
       if (ks + 2 < KSN) read(a0, b0, As, Bs, ks + 2);
-      if (ks + 1 < KSN) mma(a1, b1);
+      if (ks + 1 < KSN) {
+        mma(a1, b1);
+        hook(ks + 1);
+      }
     }
   };
+  auto compute = [&](int buf) { compute_h(buf, [](int) {}); };
 
   // K-step kt lives in register slot kt % P until it is copied to LDS buffer kt % 2
   if (nk <= 0) return;  // uniform: an empty K split (only for tiny K)
@@ -309,6 +317,18 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     if (s < nk) gload(s, s);
   sstore(0, 0);
   __syncthreads();
+  if (PIPE) {
+    static_assert(!PIPE || P == 1, "PIPE uses a single register stage");
+    if (1 < nk) gload(0, 1);  // slot 0 now holds K-step 1
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      compute_h(buf, [&](int step) {
+        if (step == 0 && kt + 1 < nk) sstore(0, buf ^ 1);
+        if (step == 1 && kt + 2 < nk) gload(0, kt + 2);
+      });
+      __syncthreads();
+    }
+  } else {
   if (P < nk) gload(0, P);
   for (int kt0 = 0; kt0 < nk; kt0 += P) {
 #pragma unroll
@@ -321,6 +341,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
         if (kt + 1 + P < nk) gload((u + 1) % P, kt + 1 + P);
       }
     }
+  }
   }
 
 #pragma unroll
@@ -357,11 +378,11 @@ struct GemmArgs {
 };
 
 template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
-          bool SCHED = false, int SWZ = 1, bool XCDMAP = true>
+          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false>
 static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
   const int n_ntiles = static_cast<int>((a.N + BN - 1) / BN);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE>), dim3(static_cast<unsigned>(grid)),
                      dim3(WM * WN * kWave), 0, stream, static_cast<const T*>(a.X), a.x_rows,
                      a.gather_slots, a.gather_k, static_cast<const T*>(a.Wt), a.N, a.K, a.C,
                      a.mtiles, a.counts, a.expert_tiles, n_ntiles, a.ksplit);
@@ -377,7 +398,9 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStre
     case 128:
       if (plan.stream)
         return lds_launch<T, 128, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
-      return lds_launch<T, 128, 128, 2, 2, 2, false, GATHER, false>(plan, a, stream);
+      return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, stream);
+    case 256:  // prefill: 256x256 tiles, 8 waves of 128x64, one barrier per K-step
+      return lds_launch<T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

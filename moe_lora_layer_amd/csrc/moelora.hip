@@ -41,7 +41,7 @@ TilePlan make_plan(const moelora_dims* d) {
   TilePlan p;
   // one M-tile per expert in the common case: mean rows per expert plus 25%
   const int64_t want = (avg * 5 + 3) / 4;
-  p.bm = want <= 32 ? 32 : (want <= 64 ? 64 : 128);
+  p.bm = want <= 32 ? 32 : (want <= 64 ? 64 : (want <= 256 ? 128 : 256));
   // at most one 128-row M-tile per expert: nothing reuses a weight tile, so the
   // weights are streamed (nontemporal loads, rotated K walk)
   p.stream = p.bm < 128 || want <= 160;
