@@ -28,6 +28,7 @@ struct TilePlan {
   bool stream;   // weight tiles are used by one M-tile only: stream them
   int ksplit_gu; // K splits of the gate_up GEMM (1 = none)
   int ksplit_dn; // K splits of the down GEMM (1 = none)
+  bool lora_db;  // LoRA tiles average many rows: double-buffer their row blocks
 };
 
 // Inverse permutation pos[slot] = sorted position, the M-tile list (tiles of

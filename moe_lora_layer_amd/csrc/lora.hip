@@ -11,6 +11,8 @@
 // Work unit of every kernel: a LoRA tile = consecutive sorted rows of one
 // (expert, adapter) bucket.  Products run on MFMA 16x16 blocks; the rank r
 // (16/32/64) is the M of the shrink and the K of the expand.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -137,16 +139,96 @@ k_shrink(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather
   }
 }
 
+// Tall tiles (many rows per bucket): each wave owns a 16-row block of the
+// tile and walks the workgroup's whole K range, STEPS MFMA steps at a time
+// with the next STEPS in flight; no cross-wave reduction is needed, and each
+// wave adds its z block to Z with one relaxed atomic per element.
+template <typename T, int R, int STEPS, bool GATHER>
+__global__ void __launch_bounds__(kLoraThreads)
+k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
+              int gather_k, const T* __restrict__ At, int E, int L, int64_t K, int64_t kwg,
+              int nsplit, float* __restrict__ Z, const int4* __restrict__ ltiles,
+              const int32_t* __restrict__ counts) {
+  typedef Mfma16<T> M;
+  typedef typename M::frag_t frag_t;
+  constexpr int RB = R / 16;
+  constexpr int KB = STEPS * M::KSTEP;
+  const int lt = blockIdx.x / nsplit;
+  const int split = blockIdx.x % nsplit;
+  if (lt >= counts[1]) return;
+  const int4 tile = ltiles[lt];
+  const int b = tile.x, row0 = tile.y, row_end = tile.z;
+  const int e = b / L, l = b % L;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t kb0 = static_cast<int64_t>(split) * kwg;
+  const int64_t kb1 = kb0 + kwg < K ? kb0 + kwg : K;
+  const T* Ab = At + (static_cast<int64_t>(l) * E + e) * R * K + g * M::KPACK;
+
+  for (int m0 = row0 + 16 * wave; m0 < row_end; m0 += 16 * kLoraWaves) {
+    const int p = m0 + c;
+    const bool ok = p < row_end;
+    const int pc = ok ? p : row_end - 1;
+    const int r = GATHER ? gather_slots[pc] / gather_k : pc;
+    const T* xp = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + g * M::KPACK;
+    f32x4_t acc[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    frag_t a0[STEPS][RB], x0[STEPS], a1[STEPS][RB], x1[STEPS];
+    auto load = [&](frag_t (&af)[STEPS][RB], frag_t (&xf)[STEPS], int64_t k0) {
+#pragma unroll
+      for (int s2 = 0; s2 < STEPS; ++s2) {
+        const int64_t k = k0 + s2 * M::KSTEP;
+        const bool in = k < kb1;
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+          af[s2][j] = in ? M::load(Ab + static_cast<int64_t>(16 * j + c) * K + k) : M::zero();
+        xf[s2] = (in && ok) ? M::load(xp + k) : M::zero();
+      }
+    };
+    auto mma = [&](const frag_t (&af)[STEPS][RB], const frag_t (&xf)[STEPS]) {
+#pragma unroll
+      for (int s2 = 0; s2 < STEPS; ++s2)
+#pragma unroll
+        for (int j = 0; j < RB; ++j) M::run(acc[j], af[s2][j], xf[s2]);
+    };
+    int64_t k0 = kb0;
+    if (k0 < kb1) load(a0, x0, k0);
+    while (k0 < kb1) {
+      if (k0 + KB < kb1) load(a1, x1, k0 + KB);
+      mma(a0, x0);
+      k0 += KB;
+      if (k0 >= kb1) break;
+      if (k0 + KB < kb1) load(a0, x0, k0 + KB);
+      mma(a1, x1);
+      k0 += KB;
+    }
+    if (ok) {
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          atomic_add_relaxed(Z + static_cast<int64_t>(p) * R + 16 * j + 4 * g + i, acc[j][i]);
+    }
+  }
+}
+
 // --------------------------------------------------------------------- expand
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
 // Each wave owns NB blocks of 16 output columns (and, for gate_up, the
 // matching up columns I + n).  Its B^T fragments are loaded once and reused
-// for every 16-row block of the tile.
+// for every 16-row block of the tile.  The base values the epilogue adds to
+// (G for gate_up, D for down) and the next block's z are loaded before the
+// current block's MFMAs, so a wave never waits on two memory round trips in a
+// row.
 // GATE_UP: ACT[p][i] = SiLU(G[p][i] + z_p.B[i]) * (G[p][I+i] + z_p.B[I+i])
 //          (ncols = I, B^T has 2I rows)
 // down:    D[p][n] += z_p.B[n] (ncols = h)
-template <typename T, int R, int NB, bool GATE_UP>
+// DB: double-buffer the row blocks (tiles of many rows); otherwise one block
+// buffer, whose first fetch still overlaps the weight loads.
+template <typename T, int R, int NB, bool GATE_UP, bool DB>
 __global__ void __launch_bounds__(kLoraThreads)
 k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L,
          const float* __restrict__ G, T* __restrict__ ACT, float* __restrict__ D, int64_t ncols,
@@ -162,13 +244,16 @@ k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L,
   const int wave = threadIdx.x / kWave;
   const int c = lane & 15, g = lane >> 4;
   const int64_t c0 = (static_cast<int64_t>(chunk) * kLoraWaves + wave) * (16 * NB);
-  if (c0 >= ncols) return;  // ncols is a multiple of 16*NB: whole waves drop out
+  if (c0 >= ncols) return;  // ncols is a multiple of 16: blocks are whole or absent
   const int4 tile = ltiles[lt];
   const int b = tile.x, row0 = tile.y, row_end = tile.z;
   const int e = b / L, l = b % L;
 
   const int64_t nfull = GATE_UP ? 2 * ncols : ncols;
   const T* Bb = Bt + (static_cast<int64_t>(l) * E + e) * nfull * R;
+  bool nb_ok[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) nb_ok[j] = c0 + 16 * j < ncols;  // uniform per wave
   frag_t bf[NH][NB][KS];
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh)
@@ -178,20 +263,37 @@ k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L,
       for (int ks = 0; ks < KS; ++ks) {
         const int q = ks * M::KSTEP + g * M::KPACK;
         const int64_t n = hh * ncols + c0 + 16 * j + c;
-        bf[hh][j][ks] = q < R ? M::load(Bb + n * R + q) : M::zero();
+        bf[hh][j][ks] = (q < R && nb_ok[j]) ? M::load(Bb + n * R + q) : M::zero();
       }
 
-  for (int m0 = row0; m0 < row_end; m0 += 16) {
-    const int p = m0 + c;
+  // per 16-row block: z fragments and the four base values per column block
+  struct Block {
     ZFrag<T> zf[KS];
+    float4 base[NH][NB];
+  };
+  auto fetch = [&](Block& blk, int m0) {
+    const int p = m0 + c;
+    const bool ok = p < row_end;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int q = ks * M::KSTEP + g * M::KPACK;
-      if (p < row_end && q < R)
-        zf[ks].load(Z + static_cast<int64_t>(p) * R + q);
+      if (ok && q < R)
+        blk.zf[ks].load(Z + static_cast<int64_t>(p) * R + q);
       else
-        zf[ks].clear();
+        blk.zf[ks].clear();
     }
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int64_t n = hh * ncols + c0 + 16 * j + 4 * g;
+        const float* src = GATE_UP ? G + static_cast<int64_t>(p) * nfull + n
+                                   : D + static_cast<int64_t>(p) * ncols + n;
+        blk.base[hh][j] = (ok && nb_ok[j]) ? *reinterpret_cast<const float4*>(src)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+  };
+  auto run = [&](const Block& blk, int m0) {
     f32x4_t acc[NH][NB];
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh)
@@ -199,35 +301,49 @@ k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L,
       for (int j = 0; j < NB; ++j) {
         acc[hh][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) zf[ks].mma(acc[hh][j], bf[hh][j][ks]);
+        for (int ks = 0; ks < KS; ++ks) blk.zf[ks].mma(acc[hh][j], bf[hh][j][ks]);
       }
-    if (p < row_end) {
+    const int p = m0 + c;
+    if (p >= row_end) return;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int64_t n = c0 + 16 * j + 4 * g;  // 4 consecutive output columns
-        if (GATE_UP) {
-          const float* gr = G + static_cast<int64_t>(p) * nfull;
-          const float4 gg = *reinterpret_cast<const float4*>(gr + n);
-          const float4 gu = *reinterpret_cast<const float4*>(gr + ncols + n);
-          const float a0 = silu(gg.x + acc[0][j][0]) * (gu.x + acc[1][j][0]);
-          const float a1 = silu(gg.y + acc[0][j][1]) * (gu.y + acc[1][j][1]);
-          const float a2 = silu(gg.z + acc[0][j][2]) * (gu.z + acc[1][j][2]);
-          const float a3 = silu(gg.w + acc[0][j][3]) * (gu.w + acc[1][j][3]);
-          T* o = ACT + static_cast<int64_t>(p) * ncols + n;
-          o[0] = from_f32<T>(a0);
-          o[1] = from_f32<T>(a1);
-          o[2] = from_f32<T>(a2);
-          o[3] = from_f32<T>(a3);
-        } else {
-          float4* dr = reinterpret_cast<float4*>(D + static_cast<int64_t>(p) * ncols + n);
-          float4 d = *dr;
-          d.x += acc[0][j][0];
-          d.y += acc[0][j][1];
-          d.z += acc[0][j][2];
-          d.w += acc[0][j][3];
-          *dr = d;
-        }
+    for (int j = 0; j < NB; ++j) {
+      if (!nb_ok[j]) continue;
+      const int64_t n = c0 + 16 * j + 4 * g;  // 4 consecutive output columns
+      if (GATE_UP) {
+        const float4 gg = blk.base[0][j], gu = blk.base[NH - 1][j];
+        const float a0 = silu(gg.x + acc[0][j][0]) * (gu.x + acc[NH - 1][j][0]);
+        const float a1 = silu(gg.y + acc[0][j][1]) * (gu.y + acc[NH - 1][j][1]);
+        const float a2 = silu(gg.z + acc[0][j][2]) * (gu.z + acc[NH - 1][j][2]);
+        const float a3 = silu(gg.w + acc[0][j][3]) * (gu.w + acc[NH - 1][j][3]);
+        T* o = ACT + static_cast<int64_t>(p) * ncols + n;
+        o[0] = from_f32<T>(a0);
+        o[1] = from_f32<T>(a1);
+        o[2] = from_f32<T>(a2);
+        o[3] = from_f32<T>(a3);
+      } else {
+        const float4 d = blk.base[0][j];
+        *reinterpret_cast<float4*>(D + static_cast<int64_t>(p) * ncols + n) =
+            make_float4(d.x + acc[0][j][0], d.y + acc[0][j][1], d.z + acc[0][j][2],
+                        d.w + acc[0][j][3]);
       }
+    }
+  };
+
+  if (DB) {
+    Block cur, nxt;
+    fetch(cur, row0);
+    for (int m0 = row0; m0 < row_end; m0 += 32) {
+      if (m0 + 16 < row_end) fetch(nxt, m0 + 16);
+      run(cur, m0);
+      if (m0 + 16 >= row_end) break;
+      if (m0 + 32 < row_end) fetch(cur, m0 + 32);
+      run(nxt, m0 + 16);
+    }
+  } else {
+    Block blk;
+    for (int m0 = row0; m0 < row_end; m0 += 16) {
+      fetch(blk, m0);
+      run(blk, m0);
     }
   }
 }
@@ -258,13 +374,31 @@ k_combine(const float* __restrict__ D, const int32_t* __restrict__ pos, const fl
 }
 
 // -------------------------------------------------------------------- launchers
-constexpr int kExpandNB = 4;  // 16-column blocks per wave: 64 columns, 256 per workgroup
+// 16-column blocks per wave: gate_up carries gate and up halves, so 4 blocks
+// (64 + 64 columns); down takes 8 blocks for r <= 32
+template <int R, bool GU> constexpr int expand_nb() { return (GU || R > 32) ? 4 : 8; }
 
 template <typename T, int R, bool GATHER>
 static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
                                 const int32_t* gather_slots, int gather_k, const void* At, int E,
                                 int L, int64_t K, float* Z, const int4* ltiles,
                                 const int32_t* counts, hipStream_t stream) {
+  if (plan.lora_db) {
+    // tall tiles: ~1024 workgroups, each wave a 16-row block over the split's K range
+    constexpr int STEPS = R > 32 ? 2 : 4;
+    constexpr int64_t KB = STEPS * Mfma16<T>::KSTEP;
+    int64_t nsplit = 1024 / std::max(1, plan.max_lt);
+    nsplit = std::max<int64_t>(1, std::min<int64_t>(nsplit, K / (4 * KB)));
+    int64_t kwg = (K + nsplit - 1) / nsplit;
+    kwg = (kwg + KB - 1) / KB * KB;
+    nsplit = (K + kwg - 1) / kwg;
+    const int64_t grid = static_cast<int64_t>(plan.max_lt) * nsplit;
+    hipLaunchKernelGGL((k_shrink_tall<T, R, STEPS, GATHER>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kLoraThreads), 0, stream, static_cast<const T*>(X), x_rows,
+                       gather_slots, gather_k, static_cast<const T*>(At), E, L, K, kwg,
+                       static_cast<int>(nsplit), Z, ltiles, counts);
+    return hipGetLastError();
+  }
   constexpr int STEPS = R <= 32 ? 8 : 4;
   constexpr int KW = STEPS * Mfma16<T>::KSTEP;
   const int nsplit = static_cast<int>((K + kLoraWaves * KW - 1) / (kLoraWaves * KW));
@@ -304,12 +438,18 @@ template <typename T, int R, bool GU>
 static hipError_t expand_launch(const TilePlan& plan, const float* Z, const void* Bt, int E, int L,
                                 const float* G, void* ACT, float* D, int64_t ncols,
                                 const int4* ltiles, const int32_t* counts, hipStream_t stream) {
-  constexpr int COLS = kLoraWaves * 16 * kExpandNB;
+  constexpr int NB = expand_nb<R, GU>();
+  constexpr int COLS = kLoraWaves * 16 * NB;
   const int n_chunks = static_cast<int>((ncols + COLS - 1) / COLS);
   const int64_t grid = static_cast<int64_t>(plan.max_lt) * n_chunks;
-  hipLaunchKernelGGL((k_expand<T, R, kExpandNB, GU>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kLoraThreads), 0, stream, Z, static_cast<const T*>(Bt), E, L, G,
-                     static_cast<T*>(ACT), D, ncols, ltiles, counts, n_chunks);
+  if (plan.lora_db)
+    hipLaunchKernelGGL((k_expand<T, R, NB, GU, true>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kLoraThreads), 0, stream, Z, static_cast<const T*>(Bt), E, L, G,
+                       static_cast<T*>(ACT), D, ncols, ltiles, counts, n_chunks);
+  else
+    hipLaunchKernelGGL((k_expand<T, R, NB, GU, false>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kLoraThreads), 0, stream, Z, static_cast<const T*>(Bt), E, L, G,
+                       static_cast<T*>(ACT), D, ncols, ltiles, counts, n_chunks);
   return hipGetLastError();
 }
 

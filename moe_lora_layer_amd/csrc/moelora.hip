@@ -58,6 +58,7 @@ TilePlan make_plan(const moelora_dims* d) {
     if (wgs >= 256) return 1;
     return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((1024 + wgs - 1) / wgs, steps / 8)));
   };
+  p.lora_db = S / std::max<int64_t>(1, std::min<int64_t>(nb, S)) > 16;
   p.ksplit_gu = splits(2 * d->intermediate, d->hidden);
   p.ksplit_dn = splits(d->hidden, d->intermediate);
   return p;
