@@ -160,8 +160,10 @@ int moelora_forward(const moelora_dims* dims, const void* x, const void* w_gate_
  * Stages of moelora_forward, in launch order (one kernel each).
  */
 enum moelora_stage {
-  MOELORA_STAGE_PREP = 0,        /* inverse permutation and tile lists              */
-  MOELORA_STAGE_ZERO = 1,        /* clear the shrink accumulators                    */
+  MOELORA_STAGE_PREP = 0,        /* inverse permutation, tile lists, clear the shrink
+                                    accumulators                                     */
+  MOELORA_STAGE_ZERO = 1,        /* clear the gate_up output when its GEMM is split
+                                    over K (empty otherwise)                          */
   MOELORA_STAGE_GEMM_GATE_UP = 2,
   MOELORA_STAGE_SHRINK_GATE_UP = 3,
   MOELORA_STAGE_EXPAND_GATE_UP = 4,  /* + base add + SiLU-mul                        */
@@ -175,10 +177,12 @@ enum moelora_stage {
 /*
  * moelora_forward with per-stage timing for profilers and benchmarks.
  * stage_events: NULL, or MOELORA_NUM_STAGES + 1 hipEvent_t handles created by
- * the caller; event i is recorded on `stream` before stage i is launched and
- * event MOELORA_NUM_STAGES after the last stage, so the elapsed time between
- * events i and i+1 is the duration of stage i.  Everything else is identical to
- * moelora_forward (which is this call with stage_events == NULL).
+ * the caller (any of them may be NULL: that boundary is not recorded); event i
+ * is recorded on `stream` before stage i is launched and event
+ * MOELORA_NUM_STAGES after the last stage, so the elapsed time between events
+ * i and i+1 is the duration of stage i.  Each recorded event adds a small gap
+ * on the stream.  Everything else is identical to moelora_forward (which is
+ * this call with stage_events == NULL).
  */
 int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void* w_gate_up,
                              const void* w_down, const void* a_gate_up, const void* b_gate_up,

@@ -13,7 +13,7 @@
 //      A wave walks its chunk 64 slots at a time; lanes with equal keys find
 //      each other with ballots, so every slot gets its rank among equal keys of
 //      lower index inside the chunk, and the chunk's per-bucket counts live in
-//      LDS (cnt[c][b]);
+//      LDS (cnt[c][b]); keys and ranks stay in LDS too when the batch is small;
 //   3. scan: bucket totals, a wavefront-level exclusive prefix scan over the
 //      buckets gives bucket_offsets, and cnt[c][b] becomes the first output
 //      position of chunk c's slots in bucket b;
@@ -28,12 +28,15 @@ namespace moelora {
 constexpr int kAlignThreads = 1024;
 constexpr int kMaxTopK = 8;
 
+// KEYS_LDS: the per-slot keys and ranks live in LDS after the counters (small
+// batches); otherwise in the workspace.
+template <bool KEYS_LDS>
 __global__ void __launch_bounds__(kAlignThreads)
 k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_ids, int T, int E,
         int k, int L, int chunks, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
         int32_t* __restrict__ sorted_slots, int32_t* __restrict__ offsets,
         int32_t* __restrict__ status, int32_t* __restrict__ ws_key, int32_t* __restrict__ ws_rank) {
-  extern __shared__ int cnt[];  // [chunks][nb]
+  extern __shared__ int cnt[];  // [chunks][nb], then (KEYS_LDS) key[S], rank[S]
   __shared__ int wave_tmp[16];
   __shared__ int bad;
 
@@ -43,6 +46,8 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
   const int nb = E * L;
   const int S = T * k;
 
+  int* key_buf = KEYS_LDS ? cnt + chunks * nb : ws_key;
+  int* rank_buf = KEYS_LDS ? cnt + chunks * nb + S : ws_rank;
   for (int i = tid; i < chunks * nb; i += kAlignThreads) cnt[i] = 0;
   if (tid == 0) bad = 0;
   __syncthreads();
@@ -96,7 +101,7 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
         int s = t * k + q;
         topk_ids[s] = id[q];
         topk_w[s] = ex[q] / sum;
-        ws_key[s] = id[q] * L + l;
+        key_buf[s] = id[q] * L + l;
       }
     }
   }
@@ -112,7 +117,7 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
     for (int base = c0; base < c1; base += kWave) {
       const int s = base + lane;
       const bool valid = s < c1;
-      const int key = valid ? ws_key[s] : -1;
+      const int key = valid ? key_buf[s] : -1;
       uint64_t remaining = __ballot(valid);
       uint64_t peers = 0;
       while (remaining) {
@@ -123,7 +128,7 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
         remaining &= ~m;
       }
       const int rank = __popcll(peers & lt_mask);
-      if (valid) ws_rank[s] = my_cnt[key] + rank;
+      if (valid) rank_buf[s] = my_cnt[key] + rank;
       __builtin_amdgcn_wave_barrier();
       if (valid && rank == 0) my_cnt[key] += __popcll(peers);
       __builtin_amdgcn_wave_barrier();
@@ -154,7 +159,7 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
   // ---- 4. scatter --------------------------------------------------------------
   for (int s = tid; s < S; s += kAlignThreads) {
     const int c = s / chunk_len;
-    const int dst = cnt[c * nb + ws_key[s]] + ws_rank[s];
+    const int dst = cnt[c * nb + key_buf[s]] + rank_buf[s];
     if (dst >= 0 && dst < S)
       sorted_slots[dst] = s;
     else
@@ -164,8 +169,13 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
   if (tid == 0 && status != nullptr) *status = bad;
 }
 
-int align_chunks(int nb) {
-  int c = kAlignLdsInts / nb;
+// Per-slot keys and ranks go to LDS when they fit beside at least one
+// chunk of counters.
+static bool keys_in_lds(int S, int nb) { return 2ll * S + nb <= kAlignLdsInts; }
+
+int align_chunks(int nb, int S) {
+  const int budget = keys_in_lds(S, nb) ? kAlignLdsInts - 2 * S : kAlignLdsInts;
+  int c = budget / nb;
   if (c > 16) c = 16;
   if (c < 1) c = 1;
   return c;
@@ -176,10 +186,18 @@ hipError_t launch_align(const float* logits, const int32_t* adapter_ids, int T, 
                         int32_t* offsets, int32_t* status, int32_t* ws_key, int32_t* ws_rank,
                         hipStream_t stream) {
   const int nb = E * L;
-  const int chunks = align_chunks(nb);
-  const size_t lds = static_cast<size_t>(chunks) * nb * sizeof(int);
-  hipLaunchKernelGGL(k_align, dim3(1), dim3(kAlignThreads), lds, stream, logits, adapter_ids, T, E,
-                     k, L, chunks, topk_ids, topk_w, sorted_slots, offsets, status, ws_key, ws_rank);
+  const int S = T * k;
+  const int chunks = align_chunks(nb, S);
+  const bool in_lds = keys_in_lds(S, nb);
+  const size_t lds = (static_cast<size_t>(chunks) * nb + (in_lds ? 2 * S : 0)) * sizeof(int);
+  if (in_lds)
+    hipLaunchKernelGGL(k_align<true>, dim3(1), dim3(kAlignThreads), lds, stream, logits,
+                       adapter_ids, T, E, k, L, chunks, topk_ids, topk_w, sorted_slots, offsets,
+                       status, ws_key, ws_rank);
+  else
+    hipLaunchKernelGGL(k_align<false>, dim3(1), dim3(kAlignThreads), lds, stream, logits,
+                       adapter_ids, T, E, k, L, chunks, topk_ids, topk_w, sorted_slots, offsets,
+                       status, ws_key, ws_rank);
   return hipGetLastError();
 }
 

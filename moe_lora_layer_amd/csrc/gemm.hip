@@ -51,9 +51,16 @@ __global__ void __launch_bounds__(kPrepThreads)
 k_prep(const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ offsets, int S,
        int E, int L, int bm, int bml, int max_mt, int max_lt, int32_t* __restrict__ pos,
        int4* __restrict__ mtiles, int4* __restrict__ ltiles, int32_t* __restrict__ counts,
-       int32_t* __restrict__ expert_tiles) {
+       int32_t* __restrict__ expert_tiles, float4* __restrict__ zero, int64_t zero_n4) {
   __shared__ int wave_tmp[16];
   const int tid = threadIdx.x;
+  if (blockIdx.x > 0) {  // the other workgroups clear the accumulator region
+    const int64_t stride = static_cast<int64_t>(gridDim.x - 1) * kPrepThreads;
+    for (int64_t i = (blockIdx.x - 1) * static_cast<int64_t>(kPrepThreads) + tid; i < zero_n4;
+         i += stride)
+      zero[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
   for (int p = tid; p < S; p += kPrepThreads) {
     const int s = sorted_slots[p];
     if (s >= 0 && s < S) pos[s] = p;
@@ -93,10 +100,15 @@ k_prep(const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ off
 
 hipError_t launch_prep(const int32_t* sorted_slots, const int32_t* offsets, int S, int E, int L,
                        const TilePlan& plan, int32_t* pos, int4* mtiles, int4* ltiles,
-                       int32_t* counts, int32_t* expert_tiles, hipStream_t stream) {
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, sorted_slots, offsets, S, E,
-                     L, plan.bm, plan.bml, plan.max_mt, plan.max_lt, pos, mtiles, ltiles, counts,
-                     expert_tiles);
+                       int32_t* counts, int32_t* expert_tiles, float* zero, int64_t zero_n,
+                       hipStream_t stream) {
+  const int64_t n4 = zero_n / 4;  // callers pass multiples of 4
+  int64_t zblocks = (n4 + kPrepThreads - 1) / kPrepThreads;
+  if (zblocks > 512) zblocks = 512;
+  hipLaunchKernelGGL(k_prep, dim3(static_cast<unsigned>(1 + zblocks)), dim3(kPrepThreads), 0,
+                     stream, sorted_slots, offsets, S, E, L, plan.bm, plan.bml, plan.max_mt,
+                     plan.max_lt, pos, mtiles, ltiles, counts, expert_tiles,
+                     reinterpret_cast<float4*>(zero), n4);
   return hipGetLastError();
 }
 

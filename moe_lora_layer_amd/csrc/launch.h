@@ -11,7 +11,7 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 
 // LDS ints available to the align kernel's per-chunk bucket counters.
 constexpr int kAlignLdsInts = 15360;
-int align_chunks(int nb);
+int align_chunks(int nb, int S);
 
 hipError_t launch_align(const float* logits, const int32_t* adapter_ids, int T, int E, int k,
                         int L, int32_t* topk_ids, float* topk_w, int32_t* sorted_slots,
@@ -33,10 +33,12 @@ struct TilePlan {
 
 // Inverse permutation pos[slot] = sorted position, the M-tile list (tiles of
 // plan.bm rows per expert, in expert order) with expert_tiles[e] = first tile
-// of expert e (expert_tiles[E] = tile count), and the LoRA tile list.
+// of expert e (expert_tiles[E] = tile count), and the LoRA tile list; the same
+// launch clears zero[0, zero_n) (a multiple of 4 floats).
 hipError_t launch_prep(const int32_t* sorted_slots, const int32_t* offsets, int S, int E, int L,
                        const TilePlan& plan, int32_t* pos, int4* mtiles, int4* ltiles,
-                       int32_t* counts, int32_t* expert_tiles, hipStream_t stream);
+                       int32_t* counts, int32_t* expert_tiles, float* zero, int64_t zero_n,
+                       hipStream_t stream);
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 

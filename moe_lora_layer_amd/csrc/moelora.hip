@@ -226,16 +226,16 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
 
   // event i is recorded right before stage i, the last one after the last stage
   auto mark = [&](int i) -> hipError_t {
-    if (stage_events == nullptr) return hipSuccess;
+    if (stage_events == nullptr || stage_events[i] == nullptr) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st);
   };
+  // the prep launch also clears Z1, Z2 (and D when the down GEMM is split)
+  const int64_t nzero = 2ll * S * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * h : 0);
   hipError_t e = mark(MOELORA_STAGE_PREP);
   if (e == hipSuccess)
     e = moelora::launch_prep(sorted_slots, bucket_offsets, S, E, Lad, plan, pos, mtiles, ltiles,
-                             counts, etiles, st);
+                             counts, etiles, Z1, nzero, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_ZERO);
-  const int64_t nzero = 2ll * S * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * h : 0);
-  if (e == hipSuccess) e = moelora::launch_zero(Z1, nzero, st);
   if (e == hipSuccess && plan.ksplit_gu > 1)
     e = moelora::launch_zero(G, static_cast<int64_t>(S) * 2 * I, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);

@@ -166,8 +166,8 @@ def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
             sorted_slots, bucket_offsets, *, out=None, workspace_buf=None, stream=None,
             stage_events=None):
     """moelora_forward (moelora_forward_profiled when stage_events, a list of
-    len(STAGES) + 1 recorded-once torch.cuda.Event(enable_timing=True), is given).
-    Returns out [T][h]."""
+    len(STAGES) + 1 recorded-once torch.cuda.Event(enable_timing=True) or None,
+    is given).  Returns out [T][h]."""
     dev = x.device
     T, h, I, E, k, L, r = d.tokens, d.hidden, d.intermediate, d.experts, d.top_k, d.adapters, d.rank
     dt = _TORCH_DT[d.dtype]
@@ -195,9 +195,10 @@ def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
     else:
         if len(stage_events) != len(STAGES) + 1:
             raise ValueError(f"need {len(STAGES) + 1} events")
-        handles = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
-        if any(not h for h in handles):
+        hs = [None if ev is None else ev.cuda_event for ev in stage_events]
+        if any(ev is not None and not h for ev, h in zip(stage_events, hs)):
             raise ValueError("record every event once before passing it (creates the handle)")
+        handles = (ctypes.c_void_p * len(hs))(*hs)
         _check(library().moelora_forward_profiled(*args, handles), "moelora_forward_profiled")
     return out
 
