@@ -401,6 +401,208 @@ static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, hipStream_
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------- prefill gemm
+// bf16 tiles of 256 x 256 outputs for M-tiles of 256 rows (many rows per
+// expert, so every weight tile is reused by several M-tiles and the GEMM is
+// bound by the matrix cores).  Eight waves (two per SIMD) of 128 x 64 outputs.
+// The K walk is staged in LDS in steps of 64 (128-byte rows) with two stages:
+// the operands go from global memory straight into LDS
+// (global_load_lds_dwordx4, no register round trip, no LDS store
+// instructions), and step kt+2 is requested as soon as every wave has read
+// step kt, so one step of loads is always in flight behind the MFMAs.  The
+// LDS rows keep the 16-byte-chunk XOR swizzle of the register-staged kernel:
+// a load instruction fills 8 whole rows, each lane fetching the global chunk
+// that belongs at its LDS position.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kDmaTile = 256;                   // BM = BN
+constexpr int kDmaRowB = 128;                   // bytes of K per LDS row (64 bf16)
+constexpr int kDmaStage = 2 * kDmaTile * kDmaRowB;  // A and B rows of one K-step: 64 KiB
+constexpr int kDmaThreads = 512;
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: expcnt and lgkmcnt at
+// their maximum), and the same with lgkmcnt(0)
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  constexpr int imm = (N & 15) | ((N >> 4) << 14) | 0x0F70;
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  constexpr int imm = (N & 15) | ((N >> 4) << 14) | 0x0070;
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// The four A and four B load instructions of one wave for K-step kt into
+// stage `slot` (8 rows of 128 bytes each).
+__device__ __forceinline__ void dma_issue(unsigned char* smem, int slot, int64_t ko,
+                                          const bf16_t* const* a_src, const bf16_t* const* b_src,
+                                          int wave) {
+  unsigned char* st = smem + slot * kDmaStage;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_global_load_lds(a_src[j] + ko,
+                                     (lds_void_t*)(st + (32 * wave + 8 * j) * kDmaRowB), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_global_load_lds(
+        b_src[j] + ko, (lds_void_t*)(st + (kDmaTile + 32 * wave + 8 * j) * kDmaRowB), 16, 0, 0);
+}
+
+template <bool GATHER>
+__global__ void __launch_bounds__(kDmaThreads)
+k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
+           int gather_k, const bf16_t* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
+           const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
+           const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDmaStage];
+  // workgroup order: as k_gemm (XCD remap over the real workgroups, then per
+  // expert N-tile by N-tile with its M-tiles innermost)
+  const int ks = static_cast<int>(blockIdx.x) % ksplit;
+  const int pid = static_cast<int>(blockIdx.x) / ksplit;
+  const int active = counts[0] * n_ntiles;
+  if (pid >= active) return;
+  const int xcd = pid % kXcds, q = active / kXcds, rem = active % kXcds;
+  const int bid = xcd * q + min(xcd, rem) + pid / kXcds;
+  const int t0 = bid / n_ntiles;
+  const int ex = mtiles[t0].x;
+  const int ta = expert_tiles[ex], tb = expert_tiles[ex + 1];
+  const int local = bid - ta * n_ntiles;
+  const int nt = local / (tb - ta);
+  const int mt = ta + local % (tb - ta);
+  const int4 tile = mtiles[mt];
+  const int e = tile.x, row0 = tile.y, row_end = tile.z;
+  const int64_t n0 = static_cast<int64_t>(nt) * kDmaTile;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int c32 = lane & 31, h = lane >> 5;
+
+  // Load instruction j of wave w fills tile rows 32w + 8j + lane/8 (A and B);
+  // the lane's LDS chunk is lane%8, so it fetches logical chunk
+  // (lane%8) ^ swz(row).  Rows past the tile's end (M) or past N read a valid
+  // clamped row: they only feed outputs that are never stored.
+  const bf16_t* a_src[4];
+  const bf16_t* b_src[4];
+  const bf16_t* We = Wt + static_cast<int64_t>(e) * N * K;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rt = 32 * wave + 8 * j + (lane >> 3);
+    const int lch = (lane & 7) ^ swz<1>(rt);
+    const int p = min(row0 + rt, row_end - 1);
+    const int r = GATHER ? gather_slots[p] / gather_k : p;
+    a_src[j] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + lch * 8;
+    b_src[j] = We + min(n0 + rt, N - 1) * K + lch * 8;
+  }
+  const int nk_all = static_cast<int>(K / 64);
+  const int nk_per = (nk_all + ksplit - 1) / ksplit;
+  const int kbeg = min(nk_all, ks * nk_per);
+  const int nk = min(nk_all, kbeg + nk_per) - kbeg;
+  if (nk <= 0) return;  // uniform: an empty K split (only for tiny K)
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = zero_acc();
+
+  // fragment reads: substep s (16 of the 64 K) of row r = 128 wm + 32 i + c32;
+  // (r >> 1) & 7 depends on c32 only
+  const int sw = swz<1>(c32);
+  const int a_off = (wm * 128 + c32) * kDmaRowB;
+  const int b_off = (kDmaTile + wn * 64 + c32) * kDmaRowB;
+  bf16x8_t fa[2][4], fb[2][2];
+  auto rd = [&](int f, const unsigned char* st, int s) {
+    const int ch = ((2 * s + h) ^ sw) << 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[f][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * kDmaRowB + ch);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      fb[f][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * kDmaRowB + ch);
+  };
+  auto mm = [&](int f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+  };
+  // workgroup barrier that orders LDS accesses only; the DMA is waited for
+  // explicitly with vmcnt
+  auto bar = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  auto ko = [&](int kt) { return static_cast<int64_t>(kbeg + kt) * 64; };
+
+  // K-step kt lives in stage kt % 2.  Both stages are requested up front;
+  // steps past the end repeat the last one (never read), which keeps the
+  // vmcnt accounting the same in every iteration.
+  dma_issue(smem, 0, ko(0), a_src, b_src, wave);
+  dma_issue(smem, 1, ko(min(1, nk - 1)), a_src, b_src, wave);
+  wait_vmcnt<8>();  // this wave's loads of step 0 are in LDS
+  bar();            // ... and every other wave's
+  rd(0, smem, 0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing scalar or LDS pending into the loop
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const unsigned char* cur = smem + (kt & 1) * kDmaStage;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      rd((s + 1) & 1, cur, s + 1);
+      mm(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // step kt+1 has landed and every wave has finished reading step kt
+    // (lgkmcnt(0) before the barrier): refill that stage with step kt+2
+    wait_vmcnt_lgkm0<0>();
+    bar();
+    dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
+    rd(0, smem + ((kt + 1) & 1) * kDmaStage, 0);
+    mm(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    const unsigned char* cur = smem + ((nk - 1) & 1) * kDmaStage;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      rd((s + 1) & 1, cur, s + 1);
+      mm(s & 1);
+    }
+    mm(1);
+  }
+  wait_vmcnt<0>();  // no LDS write of this workgroup may outlive it
+
+  auto store = [&](auto&& put) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + wn * 64 + j * 32 + c32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = row0 + wm * 128 + i * 32 + acc_row(r, h);
+          if (p < row_end && n < N) put(C + static_cast<int64_t>(p) * N + n, acc[i][j][r]);
+        }
+      }
+  };
+  if (ksplit > 1)
+    store([](float* dst, float v) { atomic_add_relaxed(dst, v); });
+  else
+    store([](float* dst, float v) { *dst = v; });
+}
+
+template <bool GATHER>
+static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
+  const int n_ntiles = static_cast<int>((a.N + kDmaTile - 1) / kDmaTile);
+  const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
+  hipLaunchKernelGGL((k_gemm_dma<GATHER>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads), 0,
+                     stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
+                     static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
+                     a.expert_tiles, n_ntiles, a.ksplit);
+  return hipGetLastError();
+}
+
 template <typename T, bool GATHER>
 static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
   // decode-sized M-tiles stream the weights: nontemporal loads, rotated K walk
@@ -411,7 +613,8 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStre
       if (plan.stream)
         return lds_launch<T, 128, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
       return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, stream);
-    case 256:  // prefill: 256x256 tiles, 8 waves of 128x64, one barrier per K-step
+    case 256:  // prefill: 256x256 tiles, 8 waves of 128x64 (bf16: operands DMA'd into LDS)
+      if (sizeof(T) == 2) return dma_launch<GATHER>(plan, a, stream);
       return lds_launch<T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, stream);
     default: return hipErrorInvalidValue;
   }
