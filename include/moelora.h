@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOELORA_ABI_VERSION 1
+#define MOELORA_ABI_VERSION 2
 
 typedef enum moelora_status {
   MOELORA_OK = 0,
@@ -164,12 +164,13 @@ enum moelora_stage {
                                     accumulators                                     */
   MOELORA_STAGE_ZERO = 1,        /* clear the gate_up output when its GEMM is split
                                     over K (empty otherwise)                          */
-  MOELORA_STAGE_GEMM_GATE_UP = 2,
-  MOELORA_STAGE_SHRINK_GATE_UP = 3,
-  MOELORA_STAGE_EXPAND_GATE_UP = 4,  /* + base add + SiLU-mul                        */
-  MOELORA_STAGE_GEMM_DOWN = 5,
-  MOELORA_STAGE_SHRINK_DOWN = 6,
-  MOELORA_STAGE_EXPAND_DOWN = 7,
+  MOELORA_STAGE_SHRINK_GATE_UP = 2,
+  MOELORA_STAGE_GEMM_GATE_UP = 3,    /* with the plan of 256-row bf16 tiles and unsplit
+                                        K, also the LoRA expand and the SiLU-mul      */
+  MOELORA_STAGE_EXPAND_GATE_UP = 4,  /* + base add + SiLU-mul; empty when fused       */
+  MOELORA_STAGE_SHRINK_DOWN = 5,
+  MOELORA_STAGE_GEMM_DOWN = 6,       /* fused LoRA expand under the same condition   */
+  MOELORA_STAGE_EXPAND_DOWN = 7,     /* empty when fused                              */
   MOELORA_STAGE_COMBINE = 8,
   MOELORA_NUM_STAGES = 9
 };
@@ -195,7 +196,10 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
  * Debug aid for layer-by-layer reconciliation: byte offsets, inside the forward
  * workspace, of the intermediates left there by moelora_forward, all indexed by
  * sorted position p (row p belongs to slot sorted_slots[p]):
- *   offsets[0]  G   float [T*k][2I]  gate_up base output xW (before the LoRA add)
+ *   offsets[0]  G   float [T*k][2I]  gate_up base output xW (before the LoRA add);
+ *                                    not written when the gate_up GEMM fuses the
+ *                                    expand (bf16, 256-row tiles, unsplit K: more
+ *                                    than about 200 rows per expert)
  *   offsets[1]  Z1  float [T*k][r]   gate_up shrink xA
  *   offsets[2]  ACT dtype [T*k][I]   SiLU(gate) * up, including both LoRA terms
  *   offsets[3]  Z2  float [T*k][r]   down shrink a A

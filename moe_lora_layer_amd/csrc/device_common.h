@@ -107,6 +107,29 @@ template <> struct Mfma16<float> {
   __device__ __forceinline__ static frag_t zero() { return 0.0f; }
 };
 
+// SiLU(v) = v / (1 + e^-v), with the device expf.
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+// Eight fp32 values as two bf16 fragments with v ~= hi + lo (about 16
+// significant bits): a bf16 MFMA against hi and then lo keeps fp32-like
+// precision for the small rank-r operand of the LoRA expand.
+__device__ __forceinline__ void split_bf16x8(const float* v8, bf16x8_t& hi, bf16x8_t& lo) {
+  const float4 a = *reinterpret_cast<const float4*>(v8);
+  const float4 b = *reinterpret_cast<const float4*>(v8 + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+    const bf16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
+    const bf16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
+    hw[i] = h0 | (static_cast<uint32_t>(h1) << 16);
+    lw[i] = l0 | (static_cast<uint32_t>(l1) << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+  lo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+}
+
 // Row (within the 32x32 block) of accumulator element i held by a lane of half h.
 __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 

@@ -448,12 +448,23 @@ __device__ __forceinline__ void dma_issue(unsigned char* smem, int slot, int64_t
         b_src[j] + ko, (lds_void_t*)(st + (kDmaTile + 32 * wave + 8 * j) * kDmaRowB), 16, 0, 0);
 }
 
-template <bool GATHER>
+// Epilogue of the prefill GEMM.  EPI_STORE writes the fp32 tile to C
+// (relaxed atomics under split K).  The two fused forms add the LoRA expand of
+// the tile's rows to the accumulators first: for every (expert, adapter)
+// bucket that meets a wave's 128 rows, acc += z_rows . B[l][e]^T on the MFMA
+// units, z (fp32, from the shrink) split into bf16 hi + lo and the rows
+// outside the bucket masked to zero.  EPI_GATE_UP then applies SiLU(gate) * up
+// and writes bf16 ACT; EPI_DOWN writes D.  The vLLM blog page "Multi-LoRA"
+// (section "Implementing Multi-LoRA inference for MoE models in vLLM") lists
+// folding the LoRA add into the base GEMM's output as the next fusion step.
+enum { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_DOWN = 2 };
+
+template <bool GATHER, int EPI>
 __global__ void __launch_bounds__(kDmaThreads)
 k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
            int gather_k, const bf16_t* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
            const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
-           const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit) {
+           const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, LoraEpilogue lora) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDmaStage];
   // workgroup order: as k_gemm (XCD remap over the real workgroups, then per
   // expert N-tile by N-tile with its M-tiles innermost)
@@ -471,7 +482,13 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   const int mt = ta + local % (tb - ta);
   const int4 tile = mtiles[mt];
   const int e = tile.x, row0 = tile.y, row_end = tile.z;
-  const int64_t n0 = static_cast<int64_t>(nt) * kDmaTile;
+  // Output columns.  EPI_GATE_UP: the tile covers 128 columns i of the
+  // intermediate width I = N/2; wave column group wn owns i in
+  // [128 nt + 32 wn, +32), as weight rows i (gate, fragment j = 0) and I + i
+  // (up, j = 1), so gate and up of one output meet in the same lane.
+  // Otherwise 256 columns n of N, wave wn owning [256 nt + 64 wn, +64).
+  const int64_t I = N / 2;
+  const int64_t n0 = static_cast<int64_t>(nt) * (EPI == EPI_GATE_UP ? 128 : kDmaTile);
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave >> 2, wn = wave & 3;
@@ -491,7 +508,14 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     const int p = min(row0 + rt, row_end - 1);
     const int r = GATHER ? gather_slots[p] / gather_k : p;
     a_src[j] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + lch * 8;
-    b_src[j] = We + min(n0 + rt, N - 1) * K + lch * 8;
+    int64_t wrow;
+    if (EPI == EPI_GATE_UP) {  // B tile row rt = 64 wn' + 32 half + c
+      const int64_t i = min(n0 + 32 * (rt >> 6) + (rt & 31), I - 1);
+      wrow = ((rt >> 5) & 1) * I + i;
+    } else {
+      wrow = min(n0 + rt, N - 1);
+    }
+    b_src[j] = We + wrow * K + lch * 8;
   }
   const int nk_all = static_cast<int>(K / 64);
   const int nk_per = (nk_all + ksplit - 1) / ksplit;
@@ -573,18 +597,88 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   }
   wait_vmcnt<0>();  // no LDS write of this workgroup may outlive it
 
+  // output column of fragment j held by this lane, and its LoRA B row
+  int64_t col[2], brow[2];
+  bool col_ok[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (EPI == EPI_GATE_UP) {
+      col[j] = n0 + 32 * wn + c32;
+      col_ok[j] = col[j] < I;
+      brow[j] = j * I + col[j];
+    } else {
+      col[j] = n0 + 64 * wn + 32 * j + c32;
+      col_ok[j] = col[j] < N;
+      brow[j] = col[j];
+    }
+  }
+  const int rw0 = row0 + 128 * wm;                 // this wave's rows [rw0, rw1)
+  const int rw1 = min(row_end, rw0 + 128);
+
+  if (EPI != EPI_STORE && rw0 < rw1) {
+    const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.adapters;
+    // last bucket of expert e starting at or before rw0
+    int lb = 0, ub = lora.adapters - 1;
+    while (lb < ub) {
+      const int mid = (lb + ub + 1) >> 1;
+      if (off[mid] <= rw0) lb = mid; else ub = mid - 1;
+    }
+    const int nks = lora.rank / 16;
+    for (int l = lb; l < lora.adapters && off[l] < rw1; ++l) {
+      const int s0 = max(rw0, off[l]), s1 = min(rw1, off[l + 1]);
+      if (s0 >= s1) continue;  // uniform: an empty bucket
+      const bf16_t* Bb = lora.b + (static_cast<int64_t>(l) * lora.experts + e) * lora.b_rows * lora.rank;
+      bf16x8_t bfr[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          bfr[j][q4] = (q4 < nks && col_ok[j])
+                           ? *reinterpret_cast<const bf16x8_t*>(Bb + brow[j] * lora.rank + 16 * q4 + 8 * h)
+                           : Mfma<bf16_t>::zero();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rb = rw0 + 32 * i;
+        if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
+        const int p = rb + c32;
+        const bool in = p >= s0 && p < s1;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if (q4 >= nks) break;
+          bf16x8_t zh = Mfma<bf16_t>::zero(), zl = zh;
+          if (in) split_bf16x8(lora.z + static_cast<int64_t>(p) * lora.rank + 16 * q4 + 8 * h, zh, zl);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zh, bfr[j][q4], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zl, bfr[j][q4], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  if (EPI == EPI_GATE_UP) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = rw0 + 32 * i + acc_row(r, h);
+        if (p < row_end && col_ok[0])
+          lora.act[static_cast<int64_t>(p) * I + col[0]] =
+              f32_to_bf16(silu(acc[i][0][r]) * acc[i][1][r]);
+      }
+    return;
+  }
   auto store = [&](auto&& put) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + wn * 64 + j * 32 + c32;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int p = row0 + wm * 128 + i * 32 + acc_row(r, h);
-          if (p < row_end && n < N) put(C + static_cast<int64_t>(p) * N + n, acc[i][j][r]);
+          const int p = rw0 + 32 * i + acc_row(r, h);
+          if (p < row_end && col_ok[j]) put(C + static_cast<int64_t>(p) * N + col[j], acc[i][j][r]);
         }
-      }
   };
   if (ksplit > 1)
     store([](float* dst, float v) { atomic_add_relaxed(dst, v); });
@@ -592,19 +686,23 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     store([](float* dst, float v) { *dst = v; });
 }
 
-template <bool GATHER>
-static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
-  const int n_ntiles = static_cast<int>((a.N + kDmaTile - 1) / kDmaTile);
+template <bool GATHER, int EPI>
+static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue& lora,
+                             hipStream_t stream) {
+  const int64_t cols = EPI == EPI_GATE_UP ? a.N / 2 : a.N;
+  const int tn = EPI == EPI_GATE_UP ? 128 : kDmaTile;
+  const int n_ntiles = static_cast<int>((cols + tn - 1) / tn);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
-  hipLaunchKernelGGL((k_gemm_dma<GATHER>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads), 0,
-                     stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
+  hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
+                     0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
-                     a.expert_tiles, n_ntiles, a.ksplit);
+                     a.expert_tiles, n_ntiles, a.ksplit, lora);
   return hipGetLastError();
 }
 
 template <typename T, bool GATHER>
-static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
+static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue* lora,
+                                hipStream_t stream) {
   // decode-sized M-tiles stream the weights: nontemporal loads, rotated K walk
   switch (plan.bm) {
     case 32: return lds_launch<T, 32, 128, 1, 4, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
@@ -614,7 +712,11 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStre
         return lds_launch<T, 128, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
       return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, stream);
     case 256:  // prefill: 256x256 tiles, 8 waves of 128x64 (bf16: operands DMA'd into LDS)
-      if (sizeof(T) == 2) return dma_launch<GATHER>(plan, a, stream);
+      if (sizeof(T) == 2) {
+        if (lora == nullptr) return dma_launch<GATHER, EPI_STORE>(plan, a, LoraEpilogue{}, stream);
+        if (lora->act != nullptr) return dma_launch<GATHER, EPI_GATE_UP>(plan, a, *lora, stream);
+        return dma_launch<GATHER, EPI_DOWN>(plan, a, *lora, stream);
+      }
       return lds_launch<T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, stream);
     default: return hipErrorInvalidValue;
   }
@@ -623,15 +725,19 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, hipStre
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, const int4* mtiles, const int32_t* counts,
-                       const int32_t* expert_tiles, int ksplit, hipStream_t stream) {
+                       const int32_t* expert_tiles, int ksplit, const LoraEpilogue* lora,
+                       hipStream_t stream) {
   const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts, expert_tiles,
                    ksplit < 1 ? 1 : ksplit};
   const bool gather = gather_slots != nullptr;
+  // the fused epilogues exist only in the bf16 256-row kernel, unsplit
+  if (lora != nullptr && (dtype != DT_BF16 || plan.bm != 256 || a.ksplit != 1))
+    return hipErrorInvalidValue;
   if (dtype == DT_BF16)
-    return gather ? gemm_dispatch<bf16_t, true>(plan, a, stream)
-                  : gemm_dispatch<bf16_t, false>(plan, a, stream);
-  return gather ? gemm_dispatch<float, true>(plan, a, stream)
-                : gemm_dispatch<float, false>(plan, a, stream);
+    return gather ? gemm_dispatch<bf16_t, true>(plan, a, lora, stream)
+                  : gemm_dispatch<bf16_t, false>(plan, a, lora, stream);
+  return gather ? gemm_dispatch<float, true>(plan, a, nullptr, stream)
+                : gemm_dispatch<float, false>(plan, a, nullptr, stream);
 }
 
 }  // namespace moelora

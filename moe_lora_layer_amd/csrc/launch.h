@@ -29,6 +29,21 @@ struct TilePlan {
   int ksplit_gu; // K splits of the gate_up GEMM (1 = none)
   int ksplit_dn; // K splits of the down GEMM (1 = none)
   bool lora_db;  // LoRA tiles average many rows: double-buffer their row blocks
+  bool fuse_gu;  // gate_up GEMM applies the LoRA expand and SiLU-mul in its epilogue
+  bool fuse_dn;  // down GEMM applies the LoRA expand in its epilogue
+};
+
+// Operands of the LoRA expand fused into a base GEMM's epilogue:
+// acc[p][n] += z[p] . b[l][e][n] for the rows p of bucket (e, l).
+// act == nullptr: down form (the GEMM writes D); otherwise gate_up form
+// (the GEMM writes act[p][i] = SiLU(g) * u in bf16, intermediate width N/2).
+struct LoraEpilogue {
+  const float* z;           // [S][rank] fp32, sorted order
+  const uint16_t* b;        // [L][E][b_rows][rank] bf16
+  const int32_t* offsets;   // bucket_offsets [E*L + 1]
+  int experts, adapters, rank;
+  int64_t b_rows;           // rows of each B block (2I for gate_up, h for down)
+  uint16_t* act;            // bf16 [S][I] output of the gate_up form, else nullptr
 };
 
 // Inverse permutation pos[slot] = sorted position, the M-tile list (tiles of
@@ -45,11 +60,14 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 // C[p][n] = sum_k X[row(p)][k] * Wt[e][n][k] over the M-tiles of `mtiles`;
 // row(p) = gather_slots[p] / gather_k when gather_slots != nullptr, else p,
 // clamped to [0, x_rows).  ksplit > 1 splits K over workgroups that add into
-// C with fp32 atomics (C must be zero beforehand).
+// C with fp32 atomics (C must be zero beforehand).  lora != nullptr fuses the
+// LoRA expand (and for gate_up the SiLU-mul) into the epilogue; only the bf16
+// 256-row plan with ksplit == 1 has it (hipErrorInvalidValue otherwise).
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, const int4* mtiles, const int32_t* counts,
-                       const int32_t* expert_tiles, int ksplit, hipStream_t stream);
+                       const int32_t* expert_tiles, int ksplit, const LoraEpilogue* lora,
+                       hipStream_t stream);
 
 // Z[p][q] += sum_k X[row(p)][k] * At[l][e][q][k] over the LoRA tiles (split-K,
 // fp32 atomics).  Z must be zero beforehand.

@@ -34,22 +34,7 @@ constexpr int kLoraWaves = kLoraThreads / kWave;
 template <typename T> struct ZFrag;
 template <> struct ZFrag<bf16_t> {
   bf16x8_t hi, lo;
-  __device__ __forceinline__ void load(const float* z) {
-    const float4 a = *reinterpret_cast<const float4*>(z);
-    const float4 b = *reinterpret_cast<const float4*>(z + 4);
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
-      const bf16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
-      const bf16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
-      hw[i] = h0 | (static_cast<uint32_t>(h1) << 16);
-      lw[i] = l0 | (static_cast<uint32_t>(l1) << 16);
-    }
-    hi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    lo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-  }
+  __device__ __forceinline__ void load(const float* z) { split_bf16x8(z, hi, lo); }
   __device__ __forceinline__ void clear() { hi = Mfma16<bf16_t>::zero(); lo = hi; }
   __device__ __forceinline__ void mma(f32x4_t& acc, bf16x8_t a) const {
     Mfma16<bf16_t>::run(acc, a, hi);
@@ -215,8 +200,6 @@ k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ g
 }
 
 // --------------------------------------------------------------------- expand
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
-
 // Each wave owns NB blocks of 16 output columns (and, for gate_up, the
 // matching up columns I + n).  Its B^T fragments are loaded once and reused
 // for every 16-row block of the tile.  The base values the epilogue adds to

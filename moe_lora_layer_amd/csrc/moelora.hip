@@ -61,6 +61,10 @@ TilePlan make_plan(const moelora_dims* d) {
   p.lora_db = S / std::max<int64_t>(1, std::min<int64_t>(nb, S)) > 16;
   p.ksplit_gu = splits(2 * d->intermediate, d->hidden);
   p.ksplit_dn = splits(d->hidden, d->intermediate);
+  // 256-row bf16 tiles run the LoRA expand in the GEMM epilogue (unsplit K)
+  const bool fusable = d->dtype == MOELORA_BF16 && p.bm == 256;
+  p.fuse_gu = fusable && p.ksplit_gu == 1;
+  p.fuse_dn = fusable && p.ksplit_dn == 1;
   return p;
 }
 
@@ -238,28 +242,36 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   if (e == hipSuccess) e = mark(MOELORA_STAGE_ZERO);
   if (e == hipSuccess && plan.ksplit_gu > 1)
     e = moelora::launch_zero(G, static_cast<int64_t>(S) * 2 * I, st);
-  if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);
-  if (e == hipSuccess)
-    e = moelora::launch_gemm(dt, plan, x, static_cast<int>(T), sorted_slots, k, w_gate_up, 2 * I,
-                             h, G, mtiles, counts, etiles, plan.ksplit_gu, st);
+  // shrinks run before their GEMMs: a fused GEMM epilogue consumes Z
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_GATE_UP);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, x, static_cast<int>(T), sorted_slots, k, a_gate_up, E,
                                Lad, h, Z1, ltiles, counts, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);
+  if (e == hipSuccess) {
+    const moelora::LoraEpilogue epi{Z1, static_cast<const uint16_t*>(b_gate_up), bucket_offsets,
+                                    E, Lad, r, 2 * I, static_cast<uint16_t*>(ACT)};
+    e = moelora::launch_gemm(dt, plan, x, static_cast<int>(T), sorted_slots, k, w_gate_up, 2 * I,
+                             h, G, mtiles, counts, etiles, plan.ksplit_gu,
+                             plan.fuse_gu ? &epi : nullptr, st);
+  }
   if (e == hipSuccess) e = mark(MOELORA_STAGE_EXPAND_GATE_UP);
-  if (e == hipSuccess)
+  if (e == hipSuccess && !plan.fuse_gu)
     e = moelora::launch_expand_gate_up(dt, r, plan, Z1, b_gate_up, E, Lad, G, ACT, I, ltiles,
                                        counts, st);
-  if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
-  if (e == hipSuccess)
-    e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, mtiles, counts, etiles,
-                             plan.ksplit_dn, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_DOWN);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, ACT, S, nullptr, 1, a_down, E, Lad, I, Z2, ltiles,
                                counts, st);
+  if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
+  if (e == hipSuccess) {
+    const moelora::LoraEpilogue epi{Z2, static_cast<const uint16_t*>(b_down), bucket_offsets,
+                                    E, Lad, r, h, nullptr};
+    e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, mtiles, counts, etiles,
+                             plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, st);
+  }
   if (e == hipSuccess) e = mark(MOELORA_STAGE_EXPAND_DOWN);
-  if (e == hipSuccess)
+  if (e == hipSuccess && !plan.fuse_dn)
     e = moelora::launch_expand_down(dt, r, plan, Z2, b_down, E, Lad, D, h, ltiles, counts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_COMBINE);
   if (e == hipSuccess)

@@ -18,8 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoelora.so")
 
 MOELORA_F32, MOELORA_BF16 = 0, 1
-STAGES = ["prep", "zero", "gemm_gate_up", "shrink_gate_up", "expand_gate_up", "gemm_down",
-          "shrink_down", "expand_down", "combine"]
+STAGES = ["prep", "zero", "shrink_gate_up", "gemm_gate_up", "expand_gate_up", "shrink_down",
+          "gemm_down", "expand_down", "combine"]
 _TORCH_DT = {MOELORA_F32: torch.float32, MOELORA_BF16: torch.bfloat16}
 _DT_NAME = {"f32": MOELORA_F32, "bf16": MOELORA_BF16}
 

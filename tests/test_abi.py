@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     assert {"moelora_align", "moelora_forward"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moelora_abi_version() == 1
+    assert lib.moelora_abi_version() == 2
 
 
 def test_status_strings():

@@ -44,9 +44,14 @@ SMALL = [
     (33, 128, 64, 3, 3, 2, 16, "bf16"),
     (1, 64, 64, 4, 2, 2, 64, "bf16"),
     (7, 64, 128, 1, 1, 3, 16, "f32"),
-    # > 200 rows per expert: 256-row tiles (N tails: 2I = 384, h = 128)
+    # > 200 rows per expert: 256-row tiles (N tails: 2I = 384, h = 128); in bf16
+    # the LoRA expand (and SiLU-mul) runs in the GEMM epilogue: I and h tails,
+    # ranks 16/32/64, many adapter buckets per tile, one expert with 16 adapters
     (600, 128, 192, 4, 2, 3, 16, "bf16"),
     (600, 192, 128, 4, 2, 2, 32, "f32"),
+    (700, 256, 320, 3, 2, 5, 32, "bf16"),
+    (520, 192, 256, 2, 1, 9, 64, "bf16"),
+    (300, 128, 256, 1, 1, 16, 16, "bf16"),
     # one expert, narrow output: split-K with atomics in the down GEMM
     (96, 128, 2048, 1, 1, 4, 16, "bf16"),
 ]
