@@ -14,9 +14,11 @@ Default workload: decode_h4096 (64 tokens, h 4096, I 11008, 16 experts top-2,
 library records on the launch stream around its kernels
 (moelora_forward_profiled): an untimed pass records every stage boundary for
 the per-stage breakdown; the timed K steps record only the two events around
-the dominant kernel, whose mean duration gives the roofline figure.  The CPU
-baseline times the plain C oracle on the host's cores over a bounded sample of
-the same workload.
+the dominant kernel, whose mean duration gives the roofline figure.  Also
+untimed: the per-step latency (p10/p50/p90 of event-bracketed align + forward),
+warm and cold (a 1 GiB write before each step evicts the MALL and the L2s).
+The CPU baseline times the plain C oracle on the host's cores over a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -39,9 +41,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_work(cfg, offsets):
+def stage_work(cfg, offsets, fusion):
     """Algorithmic bytes and flops per stage of one forward launch, from the active
-    experts and (expert, adapter) buckets of this batch."""
+    experts and (expert, adapter) buckets of this batch.  A LoRA expand fused into
+    its GEMM's epilogue moves into that GEMM's figures (no G round trip) and its
+    own stage is empty."""
     import numpy as np
     T, h, I, E, k, L, r = (cfg.tokens, cfg.hidden, cfg.intermediate, cfg.experts, cfg.top_k,
                            cfg.adapters, cfg.rank)
@@ -61,6 +65,14 @@ def stage_work(cfg, offsets):
         "expand_down": (P * r * h * b + S * r * 4 + 2 * S * h * 4, 2 * S * r * h),
         "combine": (S * h * 4 + T * h * b + S * 8, 2 * S * h),
     }
+    if fusion["gate_up"]:
+        w["gemm_gate_up"] = (Eact * 2 * I * h * b + S * h * b + P * r * 2 * I * b + S * r * 4 + S * I * b,
+                             2 * S * h * 2 * I + 2 * S * r * 2 * I)
+        w["expand_gate_up"] = (0, 0)
+    if fusion["down"]:
+        w["gemm_down"] = (Eact * h * I * b + S * I * b + P * r * h * b + S * r * 4 + S * h * 4,
+                          2 * S * I * h + 2 * S * r * h)
+        w["expand_down"] = (0, 0)
     return w, Eact, P
 
 
@@ -140,6 +152,25 @@ def main() -> int:
     dom_i = int(np.argmax(mean_ms))
     dom = ops.STAGES[dom_i]
 
+    # per-step latency (untimed): warm, and cold with a 1 GiB write before each
+    # step (outside its events) that evicts the MALL and the L2s
+    def latency(flush):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evs:
+            if flush is not None:
+                flush.zero_()
+            e0.record()
+            step()
+            e1.record()
+        torch.cuda.synchronize()
+        us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+        return {q: round(float(np.percentile(us, p)), 2) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
+    lat_warm = latency(None)
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    lat_cold = latency(flush_buf)
+    del flush_buf
+
     # timed region: exactly K steps; events only around the dominant kernel
     dom_events = []
     for _ in range(args.steps):
@@ -156,13 +187,18 @@ def main() -> int:
     dom_ms = float(np.mean([ev[dom_i].elapsed_time(ev[dom_i + 1]) for ev in dom_events]))
 
     offsets = layer.routing[3].cpu().numpy()
-    work, Eact, P = stage_work(cfg, offsets)
+    fusion = ops.forward_fusion(d)
+    work, Eact, P = stage_work(cfg, offsets, fusion)
     ms_per_step = elapsed * 1e3 / args.steps
     value = cfg.tokens * args.steps / elapsed
 
     stages = {}
     for sname, ms in zip(ops.STAGES, mean_ms):
         by, fl = work[sname]
+        if by == 0:  # fused into the GEMM epilogue: only the event gap remains
+            stages[sname] = {"us": round(ms * 1e3, 2), "fused": True}
+            log(f"[bench] {sname:15s} {ms * 1e3:9.2f} us  (fused into the GEMM epilogue)")
+            continue
         stages[sname] = {"us": round(ms * 1e3, 2), "GB/s": round(by / (ms * 1e-3) / 1e9, 1),
                          "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2)}
         log(f"[bench] {sname:15s} {ms * 1e3:9.2f} us  {stages[sname]['GB/s']:8.1f} GB/s "
@@ -185,6 +221,7 @@ def main() -> int:
     roof["algorithmic_bytes"] = by
     roof["kernel"] = dom
     roof["kernel_us"] = round(dom_s * 1e6, 2)
+    log(f"[bench] latency per step (us): warm {lat_warm}, cold {lat_cold}")
     log(f"[bench] {cfg.name}: {value:.1f} tokens/s, {ms_per_step:.3f} ms/step, "
         f"sum of stages {mean_ms.sum():.3f} ms, active experts {Eact}, active buckets {P}")
 
@@ -214,6 +251,8 @@ def main() -> int:
                    "adapters": cfg.adapters, "rank": cfg.rank, "requests": cfg.requests,
                    "adapter_dist": cfg.adapter_dist, "parallelism": "single GPU"},
         "roofline": roof,
+        "latency_us": {"warm": lat_warm, "cold_1GiB_flush": lat_cold},
+        "fusion": fusion,
         "cpu_baseline": cpu,
         "stages": stages,
     }

@@ -207,6 +207,19 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
  */
 int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]);
 
+/*
+ * Which LoRA expands moelora_forward runs inside the base GEMM's epilogue for
+ * these dimensions (the follow-on fusion named in the vLLM blog page
+ * "Multi-LoRA", section "Implementing Multi-LoRA inference for MoE models in
+ * vLLM"): *flags gets bit MOELORA_FUSED_GATE_UP (gate_up expand and SiLU-mul;
+ * G is then not written) and bit MOELORA_FUSED_DOWN (down expand).  The
+ * matching MOELORA_STAGE_EXPAND_* stages are then empty.  Host only; returns
+ * the validation status of dims (MOELORA_ERR_NULL for a NULL flags).
+ */
+#define MOELORA_FUSED_GATE_UP 1
+#define MOELORA_FUSED_DOWN 2
+int moelora_forward_fusion(const moelora_dims* dims, int* flags);
+
 #ifdef __cplusplus
 }
 #endif

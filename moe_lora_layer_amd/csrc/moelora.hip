@@ -173,6 +173,15 @@ int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]
   return MOELORA_OK;
 }
 
+int moelora_forward_fusion(const moelora_dims* dims, int* flags) {
+  if (flags == nullptr) return MOELORA_ERR_NULL;
+  const int rc = check_dims(dims);
+  if (rc != MOELORA_OK) return rc;
+  const TilePlan plan = make_plan(dims);
+  *flags = (plan.fuse_gu ? MOELORA_FUSED_GATE_UP : 0) | (plan.fuse_dn ? MOELORA_FUSED_DOWN : 0);
+  return MOELORA_OK;
+}
+
 int moelora_forward(const moelora_dims* dims, const void* x, const void* w_gate_up,
                     const void* w_down, const void* a_gate_up, const void* b_gate_up,
                     const void* a_down, const void* b_down, const float* topk_weights,

@@ -55,12 +55,13 @@ def library():
         L.moelora_align_workspace_size.argtypes = [pd, ctypes.POINTER(sz)]
         L.moelora_forward_workspace_size.argtypes = [pd, ctypes.POINTER(sz)]
         L.moelora_forward_workspace_layout.argtypes = [pd, ctypes.POINTER(sz)]
+        L.moelora_forward_fusion.argtypes = [pd, ctypes.POINTER(ctypes.c_int)]
         L.moelora_align.argtypes = [pd] + [vp] * 8 + [sz, vp]
         L.moelora_forward.argtypes = [pd] + [vp] * 12 + [sz, vp]
         L.moelora_forward_profiled.argtypes = [pd] + [vp] * 12 + [sz, vp, vp]
         for f in (L.moelora_align_workspace_size, L.moelora_forward_workspace_size,
-                  L.moelora_forward_workspace_layout, L.moelora_align, L.moelora_forward,
-                  L.moelora_forward_profiled):
+                  L.moelora_forward_workspace_layout, L.moelora_forward_fusion, L.moelora_align,
+                  L.moelora_forward, L.moelora_forward_profiled):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -109,6 +110,14 @@ def forward_workspace_layout(d: Dims) -> dict:
     _check(library().moelora_forward_workspace_layout(ctypes.byref(d), offs),
            "moelora_forward_workspace_layout")
     return dict(zip(["G", "Z1", "ACT", "Z2", "D"], list(offs)))
+
+
+def forward_fusion(d: Dims) -> dict:
+    """Which LoRA expands run inside the base GEMM epilogue for these dims."""
+    flags = ctypes.c_int()
+    _check(library().moelora_forward_fusion(ctypes.byref(d), ctypes.byref(flags)),
+           "moelora_forward_fusion")
+    return {"gate_up": bool(flags.value & 1), "down": bool(flags.value & 2)}
 
 
 def _ptr(t):

@@ -124,3 +124,21 @@ def test_forward_argument_errors():
     # T == 0 is a no-op that touches nothing
     z = good_dims(tokens=0)
     assert lib.moelora_forward(ctypes.byref(z), *([None] * 11), None, 0, None) == OK
+
+
+@pytest.mark.parametrize("kw,flags", [
+    (dict(), {"gate_up": False, "down": False}),                          # 16 rows per expert
+    (dict(tokens=4096, hidden=4096, intermediate=11008, experts=16), {"gate_up": True, "down": True}),
+    (dict(tokens=4096, hidden=4096, intermediate=11008, experts=16, dtype="f32"),
+     {"gate_up": False, "down": False}),                                   # fused forms are bf16 only
+    (dict(tokens=600, hidden=128, intermediate=192, experts=4), {"gate_up": True, "down": True}),
+])
+def test_forward_fusion_flags(kw, flags):
+    assert ops.forward_fusion(good_dims(**kw)) == flags
+
+
+def test_forward_fusion_rejects_null_and_bad_dims():
+    lib = ops.library()
+    assert lib.moelora_forward_fusion(ctypes.byref(good_dims()), None) == ERR_NULL
+    f = ctypes.c_int()
+    assert lib.moelora_forward_fusion(ctypes.byref(good_dims(rank=8)), ctypes.byref(f)) == ERR_UNSUPPORTED
