@@ -493,6 +493,11 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave >> 2, wn = wave & 3;
   const int c32 = lane & 31, h = lane >> 5;
+  // A tile of at most 128 rows (an expert's last rows) would leave half of the
+  // MFMA work on padding: both wave rows then take the same 128 rows, wave row
+  // wm doing substeps 2wm and 2wm+1 of every K-step, and the two partial
+  // tiles are summed through LDS at the end.
+  const bool half = row_end - row0 <= 128;
 
   // Load instruction j of wave w fills tile rows 32w + 8j + lane/8 (A and B);
   // the lane's LDS chunk is lane%8, so it fetches logical chunk
@@ -532,7 +537,7 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   // fragment reads: substep s (16 of the 64 K) of row r = 128 wm + 32 i + c32;
   // (r >> 1) & 7 depends on c32 only
   const int sw = swz<1>(c32);
-  const int a_off = (wm * 128 + c32) * kDmaRowB;
+  const int a_off = ((half ? 0 : wm * 128) + c32) * kDmaRowB;
   const int b_off = (kDmaTile + wn * 64 + c32) * kDmaRowB;
   bf16x8_t fa[2][4], fb[2][2];
   auto rd = [&](int f, const unsigned char* st, int s) {
@@ -567,26 +572,26 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   dma_issue(smem, 1, ko(min(1, nk - 1)), a_src, b_src, wave);
   wait_vmcnt<8>();  // this wave's loads of step 0 are in LDS
   bar();            // ... and every other wave's
-  rd(0, smem, 0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing scalar or LDS pending into the loop
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const unsigned char* cur = smem + (kt & 1) * kDmaStage;
+  if (!half) {
+    rd(0, smem, 0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing scalar or LDS pending into the loop
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const unsigned char* cur = smem + (kt & 1) * kDmaStage;
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      rd((s + 1) & 1, cur, s + 1);
-      mm(s & 1);
+      for (int s = 0; s < 3; ++s) {
+        rd((s + 1) & 1, cur, s + 1);
+        mm(s & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // step kt+1 has landed and every wave has finished reading step kt
+      // (lgkmcnt(0) before the barrier): refill that stage with step kt+2
+      wait_vmcnt_lgkm0<0>();
+      bar();
+      dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
+      rd(0, smem + ((kt + 1) & 1) * kDmaStage, 0);
+      mm(1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // step kt+1 has landed and every wave has finished reading step kt
-    // (lgkmcnt(0) before the barrier): refill that stage with step kt+2
-    wait_vmcnt_lgkm0<0>();
-    bar();
-    dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
-    rd(0, smem + ((kt + 1) & 1) * kDmaStage, 0);
-    mm(1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  {
     const unsigned char* cur = smem + ((nk - 1) & 1) * kDmaStage;
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
@@ -594,8 +599,48 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
       mm(s & 1);
     }
     mm(1);
+  } else {
+    const int s0 = 2 * wm;  // this wave row's two substeps
+    rd(0, smem, s0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      rd(1, smem + (kt & 1) * kDmaStage, s0 + 1);
+      mm(0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_lgkm0<0>();
+      bar();
+      dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
+      rd(0, smem + ((kt + 1) & 1) * kDmaStage, s0);
+      mm(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    rd(1, smem + ((nk - 1) & 1) * kDmaStage, s0 + 1);
+    mm(0);
+    mm(1);
   }
   wait_vmcnt<0>();  // no LDS write of this workgroup may outlive it
+  if (half) {
+    // sum the two partial tiles: wave row 1 hands its accumulators over through
+    // LDS (32 KiB per wave, lane-major) and leaves; wave row 0 goes on alone
+    bar();  // every wave is done with the K stages
+    float* red = reinterpret_cast<float*>(smem) + wn * (8 * 16 * kWave);
+    if (wm == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * kWave + lane] = acc[i][j][r];
+    }
+    bar();
+    if (wm == 1) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * kWave + lane];
+  }
 
   // output column of fragment j held by this lane, and its LoRA B row
   int64_t col[2], brow[2];

@@ -84,6 +84,28 @@ def test_forward_workload(name):
     assert_close(to_f64(out)[toks], ref, cfg.dtype, f"{name} out")
 
 
+def test_forward_tile_boundaries():
+    """Routing crafted so that, with 256-row tiles, one expert's last tile has
+    exactly 128 rows (the largest tile computed with both wave rows splitting K),
+    another has 129 (the smallest full tile), a third exactly 256 and a fourth
+    256 + 44."""
+    sizes = [384, 129, 256, 300]
+    cfg = _small(sum(sizes), 128, 192, len(sizes), 1, 3, 32, "bf16", seed=21)
+    inp = synth.make_inputs(cfg)
+    owner = np.repeat(np.arange(len(sizes)), sizes)
+    np.random.default_rng(4).shuffle(owner)
+    logits = np.zeros((cfg.tokens, len(sizes)), np.float32)
+    logits[np.arange(cfg.tokens), owner] = 4.0
+    inp["logits"] = logits
+    assert ops.forward_fusion(ops.dims_for(cfg)) == {"gate_up": True, "down": True}
+    _, (ids, w, ss, off), out, _ = _layer(cfg, inp)
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.array_equal(np.bincount(ref_ids.ravel(), minlength=len(sizes)), sizes)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
+    assert_close(to_f64(out), ref, cfg.dtype, "out")
+
+
 def test_forward_intermediates():
     """Layer-by-layer reconciliation: G, Z1, ACT, Z2, D read from the workspace
     against the oracle's per-slot intermediates."""
