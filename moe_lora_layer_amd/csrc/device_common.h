@@ -130,6 +130,29 @@ __device__ __forceinline__ void split_bf16x8(const float* v8, bf16x8_t& hi, bf16
   lo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
 }
 
+// LDS address space, for the destination of global_load_lds (the direct
+// global-memory-to-LDS load: lane i's bytes land at base + i * size).
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: expcnt and lgkmcnt at
+// their maximum), and the same with lgkmcnt(0).  The direct-to-LDS loads count
+// in vmcnt.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  constexpr int imm = (N & 15) | ((N >> 4) << 14) | 0x0F70;
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  constexpr int imm = (N & 15) | ((N >> 4) << 14) | 0x0070;
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// Workgroup barrier that orders LDS accesses only (no wait on global memory).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Row (within the 32x32 block) of accumulator element i held by a lane of half h.
 __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 

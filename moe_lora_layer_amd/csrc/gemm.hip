@@ -414,23 +414,11 @@ static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, hipStream_
 // LDS rows keep the 16-byte-chunk XOR swizzle of the register-staged kernel:
 // a load instruction fills 8 whole rows, each lane fetching the global chunk
 // that belongs at its LDS position.
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kDmaTile = 256;                   // BM = BN
 constexpr int kDmaRowB = 128;                   // bytes of K per LDS row (64 bf16)
 constexpr int kDmaStage = 2 * kDmaTile * kDmaRowB;  // A and B rows of one K-step: 64 KiB
 constexpr int kDmaThreads = 512;
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: expcnt and lgkmcnt at
-// their maximum), and the same with lgkmcnt(0)
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  constexpr int imm = (N & 15) | ((N >> 4) << 14) | 0x0F70;
-  __builtin_amdgcn_s_waitcnt(imm);
-}
-template <int N> __device__ __forceinline__ void wait_vmcnt_lgkm0() {
-  constexpr int imm = (N & 15) | ((N >> 4) << 14) | 0x0070;
-  __builtin_amdgcn_s_waitcnt(imm);
-}
 
 // The four A and four B load instructions of one wave for K-step kt into
 // stage `slot` (8 rows of 128 bytes each).

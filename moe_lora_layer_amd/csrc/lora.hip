@@ -199,6 +199,122 @@ k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ g
   }
 }
 
+
+// --------------------------------------------------------- tall shrink (bf16)
+// LoRA tiles of many rows (prefill): one workgroup per (tile, K range) streams
+// the tile's activation rows (at most 64) and the adapter's A^T rows through a
+// four-stage LDS ring of 64-wide K steps, loaded with global_load_lds in whole
+// 128-byte rows (swizzled 16-byte chunks, as in the base GEMM).  z = x A^T runs
+// on 32x32x16 MFMAs, activation rows on the A side and rank rows on the B
+// side.  Wave w takes rows 32 (w % 2) .. +32 and, for R <= 32, substeps
+// 2 (w / 2) and 2 (w / 2) + 1 of each K step (R = 64: rank half w / 2, all
+// substeps); it adds its 32 x 32 partial to Z with relaxed fp32 atomics, so Z
+// must be zero beforehand (the split-K of the page's "Kernel optimisation").
+constexpr int kShrinkStages = 4;
+
+template <int R> struct ShrinkDma {
+  static constexpr int RP = R < 32 ? 32 : R;        // rank rows staged (16 padded to 32)
+  static constexpr int STAGE = (64 + RP) * 128;     // activation rows, then A^T rows
+  static constexpr int XI = 2;                      // activation load instructions per wave
+  static constexpr int AI = RP / 32;                // A^T load instructions per wave
+  static constexpr int LPW = XI + AI;               // loads per wave per stage
+};
+
+template <int R>
+__device__ __forceinline__ void shrink_issue(unsigned char* smem, int slot, int64_t ko,
+                                             const bf16_t* const* x_src, const bf16_t* const* a_src,
+                                             int wave) {
+  typedef ShrinkDma<R> S;
+  unsigned char* st = smem + slot * S::STAGE;
+#pragma unroll
+  for (int j = 0; j < S::XI; ++j)
+    __builtin_amdgcn_global_load_lds(x_src[j] + ko, (lds_void_t*)(st + (16 * wave + 8 * j) * 128),
+                                     16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < S::AI; ++j)
+    __builtin_amdgcn_global_load_lds(a_src[j] + ko,
+                                     (lds_void_t*)(st + (64 + 8 * (S::AI * wave + j)) * 128), 16, 0, 0);
+}
+
+template <int R, bool GATHER>
+__global__ void __launch_bounds__(kLoraThreads)
+k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
+             int gather_k, const bf16_t* __restrict__ At, int E, int L, int64_t K, int kwg_steps,
+             int nsplit, float* __restrict__ Z, const int4* __restrict__ ltiles,
+             const int32_t* __restrict__ counts) {
+  typedef ShrinkDma<R> S;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kShrinkStages * S::STAGE];
+  const int lt = blockIdx.x / nsplit;
+  const int split = blockIdx.x % nsplit;
+  if (lt >= counts[1]) return;
+  const int4 tile = ltiles[lt];
+  const int b = tile.x, row0 = tile.y, row_end = tile.z;
+  const int e = b / L, l = b % L;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int c32 = lane & 31, h = lane >> 5;
+  const int nk_all = static_cast<int>(K / 64);
+  const int kt0 = split * kwg_steps;
+  const int nk = min(nk_all, kt0 + kwg_steps) - kt0;
+  if (nk <= 0) return;  // uniform
+
+  // load sources (rows past the tile or the rank read a clamped valid row)
+  const bf16_t* x_src[S::XI];
+  const bf16_t* a_src[S::AI];
+#pragma unroll
+  for (int j = 0; j < S::XI; ++j) {
+    const int rt = 16 * wave + 8 * j + (lane >> 3);
+    const int lch = (lane & 7) ^ ((rt >> 1) & 7);
+    const int p = min(row0 + rt, row_end - 1);
+    const int r = GATHER ? gather_slots[p] / gather_k : p;
+    x_src[j] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + kt0 * 64ll + lch * 8;
+  }
+  const bf16_t* Ab = At + (static_cast<int64_t>(l) * E + e) * R * K;
+#pragma unroll
+  for (int j = 0; j < S::AI; ++j) {
+    const int rt = 8 * (S::AI * wave + j) + (lane >> 3);
+    const int lch = (lane & 7) ^ ((rt >> 1) & 7);
+    a_src[j] = Ab + static_cast<int64_t>(min(rt, R - 1)) * K + kt0 * 64ll + lch * 8;
+  }
+
+  const int rh = wave & 1;
+  const int sel = wave >> 1;                  // substep pair (R <= 32) or rank half (R = 64)
+  const int q0 = R > 32 ? 32 * sel : 0;       // first rank column of this wave
+  const int sw = (c32 >> 1) & 7;              // row swizzle of rows 32 rh + c32 and q0 + c32
+  const int x_off = (32 * rh + c32) * 128;
+  const int a_off = (64 + q0 + c32) * 128;
+  f32x16_t acc = zero_acc();
+
+  for (int s = 0; s + 1 < kShrinkStages; ++s)
+    shrink_issue<R>(smem, s, static_cast<int64_t>(min(s, nk - 1)) * 64, x_src, a_src, wave);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt landed (two newer stages may still fly) and this wave's reads of
+    // stage kt-1 are done; after the barrier its slot takes stage kt+3 (steps
+    // past the end repeat the last one and are never read)
+    wait_vmcnt_lgkm0<S::LPW * (kShrinkStages - 2)>();
+    lds_barrier();
+    shrink_issue<R>(smem, (kt + kShrinkStages - 1) % kShrinkStages,
+                    static_cast<int64_t>(min(kt + kShrinkStages - 1, nk - 1)) * 64, x_src, a_src, wave);
+    const unsigned char* st = smem + (kt % kShrinkStages) * S::STAGE;
+#pragma unroll
+    for (int u = 0; u < (R > 32 ? 4 : 2); ++u) {
+      const int sub = R > 32 ? u : 2 * sel + u;
+      const int ch = ((2 * sub + h) ^ sw) << 4;
+      const bf16x8_t fx = *reinterpret_cast<const bf16x8_t*>(st + x_off + ch);
+      const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(st + a_off + ch);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx, fa, acc, 0, 0, 0);
+    }
+  }
+  wait_vmcnt<0>();  // no LDS write of this workgroup may outlive it
+  const int q = q0 + c32;
+  if (q < R) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int p = row0 + 32 * rh + acc_row(i, h);
+      if (p < row_end) atomic_add_relaxed(Z + static_cast<int64_t>(p) * R + q, acc[i]);
+    }
+  }
+}
+
 // --------------------------------------------------------------------- expand
 // Each wave owns NB blocks of 16 output columns (and, for gate_up, the
 // matching up columns I + n).  Its B^T fragments are loaded once and reused
@@ -366,6 +482,20 @@ static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
                                 const int32_t* gather_slots, int gather_k, const void* At, int E,
                                 int L, int64_t K, float* Z, const int4* ltiles,
                                 const int32_t* counts, hipStream_t stream) {
+  if (plan.lora_db && sizeof(T) == 2) {
+    // tall bf16 tiles: DMA ring, about 1024 workgroups of (tile, K range)
+    const int nk_all = static_cast<int>(K / 64);
+    int nsplit = (1024 + plan.max_lt - 1) / std::max(1, plan.max_lt);
+    nsplit = std::max(1, std::min(nsplit, nk_all / 4));
+    const int kwg_steps = (nk_all + nsplit - 1) / nsplit;
+    nsplit = (nk_all + kwg_steps - 1) / kwg_steps;
+    const int64_t grid = static_cast<int64_t>(plan.max_lt) * nsplit;
+    hipLaunchKernelGGL((k_shrink_dma<R, GATHER>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kLoraThreads), 0, stream, static_cast<const bf16_t*>(X), x_rows,
+                       gather_slots, gather_k, static_cast<const bf16_t*>(At), E, L, K, kwg_steps,
+                       nsplit, Z, ltiles, counts);
+    return hipGetLastError();
+  }
   if (plan.lora_db) {
     // tall tiles: ~1024 workgroups, each wave a 16-row block over the split's K range
     constexpr int STEPS = R > 32 ? 2 : 4;
