@@ -117,6 +117,26 @@ int moelora_align(const moelora_dims* dims, const float* router_logits,
                   int32_t* sorted_slots, int32_t* bucket_offsets, int32_t* device_status,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * moelora_align_topk -- the permutation of moelora_align for a caller that
+ * routes itself (its router GEMM and top-k run just before this path):
+ * topk_ids is an input and no routing weight is computed (the caller passes
+ * its own to moelora_forward).  Keys, sorted_slots and bucket_offsets are
+ * exactly those of moelora_align for the same ids; repeated ids within a token
+ * are allowed (each slot is an independent row).
+ *
+ *   topk_ids       in  int32 [T][k], each in [0, E)
+ *   adapter_ids    in  int32 [T], each in [0, L)
+ *   sorted_slots, bucket_offsets, workspace: as moelora_align
+ *   device_status  out int32 [1] or NULL: 0 = ok, 1 = an adapter id outside
+ *                  [0, L), 3 = an expert id outside [0, E) (either treated as 0,
+ *                  the outputs then unspecified; the larger code is reported).
+ */
+int moelora_align_topk(const moelora_dims* dims, const int32_t* topk_ids,
+                       const int32_t* adapter_ids, int32_t* sorted_slots,
+                       int32_t* bucket_offsets, int32_t* device_status, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace moelora_forward needs for these dimensions. */
 int moelora_forward_workspace_size(const moelora_dims* dims, size_t* bytes);
 

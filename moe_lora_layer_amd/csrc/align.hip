@@ -18,7 +18,10 @@
 //      buckets gives bucket_offsets, and cnt[c][b] becomes the first output
 //      position of chunk c's slots in bucket b;
 //   4. scatter: sorted_slots[cnt[c][key] + rank] = s.
-// device_status: 0 ok, 1 an adapter id outside [0, L), 2 internal inconsistency.
+// ROUTE = false skips the routing of phase 1: the caller's topk_ids (its own
+// router, e.g. a router GEMM and top-k just before this path) give the keys.
+// device_status: 0 ok, 1 an adapter id outside [0, L), 2 internal
+// inconsistency, 3 a given expert id outside [0, E) (the largest code wins).
 // No step depends on atomic ordering, so the result is bit-exact and stable.
 #include "device_common.h"
 #include "launch.h"
@@ -30,9 +33,10 @@ constexpr int kMaxTopK = 8;
 
 // KEYS_LDS: the per-slot keys and ranks live in LDS after the counters (small
 // batches); otherwise in the workspace.
-template <bool KEYS_LDS>
+template <bool KEYS_LDS, bool ROUTE>
 __global__ void __launch_bounds__(kAlignThreads)
-k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_ids, int T, int E,
+k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
+        const int32_t* __restrict__ adapter_ids, int T, int E,
         int k, int L, int chunks, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
         int32_t* __restrict__ sorted_slots, int32_t* __restrict__ offsets,
         int32_t* __restrict__ status, int32_t* __restrict__ ws_key, int32_t* __restrict__ ws_rank) {
@@ -56,8 +60,20 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
   for (int t = tid; t < T; t += kAlignThreads) {
     int l = adapter_ids[t];
     if (l < 0 || l >= L) {
-      bad = 1;
+      atomicMax(&bad, 1);
       l = 0;
+    }
+    if (!ROUTE) {
+      for (int q = 0; q < k; ++q) {
+        const int s = t * k + q;
+        int e = ids_in[s];
+        if (e < 0 || e >= E) {
+          atomicMax(&bad, 3);
+          e = 0;
+        }
+        key_buf[s] = e * L + l;
+      }
+      continue;
     }
     float val[kMaxTopK];
     int id[kMaxTopK];
@@ -163,7 +179,7 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
     if (dst >= 0 && dst < S)
       sorted_slots[dst] = s;
     else
-      bad = 2;  // cannot happen for consistent counts; never write out of bounds
+      atomicMax(&bad, 2);  // cannot happen for consistent counts; never write out of bounds
   }
   __syncthreads();
   if (tid == 0 && status != nullptr) *status = bad;
@@ -181,23 +197,26 @@ int align_chunks(int nb, int S) {
   return c;
 }
 
-hipError_t launch_align(const float* logits, const int32_t* adapter_ids, int T, int E, int k,
-                        int L, int32_t* topk_ids, float* topk_w, int32_t* sorted_slots,
-                        int32_t* offsets, int32_t* status, int32_t* ws_key, int32_t* ws_rank,
-                        hipStream_t stream) {
+hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_t* adapter_ids,
+                        int T, int E, int k, int L, int32_t* topk_ids, float* topk_w,
+                        int32_t* sorted_slots, int32_t* offsets, int32_t* status, int32_t* ws_key,
+                        int32_t* ws_rank, hipStream_t stream) {
   const int nb = E * L;
   const int S = T * k;
   const int chunks = align_chunks(nb, S);
   const bool in_lds = keys_in_lds(S, nb);
   const size_t lds = (static_cast<size_t>(chunks) * nb + (in_lds ? 2 * S : 0)) * sizeof(int);
-  if (in_lds)
-    hipLaunchKernelGGL(k_align<true>, dim3(1), dim3(kAlignThreads), lds, stream, logits,
-                       adapter_ids, T, E, k, L, chunks, topk_ids, topk_w, sorted_slots, offsets,
-                       status, ws_key, ws_rank);
-  else
-    hipLaunchKernelGGL(k_align<false>, dim3(1), dim3(kAlignThreads), lds, stream, logits,
-                       adapter_ids, T, E, k, L, chunks, topk_ids, topk_w, sorted_slots, offsets,
-                       status, ws_key, ws_rank);
+#define MOELORA_ALIGN_LAUNCH(KL, RT)                                                              \
+  hipLaunchKernelGGL((k_align<KL, RT>), dim3(1), dim3(kAlignThreads), lds, stream, logits, ids_in, \
+                     adapter_ids, T, E, k, L, chunks, topk_ids, topk_w, sorted_slots, offsets,     \
+                     status, ws_key, ws_rank)
+  const bool route = logits != nullptr;
+  if (in_lds) {
+    if (route) MOELORA_ALIGN_LAUNCH(true, true); else MOELORA_ALIGN_LAUNCH(true, false);
+  } else {
+    if (route) MOELORA_ALIGN_LAUNCH(false, true); else MOELORA_ALIGN_LAUNCH(false, false);
+  }
+#undef MOELORA_ALIGN_LAUNCH
   return hipGetLastError();
 }
 

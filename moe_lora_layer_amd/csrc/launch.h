@@ -13,10 +13,12 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 constexpr int kAlignLdsInts = 15360;
 int align_chunks(int nb, int S);
 
-hipError_t launch_align(const float* logits, const int32_t* adapter_ids, int T, int E, int k,
-                        int L, int32_t* topk_ids, float* topk_w, int32_t* sorted_slots,
-                        int32_t* offsets, int32_t* status, int32_t* ws_key, int32_t* ws_rank,
-                        hipStream_t stream);
+// logits == nullptr: the expert ids come from ids_in (no routing, topk_ids and
+// topk_w untouched).
+hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_t* adapter_ids,
+                        int T, int E, int k, int L, int32_t* topk_ids, float* topk_w,
+                        int32_t* sorted_slots, int32_t* offsets, int32_t* status, int32_t* ws_key,
+                        int32_t* ws_rank, hipStream_t stream);
 
 // Tile descriptor: x = expert (M-tiles) or bucket (LoRA tiles), y = first
 // sorted row, z = end row (exclusive), w unused.

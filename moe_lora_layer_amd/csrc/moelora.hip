@@ -145,11 +145,36 @@ int moelora_align(const moelora_dims* dims, const float* router_logits,
   const size_t S = static_cast<size_t>(T * dims->top_k);
   int32_t* ws_key = static_cast<int32_t*>(workspace);
   int32_t* ws_rank = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + round_up(S * 4));
-  return hip_status(moelora::launch_align(router_logits, adapter_ids, static_cast<int>(T),
-                                          dims->experts, dims->top_k, dims->adapters, topk_ids,
-                                          topk_weights, sorted_slots, bucket_offsets,
-                                          device_status, ws_key, ws_rank,
+  return hip_status(moelora::launch_align(router_logits, nullptr, adapter_ids,
+                                          static_cast<int>(T), dims->experts, dims->top_k,
+                                          dims->adapters, topk_ids, topk_weights, sorted_slots,
+                                          bucket_offsets, device_status, ws_key, ws_rank,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int moelora_align_topk(const moelora_dims* dims, const int32_t* topk_ids,
+                       const int32_t* adapter_ids, int32_t* sorted_slots,
+                       int32_t* bucket_offsets, int32_t* device_status, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != MOELORA_OK) return rc;
+  if (bucket_offsets == nullptr) return MOELORA_ERR_NULL;
+  const int64_t T = dims->tokens;
+  if (T > 0 && (topk_ids == nullptr || adapter_ids == nullptr || sorted_slots == nullptr))
+    return MOELORA_ERR_NULL;
+  size_t need = 0;
+  moelora_align_workspace_size(dims, &need);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MOELORA_ERR_WORKSPACE;
+  const void* ptrs[] = {topk_ids, adapter_ids, sorted_slots, bucket_offsets, workspace};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return MOELORA_ERR_ALIGNMENT;
+  const size_t S = static_cast<size_t>(T * dims->top_k);
+  int32_t* ws_key = static_cast<int32_t*>(workspace);
+  int32_t* ws_rank = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + round_up(S * 4));
+  return hip_status(moelora::launch_align(nullptr, topk_ids, adapter_ids, static_cast<int>(T),
+                                          dims->experts, dims->top_k, dims->adapters, nullptr,
+                                          nullptr, sorted_slots, bucket_offsets, device_status,
+                                          ws_key, ws_rank, static_cast<hipStream_t>(stream)));
 }
 
 int moelora_forward_workspace_size(const moelora_dims* dims, size_t* bytes) {

@@ -57,11 +57,12 @@ def library():
         L.moelora_forward_workspace_layout.argtypes = [pd, ctypes.POINTER(sz)]
         L.moelora_forward_fusion.argtypes = [pd, ctypes.POINTER(ctypes.c_int)]
         L.moelora_align.argtypes = [pd] + [vp] * 8 + [sz, vp]
+        L.moelora_align_topk.argtypes = [pd] + [vp] * 6 + [sz, vp]
         L.moelora_forward.argtypes = [pd] + [vp] * 12 + [sz, vp]
         L.moelora_forward_profiled.argtypes = [pd] + [vp] * 12 + [sz, vp, vp]
         for f in (L.moelora_align_workspace_size, L.moelora_forward_workspace_size,
                   L.moelora_forward_workspace_layout, L.moelora_forward_fusion, L.moelora_align,
-                  L.moelora_forward, L.moelora_forward_profiled):
+                  L.moelora_align_topk, L.moelora_forward, L.moelora_forward_profiled):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -169,6 +170,29 @@ def align(d: Dims, logits: torch.Tensor, adapter_ids: torch.Tensor, *, out=None,
                                    _ptr(workspace_buf), workspace_buf.numel(), _stream(stream)),
            "moelora_align")
     return topk_ids, topk_w, sorted_slots, offsets, status
+
+
+def align_topk(d: Dims, topk_ids: torch.Tensor, adapter_ids: torch.Tensor, *, out=None,
+               workspace_buf=None, status=None, stream=None):
+    """moelora_align_topk (the caller's own expert ids).  Returns
+    (sorted_slots, bucket_offsets, status)."""
+    dev = topk_ids.device
+    T, E, k, L = d.tokens, d.experts, d.top_k, d.adapters
+    _expect(topk_ids, "topk_ids", (T, k), torch.int32, dev)
+    _expect(adapter_ids, "adapter_ids", (T,), torch.int32, dev)
+    if out is None:
+        out = (torch.empty((T * k,), dtype=torch.int32, device=dev),
+               torch.empty((E * L + 1,), dtype=torch.int32, device=dev))
+    sorted_slots, offsets = out
+    if status is None:
+        status = torch.zeros((4,), dtype=torch.int32, device=dev)
+    if workspace_buf is None:
+        workspace_buf = workspace(align_workspace_size(d), dev)
+    _check(library().moelora_align_topk(ctypes.byref(d), _ptr(topk_ids), _ptr(adapter_ids),
+                                        _ptr(sorted_slots), _ptr(offsets), _ptr(status),
+                                        _ptr(workspace_buf), workspace_buf.numel(), _stream(stream)),
+           "moelora_align_topk")
+    return sorted_slots, offsets, status
 
 
 def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down, topk_weights,

@@ -87,3 +87,54 @@ def test_align_reports_bad_adapter():
     assert int(st[0].item()) == 1
     # still a permutation of the slots, in bounds
     assert sorted(ss.cpu().numpy().tolist()) == list(range(100))
+
+
+def _topk(cfg, ids, adapter_ids):
+    dev = device()
+    ss, off, st = ops.align_topk(ops.dims_for(cfg), torch.from_numpy(ids).to(dev),
+                                 torch.from_numpy(adapter_ids).to(dev))
+    torch.cuda.synchronize()
+    return ss.cpu().numpy(), off.cpu().numpy(), int(st[0].item())
+
+
+@pytest.mark.parametrize("T,E,k,L", [(1, 8, 2, 4), (3, 4, 4, 2), (1000, 32, 8, 16), (5000, 16, 2, 8),
+                                     (70, 8192, 1, 1), (20000, 2, 2, 3)])
+def test_align_topk_caller_ids(T, E, k, L):
+    """moelora_align_topk with the caller's expert ids (repeats within a token
+    allowed): the permutation and offsets equal the oracle's, bit for bit."""
+    cfg = _cfg(T, E, k, L, seed=3)
+    rng = np.random.default_rng(T + E)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    ad = rng.integers(0, L, T).astype(np.int32)
+    say(f"align_topk T={T} E={E} k={k} L={L}")
+    ss, off, st = _topk(cfg, ids, ad)
+    ref_ss, ref_off = oracle.align(ids, ad, E, L)
+    assert st == 0
+    assert np.array_equal(ss, ref_ss) and np.array_equal(off, ref_off)
+
+
+def test_align_topk_equals_align_on_routed_ids():
+    cfg = synth.WORKLOADS["prefill_h4096"]
+    r = synth.make_routing_inputs(cfg)
+    ref_ids, _ = oracle.route(r["logits"], cfg.top_k)
+    dev = device()
+    _, _, ss_a, off_a, _ = run_align(cfg, {"logits": torch.from_numpy(r["logits"]).to(dev),
+                                           "adapter_ids": torch.from_numpy(r["adapter_ids"]).to(dev)})
+    ss, off, st = _topk(cfg, ref_ids.astype(np.int32), r["adapter_ids"])
+    assert st == 0
+    assert np.array_equal(ss, ss_a.cpu().numpy()) and np.array_equal(off, off_a.cpu().numpy())
+
+
+def test_align_topk_reports_bad_ids():
+    cfg = _cfg(40, 8, 2, 4)
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, 8, (40, 2)).astype(np.int32)
+    ad = rng.integers(0, 4, 40).astype(np.int32)
+    bad_e = ids.copy()
+    bad_e[3, 1] = 8
+    ss, _, st = _topk(cfg, bad_e, ad)
+    assert st == 3 and sorted(ss.tolist()) == list(range(80))
+    bad_l = ad.copy()
+    bad_l[9] = -1
+    assert _topk(cfg, ids, bad_l)[2] == 1
+    assert _topk(cfg, bad_e, bad_l)[2] == 3      # the larger code is reported

@@ -191,6 +191,25 @@ def test_forward_with_oracle_permutation():
     assert_close(to_f64(out), oracle.forward(inp, oracle.dims_of(cfg), ids, w), "bf16", "out")
 
 
+def test_forward_after_align_topk():
+    """A caller that routes itself: its own expert ids (one token repeats an
+    expert) and weights (not a softmax) through moelora_align_topk and forward."""
+    cfg = _small(300, 256, 320, 6, 2, 4, 32, "bf16", seed=23)
+    inp = synth.make_inputs(cfg)
+    dev = device()
+    dinp = device_inputs(inp, cfg, dev)
+    rng = np.random.default_rng(29)
+    ids = np.stack([rng.permutation(cfg.experts)[:cfg.top_k] for _ in range(cfg.tokens)]).astype(np.int32)
+    ids[5] = ids[5, 0]
+    w = rng.uniform(0.1, 1.0, ids.shape).astype(np.float32)
+    ss, off, st = ops.align_topk(ops.dims_for(cfg), torch.from_numpy(ids).to(dev), dinp["adapter_ids"])
+    torch.cuda.synchronize()
+    assert int(st[0].item()) == 0
+    out, _ = run_forward(cfg, dinp, torch.from_numpy(w).to(dev), ss, off)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ids.astype(np.int64), w.astype(np.float64))
+    assert_close(to_f64(out), ref, "bf16", "out")
+
+
 def test_canaries_and_second_stream():
     """Guard bytes around the output and the workspace stay untouched, and a run
     on a second stream with its own workspace gives the same result."""
