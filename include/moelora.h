@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOELORA_ABI_VERSION 2
+#define MOELORA_ABI_VERSION 3
 
 typedef enum moelora_status {
   MOELORA_OK = 0,
@@ -76,7 +76,20 @@ typedef struct moelora_dims {
   int32_t adapters;      /* L: adapters resident at once                            */
   int32_t rank;          /* r                                                       */
   int32_t dtype;         /* moelora_dtype                                           */
+  int32_t flags;         /* 0, or MOELORA_FLAG_DETERMINISTIC                         */
 } moelora_dims;
+
+/*
+ * MOELORA_FLAG_DETERMINISTIC: every split-K reduction (the LoRA shrinks, and
+ * the base GEMMs when their K is split because the output is narrow) writes
+ * one fp32 partial per split to the forward workspace and a separate pass sums
+ * the partials in split order, instead of relaxed fp32 atomics.  The output is
+ * then bit-identical from run to run for the same inputs and dims (without the
+ * flag the atomics' order varies, within the layer's tolerance).  The forward
+ * workspace grows by the partials (moelora_forward_workspace_size accounts for
+ * it).
+ */
+#define MOELORA_FLAG_DETERMINISTIC 1
 
 int moelora_abi_version(void);
 

@@ -164,7 +164,8 @@ __global__ void __launch_bounds__(WM * WN * kWave)
 k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
        const T* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
        const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
-       const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit) {
+       const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, float* __restrict__ parts,
+       int64_t part_stride) {
   typedef Mfma<T> M;
   constexpr int NT_ = WM * WN * kWave;
   constexpr int ROWB = 128;                    // bytes of K per LDS row
@@ -365,11 +366,13 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
       for (int r = 0; r < 16; ++r) {
         const int p = row0 + wm * WTM + i * 32 + acc_row(r, h);
         if (p < row_end && n < N) {
-          float* dst = C + static_cast<int64_t>(p) * N + n;
-          if (ksplit > 1)
-            atomic_add_relaxed(dst, acc[i][j][r]);
+          const int64_t idx = static_cast<int64_t>(p) * N + n;
+          if (ksplit == 1)
+            C[idx] = acc[i][j][r];
+          else if (parts != nullptr)  // deterministic: this split's partial
+            parts[ks * part_stride + idx] = acc[i][j][r];
           else
-            *dst = acc[i][j][r];
+            atomic_add_relaxed(C + idx, acc[i][j][r]);
         }
       }
     }
@@ -387,6 +390,8 @@ struct GemmArgs {
   const int32_t* counts;
   const int32_t* expert_tiles;
   int ksplit;
+  float* parts;         // deterministic split-K partials, or nullptr
+  int64_t part_stride;  // elements per partial (rows of C times N)
 };
 
 template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
@@ -397,7 +402,8 @@ static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, hipStream_
   hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE>), dim3(static_cast<unsigned>(grid)),
                      dim3(WM * WN * kWave), 0, stream, static_cast<const T*>(a.X), a.x_rows,
                      a.gather_slots, a.gather_k, static_cast<const T*>(a.Wt), a.N, a.K, a.C,
-                     a.mtiles, a.counts, a.expert_tiles, n_ntiles, a.ksplit);
+                     a.mtiles, a.counts, a.expert_tiles, n_ntiles, a.ksplit, a.parts,
+                     a.part_stride);
   return hipGetLastError();
 }
 
@@ -452,7 +458,8 @@ __global__ void __launch_bounds__(kDmaThreads)
 k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
            int gather_k, const bf16_t* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
            const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
-           const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, LoraEpilogue lora) {
+           const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, LoraEpilogue lora,
+           float* __restrict__ parts, int64_t part_stride) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDmaStage];
   // workgroup order: as k_gemm (XCD remap over the real workgroups, then per
   // expert N-tile by N-tile with its M-tiles innermost)
@@ -713,10 +720,12 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
           if (p < row_end && col_ok[j]) put(C + static_cast<int64_t>(p) * N + col[j], acc[i][j][r]);
         }
   };
-  if (ksplit > 1)
-    store([](float* dst, float v) { atomic_add_relaxed(dst, v); });
-  else
+  if (ksplit == 1)
     store([](float* dst, float v) { *dst = v; });
+  else if (parts != nullptr)  // deterministic: this split's partial, same index
+    store([&](float* dst, float v) { parts[ks * part_stride + (dst - C)] = v; });
+  else
+    store([](float* dst, float v) { atomic_add_relaxed(dst, v); });
 }
 
 template <bool GATHER, int EPI>
@@ -729,7 +738,7 @@ static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const Lora
   hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
-                     a.expert_tiles, n_ntiles, a.ksplit, lora);
+                     a.expert_tiles, n_ntiles, a.ksplit, lora, a.parts, a.part_stride);
   return hipGetLastError();
 }
 
@@ -757,20 +766,54 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const L
 
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
-                       int64_t K, float* C, const int4* mtiles, const int32_t* counts,
-                       const int32_t* expert_tiles, int ksplit, const LoraEpilogue* lora,
-                       hipStream_t stream) {
+                       int64_t K, float* C, int64_t c_rows, const int4* mtiles,
+                       const int32_t* counts, const int32_t* expert_tiles, int ksplit,
+                       const LoraEpilogue* lora, float* parts, hipStream_t stream) {
+  ksplit = ksplit < 1 ? 1 : ksplit;
+  float* pp = ksplit > 1 ? parts : nullptr;
   const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts, expert_tiles,
-                   ksplit < 1 ? 1 : ksplit};
+                   ksplit, pp, c_rows * N};
   const bool gather = gather_slots != nullptr;
   // the fused epilogues exist only in the bf16 256-row kernel, unsplit
   if (lora != nullptr && (dtype != DT_BF16 || plan.bm != 256 || a.ksplit != 1))
     return hipErrorInvalidValue;
+  hipError_t e;
   if (dtype == DT_BF16)
-    return gather ? gemm_dispatch<bf16_t, true>(plan, a, lora, stream)
-                  : gemm_dispatch<bf16_t, false>(plan, a, lora, stream);
-  return gather ? gemm_dispatch<float, true>(plan, a, nullptr, stream)
-                : gemm_dispatch<float, false>(plan, a, nullptr, stream);
+    e = gather ? gemm_dispatch<bf16_t, true>(plan, a, lora, stream)
+               : gemm_dispatch<bf16_t, false>(plan, a, lora, stream);
+  else
+    e = gather ? gemm_dispatch<float, true>(plan, a, nullptr, stream)
+               : gemm_dispatch<float, false>(plan, a, nullptr, stream);
+  if (e == hipSuccess && pp != nullptr) e = launch_reduce_parts(pp, ksplit, c_rows * N, C, stream);
+  return e;
+}
+
+// ------------------------------------------------------------ partial sums
+// Deterministic split-K: out = parts[0] + parts[1] + ... in that order.
+__global__ void __launch_bounds__(256)
+k_reduce_parts(const float4* __restrict__ parts, int nparts, int64_t n4, float4* __restrict__ out) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += gridDim.x * 256ll) {
+    float4 s = parts[i];
+    for (int q = 1; q < nparts; ++q) {
+      const float4 v = parts[q * n4 + i];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    out[i] = s;
+  }
+}
+
+hipError_t launch_reduce_parts(const float* parts, int nparts, int64_t n, float* out,
+                               hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_reduce_parts, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     reinterpret_cast<const float4*>(parts), nparts, n4, reinterpret_cast<float4*>(out));
+  return hipGetLastError();
 }
 
 }  // namespace moelora

@@ -33,6 +33,7 @@ struct TilePlan {
   bool lora_db;  // LoRA tiles average many rows: double-buffer their row blocks
   bool fuse_gu;  // gate_up GEMM applies the LoRA expand and SiLU-mul in its epilogue
   bool fuse_dn;  // down GEMM applies the LoRA expand in its epilogue
+  bool det;      // split-K reductions go through ordered partial sums, not atomics
 };
 
 // Operands of the LoRA expand fused into a base GEMM's epilogue:
@@ -65,18 +66,29 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 // C with fp32 atomics (C must be zero beforehand).  lora != nullptr fuses the
 // LoRA expand (and for gate_up the SiLU-mul) into the epilogue; only the bf16
 // 256-row plan with ksplit == 1 has it (hipErrorInvalidValue otherwise).
+// parts != nullptr (deterministic mode, ksplit > 1): split s writes its partial
+// tile to parts + s * c_rows * N and a second launch sums them into C in split
+// order; C needs no clearing then.
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
-                       int64_t K, float* C, const int4* mtiles, const int32_t* counts,
-                       const int32_t* expert_tiles, int ksplit, const LoraEpilogue* lora,
-                       hipStream_t stream);
+                       int64_t K, float* C, int64_t c_rows, const int4* mtiles,
+                       const int32_t* counts, const int32_t* expert_tiles, int ksplit,
+                       const LoraEpilogue* lora, float* parts, hipStream_t stream);
+
+// out[i] = sum over p < nparts, in order, of parts[p * n + i] (n a multiple of 4).
+hipError_t launch_reduce_parts(const float* parts, int nparts, int64_t n, float* out,
+                               hipStream_t stream);
 
 // Z[p][q] += sum_k X[row(p)][k] * At[l][e][q][k] over the LoRA tiles (split-K,
-// fp32 atomics).  Z must be zero beforehand.
+// fp32 atomics; Z must be zero beforehand).  parts != nullptr (deterministic
+// mode): every split writes its partial to parts + s * S * rank and a second
+// launch sums them into Z in split order (Z needs no clearing then);
+// shrink_parts() is the number of partials, known on the host.
 hipError_t launch_shrink(int dtype, int rank, const TilePlan& plan, const void* X, int x_rows,
                          const int32_t* gather_slots, int gather_k, const void* At, int E, int L,
-                         int64_t K, float* Z, const int4* ltiles, const int32_t* counts,
-                         hipStream_t stream);
+                         int64_t K, float* Z, int S, const int4* ltiles, const int32_t* counts,
+                         float* parts, hipStream_t stream);
+int shrink_parts(int dtype, int rank, const TilePlan& plan, int64_t K);
 
 // gate_up expand + base add + SiLU-mul:
 // ACT[p][i] = SiLU(G[p][i] + Z[p].Bt[i]) * (G[p][I+i] + Z[p].Bt[I+i]).

@@ -58,7 +58,8 @@ template <typename T, int R, int STEPS, bool GATHER>
 __global__ void __launch_bounds__(kLoraThreads)
 k_shrink(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
          const T* __restrict__ At, int E, int L, int64_t K, int nsplit, float* __restrict__ Z,
-         const int4* __restrict__ ltiles, const int32_t* __restrict__ counts) {
+         const int4* __restrict__ ltiles, const int32_t* __restrict__ counts,
+         float* __restrict__ parts, int64_t part_stride) {
   typedef Mfma16<T> M;
   typedef typename M::frag_t frag_t;
   constexpr int RB = R / 16;                 // 16-row blocks of A^T
@@ -117,7 +118,11 @@ k_shrink(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather
 #pragma unroll
         for (int w = 1; w < kLoraWaves; ++w) v += red[w][idx];
         const int q = (ji >> 2) * 16 + 4 * (ln >> 4) + (ji & 3);
-        atomic_add_relaxed(Z + static_cast<int64_t>(pr) * R + q, v);
+        const int64_t idx = static_cast<int64_t>(pr) * R + q;
+        if (parts != nullptr)
+          parts[split * part_stride + idx] = v;
+        else
+          atomic_add_relaxed(Z + idx, v);
       }
     }
     __syncthreads();
@@ -133,7 +138,8 @@ __global__ void __launch_bounds__(kLoraThreads)
 k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
               int gather_k, const T* __restrict__ At, int E, int L, int64_t K, int64_t kwg,
               int nsplit, float* __restrict__ Z, const int4* __restrict__ ltiles,
-              const int32_t* __restrict__ counts) {
+              const int32_t* __restrict__ counts, float* __restrict__ parts,
+              int64_t part_stride) {
   typedef Mfma16<T> M;
   typedef typename M::frag_t frag_t;
   constexpr int RB = R / 16;
@@ -193,8 +199,13 @@ k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ g
 #pragma unroll
       for (int j = 0; j < RB; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          atomic_add_relaxed(Z + static_cast<int64_t>(p) * R + 16 * j + 4 * g + i, acc[j][i]);
+        for (int i = 0; i < 4; ++i) {
+          const int64_t idx = static_cast<int64_t>(p) * R + 16 * j + 4 * g + i;
+          if (parts != nullptr)
+            parts[split * part_stride + idx] = acc[j][i];
+          else
+            atomic_add_relaxed(Z + idx, acc[j][i]);
+        }
     }
   }
 }
@@ -209,7 +220,8 @@ k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ g
 // side.  Wave w takes rows 32 (w % 2) .. +32 and, for R <= 32, substeps
 // 2 (w / 2) and 2 (w / 2) + 1 of each K step (R = 64: rank half w / 2, all
 // substeps); it adds its 32 x 32 partial to Z with relaxed fp32 atomics, so Z
-// must be zero beforehand (the split-K of the page's "Kernel optimisation").
+// must be zero beforehand (the split-K of the page's "Kernel optimisation"),
+// or, deterministic, stores it as partial (split, substep pair).
 constexpr int kShrinkStages = 4;
 
 template <int R> struct ShrinkDma {
@@ -241,7 +253,7 @@ __global__ void __launch_bounds__(kLoraThreads)
 k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
              int gather_k, const bf16_t* __restrict__ At, int E, int L, int64_t K, int kwg_steps,
              int nsplit, float* __restrict__ Z, const int4* __restrict__ ltiles,
-             const int32_t* __restrict__ counts) {
+             const int32_t* __restrict__ counts, float* __restrict__ parts, int64_t part_stride) {
   typedef ShrinkDma<R> S;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kShrinkStages * S::STAGE];
   const int lt = blockIdx.x / nsplit;
@@ -310,7 +322,12 @@ k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int p = row0 + 32 * rh + acc_row(i, h);
-      if (p < row_end) atomic_add_relaxed(Z + static_cast<int64_t>(p) * R + q, acc[i]);
+      if (p >= row_end) continue;
+      const int64_t idx = static_cast<int64_t>(p) * R + q;
+      if (parts != nullptr)  // deterministic: partial (split, substep pair)
+        parts[(R > 32 ? split : 2 * split + sel) * part_stride + idx] = acc[i];
+      else
+        atomic_add_relaxed(Z + idx, acc[i]);
     }
   }
 }
@@ -477,74 +494,108 @@ k_combine(const float* __restrict__ D, const int32_t* __restrict__ pos, const fl
 // (64 + 64 columns); down takes 8 blocks for r <= 32
 template <int R, bool GU> constexpr int expand_nb() { return (GU || R > 32) ? 4 : 8; }
 
-template <typename T, int R, bool GATHER>
-static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
-                                const int32_t* gather_slots, int gather_k, const void* At, int E,
-                                int L, int64_t K, float* Z, const int4* ltiles,
-                                const int32_t* counts, hipStream_t stream) {
-  if (plan.lora_db && sizeof(T) == 2) {
-    // tall bf16 tiles: DMA ring, about 1024 workgroups of (tile, K range)
+// Split counts of the three shrink forms (shared by the launch and the host's
+// count of deterministic partials).
+struct ShrinkSplit {
+  int nsplit, kwg_steps, parts;  // parts = partial slices in deterministic mode
+  int64_t kwg;                   // K range per split (k_shrink_tall)
+};
+
+template <typename T, int R>
+static ShrinkSplit shrink_split(const TilePlan& plan, int64_t K) {
+  ShrinkSplit sp{1, 0, 1, K};
+  if (plan.lora_db && sizeof(T) == 2) {  // k_shrink_dma
     const int nk_all = static_cast<int>(K / 64);
     int nsplit = (1024 + plan.max_lt - 1) / std::max(1, plan.max_lt);
     nsplit = std::max(1, std::min(nsplit, nk_all / 4));
-    const int kwg_steps = (nk_all + nsplit - 1) / nsplit;
-    nsplit = (nk_all + kwg_steps - 1) / kwg_steps;
-    const int64_t grid = static_cast<int64_t>(plan.max_lt) * nsplit;
-    hipLaunchKernelGGL((k_shrink_dma<R, GATHER>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kLoraThreads), 0, stream, static_cast<const bf16_t*>(X), x_rows,
-                       gather_slots, gather_k, static_cast<const bf16_t*>(At), E, L, K, kwg_steps,
-                       nsplit, Z, ltiles, counts);
-    return hipGetLastError();
-  }
-  if (plan.lora_db) {
-    // tall tiles: ~1024 workgroups, each wave a 16-row block over the split's K range
+    sp.kwg_steps = (nk_all + nsplit - 1) / nsplit;
+    sp.nsplit = (nk_all + sp.kwg_steps - 1) / sp.kwg_steps;
+    sp.parts = R > 32 ? sp.nsplit : 2 * sp.nsplit;
+  } else if (plan.lora_db) {             // k_shrink_tall
     constexpr int STEPS = R > 32 ? 2 : 4;
     constexpr int64_t KB = STEPS * Mfma16<T>::KSTEP;
     int64_t nsplit = 1024 / std::max(1, plan.max_lt);
     nsplit = std::max<int64_t>(1, std::min<int64_t>(nsplit, K / (4 * KB)));
     int64_t kwg = (K + nsplit - 1) / nsplit;
     kwg = (kwg + KB - 1) / KB * KB;
-    nsplit = (K + kwg - 1) / kwg;
-    const int64_t grid = static_cast<int64_t>(plan.max_lt) * nsplit;
+    sp.kwg = kwg;
+    sp.nsplit = sp.parts = static_cast<int>((K + kwg - 1) / kwg);
+  } else {                               // k_shrink
+    constexpr int STEPS = R <= 32 ? 8 : 4;
+    constexpr int KW = STEPS * Mfma16<T>::KSTEP;
+    sp.nsplit = sp.parts = static_cast<int>((K + kLoraWaves * KW - 1) / (kLoraWaves * KW));
+  }
+  return sp;
+}
+
+template <typename T, int R, bool GATHER>
+static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
+                                const int32_t* gather_slots, int gather_k, const void* At, int E,
+                                int L, int64_t K, float* Z, int S, const int4* ltiles,
+                                const int32_t* counts, float* parts, hipStream_t stream) {
+  const ShrinkSplit sp = shrink_split<T, R>(plan, K);
+  const int64_t stride = static_cast<int64_t>(S) * R;
+  const int64_t grid = static_cast<int64_t>(plan.max_lt) * sp.nsplit;
+  if (plan.lora_db && sizeof(T) == 2) {
+    // tall bf16 tiles: DMA ring, about 1024 workgroups of (tile, K range)
+    hipLaunchKernelGGL((k_shrink_dma<R, GATHER>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kLoraThreads), 0, stream, static_cast<const bf16_t*>(X), x_rows,
+                       gather_slots, gather_k, static_cast<const bf16_t*>(At), E, L, K,
+                       sp.kwg_steps, sp.nsplit, Z, ltiles, counts, parts, stride);
+  } else if (plan.lora_db) {
+    // tall tiles: ~1024 workgroups, each wave a 16-row block over the split's K range
+    constexpr int STEPS = R > 32 ? 2 : 4;
     hipLaunchKernelGGL((k_shrink_tall<T, R, STEPS, GATHER>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const T*>(X), x_rows,
-                       gather_slots, gather_k, static_cast<const T*>(At), E, L, K, kwg,
-                       static_cast<int>(nsplit), Z, ltiles, counts);
-    return hipGetLastError();
+                       gather_slots, gather_k, static_cast<const T*>(At), E, L, K, sp.kwg,
+                       sp.nsplit, Z, ltiles, counts, parts, stride);
+  } else {
+    constexpr int STEPS = R <= 32 ? 8 : 4;
+    hipLaunchKernelGGL((k_shrink<T, R, STEPS, GATHER>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kLoraThreads), 0, stream, static_cast<const T*>(X), x_rows, gather_slots,
+                       gather_k, static_cast<const T*>(At), E, L, K, sp.nsplit, Z, ltiles, counts,
+                       parts, stride);
   }
-  constexpr int STEPS = R <= 32 ? 8 : 4;
-  constexpr int KW = STEPS * Mfma16<T>::KSTEP;
-  const int nsplit = static_cast<int>((K + kLoraWaves * KW - 1) / (kLoraWaves * KW));
-  const int64_t grid = static_cast<int64_t>(plan.max_lt) * nsplit;
-  hipLaunchKernelGGL((k_shrink<T, R, STEPS, GATHER>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kLoraThreads), 0, stream, static_cast<const T*>(X), x_rows, gather_slots,
-                     gather_k, static_cast<const T*>(At), E, L, K, nsplit, Z, ltiles, counts);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && parts != nullptr) e = launch_reduce_parts(parts, sp.parts, stride, Z, stream);
+  return e;
 }
 
 template <typename T, bool GATHER>
 static hipError_t shrink_dispatch(int rank, const TilePlan& plan, const void* X, int x_rows,
                                   const int32_t* gather_slots, int gather_k, const void* At, int E,
-                                  int L, int64_t K, float* Z, const int4* ltiles,
-                                  const int32_t* counts, hipStream_t stream) {
+                                  int L, int64_t K, float* Z, int S, const int4* ltiles,
+                                  const int32_t* counts, float* parts, hipStream_t stream) {
   switch (rank) {
-    case 16: return shrink_launch<T, 16, GATHER>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, ltiles, counts, stream);
-    case 32: return shrink_launch<T, 32, GATHER>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, ltiles, counts, stream);
-    case 64: return shrink_launch<T, 64, GATHER>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, ltiles, counts, stream);
+    case 16: return shrink_launch<T, 16, GATHER>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
+    case 32: return shrink_launch<T, 32, GATHER>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
+    case 64: return shrink_launch<T, 64, GATHER>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_shrink(int dtype, int rank, const TilePlan& plan, const void* X, int x_rows,
                          const int32_t* gather_slots, int gather_k, const void* At, int E, int L,
-                         int64_t K, float* Z, const int4* ltiles, const int32_t* counts,
-                         hipStream_t stream) {
+                         int64_t K, float* Z, int S, const int4* ltiles, const int32_t* counts,
+                         float* parts, hipStream_t stream) {
   const bool gather = gather_slots != nullptr;
   if (dtype == DT_BF16)
-    return gather ? shrink_dispatch<bf16_t, true>(rank, plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, ltiles, counts, stream)
-                  : shrink_dispatch<bf16_t, false>(rank, plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, ltiles, counts, stream);
-  return gather ? shrink_dispatch<float, true>(rank, plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, ltiles, counts, stream)
-                : shrink_dispatch<float, false>(rank, plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, ltiles, counts, stream);
+    return gather ? shrink_dispatch<bf16_t, true>(rank, plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream)
+                  : shrink_dispatch<bf16_t, false>(rank, plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
+  return gather ? shrink_dispatch<float, true>(rank, plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream)
+                : shrink_dispatch<float, false>(rank, plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
+}
+
+int shrink_parts(int dtype, int rank, const TilePlan& plan, int64_t K) {
+  auto pick = [&](auto tag) {
+    typedef decltype(tag) T;
+    switch (rank) {
+      case 16: return shrink_split<T, 16>(plan, K).parts;
+      case 32: return shrink_split<T, 32>(plan, K).parts;
+      default: return shrink_split<T, 64>(plan, K).parts;
+    }
+  };
+  return dtype == DT_BF16 ? pick(bf16_t{}) : pick(float{});
 }
 
 template <typename T, int R, bool GU>

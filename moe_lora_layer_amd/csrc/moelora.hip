@@ -23,6 +23,7 @@ int check_dims(const moelora_dims* d) {
   if (d == nullptr) return MOELORA_ERR_NULL;
   if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
   if (d->rank != 16 && d->rank != 32 && d->rank != 64) return MOELORA_ERR_UNSUPPORTED;
+  if ((d->flags & ~MOELORA_FLAG_DETERMINISTIC) != 0) return MOELORA_ERR_UNSUPPORTED;
   if (d->tokens < 0 || d->hidden <= 0 || d->intermediate <= 0) return MOELORA_ERR_DIMS;
   if (d->hidden % 64 != 0 || d->intermediate % 64 != 0) return MOELORA_ERR_DIMS;
   if (d->hidden > (1 << 20) || d->intermediate > (1 << 20)) return MOELORA_ERR_DIMS;
@@ -56,7 +57,11 @@ TilePlan make_plan(const moelora_dims* d) {
     const int64_t wgs = std::max<int64_t>(1, est_tiles * ((N + 127) / 128));
     const int64_t steps = K / (d->dtype == MOELORA_BF16 ? 64 : 32);
     if (wgs >= 256) return 1;
-    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((1024 + wgs - 1) / wgs, steps / 8)));
+    const int64_t want = std::max<int64_t>(1, std::min<int64_t>((1024 + wgs - 1) / wgs, steps / 8));
+    // equal K ranges with none empty: every split then owns real work (and
+    // writes its whole partial in deterministic mode)
+    const int64_t per = (steps + want - 1) / want;
+    return static_cast<int>((steps + per - 1) / per);
   };
   p.lora_db = S / std::max<int64_t>(1, std::min<int64_t>(nb, S)) > 16;
   p.ksplit_gu = splits(2 * d->intermediate, d->hidden);
@@ -65,11 +70,12 @@ TilePlan make_plan(const moelora_dims* d) {
   const bool fusable = d->dtype == MOELORA_BF16 && p.bm == 256;
   p.fuse_gu = fusable && p.ksplit_gu == 1;
   p.fuse_dn = fusable && p.ksplit_dn == 1;
+  p.det = (d->flags & MOELORA_FLAG_DETERMINISTIC) != 0;
   return p;
 }
 
 struct ForwardLayout {
-  size_t pos, counts, etiles, mtiles, ltiles, g, z1, z2, act, d, total;
+  size_t pos, counts, etiles, mtiles, ltiles, g, z1, z2, act, d, parts, total;
 };
 
 ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
@@ -90,6 +96,18 @@ ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
   L.z2 = off + S * r * 4;  // too when the down GEMM accumulates with atomics
   L.d = off + 2 * S * r * 4;
   off += round_up(2 * S * r * 4 + S * h * 4);
+  // deterministic mode: one region for the split-K partials of whichever
+  // reduction runs (they run one after another)
+  L.parts = off;
+  if (plan.det) {
+    const int dt = d->dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
+    size_t n = 0;
+    n = std::max(n, static_cast<size_t>(moelora::shrink_parts(dt, d->rank, plan, d->hidden)) * S * r);
+    n = std::max(n, static_cast<size_t>(moelora::shrink_parts(dt, d->rank, plan, d->intermediate)) * S * r);
+    if (plan.ksplit_gu > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_gu) * S * 2 * I);
+    if (plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * S * h);
+    off += round_up(n * 4);
+  }
   L.total = off;
   return L;
 }
@@ -268,26 +286,28 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
     return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st);
   };
   // the prep launch also clears Z1, Z2 (and D when the down GEMM is split)
-  const int64_t nzero = 2ll * S * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * h : 0);
+  const int64_t nzero =
+      plan.det ? 0 : 2ll * S * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * h : 0);
+  float* parts = plan.det ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
   hipError_t e = mark(MOELORA_STAGE_PREP);
   if (e == hipSuccess)
     e = moelora::launch_prep(sorted_slots, bucket_offsets, S, E, Lad, plan, pos, mtiles, ltiles,
                              counts, etiles, Z1, nzero, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_ZERO);
-  if (e == hipSuccess && plan.ksplit_gu > 1)
+  if (e == hipSuccess && plan.ksplit_gu > 1 && !plan.det)
     e = moelora::launch_zero(G, static_cast<int64_t>(S) * 2 * I, st);
   // shrinks run before their GEMMs: a fused GEMM epilogue consumes Z
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_GATE_UP);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, x, static_cast<int>(T), sorted_slots, k, a_gate_up, E,
-                               Lad, h, Z1, ltiles, counts, st);
+                               Lad, h, Z1, S, ltiles, counts, parts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);
   if (e == hipSuccess) {
     const moelora::LoraEpilogue epi{Z1, static_cast<const uint16_t*>(b_gate_up), bucket_offsets,
                                     E, Lad, r, 2 * I, static_cast<uint16_t*>(ACT)};
     e = moelora::launch_gemm(dt, plan, x, static_cast<int>(T), sorted_slots, k, w_gate_up, 2 * I,
-                             h, G, mtiles, counts, etiles, plan.ksplit_gu,
-                             plan.fuse_gu ? &epi : nullptr, st);
+                             h, G, S, mtiles, counts, etiles, plan.ksplit_gu,
+                             plan.fuse_gu ? &epi : nullptr, parts, st);
   }
   if (e == hipSuccess) e = mark(MOELORA_STAGE_EXPAND_GATE_UP);
   if (e == hipSuccess && !plan.fuse_gu)
@@ -295,14 +315,14 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
                                        counts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_DOWN);
   if (e == hipSuccess)
-    e = moelora::launch_shrink(dt, r, plan, ACT, S, nullptr, 1, a_down, E, Lad, I, Z2, ltiles,
-                               counts, st);
+    e = moelora::launch_shrink(dt, r, plan, ACT, S, nullptr, 1, a_down, E, Lad, I, Z2, S, ltiles,
+                               counts, parts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
   if (e == hipSuccess) {
     const moelora::LoraEpilogue epi{Z2, static_cast<const uint16_t*>(b_down), bucket_offsets,
                                     E, Lad, r, h, nullptr};
-    e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, mtiles, counts, etiles,
-                             plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, st);
+    e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, S, mtiles, counts,
+                             etiles, plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, parts, st);
   }
   if (e == hipSuccess) e = mark(MOELORA_STAGE_EXPAND_DOWN);
   if (e == hipSuccess && !plan.fuse_dn)

@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoelora.so")
 
 MOELORA_F32, MOELORA_BF16 = 0, 1
+MOELORA_FLAG_DETERMINISTIC = 1
 STAGES = ["prep", "zero", "shrink_gate_up", "gemm_gate_up", "expand_gate_up", "shrink_down",
           "gemm_down", "expand_down", "combine"]
 _TORCH_DT = {MOELORA_F32: torch.float32, MOELORA_BF16: torch.bfloat16}
@@ -28,12 +29,12 @@ class Dims(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("intermediate", ctypes.c_int64), ("experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("adapters", ctypes.c_int32),
-                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
     def __repr__(self):
-        return ("Dims(T=%d, h=%d, I=%d, E=%d, k=%d, L=%d, r=%d, dtype=%d)" %
+        return ("Dims(T=%d, h=%d, I=%d, E=%d, k=%d, L=%d, r=%d, dtype=%d, flags=%d)" %
                 (self.tokens, self.hidden, self.intermediate, self.experts, self.top_k,
-                 self.adapters, self.rank, self.dtype))
+                 self.adapters, self.rank, self.dtype, self.flags))
 
 
 _lib = None
@@ -77,19 +78,23 @@ def _check(rc: int, what: str):
         raise RuntimeError(f"{what}: {status_string(rc)} (status {rc})")
 
 
-def make_dims(tokens, hidden, intermediate, experts, top_k, adapters, rank, dtype) -> Dims:
+def make_dims(tokens, hidden, intermediate, experts, top_k, adapters, rank, dtype,
+              deterministic=False, flags=None) -> Dims:
     if isinstance(dtype, str):
         dtype = _DT_NAME[dtype]
     elif isinstance(dtype, torch.dtype):
         dtype = MOELORA_BF16 if dtype == torch.bfloat16 else MOELORA_F32
+    if flags is None:
+        flags = MOELORA_FLAG_DETERMINISTIC if deterministic else 0
     return Dims(int(tokens), int(hidden), int(intermediate), int(experts), int(top_k),
-                int(adapters), int(rank), int(dtype))
+                int(adapters), int(rank), int(dtype), int(flags))
 
 
-def dims_for(cfg, tokens=None) -> Dims:
+def dims_for(cfg, tokens=None, deterministic=False) -> Dims:
     """Dims of a workload config (moe_lora_layer_amd.synth.LayerConfig)."""
     return make_dims(cfg.tokens if tokens is None else tokens, cfg.hidden, cfg.intermediate,
-                     cfg.experts, cfg.top_k, cfg.adapters, cfg.rank, cfg.dtype)
+                     cfg.experts, cfg.top_k, cfg.adapters, cfg.rank, cfg.dtype,
+                     deterministic=deterministic)
 
 
 def align_workspace_size(d: Dims) -> int:

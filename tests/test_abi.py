@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     assert {"moelora_align", "moelora_forward"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moelora_abi_version() == 2
+    assert lib.moelora_abi_version() == 3
 
 
 def test_status_strings():
@@ -50,7 +50,8 @@ def test_status_strings():
     (dict(hidden=100), ERR_DIMS), (dict(intermediate=96), ERR_DIMS), (dict(tokens=-1), ERR_DIMS),
     (dict(top_k=9, experts=16), ERR_DIMS), (dict(top_k=3, experts=2), ERR_DIMS), (dict(experts=0), ERR_DIMS),
     (dict(adapters=0), ERR_DIMS), (dict(experts=128, adapters=65), ERR_DIMS),
-    (dict(tokens=1 << 30, top_k=2), ERR_DIMS),
+    (dict(tokens=1 << 30, top_k=2), ERR_DIMS), (dict(flags=2), ERR_UNSUPPORTED),
+    (dict(flags=-1), ERR_UNSUPPORTED),
 ])
 def test_dims_validation(kw, rc):
     d = good_dims(**kw)
@@ -142,3 +143,13 @@ def test_forward_fusion_rejects_null_and_bad_dims():
     assert lib.moelora_forward_fusion(ctypes.byref(good_dims()), None) == ERR_NULL
     f = ctypes.c_int()
     assert lib.moelora_forward_fusion(ctypes.byref(good_dims(rank=8)), ctypes.byref(f)) == ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(tokens=96, hidden=128, intermediate=2048, experts=1, top_k=1),
+                                dict(tokens=4096, hidden=4096, intermediate=11008, experts=16)])
+def test_deterministic_workspace_holds_the_partials(kw):
+    n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    lib = ops.library()
+    assert lib.moelora_forward_workspace_size(ctypes.byref(good_dims(**kw)), ctypes.byref(n0)) == OK
+    assert lib.moelora_forward_workspace_size(ctypes.byref(good_dims(flags=1, **kw)), ctypes.byref(n1)) == OK
+    assert n1.value > n0.value

@@ -274,3 +274,57 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(a, b), rep
         assert_close(to_f64(layer.out), to_f64(eager), "bf16", f"replay {rep}")
         del junk
+
+
+DET_SHAPES = [
+    (96, 128, 2048, 1, 1, 4, 16, "bf16"),    # down GEMM split over K
+    (64, 256, 512, 8, 2, 4, 16, "f32"),      # short buckets: k_shrink
+    (600, 128, 192, 4, 2, 3, 16, "bf16"),    # tall buckets: DMA shrink, fused epilogues
+    (520, 192, 256, 2, 1, 9, 64, "bf16"),
+    (600, 192, 128, 4, 2, 2, 32, "f32"),     # tall fp32 shrink
+]
+
+
+@pytest.mark.parametrize("shape", DET_SHAPES, ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
+def test_deterministic_mode_is_bit_reproducible(shape):
+    """MOELORA_FLAG_DETERMINISTIC: three runs, each on a fresh workspace filled
+    with NaN (nothing may rely on cleared memory), give the same output bit for
+    bit, within tolerance of the oracle."""
+    cfg = _small(*shape, seed=sum(shape[:7]) + 1)
+    inp = synth.make_inputs(cfg)
+    dev = device()
+    dinp = device_inputs(inp, cfg, dev)
+    _, w, ss, off, st = run_align(cfg, dinp)
+    d = ops.dims_for(cfg, deterministic=True)
+    outs = []
+    for _ in range(3):
+        ws = ops.workspace(ops.forward_workspace_size(d), dev)
+        ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+        out, _ = run_forward(cfg, dinp, w, ss, off, dims=d, workspace_buf=ws)
+        outs.append(out.clone())
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else o.view(torch.int32),
+                           outs[0].view(torch.int16) if o.dtype == torch.bfloat16 else outs[0].view(torch.int32))
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
+    assert_close(to_f64(outs[0]), ref, cfg.dtype, "out")
+
+
+def test_deterministic_mode_dense_workload():
+    """The dense workload splits its down GEMM 16 ways: deterministic mode gives
+    identical outputs on two runs and stays within tolerance on sampled tokens."""
+    cfg = synth.WORKLOADS["dense_h8192"]
+    inp = synth.make_inputs(cfg)
+    dev = device()
+    dinp = device_inputs(inp, cfg, dev)
+    _, w, ss, off, st = run_align(cfg, dinp)
+    d = ops.dims_for(cfg, deterministic=True)
+    ws = ops.workspace(ops.forward_workspace_size(d), dev)
+    a, _ = run_forward(cfg, dinp, w, ss, off, dims=d, workspace_buf=ws)
+    a = a.clone()
+    b, _ = run_forward(cfg, dinp, w, ss, off, dims=d, workspace_buf=ws)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    toks = sample_tokens(cfg.tokens, 16)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w, tokens=toks)
+    assert_close(to_f64(a)[toks], ref, cfg.dtype, "dense det out")
