@@ -85,6 +85,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_h4096", choices=synth.WORKLOAD_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="MOELORA_FLAG_DETERMINISTIC: ordered split-K partial sums, no atomics")
     ap.add_argument("--cpu-tokens", type=int, default=64,
                     help="tokens in the oracle's timed sample (default 64)")
     args = ap.parse_args()
@@ -117,7 +119,7 @@ def main() -> int:
     x = dev_t(inp["x"])
     logits = torch.from_numpy(inp["logits"]).to(dev)
     adapter_ids = torch.from_numpy(inp["adapter_ids"]).to(dev)
-    d = ops.dims_for(cfg)
+    d = ops.dims_for(cfg, deterministic=args.deterministic)
     layer = ops.MoELoRALayer(d, W, dev)
     nst = len(ops.STAGES)
 
@@ -253,6 +255,7 @@ def main() -> int:
         "roofline": roof,
         "latency_us": {"warm": lat_warm, "cold_1GiB_flush": lat_cold},
         "fusion": fusion,
+        "deterministic": args.deterministic,
         "cpu_baseline": cpu,
         "stages": stages,
     }
