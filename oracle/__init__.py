@@ -50,7 +50,7 @@ def load_library(path: str):
     L = ctypes.CDLL(path)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     L.oracle_route.argtypes = [i64, i32, i32, vp, vp, vp]
-    L.oracle_align.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
+    L.oracle_align.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp]
     L.oracle_slot.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 7 + [i64, i32, i32] + [vp] * 5
     L.oracle_forward.argtypes = ([i64, i64, i64, i32, i32, i32, i32, i32] + [vp] * 7 +
                                  [vp, vp, vp, i64, vp, vp, i32])
@@ -93,15 +93,18 @@ def route(logits: np.ndarray, k: int):
     return ids, w
 
 
-def align(topk_ids: np.ndarray, adapter_ids: np.ndarray, experts: int, adapters: int):
-    """Stable (expert, adapter)-bucketed permutation: (sorted_slots [S], bucket_offsets [E*L+1])."""
+def align(topk_ids: np.ndarray, adapter_ids: np.ndarray, experts: int, adapters: int,
+          base_only: bool = False):
+    """Stable (expert, adapter)-bucketed permutation: (sorted_slots [S], bucket_offsets
+    [E*Lb+1]) with Lb = adapters, or adapters + 1 when base_only (adapter id -1
+    allowed, its slots in each expert's last bucket)."""
     topk_ids = _c(topk_ids, np.int32)
     adapter_ids = _c(adapter_ids, np.int32)
     T, k = topk_ids.shape
     sorted_slots = np.empty(T * k, np.int32)
-    offsets = np.empty(experts * adapters + 1, np.int32)
-    rc = lib().oracle_align(T, k, experts, adapters, _p(topk_ids), _p(adapter_ids),
-                            _p(sorted_slots), _p(offsets))
+    offsets = np.empty(experts * (adapters + (1 if base_only else 0)) + 1, np.int32)
+    rc = lib().oracle_align(T, k, experts, adapters, int(bool(base_only)), _p(topk_ids),
+                            _p(adapter_ids), _p(sorted_slots), _p(offsets))
     if rc != 0:
         raise ValueError(f"oracle_align failed: {rc}")
     return sorted_slots, offsets
@@ -157,6 +160,7 @@ def layer(inp: dict, cfg, tokens=None, threads: int = 0):
     """Route + permutation + forward, as one call; returns (topk_ids, topk_w, sorted_slots,
     bucket_offsets, out)."""
     ids, w = route(inp["logits"], cfg.top_k)
-    ss, off = align(ids, inp["adapter_ids"], cfg.experts, cfg.adapters)
+    base_only = bool(np.any(np.asarray(inp["adapter_ids"]) < 0))
+    ss, off = align(ids, inp["adapter_ids"], cfg.experts, cfg.adapters, base_only=base_only)
     out = forward(inp, dims_of(cfg), ids, w, tokens=tokens, threads=threads)
     return ids, w, ss, off, out

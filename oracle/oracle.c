@@ -134,26 +134,39 @@ int oracle_route(int64_t T, int32_t E, int32_t k, const float* logits,
 
 /*
  * The (expert, adapter)-bucketed permutation: slot s = t*k + j gets key
- * topk_ids[s] * L + adapter_ids[t]; bucket_offsets[b] is the number of slots
- * with key < b (b in [0, E*L]); sorted_slots lists the slots bucket by bucket,
- * ascending slot index inside a bucket (a stable counting sort).
- * Returns ORC_EADAPTER if an adapter id is outside [0, L).
+ * topk_ids[s] * Lb + l(t), with Lb = L buckets per expert and l(t) =
+ * adapter_ids[t]; bucket_offsets[b] is the number of slots with key < b
+ * (b in [0, E*Lb]); sorted_slots lists the slots bucket by bucket, ascending
+ * slot index inside a bucket (a stable counting sort).
+ * base_only != 0: a token may also carry adapter id -1 (the base model with no
+ * adapter; the pages do not cover it, and this reading gives it no LoRA term).
+ * Each expert then has Lb = L + 1 buckets, its base-only slots in the last one
+ * (l(t) = L for adapter -1).
+ * Returns ORC_EADAPTER if an adapter id is outside [0, L) (and not an allowed -1).
  */
-int oracle_align(int64_t T, int32_t k, int32_t E, int32_t L, const int32_t* topk_ids,
-                 const int32_t* adapter_ids, int32_t* sorted_slots, int32_t* bucket_offsets) {
+int oracle_align(int64_t T, int32_t k, int32_t E, int32_t L, int32_t base_only,
+                 const int32_t* topk_ids, const int32_t* adapter_ids, int32_t* sorted_slots,
+                 int32_t* bucket_offsets) {
   if (T < 0 || k < 1 || E < 1 || L < 1) return ORC_EARG;
-  int64_t S = T * k, nb = (int64_t)E * L;
-  for (int64_t t = 0; t < T; ++t)
-    if (adapter_ids[t] < 0 || adapter_ids[t] >= L) return ORC_EADAPTER;
+  int64_t Lb = L + (base_only ? 1 : 0);
+  int64_t S = T * k, nb = (int64_t)E * Lb;
+  for (int64_t t = 0; t < T; ++t) {
+    int32_t l = adapter_ids[t];
+    if (!(l >= 0 && l < L) && !(base_only && l == -1)) return ORC_EADAPTER;
+  }
   for (int64_t s = 0; s < S; ++s)
     if (topk_ids[s] < 0 || topk_ids[s] >= E) return ORC_EARG;
   int64_t* next = (int64_t*)calloc((size_t)nb + 1, sizeof(int64_t));
   if (!next) return ORC_ENOMEM;
-  for (int64_t s = 0; s < S; ++s) next[(int64_t)topk_ids[s] * L + adapter_ids[s / k] + 1] += 1;
+  for (int64_t s = 0; s < S; ++s) {
+    int32_t l = adapter_ids[s / k];
+    next[(int64_t)topk_ids[s] * Lb + (l < 0 ? L : l) + 1] += 1;
+  }
   for (int64_t b = 0; b < nb; ++b) next[b + 1] += next[b];
   for (int64_t b = 0; b <= nb; ++b) bucket_offsets[b] = (int32_t)next[b];
   for (int64_t s = 0; s < S; ++s) {
-    int64_t key = (int64_t)topk_ids[s] * L + adapter_ids[s / k];
+    int32_t l = adapter_ids[s / k];
+    int64_t key = (int64_t)topk_ids[s] * Lb + (l < 0 ? L : l);
     sorted_slots[next[key]++] = (int32_t)s;
   }
   free(next);
@@ -164,15 +177,16 @@ int oracle_align(int64_t T, int32_t k, int32_t E, int32_t L, const int32_t* topk
  * One LoRA projection of an input row v (length K) with base weight W^T rows
  * Wt (N rows of K), shrink factor At (r rows of K) and expand factor Bt
  * (N rows of r):  y = vW + (vA)B.  z receives the shrink result vA.
+ * adapter == 0 (a base-only token): y = vW and z = 0.
  */
 static void lora_projection(const double* v, int64_t K, int64_t N, int32_t r,
                             const void* Wt, int64_t w_off, const void* At, int64_t a_off,
-                            const void* Bt, int64_t b_off, int dtype, double* z, double* y) {
-  for (int32_t q = 0; q < r; ++q) z[q] = dot(v, At, a_off + (int64_t)q * K, K, dtype);
+                            const void* Bt, int64_t b_off, int dtype, int adapter, double* z,
+                            double* y) {
+  for (int32_t q = 0; q < r; ++q) z[q] = adapter ? dot(v, At, a_off + (int64_t)q * K, K, dtype) : 0.0;
   for (int64_t n = 0; n < N; ++n) {
     double base = dot(v, Wt, w_off + n * K, K, dtype);
-    double lora = dot(z, Bt, b_off + n * r, r, dtype);
-    y[n] = base + lora;
+    y[n] = adapter ? base + dot(z, Bt, b_off + n * r, r, dtype) : base;
   }
 }
 
@@ -183,30 +197,31 @@ static double silu(double v) { return v / (1.0 + exp(-v)); }
  *   g  [2I] = x_t W_gu[e] + (x_t A_gu[l][e]) B_gu[l][e]     (z1 [r] = x_t A_gu)
  *   a  [I]  = SiLU(g[0:I]) * g[I:2I]
  *   d  [h]  = a W_dn[e] + (a A_dn[l][e]) B_dn[l][e]           (z2 [r] = a A_dn)
- * Any output pointer may be NULL except where needed internally.
+ * l = -1 (a base-only token): both LoRA terms are absent (z1 = z2 = 0).
  */
 int oracle_slot(int64_t T, int64_t h, int64_t I, int32_t E, int32_t L, int32_t r, int32_t dtype,
                 const void* x, const void* w_gu, const void* w_dn, const void* a_gu,
                 const void* b_gu, const void* a_dn, const void* b_dn, int64_t t, int32_t e,
                 int32_t l, double* g, double* z1, double* a, double* z2, double* d) {
-  if (t < 0 || t >= T || e < 0 || e >= E || l < 0 || l >= L || r < 1 || h < 1 || I < 1)
+  if (t < 0 || t >= T || e < 0 || e >= E || l < -1 || l >= L || r < 1 || h < 1 || I < 1)
     return ORC_EARG;
   double* xin = (double*)malloc(sizeof(double) * (size_t)h);
   if (!xin) return ORC_ENOMEM;
   for (int64_t i = 0; i < h; ++i) xin[i] = elem(x, t * h + i, dtype);
-  int64_t le = (int64_t)l * E + e;
+  int64_t le = (int64_t)(l < 0 ? 0 : l) * E + e;
   lora_projection(xin, h, 2 * I, r, w_gu, (int64_t)e * 2 * I * h, a_gu, le * r * h, b_gu,
-                  le * 2 * I * r, dtype, z1, g);
+                  le * 2 * I * r, dtype, l >= 0, z1, g);
   for (int64_t i = 0; i < I; ++i) a[i] = silu(g[i]) * g[I + i];
   lora_projection(a, I, h, r, w_dn, (int64_t)e * h * I, a_dn, le * r * I, b_dn, le * h * r, dtype,
-                  z2, d);
+                  l >= 0, z2, d);
   free(xin);
   return ORC_OK;
 }
 
 /*
  * Layer output for the selected tokens sel[0..n_sel): out[i][:] (double,
- * [n_sel][h]) = sum_{j<k} topk_w[t][j] * d(t, topk_ids[t][j], adapter_ids[t]),
+ * [n_sel][h]) = sum_{j<k} topk_w[t][j] * d(t, topk_ids[t][j], adapter_ids[t])
+ * (adapter id -1: base-only, see oracle_slot),
  * accumulated in ascending j starting from zero.  Tokens are independent, so
  * they are spread over nthreads OpenMP threads (0 = library default).
  */
@@ -221,7 +236,7 @@ int oracle_forward(int64_t T, int64_t h, int64_t I, int32_t E, int32_t k, int32_
   for (int64_t i = 0; i < n_sel; ++i) {
     if (sel[i] < 0 || sel[i] >= T) return ORC_EARG;
     int32_t l = adapter_ids[sel[i]];
-    if (l < 0 || l >= L) return ORC_EADAPTER;
+    if (l < -1 || l >= L) return ORC_EADAPTER;
   }
   int status = ORC_OK;
 #ifdef _OPENMP

@@ -53,16 +53,18 @@ def dense_reference(inp, cfg):
     kept = np.take_along_axis(probs, order, axis=1)
     gates = np.zeros((T, E))
     np.put_along_axis(gates, order, kept / kept.sum(axis=1, keepdims=True), axis=1)
-    ad = inp["adapter_ids"]
+    ad = np.asarray(inp["adapter_ids"])
+    has = (ad >= 0).astype(np.float64)[:, None, None]   # adapter -1: base model only
+    adc = np.maximum(ad, 0)
     X = f["x"]
-    A1, B1, A2, B2 = f["a_gate_up"][ad], f["b_gate_up"][ad], f["a_down"][ad], f["b_down"][ad]
+    A1, B1, A2, B2 = f["a_gate_up"][adc], f["b_gate_up"][adc], f["a_down"][adc], f["b_down"][adc]
     G = np.einsum("th,enh->ten", X, f["w_gate_up"])
     Z1 = np.einsum("th,terh->ter", X, A1)
-    G = G + np.einsum("ter,tenr->ten", Z1, B1)
+    G = G + has * np.einsum("ter,tenr->ten", Z1, B1)
     act = G[..., :I] * scipy.special.expit(G[..., :I]) * G[..., I:]
     D = np.einsum("tei,ehi->teh", act, f["w_down"])
     Z2 = np.einsum("tei,teri->ter", act, A2)
-    D = D + np.einsum("ter,tehr->teh", Z2, B2)
+    D = D + has * np.einsum("ter,tehr->teh", Z2, B2)
     return np.einsum("te,teh->th", gates, D)
 
 
@@ -117,6 +119,28 @@ def check_align_stable_argsort():
     ids = np.full((9, 2), 1, np.int32)
     ss, off = oracle.align(ids, np.zeros(9, np.int32), 3, 2)
     assert ss.tolist() == list(range(18)) and off.tolist() == [0, 0, 0, 18, 18, 18, 18]
+
+
+def check_align_base_only_argsort():
+    """Adapter id -1 (base model only, with the base-only switch): each expert gets
+    L + 1 buckets, its base-only slots in the last one."""
+    rng = np.random.default_rng(8)
+    for T, k, E, L in [(100, 2, 8, 4), (37, 4, 32, 5), (64, 1, 1, 16), (40, 2, 3, 1)]:
+        ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+        ad = rng.integers(-1, L, size=T).astype(np.int32)
+        ss, off = oracle.align(ids, ad, E, L, base_only=True)
+        lk = np.where(ad < 0, L, ad)
+        keys = (ids.astype(np.int64) * (L + 1) + lk[:, None]).reshape(-1)
+        assert np.array_equal(ss, np.argsort(keys, kind="stable").astype(np.int32)), (T, k, E, L)
+        ref_off = np.concatenate([[0], np.cumsum(np.bincount(keys, minlength=E * (L + 1)))])
+        assert np.array_equal(off, ref_off), (T, k, E, L)
+    # without the switch, adapter -1 is an error
+    try:
+        oracle.align(np.zeros((2, 1), np.int32), np.array([0, -1], np.int32), 2, 2)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("adapter -1 accepted without the base-only switch")
 
 
 # ----------------------------------------------------------------------------- forward
@@ -174,6 +198,27 @@ def check_lora_zero_is_base_moe():
     assert _rel_err(out_b0, dense_reference(zero_b, cfg)) <= REL
 
 
+def check_base_only_is_base_moe():
+    """A base-only token (adapter -1) gets exactly the output it would get if its
+    adapter's B were zero (the LoRA term is then exactly 0.0 in fp64); the other
+    tokens are unchanged bit for bit, and the dense formulation agrees."""
+    cfg = tiny_cfg(T=10, h=16, I=8, E=4, k=2, L=3, r=2, dtype="bf16", seed=33)
+    inp = synth.make_inputs(cfg)
+    *_, out = oracle.layer(inp, cfg, threads=1)
+    ad = inp["adapter_ids"].copy()
+    base_toks = np.array([1, 4, 7])
+    ad_b = ad.copy()
+    ad_b[base_toks] = -1
+    *_, out_b = oracle.layer(dict(inp, adapter_ids=ad_b), cfg, threads=1)
+    zero_b = dict(inp, b_gate_up=np.zeros_like(inp["b_gate_up"]), b_down=np.zeros_like(inp["b_down"]))
+    *_, out_z = oracle.layer(zero_b, cfg, threads=1)
+    assert np.array_equal(out_b[base_toks], out_z[base_toks])
+    keep = np.setdiff1d(np.arange(cfg.tokens), base_toks)
+    assert np.array_equal(out_b[keep], out[keep])
+    assert _rel_err(out_b[base_toks], out[base_toks]) > 1e-3     # the LoRA term did matter
+    assert _rel_err(out_b, dense_reference(dict(inp, adapter_ids=ad_b), cfg)) <= REL
+
+
 def check_merged_weight_identity():
     cfg = tiny_cfg(T=9, h=16, I=8, E=3, k=2, L=3, r=2, dtype="f32", seed=41)
     inp = synth.make_inputs(cfg)
@@ -227,5 +272,6 @@ def check_token_permutation_invariance():
 
 
 ALL_CHECKS = [check_route_ids_stable_argsort, check_route_weights_softmax, check_align_stable_argsort,
-              check_forward_dense_formulation, check_gate_up_integer_exact, check_lora_zero_is_base_moe,
+              check_align_base_only_argsort, check_forward_dense_formulation,
+              check_gate_up_integer_exact, check_lora_zero_is_base_moe, check_base_only_is_base_moe,
               check_merged_weight_identity, check_dense_case_torch, check_token_permutation_invariance]

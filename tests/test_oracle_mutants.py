@@ -11,15 +11,17 @@ import oracle
 import oracle_pins
 
 MUTANTS = {
-    "lora_term_dropped": ("y[n] = base + lora;", "y[n] = base;"),
+    "lora_term_dropped": ("? base + dot(z, Bt, b_off + n * r, r, dtype) : base", "? base : base"),
     "silu_sign": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
     "gate_up_swapped": ("a[i] = silu(g[i]) * g[I + i];", "a[i] = silu(g[I + i]) * g[i];"),
     "tie_to_higher_id": ("lg[e] > lg[best]", "lg[e] >= lg[best]"),
     "b_stride": ("b_off + n * r", "b_off + n"),
     "w_stride": ("w_off + n * K", "w_off + n"),
-    "adapter_expert_index": ("int64_t le = (int64_t)l * E + e;", "int64_t le = (int64_t)e * L + l;"),
+    "adapter_expert_index": ("(int64_t)(l < 0 ? 0 : l) * E + e;", "(int64_t)e * L + (l < 0 ? 0 : l);"),
     "no_renormalisation": ("topk_w[t * k + j] = ex[j] / sum;", "topk_w[t * k + j] = ex[j];"),
-    "adapter_major_keys": ("(int64_t)topk_ids[s] * L + adapter_ids[s / k]", "(int64_t)adapter_ids[s / k] * E + topk_ids[s]"),
+    "adapter_major_keys": ("(int64_t)topk_ids[s] * Lb + (l < 0 ? L : l)", "(int64_t)(l < 0 ? L : l) * E + topk_ids[s]"),
+    "base_only_gets_adapter0_lora": ("le * 2 * I * r, dtype, l >= 0, z1, g);", "le * 2 * I * r, dtype, 1, z1, g);"),
+    "base_only_bucket_first": ("topk_ids[s] * Lb + (l < 0 ? L : l)", "topk_ids[s] * Lb + (l < 0 ? 0 : l + 1)"),
     "combine_weight_dropped": ("o[n] += w * d[n];", "o[n] += d[n];"),
     "x_transposed": ("xin[i] = elem(x, t * h + i, dtype);", "xin[i] = elem(x, i * T + t, dtype);"),
     "down_uses_up_half": ("lora_projection(a, I, h, r, w_dn,", "lora_projection(g + I, I, h, r, w_dn,"),
