@@ -53,7 +53,7 @@ def stage_work(cfg, offsets, fusion):
     b = 2 if cfg.dtype == "bf16" else 4
     counts = np.diff(offsets)
     P = int(np.count_nonzero(counts))                            # active buckets
-    Eact = int(np.count_nonzero(counts.reshape(E, L).sum(axis=1)))  # active experts
+    Eact = int(np.count_nonzero(counts.reshape(E, -1).sum(axis=1)))  # active experts
     w = {
         "prep": (S * 4 * 3 + (E * L + 1) * 4, 0),
         "zero": (2 * S * r * 4, 0),

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOELORA_ABI_VERSION 3
+#define MOELORA_ABI_VERSION 4
 
 typedef enum moelora_status {
   MOELORA_OK = 0,
@@ -76,7 +76,7 @@ typedef struct moelora_dims {
   int32_t adapters;      /* L: adapters resident at once                            */
   int32_t rank;          /* r                                                       */
   int32_t dtype;         /* moelora_dtype                                           */
-  int32_t flags;         /* 0, or MOELORA_FLAG_DETERMINISTIC                         */
+  int32_t flags;         /* 0, or MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_BASE_ONLY */
 } moelora_dims;
 
 /*
@@ -90,6 +90,16 @@ typedef struct moelora_dims {
  * it).
  */
 #define MOELORA_FLAG_DETERMINISTIC 1
+
+/*
+ * MOELORA_FLAG_BASE_ONLY: a token may carry adapter id -1, meaning the base
+ * model without any adapter (the Multi-LoRA page does not cover it; the
+ * reading taken is that such a token has no LoRA term in either projection,
+ * exactly as if its B were zero).  Every expert then has Lb = L + 1 buckets,
+ * its base-only slots in the last one: bucket_offsets has E * (L + 1) + 1
+ * entries (E * L + 1 without the flag), and E * Lb must stay <= 8192.
+ */
+#define MOELORA_FLAG_BASE_ONLY 2
 
 int moelora_abi_version(void);
 
@@ -115,11 +125,13 @@ int moelora_align_workspace_size(const moelora_dims* dims, size_t* bytes);
  * number of slots with key < b.  Both are deterministic and bit-exact.
  *
  *   router_logits  in  float [T][E]
- *   adapter_ids    in  int32 [T], each in [0, L)
+ *   adapter_ids    in  int32 [T], each in [0, L) (or -1 with MOELORA_FLAG_BASE_ONLY)
  *   topk_ids       out int32 [T][k]
  *   topk_weights   out float [T][k]
  *   sorted_slots   out int32 [T*k]
- *   bucket_offsets out int32 [E*L + 1]   (bucket_offsets[E*L] = T*k)
+ *   bucket_offsets out int32 [E*Lb + 1]  (Lb = L, or L + 1 with MOELORA_FLAG_BASE_ONLY;
+ *                  bucket_offsets[E*Lb] = T*k; a base-only token's key is
+ *                  topk_ids[s] * Lb + L)
  *   device_status  out int32 [1] or NULL: 0 = ok, 1 = an adapter id was outside
  *                  [0, L) (it was treated as 0; the outputs are then unspecified).
  *                  Read it after the stream has executed the call.

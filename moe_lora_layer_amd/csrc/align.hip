@@ -37,7 +37,7 @@ template <bool KEYS_LDS, bool ROUTE>
 __global__ void __launch_bounds__(kAlignThreads)
 k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
         const int32_t* __restrict__ adapter_ids, int T, int E,
-        int k, int L, int chunks, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+        int k, int L, int Lb, int chunks, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
         int32_t* __restrict__ sorted_slots, int32_t* __restrict__ offsets,
         int32_t* __restrict__ status, int32_t* __restrict__ ws_key, int32_t* __restrict__ ws_rank) {
   extern __shared__ int cnt[];  // [chunks][nb], then (KEYS_LDS) key[S], rank[S]
@@ -47,7 +47,7 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int nb = E * L;
+  const int nb = E * Lb;
   const int S = T * k;
 
   int* key_buf = KEYS_LDS ? cnt + chunks * nb : ws_key;
@@ -59,7 +59,9 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
   // ---- 1. route --------------------------------------------------------------
   for (int t = tid; t < T; t += kAlignThreads) {
     int l = adapter_ids[t];
-    if (l < 0 || l >= L) {
+    if (l == -1 && Lb > L) {
+      l = L;  // base-only token: the expert's last bucket
+    } else if (l < 0 || l >= L) {
       atomicMax(&bad, 1);
       l = 0;
     }
@@ -71,7 +73,7 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
           atomicMax(&bad, 3);
           e = 0;
         }
-        key_buf[s] = e * L + l;
+        key_buf[s] = e * Lb + l;
       }
       continue;
     }
@@ -117,7 +119,7 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
         int s = t * k + q;
         topk_ids[s] = id[q];
         topk_w[s] = ex[q] / sum;
-        key_buf[s] = id[q] * L + l;
+        key_buf[s] = id[q] * Lb + l;
       }
     }
   }
@@ -198,17 +200,17 @@ int align_chunks(int nb, int S) {
 }
 
 hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_t* adapter_ids,
-                        int T, int E, int k, int L, int32_t* topk_ids, float* topk_w,
+                        int T, int E, int k, int L, int Lb, int32_t* topk_ids, float* topk_w,
                         int32_t* sorted_slots, int32_t* offsets, int32_t* status, int32_t* ws_key,
                         int32_t* ws_rank, hipStream_t stream) {
-  const int nb = E * L;
+  const int nb = E * Lb;
   const int S = T * k;
   const int chunks = align_chunks(nb, S);
   const bool in_lds = keys_in_lds(S, nb);
   const size_t lds = (static_cast<size_t>(chunks) * nb + (in_lds ? 2 * S : 0)) * sizeof(int);
 #define MOELORA_ALIGN_LAUNCH(KL, RT)                                                              \
   hipLaunchKernelGGL((k_align<KL, RT>), dim3(1), dim3(kAlignThreads), lds, stream, logits, ids_in, \
-                     adapter_ids, T, E, k, L, chunks, topk_ids, topk_w, sorted_slots, offsets,     \
+                     adapter_ids, T, E, k, L, Lb, chunks, topk_ids, topk_w, sorted_slots, offsets, \
                      status, ws_key, ws_rank)
   const bool route = logits != nullptr;
   if (in_lds) {

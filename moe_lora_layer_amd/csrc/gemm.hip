@@ -656,7 +656,8 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   const int rw1 = min(row_end, rw0 + 128);
 
   if (EPI != EPI_STORE && rw0 < rw1) {
-    const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.adapters;
+    // the expert's adapter buckets (a base-only bucket, if any, comes last and is skipped)
+    const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
     // last bucket of expert e starting at or before rw0
     int lb = 0, ub = lora.adapters - 1;
     while (lb < ub) {

@@ -15,8 +15,10 @@ int align_chunks(int nb, int S);
 
 // logits == nullptr: the expert ids come from ids_in (no routing, topk_ids and
 // topk_w untouched).
+// L adapters; Lb buckets per expert (L, or L + 1 when adapter id -1 marks a
+// base-only token, keyed to bucket L of its expert).
 hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_t* adapter_ids,
-                        int T, int E, int k, int L, int32_t* topk_ids, float* topk_w,
+                        int T, int E, int k, int L, int Lb, int32_t* topk_ids, float* topk_w,
                         int32_t* sorted_slots, int32_t* offsets, int32_t* status, int32_t* ws_key,
                         int32_t* ws_rank, hipStream_t stream);
 
@@ -34,6 +36,7 @@ struct TilePlan {
   bool fuse_gu;  // gate_up GEMM applies the LoRA expand and SiLU-mul in its epilogue
   bool fuse_dn;  // down GEMM applies the LoRA expand in its epilogue
   bool det;      // split-K reductions go through ordered partial sums, not atomics
+  int nad;       // adapters; bucket index nad of an expert (base-only tokens) has no LoRA
 };
 
 // Operands of the LoRA expand fused into a base GEMM's epilogue:
@@ -43,8 +46,9 @@ struct TilePlan {
 struct LoraEpilogue {
   const float* z;           // [S][rank] fp32, sorted order
   const uint16_t* b;        // [L][E][b_rows][rank] bf16
-  const int32_t* offsets;   // bucket_offsets [E*L + 1]
+  const int32_t* offsets;   // bucket_offsets [E*buckets + 1]
   int experts, adapters, rank;
+  int buckets;              // buckets per expert (adapters, + 1 with base-only tokens)
   int64_t b_rows;           // rows of each B block (2I for gate_up, h for down)
   uint16_t* act;            // bf16 [S][I] output of the gate_up form, else nullptr
 };

@@ -57,8 +57,8 @@ template <> struct ZFrag<float> {
 template <typename T, int R, int STEPS, bool GATHER>
 __global__ void __launch_bounds__(kLoraThreads)
 k_shrink(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
-         const T* __restrict__ At, int E, int L, int64_t K, int nsplit, float* __restrict__ Z,
-         const int4* __restrict__ ltiles, const int32_t* __restrict__ counts,
+         const T* __restrict__ At, int E, int L, int nad, int64_t K, int nsplit,
+         float* __restrict__ Z, const int4* __restrict__ ltiles, const int32_t* __restrict__ counts,
          float* __restrict__ parts, int64_t part_stride) {
   typedef Mfma16<T> M;
   typedef typename M::frag_t frag_t;
@@ -72,6 +72,7 @@ k_shrink(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather
   const int4 tile = ltiles[lt];
   const int b = tile.x, row0 = tile.y, row_end = tile.z;
   const int e = b / L, l = b % L;
+  if (l >= nad) return;  // base-only bucket: no LoRA term
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -136,7 +137,7 @@ k_shrink(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather
 template <typename T, int R, int STEPS, bool GATHER>
 __global__ void __launch_bounds__(kLoraThreads)
 k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
-              int gather_k, const T* __restrict__ At, int E, int L, int64_t K, int64_t kwg,
+              int gather_k, const T* __restrict__ At, int E, int L, int nad, int64_t K, int64_t kwg,
               int nsplit, float* __restrict__ Z, const int4* __restrict__ ltiles,
               const int32_t* __restrict__ counts, float* __restrict__ parts,
               int64_t part_stride) {
@@ -150,6 +151,7 @@ k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ g
   const int4 tile = ltiles[lt];
   const int b = tile.x, row0 = tile.y, row_end = tile.z;
   const int e = b / L, l = b % L;
+  if (l >= nad) return;  // base-only bucket: no LoRA term
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int c = lane & 15, g = lane >> 4;
@@ -251,7 +253,7 @@ __device__ __forceinline__ void shrink_issue(unsigned char* smem, int slot, int6
 template <int R, bool GATHER>
 __global__ void __launch_bounds__(kLoraThreads)
 k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
-             int gather_k, const bf16_t* __restrict__ At, int E, int L, int64_t K, int kwg_steps,
+             int gather_k, const bf16_t* __restrict__ At, int E, int L, int nad, int64_t K, int kwg_steps,
              int nsplit, float* __restrict__ Z, const int4* __restrict__ ltiles,
              const int32_t* __restrict__ counts, float* __restrict__ parts, int64_t part_stride) {
   typedef ShrinkDma<R> S;
@@ -262,6 +264,7 @@ k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict
   const int4 tile = ltiles[lt];
   const int b = tile.x, row0 = tile.y, row_end = tile.z;
   const int e = b / L, l = b % L;
+  if (l >= nad) return;  // base-only bucket: no LoRA term
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int c32 = lane & 31, h = lane >> 5;
   const int nk_all = static_cast<int>(K / 64);
@@ -346,7 +349,7 @@ k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict
 // buffer, whose first fetch still overlaps the weight loads.
 template <typename T, int R, int NB, bool GATE_UP, bool DB>
 __global__ void __launch_bounds__(kLoraThreads)
-k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L,
+k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L, int nad,
          const float* __restrict__ G, T* __restrict__ ACT, float* __restrict__ D, int64_t ncols,
          const int4* __restrict__ ltiles, const int32_t* __restrict__ counts, int n_chunks) {
   typedef Mfma16<T> M;
@@ -364,9 +367,13 @@ k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L,
   const int4 tile = ltiles[lt];
   const int b = tile.x, row0 = tile.y, row_end = tile.z;
   const int e = b / L, l = b % L;
+  // base-only bucket: no LoRA term; gate_up still produces ACT from G alone
+  const bool lora = l < nad;
+  if (!GATE_UP && !lora) return;
 
   const int64_t nfull = GATE_UP ? 2 * ncols : ncols;
-  const T* Bb = Bt + (static_cast<int64_t>(l) * E + e) * nfull * R;
+  // (a base-only tile never loads B; its pointer still stays inside the array)
+  const T* Bb = Bt + (static_cast<int64_t>(lora ? l : 0) * E + e) * nfull * R;
   bool nb_ok[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) nb_ok[j] = c0 + 16 * j < ncols;  // uniform per wave
@@ -379,7 +386,7 @@ k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L,
       for (int ks = 0; ks < KS; ++ks) {
         const int q = ks * M::KSTEP + g * M::KPACK;
         const int64_t n = hh * ncols + c0 + 16 * j + c;
-        bf[hh][j][ks] = (q < R && nb_ok[j]) ? M::load(Bb + n * R + q) : M::zero();
+        bf[hh][j][ks] = (lora && q < R && nb_ok[j]) ? M::load(Bb + n * R + q) : M::zero();
       }
 
   // per 16-row block: z fragments and the four base values per column block
@@ -393,7 +400,7 @@ k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int q = ks * M::KSTEP + g * M::KPACK;
-      if (ok && q < R)
+      if (lora && ok && q < R)
         blk.zf[ks].load(Z + static_cast<int64_t>(p) * R + q);
       else
         blk.zf[ks].clear();
@@ -540,21 +547,21 @@ static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
     // tall bf16 tiles: DMA ring, about 1024 workgroups of (tile, K range)
     hipLaunchKernelGGL((k_shrink_dma<R, GATHER>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const bf16_t*>(X), x_rows,
-                       gather_slots, gather_k, static_cast<const bf16_t*>(At), E, L, K,
+                       gather_slots, gather_k, static_cast<const bf16_t*>(At), E, L, plan.nad, K,
                        sp.kwg_steps, sp.nsplit, Z, ltiles, counts, parts, stride);
   } else if (plan.lora_db) {
     // tall tiles: ~1024 workgroups, each wave a 16-row block over the split's K range
     constexpr int STEPS = R > 32 ? 2 : 4;
     hipLaunchKernelGGL((k_shrink_tall<T, R, STEPS, GATHER>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const T*>(X), x_rows,
-                       gather_slots, gather_k, static_cast<const T*>(At), E, L, K, sp.kwg,
+                       gather_slots, gather_k, static_cast<const T*>(At), E, L, plan.nad, K, sp.kwg,
                        sp.nsplit, Z, ltiles, counts, parts, stride);
   } else {
     constexpr int STEPS = R <= 32 ? 8 : 4;
     hipLaunchKernelGGL((k_shrink<T, R, STEPS, GATHER>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const T*>(X), x_rows, gather_slots,
-                       gather_k, static_cast<const T*>(At), E, L, K, sp.nsplit, Z, ltiles, counts,
-                       parts, stride);
+                       gather_k, static_cast<const T*>(At), E, L, plan.nad, K, sp.nsplit, Z, ltiles,
+                       counts, parts, stride);
   }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && parts != nullptr) e = launch_reduce_parts(parts, sp.parts, stride, Z, stream);
@@ -608,11 +615,11 @@ static hipError_t expand_launch(const TilePlan& plan, const float* Z, const void
   const int64_t grid = static_cast<int64_t>(plan.max_lt) * n_chunks;
   if (plan.lora_db)
     hipLaunchKernelGGL((k_expand<T, R, NB, GU, true>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kLoraThreads), 0, stream, Z, static_cast<const T*>(Bt), E, L, G,
+                       dim3(kLoraThreads), 0, stream, Z, static_cast<const T*>(Bt), E, L, plan.nad, G,
                        static_cast<T*>(ACT), D, ncols, ltiles, counts, n_chunks);
   else
     hipLaunchKernelGGL((k_expand<T, R, NB, GU, false>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kLoraThreads), 0, stream, Z, static_cast<const T*>(Bt), E, L, G,
+                       dim3(kLoraThreads), 0, stream, Z, static_cast<const T*>(Bt), E, L, plan.nad, G,
                        static_cast<T*>(ACT), D, ncols, ltiles, counts, n_chunks);
   return hipGetLastError();
 }

@@ -19,25 +19,31 @@ size_t round_up(size_t x) { return (x + kSectionAlign - 1) / kSectionAlign * kSe
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// buckets per expert: the adapters, plus one for base-only tokens when enabled
+int64_t buckets_per_expert(const moelora_dims* d) {
+  return static_cast<int64_t>(d->adapters) + ((d->flags & MOELORA_FLAG_BASE_ONLY) ? 1 : 0);
+}
+
 int check_dims(const moelora_dims* d) {
   if (d == nullptr) return MOELORA_ERR_NULL;
   if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
   if (d->rank != 16 && d->rank != 32 && d->rank != 64) return MOELORA_ERR_UNSUPPORTED;
-  if ((d->flags & ~MOELORA_FLAG_DETERMINISTIC) != 0) return MOELORA_ERR_UNSUPPORTED;
+  if ((d->flags & ~(MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_BASE_ONLY)) != 0)
+    return MOELORA_ERR_UNSUPPORTED;
   if (d->tokens < 0 || d->hidden <= 0 || d->intermediate <= 0) return MOELORA_ERR_DIMS;
   if (d->hidden % 64 != 0 || d->intermediate % 64 != 0) return MOELORA_ERR_DIMS;
   if (d->hidden > (1 << 20) || d->intermediate > (1 << 20)) return MOELORA_ERR_DIMS;
   if (d->experts < 1 || d->adapters < 1 || d->top_k < 1 || d->top_k > 8 ||
       d->top_k > d->experts)
     return MOELORA_ERR_DIMS;
-  if (static_cast<int64_t>(d->experts) * d->adapters > 8192) return MOELORA_ERR_DIMS;
+  if (static_cast<int64_t>(d->experts) * buckets_per_expert(d) > 8192) return MOELORA_ERR_DIMS;
   if (d->tokens * d->top_k >= (1ll << 31)) return MOELORA_ERR_DIMS;
   return MOELORA_OK;
 }
 
 TilePlan make_plan(const moelora_dims* d) {
   const int64_t S = d->tokens * d->top_k;
-  const int64_t E = d->experts, nb = E * d->adapters;
+  const int64_t E = d->experts, nb = E * buckets_per_expert(d);
   const int64_t avg = (S + E - 1) / E;  // mean rows per expert
   TilePlan p;
   // one M-tile per expert in the common case: mean rows per expert plus 25%
@@ -71,6 +77,7 @@ TilePlan make_plan(const moelora_dims* d) {
   p.fuse_gu = fusable && p.ksplit_gu == 1;
   p.fuse_dn = fusable && p.ksplit_dn == 1;
   p.det = (d->flags & MOELORA_FLAG_DETERMINISTIC) != 0;
+  p.nad = d->adapters;
   return p;
 }
 
@@ -165,7 +172,8 @@ int moelora_align(const moelora_dims* dims, const float* router_logits,
   int32_t* ws_rank = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + round_up(S * 4));
   return hip_status(moelora::launch_align(router_logits, nullptr, adapter_ids,
                                           static_cast<int>(T), dims->experts, dims->top_k,
-                                          dims->adapters, topk_ids, topk_weights, sorted_slots,
+                                          dims->adapters, static_cast<int>(buckets_per_expert(dims)),
+                                          topk_ids, topk_weights, sorted_slots,
                                           bucket_offsets, device_status, ws_key, ws_rank,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -190,7 +198,8 @@ int moelora_align_topk(const moelora_dims* dims, const int32_t* topk_ids,
   int32_t* ws_key = static_cast<int32_t*>(workspace);
   int32_t* ws_rank = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + round_up(S * 4));
   return hip_status(moelora::launch_align(nullptr, topk_ids, adapter_ids, static_cast<int>(T),
-                                          dims->experts, dims->top_k, dims->adapters, nullptr,
+                                          dims->experts, dims->top_k, dims->adapters,
+                                          static_cast<int>(buckets_per_expert(dims)), nullptr,
                                           nullptr, sorted_slots, bucket_offsets, device_status,
                                           ws_key, ws_rank, static_cast<hipStream_t>(stream)));
 }
@@ -256,7 +265,10 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
     if (!aligned16(p)) return MOELORA_ERR_ALIGNMENT;
   if (!aligned16(workspace)) return MOELORA_ERR_ALIGNMENT;
 
-  const int k = dims->top_k, E = dims->experts, Lad = dims->adapters, r = dims->rank;
+  // Lad: buckets per expert in bucket_offsets (adapters, + 1 for base-only tokens);
+  // plan.nad: the adapters themselves
+  const int k = dims->top_k, E = dims->experts, r = dims->rank;
+  const int Lad = static_cast<int>(buckets_per_expert(dims));
   const int dt = dims->dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
   const int64_t h = dims->hidden, I = dims->intermediate;
   const int S = static_cast<int>(T * k);
@@ -304,7 +316,7 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);
   if (e == hipSuccess) {
     const moelora::LoraEpilogue epi{Z1, static_cast<const uint16_t*>(b_gate_up), bucket_offsets,
-                                    E, Lad, r, 2 * I, static_cast<uint16_t*>(ACT)};
+                                    E, dims->adapters, r, Lad, 2 * I, static_cast<uint16_t*>(ACT)};
     e = moelora::launch_gemm(dt, plan, x, static_cast<int>(T), sorted_slots, k, w_gate_up, 2 * I,
                              h, G, S, mtiles, counts, etiles, plan.ksplit_gu,
                              plan.fuse_gu ? &epi : nullptr, parts, st);
@@ -320,7 +332,7 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
   if (e == hipSuccess) {
     const moelora::LoraEpilogue epi{Z2, static_cast<const uint16_t*>(b_down), bucket_offsets,
-                                    E, Lad, r, h, nullptr};
+                                    E, dims->adapters, r, Lad, h, nullptr};
     e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, S, mtiles, counts,
                              etiles, plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, parts, st);
   }

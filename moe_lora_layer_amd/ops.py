@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoelora.so")
 
 MOELORA_F32, MOELORA_BF16 = 0, 1
 MOELORA_FLAG_DETERMINISTIC = 1
+MOELORA_FLAG_BASE_ONLY = 2
 STAGES = ["prep", "zero", "shrink_gate_up", "gemm_gate_up", "expand_gate_up", "shrink_down",
           "gemm_down", "expand_down", "combine"]
 _TORCH_DT = {MOELORA_F32: torch.float32, MOELORA_BF16: torch.bfloat16}
@@ -79,22 +80,28 @@ def _check(rc: int, what: str):
 
 
 def make_dims(tokens, hidden, intermediate, experts, top_k, adapters, rank, dtype,
-              deterministic=False, flags=None) -> Dims:
+              deterministic=False, base_only=False, flags=None) -> Dims:
     if isinstance(dtype, str):
         dtype = _DT_NAME[dtype]
     elif isinstance(dtype, torch.dtype):
         dtype = MOELORA_BF16 if dtype == torch.bfloat16 else MOELORA_F32
     if flags is None:
-        flags = MOELORA_FLAG_DETERMINISTIC if deterministic else 0
+        flags = ((MOELORA_FLAG_DETERMINISTIC if deterministic else 0) |
+                 (MOELORA_FLAG_BASE_ONLY if base_only else 0))
     return Dims(int(tokens), int(hidden), int(intermediate), int(experts), int(top_k),
                 int(adapters), int(rank), int(dtype), int(flags))
 
 
-def dims_for(cfg, tokens=None, deterministic=False) -> Dims:
+def dims_for(cfg, tokens=None, deterministic=False, base_only=False) -> Dims:
     """Dims of a workload config (moe_lora_layer_amd.synth.LayerConfig)."""
     return make_dims(cfg.tokens if tokens is None else tokens, cfg.hidden, cfg.intermediate,
                      cfg.experts, cfg.top_k, cfg.adapters, cfg.rank, cfg.dtype,
-                     deterministic=deterministic)
+                     deterministic=deterministic, base_only=base_only)
+
+
+def buckets(d: Dims) -> int:
+    """(expert, adapter) buckets: E * L, or E * (L + 1) with base-only tokens."""
+    return d.experts * (d.adapters + (1 if d.flags & MOELORA_FLAG_BASE_ONLY else 0))
 
 
 def align_workspace_size(d: Dims) -> int:
@@ -164,7 +171,7 @@ def align(d: Dims, logits: torch.Tensor, adapter_ids: torch.Tensor, *, out=None,
         out = (torch.empty((T, k), dtype=torch.int32, device=dev),
                torch.empty((T, k), dtype=torch.float32, device=dev),
                torch.empty((T * k,), dtype=torch.int32, device=dev),
-               torch.empty((E * L + 1,), dtype=torch.int32, device=dev))
+               torch.empty((buckets(d) + 1,), dtype=torch.int32, device=dev))
     topk_ids, topk_w, sorted_slots, offsets = out
     if status is None:
         status = torch.zeros((4,), dtype=torch.int32, device=dev)
@@ -187,7 +194,7 @@ def align_topk(d: Dims, topk_ids: torch.Tensor, adapter_ids: torch.Tensor, *, ou
     _expect(adapter_ids, "adapter_ids", (T,), torch.int32, dev)
     if out is None:
         out = (torch.empty((T * k,), dtype=torch.int32, device=dev),
-               torch.empty((E * L + 1,), dtype=torch.int32, device=dev))
+               torch.empty((buckets(d) + 1,), dtype=torch.int32, device=dev))
     sorted_slots, offsets = out
     if status is None:
         status = torch.zeros((4,), dtype=torch.int32, device=dev)
@@ -218,7 +225,7 @@ def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
     _expect(b_down, "b_down", (L, E, h, r), dt, dev)
     _expect(topk_weights, "topk_weights", (T, k), torch.float32, dev)
     _expect(sorted_slots, "sorted_slots", (T * k,), torch.int32, dev)
-    _expect(bucket_offsets, "bucket_offsets", (E * L + 1,), torch.int32, dev)
+    _expect(bucket_offsets, "bucket_offsets", (buckets(d) + 1,), torch.int32, dev)
     if out is None:
         out = torch.empty((T, h), dtype=dt, device=dev)
     _expect(out, "out", (T, h), dt, dev)
@@ -254,7 +261,7 @@ class MoELoRALayer:
         self.routing = (torch.empty((T, k), dtype=torch.int32, device=device),
                         torch.empty((T, k), dtype=torch.float32, device=device),
                         torch.empty((T * k,), dtype=torch.int32, device=device),
-                        torch.empty((E * L + 1,), dtype=torch.int32, device=device))
+                        torch.empty((buckets(d) + 1,), dtype=torch.int32, device=device))
         self.status = torch.zeros((4,), dtype=torch.int32, device=device)
         self.ws_align = workspace(align_workspace_size(d), device)
         self.ws_fwd = workspace(forward_workspace_size(d), device)

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     assert {"moelora_align", "moelora_forward"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moelora_abi_version() == 3
+    assert lib.moelora_abi_version() == 4
 
 
 def test_status_strings():
@@ -50,8 +50,9 @@ def test_status_strings():
     (dict(hidden=100), ERR_DIMS), (dict(intermediate=96), ERR_DIMS), (dict(tokens=-1), ERR_DIMS),
     (dict(top_k=9, experts=16), ERR_DIMS), (dict(top_k=3, experts=2), ERR_DIMS), (dict(experts=0), ERR_DIMS),
     (dict(adapters=0), ERR_DIMS), (dict(experts=128, adapters=65), ERR_DIMS),
-    (dict(tokens=1 << 30, top_k=2), ERR_DIMS), (dict(flags=2), ERR_UNSUPPORTED),
-    (dict(flags=-1), ERR_UNSUPPORTED),
+    (dict(tokens=1 << 30, top_k=2), ERR_DIMS), (dict(flags=4), ERR_UNSUPPORTED),
+    (dict(flags=-1), ERR_UNSUPPORTED), (dict(flags=3), OK),
+    (dict(experts=128, adapters=64), OK), (dict(experts=128, adapters=64, flags=2), ERR_DIMS),
 ])
 def test_dims_validation(kw, rc):
     d = good_dims(**kw)

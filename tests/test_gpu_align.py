@@ -138,3 +138,38 @@ def test_align_topk_reports_bad_ids():
     bad_l[9] = -1
     assert _topk(cfg, ids, bad_l)[2] == 1
     assert _topk(cfg, bad_e, bad_l)[2] == 3      # the larger code is reported
+
+
+@pytest.mark.parametrize("T,E,k,L", [(50, 8, 2, 4), (1000, 32, 8, 16), (5000, 16, 2, 8), (300, 64, 4, 1)])
+def test_align_base_only_tokens(T, E, k, L):
+    """MOELORA_FLAG_BASE_ONLY: adapter id -1 goes to each expert's extra last
+    bucket; routing and permutation equal the oracle's bit for bit, for
+    moelora_align and moelora_align_topk."""
+    cfg = _cfg(T, E, k, L, seed=6)
+    r = synth.make_routing_inputs(cfg)
+    rng = np.random.default_rng(T)
+    ad = np.where(rng.random(T) < 0.3, -1, r["adapter_ids"]).astype(np.int32)
+    dev = device()
+    d = ops.dims_for(cfg, base_only=True)
+    ids, w, ss, off, st = ops.align(d, torch.from_numpy(r["logits"]).to(dev), torch.from_numpy(ad).to(dev))
+    torch.cuda.synchronize()
+    ref_ids, _ = oracle.route(r["logits"], k)
+    ref_ss, ref_off = oracle.align(ref_ids, ad, E, L, base_only=True)
+    assert int(st[0].item()) == 0
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.array_equal(ss.cpu().numpy(), ref_ss) and np.array_equal(off.cpu().numpy(), ref_off)
+    ss2, off2, st2 = ops.align_topk(d, ids, torch.from_numpy(ad).to(dev))
+    torch.cuda.synchronize()
+    assert int(st2[0].item()) == 0
+    assert np.array_equal(ss2.cpu().numpy(), ref_ss) and np.array_equal(off2.cpu().numpy(), ref_off)
+
+
+def test_align_minus_one_needs_the_flag():
+    cfg = _cfg(20, 4, 2, 3)
+    r = synth.make_routing_inputs(cfg)
+    r["adapter_ids"][2] = -1
+    dev = device()
+    _, _, ss, _, st = ops.align(ops.dims_for(cfg), torch.from_numpy(r["logits"]).to(dev),
+                                torch.from_numpy(r["adapter_ids"]).to(dev))
+    torch.cuda.synchronize()
+    assert int(st[0].item()) == 1 and sorted(ss.cpu().numpy().tolist()) == list(range(40))

@@ -328,3 +328,37 @@ def test_deterministic_mode_dense_workload():
     toks = sample_tokens(cfg.tokens, 16)
     ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w, tokens=toks)
     assert_close(to_f64(a)[toks], ref, cfg.dtype, "dense det out")
+
+
+BASE_ONLY_SHAPES = [
+    (64, 256, 512, 8, 2, 4, 16, "bf16", 0.3),    # 32-row tiles
+    (96, 192, 320, 5, 2, 3, 32, "f32", 0.3),     # 64-row tiles, fp32
+    (200, 320, 192, 6, 2, 3, 64, "bf16", 0.3),   # 128-row tiles
+    (600, 128, 192, 4, 2, 3, 16, "bf16", 0.3),   # 256-row tiles: fused epilogues, DMA shrink
+    (600, 192, 128, 4, 2, 2, 32, "f32", 0.5),    # 256-row fp32 tiles, tall shrink
+    (96, 128, 2048, 1, 1, 4, 16, "bf16", 0.3),   # split-K down GEMM
+    (300, 128, 256, 3, 2, 2, 32, "bf16", 1.0),   # every token base-only
+]
+
+
+@pytest.mark.parametrize("shape", BASE_ONLY_SHAPES, ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s_p%.1f" % s)
+@pytest.mark.parametrize("det", [False, True], ids=["atomics", "deterministic"])
+def test_forward_base_only_tokens(shape, det):
+    """MOELORA_FLAG_BASE_ONLY: tokens with adapter id -1 get the base MoE output
+    (no LoRA term), the others their adapter's, against the oracle."""
+    *dims, frac = shape
+    cfg = _small(*dims, seed=sum(dims[:7]) + 3)
+    inp = synth.make_inputs(cfg)
+    rng = np.random.default_rng(cfg.tokens)
+    inp["adapter_ids"] = np.where(rng.random(cfg.tokens) < frac, -1, inp["adapter_ids"]).astype(np.int32)
+    dev = device()
+    dinp = device_inputs(inp, cfg, dev)
+    d = ops.dims_for(cfg, deterministic=det, base_only=True)
+    ids, w, ss, off, st = run_align(cfg, dinp, dims=d)
+    assert int(st[0].item()) == 0
+    ws = ops.workspace(ops.forward_workspace_size(d), dev)
+    ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+    out, _ = run_forward(cfg, dinp, w, ss, off, dims=d, workspace_buf=ws)
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
+    assert_close(to_f64(out), ref, cfg.dtype, "out")
