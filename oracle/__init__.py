@@ -54,7 +54,8 @@ def load_library(path: str):
     L.oracle_slot.argtypes = [i64, i64, i64, i32, i32, i32, i32] + [vp] * 7 + [i64, i32, i32] + [vp] * 5
     L.oracle_forward.argtypes = ([i64, i64, i64, i32, i32, i32, i32, i32] + [vp] * 7 +
                                  [vp, vp, vp, i64, vp, vp, i32])
-    for f in (L.oracle_route, L.oracle_align, L.oracle_slot, L.oracle_forward):
+    L.oracle_dense.argtypes = [i64, i64, i64, i32, i32, i32] + [vp] * 5 + [i64, vp, vp, i32]
+    for f in (L.oracle_route, L.oracle_align, L.oracle_slot, L.oracle_forward, L.oracle_dense):
         f.restype = ctypes.c_int
     L.oracle_max_threads.restype = ctypes.c_int
     return L
@@ -147,6 +148,25 @@ def forward(inp: dict, dims: dict, topk_ids: np.ndarray, topk_w: np.ndarray,
                               _p(ids), _p(w), _p(ad), len(sel), _p(sel), _p(out), threads)
     if rc != 0:
         raise ValueError(f"oracle_forward failed: {rc}")
+    return out
+
+
+def dense(x: np.ndarray, w: np.ndarray, a: np.ndarray, b: np.ndarray, adapter_ids: np.ndarray,
+          dtype: str, tokens=None, threads: int = 0) -> np.ndarray:
+    """Dense multi-LoRA projection y_t = x_t W + (x_t A[l]) B[l] (float64 [len(tokens)][N]);
+    x [T][K], w = W^T [N][K], a = A^T [L][r][K], b = B^T [L][N][r], adapter -1 = base only."""
+    np_dt = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}[dtype]
+    x, w, a, b = (_c(v, np_dt) for v in (x, w, a, b))
+    T, K = x.shape
+    N = w.shape[0]
+    L, r = a.shape[0], a.shape[1]
+    sel = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    out = np.empty((len(sel), N), np.float64)
+    ad = _c(adapter_ids, np.int32)
+    rc = lib().oracle_dense(T, K, N, L, r, _DT[dtype], _p(x), _p(w), _p(a), _p(b), _p(ad),
+                            len(sel), _p(sel), _p(out), threads)
+    if rc != 0:
+        raise ValueError(f"oracle_dense failed: {rc}")
     return out
 
 

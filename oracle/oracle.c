@@ -273,6 +273,51 @@ int oracle_forward(int64_t T, int64_t h, int64_t I, int32_t E, int32_t k, int32_
   return status;
 }
 
+/*
+ * Dense multi-LoRA projection (no experts, no routing, no activation): the
+ * same page notes that the multi-LoRA kernels serve dense layers too, e.g.
+ * attention projections.  For each selected token t with adapter l = ids[t]:
+ *   out[i][:] = x_t W + (x_t A[l]) B[l]      (out [n_sel][N], double)
+ * with W^T rows Wt [N][K], A^T rows At [L][r][K], B^T rows Bt [L][N][r];
+ * adapter -1 (base model only) drops the LoRA term.
+ */
+int oracle_dense(int64_t T, int64_t K, int64_t N, int32_t L, int32_t r, int32_t dtype,
+                 const void* x, const void* Wt, const void* At, const void* Bt,
+                 const int32_t* adapter_ids, int64_t n_sel, const int64_t* sel, double* out,
+                 int32_t nthreads) {
+  if (T < 0 || K < 1 || N < 1 || L < 1 || r < 1 || n_sel < 0) return ORC_EARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F64) return ORC_EARG;
+  for (int64_t i = 0; i < n_sel; ++i) {
+    if (sel[i] < 0 || sel[i] >= T) return ORC_EARG;
+    if (adapter_ids[sel[i]] < -1 || adapter_ids[sel[i]] >= L) return ORC_EADAPTER;
+  }
+  int status = ORC_OK;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+#endif
+  for (int64_t i = 0; i < n_sel; ++i) {
+    int64_t t = sel[i];
+    int32_t l = adapter_ids[t];
+    double* xin = (double*)malloc(sizeof(double) * (size_t)K);
+    double* z = (double*)malloc(sizeof(double) * (size_t)r);
+    if (!xin || !z) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      status = ORC_ENOMEM;
+    } else {
+      for (int64_t k = 0; k < K; ++k) xin[k] = elem(x, t * K + k, dtype);
+      int64_t lc = l < 0 ? 0 : l;
+      lora_projection(xin, K, N, r, Wt, 0, At, lc * r * K, Bt, lc * N * r, dtype, l >= 0, z,
+                      out + i * N);
+    }
+    free(xin);
+    free(z);
+  }
+  return status;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

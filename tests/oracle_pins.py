@@ -271,7 +271,37 @@ def check_token_permutation_invariance():
     assert np.array_equal(out_p, out[perm])
 
 
+def check_dense_projection():
+    """Dense multi-LoRA projection: against numpy matmul per adapter (the LoRA
+    term as two library products), against the merged weight W + A B, and a
+    base-only token equal bit for bit to its zero-B result."""
+    rng = np.random.default_rng(71)
+    T, K, N, L, r = 11, 32, 24, 3, 4
+    for dtype in ("f32", "bf16"):
+        x = synth.from_float(rng.standard_normal((T, K)).astype(np.float32), dtype)
+        w = synth.from_float((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32), dtype)
+        a = synth.from_float((rng.standard_normal((L, r, K)) / np.sqrt(K)).astype(np.float32), dtype)
+        b = synth.from_float((rng.standard_normal((L, N, r)) / np.sqrt(r)).astype(np.float32), dtype)
+        ad = rng.integers(-1, L, T).astype(np.int32)
+        ad[:3] = [0, -1, L - 1]
+        got = oracle.dense(x, w, a, b, ad, dtype)
+        xf, wf, af, bf = (synth.to_float(v, dtype).astype(np.float64) for v in (x, w, a, b))
+        ref = xf @ wf.T
+        for t in range(T):
+            if ad[t] >= 0:
+                ref[t] += (xf[t] @ af[ad[t]].T) @ bf[ad[t]].T
+        assert _rel_err(got, ref) <= REL, dtype
+        for l in range(L):
+            toks = np.nonzero(ad == l)[0]
+            merged = xf[toks] @ (wf + bf[l] @ af[l]).T
+            assert _rel_err(got[toks], merged) <= REL, (dtype, l)
+        zb = oracle.dense(x, w, a, np.zeros_like(b), np.maximum(ad, 0), dtype)
+        base = np.nonzero(ad < 0)[0]
+        assert np.array_equal(got[base], zb[base])
+
+
 ALL_CHECKS = [check_route_ids_stable_argsort, check_route_weights_softmax, check_align_stable_argsort,
               check_align_base_only_argsort, check_forward_dense_formulation,
               check_gate_up_integer_exact, check_lora_zero_is_base_moe, check_base_only_is_base_moe,
-              check_merged_weight_identity, check_dense_case_torch, check_token_permutation_invariance]
+              check_merged_weight_identity, check_dense_case_torch, check_token_permutation_invariance,
+              check_dense_projection]

@@ -22,6 +22,8 @@ MUTANTS = {
     "adapter_major_keys": ("(int64_t)topk_ids[s] * Lb + (l < 0 ? L : l)", "(int64_t)(l < 0 ? L : l) * E + topk_ids[s]"),
     "base_only_gets_adapter0_lora": ("le * 2 * I * r, dtype, l >= 0, z1, g);", "le * 2 * I * r, dtype, 1, z1, g);"),
     "base_only_bucket_first": ("topk_ids[s] * Lb + (l < 0 ? L : l)", "topk_ids[s] * Lb + (l < 0 ? 0 : l + 1)"),
+    "dense_b_block_offset": ("Bt, lc * N * r, dtype", "Bt, lc * r * K, dtype"),
+    "dense_x_row_stride": ("xin[k] = elem(x, t * K + k, dtype);", "xin[k] = elem(x, t + k * T, dtype);"),
     "combine_weight_dropped": ("o[n] += w * d[n];", "o[n] += d[n];"),
     "x_transposed": ("xin[i] = elem(x, t * h + i, dtype);", "xin[i] = elem(x, i * T + t, dtype);"),
     "down_uses_up_half": ("lora_projection(a, I, h, r, w_dn,", "lora_projection(g + I, I, h, r, w_dn,"),
