@@ -265,6 +265,45 @@ int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]
 #define MOELORA_FUSED_DOWN 2
 int moelora_forward_fusion(const moelora_dims* dims, int* flags);
 
+/*
+ * Dense multi-LoRA projection: the vLLM blog page "Multi-LoRA", section
+ * "Implementing Multi-LoRA inference for MoE models in vLLM", notes that the
+ * same multi-LoRA kernels serve dense layers (e.g. attention projections).  For
+ * every token t with adapter l = adapter_ids[t]:
+ *   out[t] = x_t W + (x_t A[l]) B[l]
+ * with no experts, routing or activation.  Runs the layer's own kernels with
+ * one expert and k = 1: tokens bucketed by adapter, the shrink, the grouped
+ * GEMM (with the LoRA expand in its epilogue for 256-row bf16 tiles), the
+ * expand otherwise, and the write-back to token order in the output dtype.
+ * flags as in moelora_dims (deterministic split-K, base-only adapter -1).
+ */
+typedef struct moelora_dense_dims {
+  int64_t tokens;        /* T                                                       */
+  int64_t in_features;   /* K, a multiple of 64                                     */
+  int64_t out_features;  /* N, a multiple of 64                                     */
+  int32_t adapters;      /* L                                                       */
+  int32_t rank;          /* r: 16, 32 or 64                                         */
+  int32_t dtype;         /* moelora_dtype of x, weights and out                     */
+  int32_t flags;         /* MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_BASE_ONLY     */
+} moelora_dense_dims;
+
+int moelora_dense_workspace_size(const moelora_dense_dims* dims, size_t* bytes);
+
+/*
+ *   x              in  dtype [T][K]
+ *   w              in  dtype [N][K]      (W^T rows)
+ *   a              in  dtype [L][r][K]   (A^T rows per adapter)
+ *   b              in  dtype [L][N][r]   (B^T rows per adapter)
+ *   adapter_ids    in  int32 [T], in [0, L) (or -1 with MOELORA_FLAG_BASE_ONLY)
+ *   out            out dtype [T][N], fully overwritten
+ *   device_status  out int32 [1] or NULL: 0 ok, 1 an adapter id out of range
+ *   workspace      device scratch of at least moelora_dense_workspace_size bytes
+ */
+int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const void* w,
+                          const void* a, const void* b, const int32_t* adapter_ids, void* out,
+                          int32_t* device_status, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,7 +68,7 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
     if (!ROUTE) {
       for (int q = 0; q < k; ++q) {
         const int s = t * k + q;
-        int e = ids_in[s];
+        int e = ids_in != nullptr ? ids_in[s] : 0;
         if (e < 0 || e >= E) {
           atomicMax(&bad, 3);
           e = 0;

@@ -14,7 +14,7 @@ constexpr int kAlignLdsInts = 15360;
 int align_chunks(int nb, int S);
 
 // logits == nullptr: the expert ids come from ids_in (no routing, topk_ids and
-// topk_w untouched).
+// topk_w untouched); ids_in == nullptr too: every slot goes to expert 0.
 // L adapters; Lb buckets per expert (L, or L + 1 when adapter id -1 marks a
 // base-only token, keyed to bucket L of its expert).
 hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_t* adapter_ids,
@@ -107,6 +107,7 @@ hipError_t launch_expand_down(int dtype, int rank, const TilePlan& plan, const f
                               const int4* ltiles, const int32_t* counts, hipStream_t stream);
 
 // out[t][n] = sum_{j<k} w[t][j] * D[pos[t*k+j]][n], in j order.
+// out[t] = sum_j w[t][j] * D[pos[t*k + j]] in j order (w == nullptr: weights 1).
 hipError_t launch_combine(int dtype, const float* D, const int32_t* pos, const float* w, int T,
                           int k, int64_t h, void* out, hipStream_t stream);
 

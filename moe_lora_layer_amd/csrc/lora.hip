@@ -482,7 +482,7 @@ k_combine(const float* __restrict__ D, const int32_t* __restrict__ pos, const fl
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
     const int p = min(max(pos[t * k + j], 0), S - 1);
-    const float wj = w[t * k + j];
+    const float wj = w != nullptr ? w[t * k + j] : 1.0f;
     const float4 d = *reinterpret_cast<const float4*>(D + static_cast<int64_t>(p) * h + c);
     acc.x += wj * d.x;
     acc.y += wj * d.y;

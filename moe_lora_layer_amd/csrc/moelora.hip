@@ -119,6 +119,54 @@ ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
   return L;
 }
 
+// The dense projection planned as the layer's down GEMM with one expert and
+// k = 1: hidden = out_features (N), intermediate = in_features (K).
+moelora_dims dense_as_layer(const moelora_dense_dims* d) {
+  moelora_dims m{};
+  m.tokens = d->tokens;
+  m.hidden = d->out_features;
+  m.intermediate = d->in_features;
+  m.experts = 1;
+  m.top_k = 1;
+  m.adapters = d->adapters;
+  m.rank = d->rank;
+  m.dtype = d->dtype;
+  m.flags = d->flags;
+  return m;
+}
+
+struct DenseLayout {
+  size_t key, rank, slots, offsets, pos, counts, etiles, mtiles, ltiles, z, d, parts, total;
+};
+
+DenseLayout dense_layout(const moelora_dims* m, const TilePlan& plan) {
+  const size_t T = static_cast<size_t>(m->tokens), N = static_cast<size_t>(m->hidden);
+  const size_t r = static_cast<size_t>(m->rank), Lb = static_cast<size_t>(buckets_per_expert(m));
+  DenseLayout L;
+  size_t off = 0;
+  L.key = off;     off += round_up(T * 4);
+  L.rank = off;    off += round_up(T * 4);
+  L.slots = off;   off += round_up(T * 4);
+  L.offsets = off; off += round_up((Lb + 1) * 4);
+  L.pos = off;     off += round_up(T * 4);
+  L.counts = off;  off += round_up(4 * 4);
+  L.etiles = off;  off += round_up(2 * 4);
+  L.mtiles = off;  off += round_up(static_cast<size_t>(plan.max_mt) * 16);
+  L.ltiles = off;  off += round_up(static_cast<size_t>(plan.max_lt) * 16);
+  L.z = off;       // Z and D adjacent: the prep launch clears Z (and D under atomic split-K)
+  L.d = off + T * r * 4;
+  off += round_up(T * r * 4 + T * N * 4);
+  L.parts = off;
+  if (plan.det) {
+    const int dt = m->dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
+    size_t n = static_cast<size_t>(moelora::shrink_parts(dt, m->rank, plan, m->intermediate)) * T * r;
+    if (plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * T * N);
+    off += round_up(n * 4);
+  }
+  L.total = off;
+  return L;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? MOELORA_OK : MOELORA_ERR_HIP; }
 
 }  // namespace
@@ -343,6 +391,82 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   if (e == hipSuccess)
     e = moelora::launch_combine(dt, D, pos, topk_weights, static_cast<int>(T), k, h, out, st);
   if (e == hipSuccess) e = mark(MOELORA_NUM_STAGES);
+  return hip_status(e);
+}
+
+int moelora_dense_workspace_size(const moelora_dense_dims* dims, size_t* bytes) {
+  if (dims == nullptr) return MOELORA_ERR_NULL;
+  const moelora_dims m = dense_as_layer(dims);
+  const int rc = check_dims(&m);
+  if (rc != MOELORA_OK) return rc;
+  if (bytes == nullptr) return MOELORA_ERR_NULL;
+  *bytes = m.tokens == 0 ? 0 : dense_layout(&m, make_plan(&m)).total;
+  return MOELORA_OK;
+}
+
+int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const void* w,
+                          const void* a, const void* b, const int32_t* adapter_ids, void* out,
+                          int32_t* device_status, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (dims == nullptr) return MOELORA_ERR_NULL;
+  const moelora_dims m = dense_as_layer(dims);
+  int rc = check_dims(&m);
+  if (rc != MOELORA_OK) return rc;
+  const int64_t T = m.tokens;
+  if (T == 0) return MOELORA_OK;
+  const void* ptrs[] = {x, w, a, b, adapter_ids, out};
+  for (const void* p : ptrs)
+    if (p == nullptr) return MOELORA_ERR_NULL;
+  const TilePlan plan = make_plan(&m);
+  const DenseLayout L = dense_layout(&m, plan);
+  if (workspace == nullptr || workspace_bytes < L.total) return MOELORA_ERR_WORKSPACE;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOELORA_ERR_ALIGNMENT;
+  if (!aligned16(workspace)) return MOELORA_ERR_ALIGNMENT;
+  const int64_t N = m.hidden, K = m.intermediate;
+  const int r = m.rank, nad = m.adapters, Lb = static_cast<int>(buckets_per_expert(&m));
+  const int dt = m.dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
+  const int S = static_cast<int>(T);
+  const int64_t ntiles_max = (N + 31) / 32;
+  if (static_cast<int64_t>(plan.max_mt) * ntiles_max * plan.ksplit_dn > kMaxGrid ||
+      static_cast<int64_t>(plan.max_lt) * 2048 > kMaxGrid)
+    return MOELORA_ERR_DIMS;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ws_key = reinterpret_cast<int32_t*>(ws + L.key);
+  int32_t* ws_rank = reinterpret_cast<int32_t*>(ws + L.rank);
+  int32_t* slots = reinterpret_cast<int32_t*>(ws + L.slots);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* etiles = reinterpret_cast<int32_t*>(ws + L.etiles);
+  int4* mtiles = reinterpret_cast<int4*>(ws + L.mtiles);
+  int4* ltiles = reinterpret_cast<int4*>(ws + L.ltiles);
+  float* Z = reinterpret_cast<float*>(ws + L.z);
+  float* D = reinterpret_cast<float*>(ws + L.d);
+  float* parts = plan.det ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // tokens bucketed by adapter (one expert, k = 1)
+  hipError_t e = moelora::launch_align(nullptr, nullptr, adapter_ids, S, 1, 1, nad, Lb, nullptr,
+                                       nullptr, slots, offsets, device_status, ws_key, ws_rank, st);
+  const int64_t nzero =
+      plan.det ? 0 : static_cast<int64_t>(S) * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * N : 0);
+  if (e == hipSuccess)
+    e = moelora::launch_prep(slots, offsets, S, 1, Lb, plan, pos, mtiles, ltiles, counts, etiles, Z,
+                             nzero, st);
+  if (e == hipSuccess)
+    e = moelora::launch_shrink(dt, r, plan, x, S, slots, 1, a, 1, Lb, K, Z, S, ltiles, counts,
+                               parts, st);
+  if (e == hipSuccess) {
+    const moelora::LoraEpilogue epi{Z, static_cast<const uint16_t*>(b), offsets, 1, nad, r, Lb, N,
+                                    nullptr};
+    e = moelora::launch_gemm(dt, plan, x, S, slots, 1, w, N, K, D, S, mtiles, counts, etiles,
+                             plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, parts, st);
+  }
+  if (e == hipSuccess && !plan.fuse_dn)
+    e = moelora::launch_expand_down(dt, r, plan, Z, b, 1, Lb, D, N, ltiles, counts, st);
+  if (e == hipSuccess) e = moelora::launch_combine(dt, D, pos, nullptr, S, 1, N, out, st);
   return hip_status(e);
 }
 

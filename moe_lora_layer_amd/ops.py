@@ -38,6 +38,12 @@ class Dims(ctypes.Structure):
                  self.adapters, self.rank, self.dtype, self.flags))
 
 
+class DenseDims(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("in_features", ctypes.c_int64),
+                ("out_features", ctypes.c_int64), ("adapters", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -62,9 +68,13 @@ def library():
         L.moelora_align_topk.argtypes = [pd] + [vp] * 6 + [sz, vp]
         L.moelora_forward.argtypes = [pd] + [vp] * 12 + [sz, vp]
         L.moelora_forward_profiled.argtypes = [pd] + [vp] * 12 + [sz, vp, vp]
+        pdd = ctypes.POINTER(DenseDims)
+        L.moelora_dense_workspace_size.argtypes = [pdd, ctypes.POINTER(sz)]
+        L.moelora_dense_forward.argtypes = [pdd] + [vp] * 8 + [sz, vp]
         for f in (L.moelora_align_workspace_size, L.moelora_forward_workspace_size,
                   L.moelora_forward_workspace_layout, L.moelora_forward_fusion, L.moelora_align,
-                  L.moelora_align_topk, L.moelora_forward, L.moelora_forward_profiled):
+                  L.moelora_align_topk, L.moelora_forward, L.moelora_forward_profiled,
+                  L.moelora_dense_workspace_size, L.moelora_dense_forward):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -274,3 +284,45 @@ class MoELoRALayer:
         return forward(self.d, x, W["w_gate_up"], W["w_down"], W["a_gate_up"], W["b_gate_up"],
                        W["a_down"], W["b_down"], w, ss, off, out=self.out,
                        workspace_buf=self.ws_fwd, stream=stream)
+
+
+def make_dense_dims(tokens, in_features, out_features, adapters, rank, dtype, deterministic=False,
+                    base_only=False) -> DenseDims:
+    if isinstance(dtype, str):
+        dtype = _DT_NAME[dtype]
+    flags = ((MOELORA_FLAG_DETERMINISTIC if deterministic else 0) |
+             (MOELORA_FLAG_BASE_ONLY if base_only else 0))
+    return DenseDims(int(tokens), int(in_features), int(out_features), int(adapters), int(rank),
+                     int(dtype), flags)
+
+
+def dense_workspace_size(d: DenseDims) -> int:
+    n = ctypes.c_size_t()
+    _check(library().moelora_dense_workspace_size(ctypes.byref(d), ctypes.byref(n)),
+           "moelora_dense_workspace_size")
+    return n.value
+
+
+def dense_forward(d: DenseDims, x, w, a, b, adapter_ids, *, out=None, workspace_buf=None,
+                  status=None, stream=None):
+    """moelora_dense_forward: out[t] = x_t W + (x_t A[l]) B[l].  Returns (out, status)."""
+    dev = x.device
+    T, K, N, L, r = d.tokens, d.in_features, d.out_features, d.adapters, d.rank
+    dt = _TORCH_DT[d.dtype]
+    _expect(x, "x", (T, K), dt, dev)
+    _expect(w, "w", (N, K), dt, dev)
+    _expect(a, "a", (L, r, K), dt, dev)
+    _expect(b, "b", (L, N, r), dt, dev)
+    _expect(adapter_ids, "adapter_ids", (T,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((T, N), dtype=dt, device=dev)
+    _expect(out, "out", (T, N), dt, dev)
+    if status is None:
+        status = torch.zeros((4,), dtype=torch.int32, device=dev)
+    if workspace_buf is None:
+        workspace_buf = workspace(dense_workspace_size(d), dev)
+    _check(library().moelora_dense_forward(ctypes.byref(d), _ptr(x), _ptr(w), _ptr(a), _ptr(b),
+                                           _ptr(adapter_ids), _ptr(out), _ptr(status),
+                                           _ptr(workspace_buf), workspace_buf.numel(), _stream(stream)),
+           "moelora_dense_forward")
+    return out, status
