@@ -76,6 +76,75 @@ def stage_work(cfg, offsets, fusion):
     return w, Eact, P
 
 
+def run_dense(args, cfg) -> int:
+    """The dense multi-LoRA projection (moelora_dense_forward): a step is one
+    call over the batch.  It has no per-stage events, so its roofline line is
+    the whole call against the bytes it must move (the weight, the active
+    adapters, x and out, plus the fp32 partial output round trip of this
+    decomposition)."""
+    import numpy as np
+    import torch
+    from moe_lora_layer_amd import ops, synth
+
+    dev = torch.device("cuda:0")
+    inp = synth.make_dense_inputs(cfg)
+    t = lambda a: (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16
+                   else torch.from_numpy(a)).to(dev)
+    x, w, a, b = t(inp["x"]), t(inp["w"]), t(inp["a"]), t(inp["b"])
+    ad = torch.from_numpy(inp["adapter_ids"]).to(dev)
+    d = ops.make_dense_dims(cfg.tokens, cfg.in_features, cfg.out_features, cfg.adapters, cfg.rank,
+                            cfg.dtype, deterministic=args.deterministic)
+    ws = ops.workspace(ops.dense_workspace_size(d), dev)
+    out = torch.empty((cfg.tokens, cfg.out_features), dtype=x.dtype, device=dev)
+    st = torch.zeros((4,), dtype=torch.int32, device=dev)
+    step = lambda: ops.dense_forward(d, x, w, a, b, ad, out=out, workspace_buf=ws, status=st)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    T, K, N, r = cfg.tokens, cfg.in_features, cfg.out_features, cfg.rank
+    bsz = 2 if cfg.dtype == "bf16" else 4
+    P = int(np.unique(inp["adapter_ids"]).size)
+    by = N * K * bsz + P * r * (K + N) * bsz + T * K * bsz + T * N * bsz + 2 * T * N * 4
+    roof = {"bound": "hbm", "achieved": round(by / (call_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s"}
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, algorithmic_bytes=by,
+                kernel="whole dense call", kernel_us=round(call_ms * 1e3, 2))
+    value = T * args.steps / elapsed
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(T, args.cpu_tokens)
+        sel = np.linspace(0, T - 1, n).round().astype(np.int64)
+        tc = time.perf_counter()
+        oracle.dense(inp["x"], inp["w"], inp["a"], inp["b"], inp["adapter_ids"], cfg.dtype, tokens=sel,
+                     threads=oracle.max_threads())
+        tcpu = time.perf_counter() - tc
+        cpu = {"value": round(n / tcpu, 3), "unit": "tokens/s", "cores": oracle.max_threads(),
+               "kind": "oracle", "sample": f"{n} of {T} tokens, fp64 C oracle, {tcpu:.1f} s wall"}
+    log(f"[bench] {cfg.name}: {value:.1f} tokens/s, call {call_ms * 1e3:.1f} us, "
+        f"{roof['achieved']:.0f} GB/s")
+    rec = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+           "data": "synthetic (seeded normal inputs, random-init weights)",
+           "config": {"workload": cfg.name, "tokens": T, "in_features": K, "out_features": N,
+                      "adapters": cfg.adapters, "rank": r, "parallelism": "single GPU"},
+           "roofline": roof, "cpu_baseline": cpu, "deterministic": args.deterministic}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     from moe_lora_layer_amd import synth
 
@@ -83,7 +152,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_h4096", choices=synth.WORKLOAD_ORDER)
+    ap.add_argument("--workload", default="decode_h4096",
+                    choices=synth.WORKLOAD_ORDER + list(synth.DENSE_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true",
                     help="MOELORA_FLAG_DETERMINISTIC: ordered split-K partial sums, no atomics")
@@ -103,6 +173,8 @@ def main() -> int:
     import torch
     from moe_lora_layer_amd import ops
 
+    if args.workload in synth.DENSE_WORKLOADS:
+        return run_dense(args, synth.DENSE_WORKLOADS[args.workload])
     cfg = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     t0 = time.time()

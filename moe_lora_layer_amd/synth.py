@@ -86,6 +86,41 @@ WORKLOADS: dict[str, LayerConfig] = {
 WORKLOAD_ORDER = ["tiny_f32", "decode_h4096", "prefill_h4096", "gptoss_h2880", "dense_h8192"]
 
 
+@dataclasses.dataclass(frozen=True)
+class DenseConfig:
+    """A dense multi-LoRA projection: y_t = x_t W + (x_t A[l]) B[l] (no experts)."""
+    name: str
+    tokens: int          # T
+    in_features: int     # K
+    out_features: int    # N
+    adapters: int        # L
+    rank: int            # r
+    dtype: str
+    requests: int        # tokens split into this many equal contiguous requests (one adapter each)
+    seed: int = 0
+
+
+DENSE_WORKLOADS: dict[str, DenseConfig] = {
+    # Llama-3.3-70B fused q/k/v projection (8192 -> 8192 + 2 x 1024 with 8 KV heads),
+    # 128 decode tokens, 16 adapters rank 16, uniform per token
+    "qkv_dense_h8192": DenseConfig("qkv_dense_h8192", 128, 8192, 10240, 16, 16, DTYPE_BF16,
+                                   requests=128, seed=1005),
+}
+
+
+def make_dense_inputs(cfg: DenseConfig) -> dict:
+    """x [T][K], w = W^T [N][K], a = A^T [L][r][K], b = B^T [L][N][r] (W, A ~ N(0, 1/K),
+    B ~ N(0, 1/r)), adapter ids uniform per request."""
+    T, K, N, L, r = cfg.tokens, cfg.in_features, cfg.out_features, cfg.adapters, cfg.rank
+    g = _rng(cfg.seed, TID_ADAPTERS)
+    req = g.integers(0, L, size=cfg.requests)
+    return {"x": _normal_tensor(cfg.seed, TID_X, (T, K), 1.0, cfg.dtype),
+            "w": _normal_tensor(cfg.seed, TID_W_GU, (N, K), K ** -0.5, cfg.dtype),
+            "a": _normal_tensor(cfg.seed, TID_A_GU, (L, r, K), K ** -0.5, cfg.dtype),
+            "b": _normal_tensor(cfg.seed, TID_B_GU, (L, N, r), r ** -0.5, cfg.dtype),
+            "adapter_ids": np.repeat(req.astype(np.int32), T // cfg.requests)}
+
+
 def _threads() -> int:
     n = os.cpu_count() or 1
     return max(1, min(16, n))

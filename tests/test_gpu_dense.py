@@ -70,9 +70,11 @@ def test_dense_forward(shape, mode):
 
 def test_dense_qkv_projection():
     """Llama-3.3-70B-shaped fused q/k/v projection (8192 -> 10240), 128 decode
-    tokens over 16 rank-16 adapters; sampled tokens against the oracle."""
-    T, K, N, L, r, dtype = 128, 8192, 10240, 16, 16, "bf16"
-    inp = _inputs(T, K, N, L, r, dtype, seed=5)
+    tokens over 16 rank-16 adapters (the benchmark's dense workload); sampled
+    tokens against the oracle."""
+    cfg = synth.DENSE_WORKLOADS["qkv_dense_h8192"]
+    T, K, N, L, r, dtype = cfg.tokens, cfg.in_features, cfg.out_features, cfg.adapters, cfg.rank, cfg.dtype
+    inp = synth.make_dense_inputs(cfg)
     out, st = _run(inp, T, K, N, L, r, dtype)
     assert st == 0
     toks = np.arange(0, T, 9)
