@@ -113,9 +113,7 @@ __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 // Eight fp32 values as two bf16 fragments with v ~= hi + lo (about 16
 // significant bits): a bf16 MFMA against hi and then lo keeps fp32-like
 // precision for the small rank-r operand of the LoRA expand.
-__device__ __forceinline__ void split_bf16x8(const float* v8, bf16x8_t& hi, bf16x8_t& lo) {
-  const float4 a = *reinterpret_cast<const float4*>(v8);
-  const float4 b = *reinterpret_cast<const float4*>(v8 + 4);
+__device__ __forceinline__ void split_bf16x8(float4 a, float4 b, bf16x8_t& hi, bf16x8_t& lo) {
   const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t hw[4], lw[4];
 #pragma unroll
@@ -128,6 +126,9 @@ __device__ __forceinline__ void split_bf16x8(const float* v8, bf16x8_t& hi, bf16
   }
   hi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
   lo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+}
+__device__ __forceinline__ void split_bf16x8(const float* v8, bf16x8_t& hi, bf16x8_t& lo) {
+  split_bf16x8(*reinterpret_cast<const float4*>(v8), *reinterpret_cast<const float4*>(v8 + 4), hi, lo);
 }
 
 // LDS address space, for the destination of global_load_lds (the direct

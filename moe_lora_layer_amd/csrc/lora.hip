@@ -335,6 +335,156 @@ k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict
   }
 }
 
+// ------------------------------------------------------------ streaming shrink
+// LoRA tiles of at most 16 rows and many of them (large decode batches over
+// many adapters): the adapter weights are nearly all of the bytes and each is
+// used by a handful of rows, so the kernel is a weight stream.  The work is a
+// flat list of items (LoRA tile, K chunk), tile-major; an item is 8 or 16
+// MFMA fragments of A^T (R rows x KC columns) and the tile's activation rows
+// over the same chunk.  Each wave of a persistent grid takes one contiguous
+// run of items, so it walks along the rows of one A^T block after another
+// (sequential DRAM pages), sums a tile's chunks in registers and adds them to
+// Z with relaxed fp32 atomics only when its run leaves the tile (once or twice
+// per tile and wave instead of once per chunk).  The next item is loaded while
+// the current one is multiplied.  Every item is whole (the chunk width
+// divides K), so the loop is straight-line code and the compiler's in-order
+// vmcnt waits leave the prefetched item in flight.  Deterministic mode writes
+// every item's partial to its own slot (parts[kc]) instead of using atomics.
+template <int R> struct ShrinkStream {
+  static constexpr int RB = R / 16;               // 16-row blocks of A^T
+  static constexpr int ST = R == 64 ? 4 : 8;      // MFMA K steps per item (8 or 16 A^T fragments)
+  // K steps per item for a given K: ST when its chunks divide K, else 2 (K is
+  // a multiple of 64), so that every item is whole
+  static int steps(int64_t K) { return (K / 32) % ST == 0 ? ST : 2; }
+};
+// persistent grid of the streaming shrink: two workgroups (eight waves) per CU
+// of an MI355X, used when the host's bound of the item count gives every wave
+// a run of at least four items
+constexpr int kStreamWgs = 2 * 256;
+constexpr int64_t kStreamMinItems = 4ll * kStreamWgs * kLoraWaves;
+
+// Row of X read by lane c for the 16 sorted rows from m0 of a tile ending at
+// row_end (clamped rows are computed but never stored).  m0 and row_end are
+// wave-uniform, so the slot indices come from scalar loads.
+template <bool GATHER>
+__device__ __forceinline__ int64_t stream_x_row(const int32_t* __restrict__ gather_slots,
+                                                int gather_k, int x_rows, int m0, int row_end,
+                                                int c) {
+  int v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = GATHER ? gather_slots[min(m0 + i, row_end - 1)] : m0 + i;
+  int r = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) r = c == i ? v[i] : r;
+  if (GATHER) r /= gather_k;
+  else r = min(r, row_end - 1);
+  return min(max(r, 0), x_rows - 1);
+}
+
+template <int R, int ST, bool GATHER, bool DET>
+__global__ void __launch_bounds__(kLoraThreads, 2)
+k_shrink_stream(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
+                int gather_k, const bf16_t* __restrict__ At, int E, int L, int nad, int64_t K,
+                float* __restrict__ Z, const int4* __restrict__ ltiles,
+                const int32_t* __restrict__ counts, float* __restrict__ parts,
+                int64_t part_stride) {
+  typedef Mfma16<bf16_t> M;
+  typedef M::frag_t frag_t;
+  constexpr int RB = R / 16, KC = ST * M::KSTEP;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int c = lane & 15, g = lane >> 4;
+  const int nwaves = gridDim.x * kLoraWaves;
+  const int wid = blockIdx.x * kLoraWaves + wave;
+  const int nkc = static_cast<int>(K / KC);  // K chunks (KC divides K)
+
+  struct Work {
+    int row0, row_end;
+    const bf16_t* ab;   // A^T block of the bucket, nullptr for a base-only bucket
+    const bf16_t* xp;   // lane's activation row
+  };
+  auto describe = [&](int tl) {
+    const int4 t = ltiles[tl];
+    const int e = t.x / L, l = t.x % L;
+    const int row_end = min(t.z, t.y + 16);
+    const bf16_t* xr = X + stream_x_row<GATHER>(gather_slots, gather_k, x_rows, t.y, row_end, c) * K;
+    return Work{t.y, row_end, l < nad ? At + (static_cast<int64_t>(l) * E + e) * R * K : nullptr, xr};
+  };
+  f32x4_t acc[RB];
+  auto clear = [&]() {
+#pragma unroll
+    for (int j = 0; j < RB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  // deterministic: the partial of K chunk kc into its own slot
+  auto flush = [&](const Work& w, int kc) {
+    const int p = w.row0 + c;
+    if (w.ab != nullptr && p < w.row_end) {
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t idx = static_cast<int64_t>(p) * R + 16 * j + 4 * g + i;
+          if (DET)
+            parts[kc * part_stride + idx] = acc[j][i];
+          else
+            atomic_add_relaxed(Z + idx, acc[j][i]);
+        }
+    }
+    clear();
+  };
+  // A base-only bucket's items read the A^T block of adapter 0 (in bounds;
+  // their sum is never stored).
+  auto load = [&](frag_t (&af)[ST][RB], frag_t (&xf)[ST], const Work& w, int kc) {
+    const bf16_t* ab = w.ab != nullptr ? w.ab : At;
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+      const int64_t k = static_cast<int64_t>(kc) * KC + s * M::KSTEP + g * M::KPACK;
+#pragma unroll
+      for (int j = 0; j < RB; ++j) af[s][j] = M::load(ab + static_cast<int64_t>(16 * j + c) * K + k);
+      xf[s] = M::load(w.xp + k);
+    }
+  };
+  auto mma = [&](const frag_t (&af)[ST][RB], const frag_t (&xf)[ST]) {
+#pragma unroll
+    for (int s = 0; s < ST; ++s)
+#pragma unroll
+      for (int j = 0; j < RB; ++j) M::run(acc[j], af[s][j], xf[s]);
+  };
+
+  // this wave's contiguous run [i0, i1) of the item list, taken one tile at a
+  // time: the chunks of a tile share its activation rows and A^T block, and
+  // the pipelined inner loop has no stores (a store's registers would hold up
+  // the next loads behind the waits of the one in-order counter)
+  const int n = counts[1] * nkc;
+  const int i0 = static_cast<int>(static_cast<int64_t>(n) * wid / nwaves);
+  const int i1 = static_cast<int>(static_cast<int64_t>(n) * (wid + 1) / nwaves);
+  clear();
+  frag_t a0[ST][RB], x0[ST], a1[ST][RB], x1[ST];
+  for (int it = i0; it < i1;) {
+    const int tl = it / nkc;
+    const Work w = describe(tl);
+    const int kc0 = it - tl * nkc;
+    const int kc1 = min(nkc, kc0 + (i1 - it));  // this run's chunks of the tile
+    int kc = kc0;
+    load(a0, x0, w, kc);
+    for (;;) {
+      // past the tile's last chunk the last one is loaded again (never used)
+      load(a1, x1, w, min(kc + 1, kc1 - 1));
+      __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of these MFMAs
+      mma(a0, x0);
+      if (DET) flush(w, kc);
+      if (++kc >= kc1) break;
+      load(a0, x0, w, min(kc + 1, kc1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a1, x1);
+      if (DET) flush(w, kc);
+      if (++kc >= kc1) break;
+    }
+    if (!DET) flush(w, 0);
+    it += kc1 - kc0;
+  }
+}
+
 // --------------------------------------------------------------------- expand
 // Each wave owns NB blocks of 16 output columns (and, for gate_up, the
 // matching up columns I + n).  Its B^T fragments are loaded once and reused
@@ -506,12 +656,19 @@ template <int R, bool GU> constexpr int expand_nb() { return (GU || R > 32) ? 4 
 struct ShrinkSplit {
   int nsplit, kwg_steps, parts;  // parts = partial slices in deterministic mode
   int64_t kwg;                   // K range per split (k_shrink_tall)
+  bool stream;                   // k_shrink_stream (nsplit = K chunks per tile)
 };
 
 template <typename T, int R>
 static ShrinkSplit shrink_split(const TilePlan& plan, int64_t K) {
-  ShrinkSplit sp{1, 0, 1, K};
-  if (plan.lora_db && sizeof(T) == 2) {  // k_shrink_dma
+  ShrinkSplit sp{1, 0, 1, K, false};
+  const int64_t nkc = K / (32 * ShrinkStream<R>::steps(K));
+  if (!plan.lora_db && sizeof(T) == 2 && plan.bml == 16 &&
+      static_cast<int64_t>(plan.max_lt) * nkc >= kStreamMinItems) {
+    // k_shrink_stream: one partial per K chunk
+    sp.stream = true;
+    sp.nsplit = sp.parts = static_cast<int>(nkc);
+  } else if (plan.lora_db && sizeof(T) == 2) {  // k_shrink_dma
     const int nk_all = static_cast<int>(K / 64);
     int nsplit = (1024 + plan.max_lt - 1) / std::max(1, plan.max_lt);
     nsplit = std::max(1, std::min(nsplit, nk_all / 4));
@@ -543,7 +700,18 @@ static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
   const ShrinkSplit sp = shrink_split<T, R>(plan, K);
   const int64_t stride = static_cast<int64_t>(S) * R;
   const int64_t grid = static_cast<int64_t>(plan.max_lt) * sp.nsplit;
-  if (plan.lora_db && sizeof(T) == 2) {
+  if (sp.stream) {
+    // many short tiles: persistent waves stream runs of (tile, K chunk) items
+    constexpr int ST = ShrinkStream<R>::ST;
+    const bool det = parts != nullptr;
+    auto kern = ShrinkStream<R>::steps(K) == ST
+                    ? (det ? k_shrink_stream<R, ST, GATHER, true> : k_shrink_stream<R, ST, GATHER, false>)
+                    : (det ? k_shrink_stream<R, 2, GATHER, true> : k_shrink_stream<R, 2, GATHER, false>);
+    hipLaunchKernelGGL(kern, dim3(kStreamWgs), dim3(kLoraThreads), 0, stream,
+                       static_cast<const bf16_t*>(X), x_rows, gather_slots, gather_k,
+                       static_cast<const bf16_t*>(At), E, L, plan.nad, K, Z, ltiles, counts,
+                       parts, stride);
+  } else if (plan.lora_db && sizeof(T) == 2) {
     // tall bf16 tiles: DMA ring, about 1024 workgroups of (tile, K range)
     hipLaunchKernelGGL((k_shrink_dma<R, GATHER>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const bf16_t*>(X), x_rows,

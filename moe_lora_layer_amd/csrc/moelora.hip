@@ -52,7 +52,10 @@ TilePlan make_plan(const moelora_dims* d) {
   // at most one 128-row M-tile per expert: nothing reuses a weight tile, so the
   // weights are streamed (nontemporal loads, rotated K walk)
   p.stream = p.bm < 128 || want <= 160;
-  p.bml = 64;
+  // LoRA tiles: 64 rows when buckets average many rows (the tall-tile kernels),
+  // else one 16-row MFMA block (the weight-streaming kernels)
+  p.lora_db = S / std::max<int64_t>(1, std::min<int64_t>(nb, S)) > 16;
+  p.bml = p.lora_db ? 64 : 16;
   p.max_mt = static_cast<int>(S / p.bm + (E < S ? E : S) + 1);
   p.max_lt = static_cast<int>(S / p.bml + (nb < S ? nb : S) + 1);
   // Split K only when the real M x N tiles cannot give every CU a workgroup
@@ -69,7 +72,6 @@ TilePlan make_plan(const moelora_dims* d) {
     const int64_t per = (steps + want - 1) / want;
     return static_cast<int>((steps + per - 1) / per);
   };
-  p.lora_db = S / std::max<int64_t>(1, std::min<int64_t>(nb, S)) > 16;
   p.ksplit_gu = splits(2 * d->intermediate, d->hidden);
   p.ksplit_dn = splits(d->hidden, d->intermediate);
   // 256-row bf16 tiles run the LoRA expand in the GEMM epilogue (unsplit K)

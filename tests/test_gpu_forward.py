@@ -31,6 +31,11 @@ def _small(T, h, I, E, k, L, r, dtype, seed, requests=None, **kw):
                              requests=requests if requests is not None else T, seed=seed, **kw)
 
 
+# 1024 (expert, adapter) buckets over 2048 slots: enough 16-row LoRA tiles
+# times K chunks for the persistent streaming shrink (gate_up only; the down
+# shrink, K = 256, stays on the per-tile kernel)
+STREAM_SHAPE = (512, 1088, 256, 16, 4, 64, 64, "bf16")
+
 SMALL = [
     # (T, h, I, E, k, L, r, dtype): rows/expert 16 (BM 32), 38 (BM 64), 67 (BM 128);
     # N tails (2I, h not multiples of 128), K of 64..640, ranks 16/32/64
@@ -54,6 +59,9 @@ SMALL = [
     (300, 128, 256, 1, 1, 16, 16, "bf16"),
     # one expert, narrow output: split-K with atomics in the down GEMM
     (96, 128, 2048, 1, 1, 4, 16, "bf16"),
+    # many short adapter buckets (~2 rows each): the gate_up shrink streams
+    # (tile, K chunk) items, h = 1088 ends in a half chunk
+    STREAM_SHAPE,
 ]
 
 
@@ -282,6 +290,7 @@ DET_SHAPES = [
     (600, 128, 192, 4, 2, 3, 16, "bf16"),    # tall buckets: DMA shrink, fused epilogues
     (520, 192, 256, 2, 1, 9, 64, "bf16"),
     (600, 192, 128, 4, 2, 2, 32, "f32"),     # tall fp32 shrink
+    STREAM_SHAPE,                            # streaming shrink: one partial per K chunk
 ]
 
 
@@ -338,6 +347,7 @@ BASE_ONLY_SHAPES = [
     (600, 192, 128, 4, 2, 2, 32, "f32", 0.5),    # 256-row fp32 tiles, tall shrink
     (96, 128, 2048, 1, 1, 4, 16, "bf16", 0.3),   # split-K down GEMM
     (300, 128, 256, 3, 2, 2, 32, "bf16", 1.0),   # every token base-only
+    STREAM_SHAPE + (0.3,),                       # streaming shrink over base-only tiles
 ]
 
 
