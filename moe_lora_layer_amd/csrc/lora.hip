@@ -250,27 +250,21 @@ __device__ __forceinline__ void shrink_issue(unsigned char* smem, int slot, int6
                                      (lds_void_t*)(st + (64 + 8 * (S::AI * wave + j)) * 128), 16, 0, 0);
 }
 
+// One K range [kt0, kt0 + nk) (in 64-wide steps) of one tall LoRA tile through
+// the ring; the wave's 32 x 32 partial is left in acc.  `tile` is the tile's
+// (bucket, row0, row_end); the caller has checked that its bucket has an
+// adapter.
 template <int R, bool GATHER>
-__global__ void __launch_bounds__(kLoraThreads)
-k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
-             int gather_k, const bf16_t* __restrict__ At, int E, int L, int nad, int64_t K, int kwg_steps,
-             int nsplit, float* __restrict__ Z, const int4* __restrict__ ltiles,
-             const int32_t* __restrict__ counts, float* __restrict__ parts, int64_t part_stride) {
+__device__ __forceinline__ void shrink_dma_range(unsigned char* smem, const bf16_t* __restrict__ X,
+                                                 int x_rows, const int32_t* __restrict__ gather_slots,
+                                                 int gather_k, const bf16_t* __restrict__ At, int E,
+                                                 int L, int64_t K, int4 tile, int kt0, int nk,
+                                                 f32x16_t& acc) {
   typedef ShrinkDma<R> S;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kShrinkStages * S::STAGE];
-  const int lt = blockIdx.x / nsplit;
-  const int split = blockIdx.x % nsplit;
-  if (lt >= counts[1]) return;
-  const int4 tile = ltiles[lt];
   const int b = tile.x, row0 = tile.y, row_end = tile.z;
   const int e = b / L, l = b % L;
-  if (l >= nad) return;  // base-only bucket: no LoRA term
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int c32 = lane & 31, h = lane >> 5;
-  const int nk_all = static_cast<int>(K / 64);
-  const int kt0 = split * kwg_steps;
-  const int nk = min(nk_all, kt0 + kwg_steps) - kt0;
-  if (nk <= 0) return;  // uniform
 
   // load sources (rows past the tile or the rank read a clamped valid row)
   const bf16_t* x_src[S::XI];
@@ -297,7 +291,6 @@ k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict
   const int sw = (c32 >> 1) & 7;              // row swizzle of rows 32 rh + c32 and q0 + c32
   const int x_off = (32 * rh + c32) * 128;
   const int a_off = (64 + q0 + c32) * 128;
-  f32x16_t acc = zero_acc();
 
   for (int s = 0; s + 1 < kShrinkStages; ++s)
     shrink_issue<R>(smem, s, static_cast<int64_t>(min(s, nk - 1)) * 64, x_src, a_src, wave);
@@ -319,19 +312,85 @@ k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx, fa, acc, 0, 0, 0);
     }
   }
-  wait_vmcnt<0>();  // no LDS write of this workgroup may outlive it
-  const int q = q0 + c32;
-  if (q < R) {
+  wait_vmcnt<0>();  // no LDS write of this workgroup may outlive the range
+}
+
+// The wave's 32 x 32 partial of a tall tile: into Z with relaxed atomics, or,
+// deterministic, into partial slot `slot` (R > 32: the split; else split and
+// substep pair).
+template <int R>
+__device__ __forceinline__ void shrink_dma_emit(const f32x16_t& acc, int4 tile, float* __restrict__ Z,
+                                                float* __restrict__ parts, int64_t part_stride,
+                                                int slot) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int c32 = lane & 31, h = lane >> 5;
+  const int rh = wave & 1, sel = wave >> 1;
+  const int q = (R > 32 ? 32 * sel : 0) + c32;
+  if (q >= R) return;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int p = row0 + 32 * rh + acc_row(i, h);
-      if (p >= row_end) continue;
-      const int64_t idx = static_cast<int64_t>(p) * R + q;
-      if (parts != nullptr)  // deterministic: partial (split, substep pair)
-        parts[(R > 32 ? split : 2 * split + sel) * part_stride + idx] = acc[i];
-      else
-        atomic_add_relaxed(Z + idx, acc[i]);
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int p = tile.y + 32 * rh + acc_row(i, h);
+    if (p >= tile.z) continue;
+    const int64_t idx = static_cast<int64_t>(p) * R + q;
+    if (parts != nullptr)
+      parts[slot * part_stride + idx] = acc[i];
+    else
+      atomic_add_relaxed(Z + idx, acc[i]);
+  }
+}
+
+// Workgroup (tile, split): one K range of kwg_steps steps.
+template <int R, bool GATHER>
+__global__ void __launch_bounds__(kLoraThreads)
+k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
+             int gather_k, const bf16_t* __restrict__ At, int E, int L, int nad, int64_t K, int kwg_steps,
+             int nsplit, float* __restrict__ Z, const int4* __restrict__ ltiles,
+             const int32_t* __restrict__ counts, float* __restrict__ parts, int64_t part_stride) {
+  typedef ShrinkDma<R> S;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kShrinkStages * S::STAGE];
+  const int lt = blockIdx.x / nsplit;
+  const int split = blockIdx.x % nsplit;
+  if (lt >= counts[1]) return;
+  const int4 tile = ltiles[lt];
+  if (tile.x % L >= nad) return;  // base-only bucket: no LoRA term
+  const int nk_all = static_cast<int>(K / 64);
+  const int kt0 = split * kwg_steps;
+  const int nk = min(nk_all, kt0 + kwg_steps) - kt0;
+  if (nk <= 0) return;  // uniform
+  f32x16_t acc = zero_acc();
+  shrink_dma_range<R, GATHER>(smem, X, x_rows, gather_slots, gather_k, At, E, L, K, tile, kt0, nk, acc);
+  shrink_dma_emit<R>(acc, tile, Z, parts, part_stride, R > 32 ? split : 2 * split + (threadIdx.x / kWave >> 1));
+}
+
+// Persistent form (atomics only): the work is the list of (tall tile, K step)
+// items, tile-major, and workgroup w of W takes the contiguous run
+// [n w / W, n (w+1) / W), one K range per tile it meets.  Every workgroup
+// streams the same number of steps, so the grid drains evenly, and a tile's
+// steps mostly stay in one workgroup (few atomics per Z element).
+template <int R> constexpr int shrink_run_wgs() { return R > 32 ? 2 * 256 : 3 * 256; }  // LDS-resident per CU
+
+template <int R, bool GATHER>
+__global__ void __launch_bounds__(kLoraThreads)
+k_shrink_dma_run(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
+                 int gather_k, const bf16_t* __restrict__ At, int E, int L, int nad, int64_t K,
+                 float* __restrict__ Z, const int4* __restrict__ ltiles,
+                 const int32_t* __restrict__ counts) {
+  typedef ShrinkDma<R> S;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kShrinkStages * S::STAGE];
+  const int nk_all = static_cast<int>(K / 64);
+  const int64_t n = static_cast<int64_t>(counts[1]) * nk_all;
+  const int64_t i0 = n * blockIdx.x / gridDim.x, i1 = n * (blockIdx.x + 1) / gridDim.x;
+  for (int64_t it = i0; it < i1;) {
+    const int lt = static_cast<int>(it / nk_all);
+    const int kt0 = static_cast<int>(it - static_cast<int64_t>(lt) * nk_all);
+    const int nk = static_cast<int>(min<int64_t>(nk_all - kt0, i1 - it));
+    it += nk;
+    const int4 tile = ltiles[lt];
+    if (tile.x % L >= nad) continue;  // base-only bucket: no LoRA term (uniform)
+    lds_barrier();  // every wave is done with the previous range's stages
+    f32x16_t acc = zero_acc();
+    shrink_dma_range<R, GATHER>(smem, X, x_rows, gather_slots, gather_k, At, E, L, K, tile, kt0, nk, acc);
+    shrink_dma_emit<R>(acc, tile, Z, nullptr, 0, 0);
   }
 }
 
@@ -700,7 +759,12 @@ static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
   const ShrinkSplit sp = shrink_split<T, R>(plan, K);
   const int64_t stride = static_cast<int64_t>(S) * R;
   const int64_t grid = static_cast<int64_t>(plan.max_lt) * sp.nsplit;
-  if (sp.stream) {
+  if (plan.lora_db && sizeof(T) == 2 && parts == nullptr) {
+    // tall bf16 tiles: persistent workgroups stream runs of (tile, K step) items
+    hipLaunchKernelGGL((k_shrink_dma_run<R, GATHER>), dim3(shrink_run_wgs<R>()), dim3(kLoraThreads),
+                       0, stream, static_cast<const bf16_t*>(X), x_rows, gather_slots, gather_k,
+                       static_cast<const bf16_t*>(At), E, L, plan.nad, K, Z, ltiles, counts);
+  } else if (sp.stream) {
     // many short tiles: persistent waves stream runs of (tile, K chunk) items
     constexpr int ST = ShrinkStream<R>::ST;
     const bool det = parts != nullptr;
@@ -712,7 +776,7 @@ static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
                        static_cast<const bf16_t*>(At), E, L, plan.nad, K, Z, ltiles, counts,
                        parts, stride);
   } else if (plan.lora_db && sizeof(T) == 2) {
-    // tall bf16 tiles: DMA ring, about 1024 workgroups of (tile, K range)
+    // tall bf16 tiles, deterministic: DMA ring, about 1024 workgroups of (tile, K range)
     hipLaunchKernelGGL((k_shrink_dma<R, GATHER>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const bf16_t*>(X), x_rows,
                        gather_slots, gather_k, static_cast<const bf16_t*>(At), E, L, plan.nad, K,
