@@ -33,7 +33,9 @@ constexpr int kMaxTopK = 8;
 
 // KEYS_LDS: the per-slot keys and ranks live in LDS after the counters (small
 // batches); otherwise in the workspace.
-template <bool KEYS_LDS, bool ROUTE>
+// KMAX: the routing list length compiled in, the smallest of 1, 2, 4, 8 that
+// holds k (a longer list only adds compare-and-select steps).
+template <bool KEYS_LDS, bool ROUTE, int KMAX>
 __global__ void __launch_bounds__(kAlignThreads)
 k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
         const int32_t* __restrict__ adapter_ids, int T, int E,
@@ -77,44 +79,53 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
       }
       continue;
     }
-    float val[kMaxTopK];
-    int id[kMaxTopK];
+    float val[KMAX];
+    int id[KMAX];
 #pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q) {
+    for (int q = 0; q < KMAX; ++q) {
       val[q] = -INFINITY;
       id[q] = 0x7fffffff;
     }
     const float* lg = logits + static_cast<int64_t>(t) * E;
-    for (int e = 0; e < E; ++e) {
-      float cv = lg[e];
-      int ci = e;
-      // carry the candidate down the list: it passes every entry it beats
+    // logits in batches of 16 loads issued together (one memory latency per
+    // batch, not per expert); past E the batch holds -inf candidates, which
+    // never pass a real logit (E >= k real ones come first)
+    constexpr int kBatch = 16;
+    for (int e0 = 0; e0 < E; e0 += kBatch) {
+      float lv[kBatch];
 #pragma unroll
-      for (int q = 0; q < kMaxTopK; ++q) {
-        if (q < k) {
-          bool before = cv > val[q] || (cv == val[q] && ci < id[q]);
-          if (before) {
-            float tv = val[q];
-            int ti = id[q];
-            val[q] = cv;
-            id[q] = ci;
-            cv = tv;
-            ci = ti;
-          }
+      for (int u = 0; u < kBatch; ++u) lv[u] = lg[min(e0 + u, E - 1)];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) lv[u] = e0 + u < E ? lv[u] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        float cv = lv[u];
+        int ci = e0 + u;
+        // carry the candidate down the list: it passes every entry it beats
+        // (selects, no branches)
+#pragma unroll
+        for (int q = 0; q < KMAX; ++q) {
+          const bool before = (q < k) & ((cv > val[q]) | ((cv == val[q]) & (ci < id[q])));
+          const float tv = val[q];
+          const int ti = id[q];
+          val[q] = before ? cv : tv;
+          id[q] = before ? ci : ti;
+          cv = before ? tv : cv;
+          ci = before ? ti : ci;
         }
       }
     }
-    float ex[kMaxTopK];
+    float ex[KMAX];
     float sum = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q) {
+    for (int q = 0; q < KMAX; ++q) {
       if (q < k) {
         ex[q] = expf(val[q] - val[0]);
         sum += ex[q];
       }
     }
 #pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q) {
+    for (int q = 0; q < KMAX; ++q) {
       if (q < k) {
         int s = t * k + q;
         topk_ids[s] = id[q];
@@ -126,29 +137,52 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
   __syncthreads();
 
   // ---- 2. ranks inside each chunk -------------------------------------------
+  // 64 slots at a time: a bitonic sort of (key, lane) across the wave puts
+  // equal keys next to each other in lane order; a lane's rank among equal
+  // keys is its sorted position minus its key's first position, and goes
+  // back to the slot's lane with a permute.  The last lane of each key adds
+  // the key's count to the chunk's counter.  Cost: 21 exchange steps,
+  // whatever the number of distinct keys.
   const int chunk_len = (S + chunks - 1) / chunks;
   if (wave < chunks) {
     const int c0 = wave * chunk_len;
     const int c1 = min(S, c0 + chunk_len);
     int* my_cnt = cnt + wave * nb;
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
     for (int base = c0; base < c1; base += kWave) {
       const int s = base + lane;
       const bool valid = s < c1;
-      const int key = valid ? key_buf[s] : -1;
-      uint64_t remaining = __ballot(valid);
-      uint64_t peers = 0;
-      while (remaining) {
-        const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
-        const int lk = __shfl(key, leader, kWave);
-        const uint64_t m = __ballot(valid && key == lk);
-        if (valid && key == lk) peers = m;
-        remaining &= ~m;
+      const int key = valid ? key_buf[s] : nb;  // invalid lanes sort last
+      // packed (key, lane): keys < 2^24 / 64 by the bucket limit
+      int v = (key << 6) | lane;
+#pragma unroll
+      for (int kk = 2; kk <= kWave; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+          const int o = __shfl_xor(v, j, kWave);
+          const bool up = (lane & kk) == 0;       // this pair sorts ascending
+          const bool low = (lane & j) == 0;       // this lane keeps the smaller
+          v = (low == up) ? min(v, o) : max(v, o);
+        }
       }
-      const int rank = __popcll(peers & lt_mask);
-      if (valid) rank_buf[s] = my_cnt[key] + rank;
+      const int skey = v >> 6, src = v & 63;
+      const int prev = __shfl_up(skey, 1, kWave);
+      const int next = __shfl_down(skey, 1, kWave);
+      const bool head = lane == 0 || prev != skey;
+      const bool tail = lane == kWave - 1 || next != skey;
+      // first sorted position of this lane's key: inclusive max-scan of head positions
+      int first = head ? lane : 0;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(first, d, kWave);
+        if (lane >= d) first = max(first, y);
+      }
+      const int rank = lane - first;
+      const int before = skey < nb ? my_cnt[skey] : 0;
+      // back to the slot's own lane
+      const int r_src = __builtin_amdgcn_ds_permute(src << 2, before + rank);
+      if (valid) rank_buf[s] = r_src;
       __builtin_amdgcn_wave_barrier();
-      if (valid && rank == 0) my_cnt[key] += __popcll(peers);
+      if (tail && skey < nb) my_cnt[skey] = before + rank + 1;
       __builtin_amdgcn_wave_barrier();
     }
   }
@@ -208,16 +242,24 @@ hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_
   const int chunks = align_chunks(nb, S);
   const bool in_lds = keys_in_lds(S, nb);
   const size_t lds = (static_cast<size_t>(chunks) * nb + (in_lds ? 2 * S : 0)) * sizeof(int);
-#define MOELORA_ALIGN_LAUNCH(KL, RT)                                                              \
-  hipLaunchKernelGGL((k_align<KL, RT>), dim3(1), dim3(kAlignThreads), lds, stream, logits, ids_in, \
-                     adapter_ids, T, E, k, L, Lb, chunks, topk_ids, topk_w, sorted_slots, offsets, \
-                     status, ws_key, ws_rank)
+#define MOELORA_ALIGN_LAUNCH(KL, RT, KM)                                                          \
+  hipLaunchKernelGGL((k_align<KL, RT, KM>), dim3(1), dim3(kAlignThreads), lds, stream, logits,    \
+                     ids_in, adapter_ids, T, E, k, L, Lb, chunks, topk_ids, topk_w, sorted_slots, \
+                     offsets, status, ws_key, ws_rank)
+#define MOELORA_ALIGN_ROUTE(KL)                                      \
+  do {                                                               \
+    if (k <= 1) MOELORA_ALIGN_LAUNCH(KL, true, 1);                   \
+    else if (k <= 2) MOELORA_ALIGN_LAUNCH(KL, true, 2);              \
+    else if (k <= 4) MOELORA_ALIGN_LAUNCH(KL, true, 4);              \
+    else MOELORA_ALIGN_LAUNCH(KL, true, kMaxTopK);                   \
+  } while (0)
   const bool route = logits != nullptr;
   if (in_lds) {
-    if (route) MOELORA_ALIGN_LAUNCH(true, true); else MOELORA_ALIGN_LAUNCH(true, false);
+    if (route) MOELORA_ALIGN_ROUTE(true); else MOELORA_ALIGN_LAUNCH(true, false, 1);
   } else {
-    if (route) MOELORA_ALIGN_LAUNCH(false, true); else MOELORA_ALIGN_LAUNCH(false, false);
+    if (route) MOELORA_ALIGN_ROUTE(false); else MOELORA_ALIGN_LAUNCH(false, false, 1);
   }
+#undef MOELORA_ALIGN_ROUTE
 #undef MOELORA_ALIGN_LAUNCH
   return hipGetLastError();
 }

@@ -9,8 +9,10 @@ namespace moelora {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
-// LDS ints available to the align kernel's per-chunk bucket counters.
-constexpr int kAlignLdsInts = 15360;
+// LDS ints available to the align kernel's per-chunk bucket counters and,
+// when they fit, the per-slot keys and ranks (144 KiB of the 160 KiB a gfx950
+// workgroup may use).
+constexpr int kAlignLdsInts = 36864;
 int align_chunks(int nb, int S);
 
 // logits == nullptr: the expert ids come from ids_in (no routing, topk_ids and
