@@ -144,6 +144,15 @@ int oracle_route(int64_t T, int32_t E, int32_t k, const float* logits,
  * (l(t) = L for adapter -1).
  * Returns ORC_EADAPTER if an adapter id is outside [0, L) (and not an allowed -1).
  */
+/* Bucket key of slot s: expert-major, then the token's adapter (a base-only
+ * token, adapter id -1, goes to its expert's bucket L). */
+static int64_t slot_key(const int32_t* topk_ids, const int32_t* adapter_ids, int64_t s, int32_t k,
+                        int32_t E, int64_t Lb, int32_t L) {
+  int32_t l = adapter_ids[s / k];
+  (void)E;  /* the key is expert-major: E does not enter it */
+  return (int64_t)topk_ids[s] * Lb + (l < 0 ? L : l);
+}
+
 int oracle_align(int64_t T, int32_t k, int32_t E, int32_t L, int32_t base_only,
                  const int32_t* topk_ids, const int32_t* adapter_ids, int32_t* sorted_slots,
                  int32_t* bucket_offsets) {
@@ -159,16 +168,17 @@ int oracle_align(int64_t T, int32_t k, int32_t E, int32_t L, int32_t base_only,
   int64_t* next = (int64_t*)calloc((size_t)nb + 1, sizeof(int64_t));
   if (!next) return ORC_ENOMEM;
   for (int64_t s = 0; s < S; ++s) {
-    int32_t l = adapter_ids[s / k];
-    next[(int64_t)topk_ids[s] * Lb + (l < 0 ? L : l) + 1] += 1;
+    int64_t key = slot_key(topk_ids, adapter_ids, s, k, E, Lb, L);
+    if (key < 0 || key >= nb) { /* a key outside the buckets: refuse, write nothing */
+      free(next);
+      return ORC_EARG;
+    }
+    next[key + 1] += 1;
   }
   for (int64_t b = 0; b < nb; ++b) next[b + 1] += next[b];
   for (int64_t b = 0; b <= nb; ++b) bucket_offsets[b] = (int32_t)next[b];
-  for (int64_t s = 0; s < S; ++s) {
-    int32_t l = adapter_ids[s / k];
-    int64_t key = (int64_t)topk_ids[s] * Lb + (l < 0 ? L : l);
-    sorted_slots[next[key]++] = (int32_t)s;
-  }
+  for (int64_t s = 0; s < S; ++s)
+    sorted_slots[next[slot_key(topk_ids, adapter_ids, s, k, E, Lb, L)]++] = (int32_t)s;
   free(next);
   return ORC_OK;
 }
