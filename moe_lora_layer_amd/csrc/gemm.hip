@@ -751,8 +751,8 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const L
     case 32: return lds_launch<T, 32, 128, 1, 4, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
     case 64: return lds_launch<T, 64, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
     case 128:
-      if (plan.stream)
-        return lds_launch<T, 128, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
+      if (plan.stream)  // eight waves of 64 x 32
+        return lds_launch<T, 128, 128, 2, 4, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
       return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, stream);
     case 256:  // prefill: 256x256 tiles, 8 waves of 128x64 (bf16: operands DMA'd into LDS)
       if (sizeof(T) == 2) {

@@ -59,14 +59,15 @@ TilePlan make_plan(const moelora_dims* d) {
   p.max_mt = static_cast<int>(S / p.bm + (E < S ? E : S) + 1);
   p.max_lt = static_cast<int>(S / p.bml + (nb < S ? nb : S) + 1);
   // Split K only when the real M x N tiles cannot give every CU a workgroup
-  // (e.g. one expert and a narrow output): ~1024 workgroups, >= 8 K-steps
-  // per split.
+  // (e.g. one expert and a narrow output): ~512 workgroups (two per CU;
+  // more splits cost more in fp32 atomics than they gain), >= 8 K-steps per
+  // split.
   const int64_t est_tiles = std::max<int64_t>((S + p.bm - 1) / p.bm, std::min<int64_t>(E, S));
   auto splits = [&](int64_t N, int64_t K) {
     const int64_t wgs = std::max<int64_t>(1, est_tiles * ((N + 127) / 128));
     const int64_t steps = K / (d->dtype == MOELORA_BF16 ? 64 : 32);
     if (wgs >= 256) return 1;
-    const int64_t want = std::max<int64_t>(1, std::min<int64_t>((1024 + wgs - 1) / wgs, steps / 8));
+    const int64_t want = std::max<int64_t>(1, std::min<int64_t>((512 + wgs - 1) / wgs, steps / 8));
     // equal K ranges with none empty: every split then owns real work (and
     // writes its whole partial in deterministic mode)
     const int64_t per = (steps + want - 1) / want;
