@@ -35,6 +35,11 @@ def _small(T, h, I, E, k, L, r, dtype, seed, requests=None, **kw):
 # times K chunks for the persistent streaming shrink (gate_up only; the down
 # shrink, K = 256, stays on the per-tile kernel)
 STREAM_SHAPE = (512, 1088, 256, 16, 4, 64, 64, "bf16")
+# the streaming shrink's other item shapes: rank 32 with 8-step chunks
+# (h = 2048), rank 16 with 2-step chunks (h = 1088: 34 steps of 32), rank 64
+# with 4-step chunks (h = 1024)
+STREAM_SHAPES_R32_R16 = [(512, 2048, 128, 16, 4, 64, 32, "bf16"), (512, 1088, 128, 16, 4, 64, 16, "bf16"),
+                         (512, 1024, 128, 16, 4, 64, 64, "bf16")]
 
 SMALL = [
     # (T, h, I, E, k, L, r, dtype): rows/expert 16 (BM 32), 38 (BM 64), 67 (BM 128);
@@ -62,6 +67,7 @@ SMALL = [
     # many short adapter buckets (~2 rows each): the gate_up shrink streams
     # (tile, K chunk) items, h = 1088 ends in a half chunk
     STREAM_SHAPE,
+    *STREAM_SHAPES_R32_R16,
 ]
 
 
@@ -291,6 +297,7 @@ DET_SHAPES = [
     (520, 192, 256, 2, 1, 9, 64, "bf16"),
     (600, 192, 128, 4, 2, 2, 32, "f32"),     # tall fp32 shrink
     STREAM_SHAPE,                            # streaming shrink: one partial per K chunk
+    STREAM_SHAPES_R32_R16[0],
 ]
 
 
