@@ -5,10 +5,13 @@
 // token goes to its most relevant experts, and expert routing compounds with
 // the per-request adapter choice, so slots are grouped by (expert, adapter).
 //
-// One workgroup of 1024 threads runs four phases separated by barriers:
-//   1. route: per token, a k-deep insertion list over the E logits (ties keep
-//      the lower id), softmax weights renormalised over the kept k; the slot
-//      keys e*L + l go to the workspace;
+// Routing runs first in its own launch over as many workgroups as the batch
+// needs (k_route): per token, k rounds of an arg-max over the E logits across
+// a segment of lanes (ties keep the lower id), softmax weights renormalised
+// over the kept k; the slot keys e*Lb + l go to the workspace.  Then one workgroup of 1024
+// threads runs four phases separated by barriers:
+//   1. keys: read the routed keys (or, without routing, form them from the
+//      caller's expert ids) into LDS when they fit;
 //   2. chunk ranks: the S slots are cut into C contiguous chunks, one per wave.
 //      A wave walks its chunk 64 slots at a time; lanes with equal keys find
 //      each other with ballots, so every slot gets its rank among equal keys of
@@ -18,8 +21,8 @@
 //      buckets gives bucket_offsets, and cnt[c][b] becomes the first output
 //      position of chunk c's slots in bucket b;
 //   4. scatter: sorted_slots[cnt[c][key] + rank] = s.
-// ROUTE = false skips the routing of phase 1: the caller's topk_ids (its own
-// router, e.g. a router GEMM and top-k just before this path) give the keys.
+// ROUTED = false: no k_route launch; the caller's topk_ids (its own router,
+// e.g. a router GEMM and top-k just before this path) give the keys.
 // device_status: 0 ok, 1 an adapter id outside [0, L), 2 internal
 // inconsistency, 3 a given expert id outside [0, E) (the largest code wins).
 // No step depends on atomic ordering, so the result is bit-exact and stable.
@@ -33,15 +36,108 @@ constexpr int kMaxTopK = 8;
 
 // KEYS_LDS: the per-slot keys and ranks live in LDS after the counters (small
 // batches); otherwise in the workspace.
-// KMAX: the routing list length compiled in, the smallest of 1, 2, 4, 8 that
-// holds k (a longer list only adds compare-and-select steps).
-template <bool KEYS_LDS, bool ROUTE, int KMAX>
+// Set in a routed key whose token had an adapter id outside [0, L) (keys stay
+// below 2^13 by the bucket limit).
+constexpr int kKeyBadAdapter = 1 << 30;
+
+// Routing.  A segment of W lanes (the smallest power of two >= E, at most 64)
+// holds one token, lane i of it the experts i, i + W, ...; k rounds of a
+// segmented arg-max (larger logit, ties to the lower expert id) across the
+// segment pick the token's experts in order, each round skipping the ones
+// already picked; the segment's first lane writes the token.  Each wave makes
+// one pass over 64 / W tokens, so a batch spreads over T W / 256 workgroups
+// of four waves.  KMAX: the routing list length compiled in, the smallest of
+// 1, 2, 4, 8 that holds k.
+constexpr int kRouteWaves = 4;
+constexpr int kRouteCached = 4;  // logits per lane kept in registers (E <= 256)
+
+template <int KMAX>
+__global__ void __launch_bounds__(kRouteWaves * kWave)
+k_route(const float* __restrict__ logits, const int32_t* __restrict__ adapter_ids, int T, int E,
+        int k, int L, int Lb, int W, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+        int32_t* __restrict__ ws_key) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int seg = lane / W, sl = lane % W;
+  const int t = (blockIdx.x * kRouteWaves + wave) * (kWave / W) + seg;
+  const bool tok = t < T;
+  const float* lg = logits + static_cast<int64_t>(tok ? t : 0) * E;
+  float lv[kRouteCached];
+#pragma unroll
+  for (int j = 0; j < kRouteCached; ++j) {
+    const int e = sl + W * j;
+    lv[j] = (tok && e < E) ? lg[e] : -INFINITY;
+  }
+  float win_v[KMAX];
+  int win_id[KMAX];
+#pragma unroll
+  for (int q = 0; q < KMAX; ++q) {
+    win_v[q] = -INFINITY;
+    win_id[q] = 0x7fffffff;
+    if (q >= k) continue;  // uniform
+    // this lane's best expert not picked yet
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    auto consider = [&](float v, int e) {
+      bool taken = false;
+#pragma unroll
+      for (int p = 0; p < q; ++p) taken |= win_id[p] == e;
+      const bool better = !taken & ((v > bv) | ((v == bv) & (e < bi)));
+      bv = better ? v : bv;
+      bi = better ? e : bi;
+    };
+#pragma unroll
+    for (int j = 0; j < kRouteCached; ++j) {
+      const int e = sl + W * j;
+      if (e < E) consider(lv[j], e);
+    }
+    for (int e = sl + W * kRouteCached; tok && e < E; e += W) consider(lg[e], e);  // E > 256
+    // segmented arg-max over aligned groups of W lanes
+    for (int d = 1; d < W; d <<= 1) {
+      const float ov = __shfl_xor(bv, d, kWave);
+      const int oi = __shfl_xor(bi, d, kWave);
+      const bool better = (ov > bv) | ((ov == bv) & (oi < bi));
+      bv = better ? ov : bv;
+      bi = better ? oi : bi;
+    }
+    win_v[q] = bv;
+    win_id[q] = bi;
+  }
+  if (!tok || sl != 0) return;
+  int l = adapter_ids[t];
+  int flag = 0;
+  if (l == -1 && Lb > L) {
+    l = L;  // base-only token: the expert's last bucket
+  } else if (l < 0 || l >= L) {
+    flag = kKeyBadAdapter;
+    l = 0;
+  }
+  float ex[KMAX];
+  float sum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < KMAX; ++q) {
+    if (q < k) {
+      ex[q] = expf(win_v[q] - win_v[0]);
+      sum += ex[q];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < KMAX; ++q) {
+    if (q < k) {
+      const int s = t * k + q;
+      topk_ids[s] = win_id[q];
+      topk_w[s] = ex[q] / sum;
+      ws_key[s] = (win_id[q] * Lb + l) | flag;
+    }
+  }
+}
+
+template <bool KEYS_LDS, bool ROUTED>
 __global__ void __launch_bounds__(kAlignThreads)
-k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
-        const int32_t* __restrict__ adapter_ids, int T, int E,
-        int k, int L, int Lb, int chunks, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-        int32_t* __restrict__ sorted_slots, int32_t* __restrict__ offsets,
-        int32_t* __restrict__ status, int32_t* __restrict__ ws_key, int32_t* __restrict__ ws_rank) {
+k_align(const int32_t* __restrict__ ids_in, const int32_t* __restrict__ adapter_ids, int T, int E,
+        int k, int L, int Lb, int chunks, int32_t* __restrict__ sorted_slots,
+        int32_t* __restrict__ offsets, int32_t* __restrict__ status, int32_t* __restrict__ ws_key,
+        int32_t* __restrict__ ws_rank) {
   extern __shared__ int cnt[];  // [chunks][nb], then (KEYS_LDS) key[S], rank[S]
   __shared__ int wave_tmp[16];
   __shared__ int bad;
@@ -58,16 +154,26 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
   if (tid == 0) bad = 0;
   __syncthreads();
 
-  // ---- 1. route --------------------------------------------------------------
-  for (int t = tid; t < T; t += kAlignThreads) {
-    int l = adapter_ids[t];
-    if (l == -1 && Lb > L) {
-      l = L;  // base-only token: the expert's last bucket
-    } else if (l < 0 || l >= L) {
-      atomicMax(&bad, 1);
-      l = 0;
+  // ---- 1. keys -----------------------------------------------------------------
+  if (ROUTED) {
+    // keys from k_route; a flagged key marks a token whose adapter id was out of range
+    for (int s = tid; s < S; s += kAlignThreads) {
+      int key = ws_key[s];
+      if (key & kKeyBadAdapter) {
+        atomicMax(&bad, 1);
+        key &= ~kKeyBadAdapter;
+      }
+      key_buf[s] = key;
     }
-    if (!ROUTE) {
+  } else {
+    for (int t = tid; t < T; t += kAlignThreads) {
+      int l = adapter_ids[t];
+      if (l == -1 && Lb > L) {
+        l = L;  // base-only token: the expert's last bucket
+      } else if (l < 0 || l >= L) {
+        atomicMax(&bad, 1);
+        l = 0;
+      }
       for (int q = 0; q < k; ++q) {
         const int s = t * k + q;
         int e = ids_in != nullptr ? ids_in[s] : 0;
@@ -76,61 +182,6 @@ k_align(const float* __restrict__ logits, const int32_t* __restrict__ ids_in,
           e = 0;
         }
         key_buf[s] = e * Lb + l;
-      }
-      continue;
-    }
-    float val[KMAX];
-    int id[KMAX];
-#pragma unroll
-    for (int q = 0; q < KMAX; ++q) {
-      val[q] = -INFINITY;
-      id[q] = 0x7fffffff;
-    }
-    const float* lg = logits + static_cast<int64_t>(t) * E;
-    // logits in batches of 16 loads issued together (one memory latency per
-    // batch, not per expert); past E the batch holds -inf candidates, which
-    // never pass a real logit (E >= k real ones come first)
-    constexpr int kBatch = 16;
-    for (int e0 = 0; e0 < E; e0 += kBatch) {
-      float lv[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) lv[u] = lg[min(e0 + u, E - 1)];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) lv[u] = e0 + u < E ? lv[u] : -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        float cv = lv[u];
-        int ci = e0 + u;
-        // carry the candidate down the list: it passes every entry it beats
-        // (selects, no branches)
-#pragma unroll
-        for (int q = 0; q < KMAX; ++q) {
-          const bool before = (q < k) & ((cv > val[q]) | ((cv == val[q]) & (ci < id[q])));
-          const float tv = val[q];
-          const int ti = id[q];
-          val[q] = before ? cv : tv;
-          id[q] = before ? ci : ti;
-          cv = before ? tv : cv;
-          ci = before ? ti : ci;
-        }
-      }
-    }
-    float ex[KMAX];
-    float sum = 0.0f;
-#pragma unroll
-    for (int q = 0; q < KMAX; ++q) {
-      if (q < k) {
-        ex[q] = expf(val[q] - val[0]);
-        sum += ex[q];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < KMAX; ++q) {
-      if (q < k) {
-        int s = t * k + q;
-        topk_ids[s] = id[q];
-        topk_w[s] = ex[q] / sum;
-        key_buf[s] = id[q] * Lb + l;
       }
     }
   }
@@ -242,24 +293,32 @@ hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_
   const int chunks = align_chunks(nb, S);
   const bool in_lds = keys_in_lds(S, nb);
   const size_t lds = (static_cast<size_t>(chunks) * nb + (in_lds ? 2 * S : 0)) * sizeof(int);
-#define MOELORA_ALIGN_LAUNCH(KL, RT, KM)                                                          \
-  hipLaunchKernelGGL((k_align<KL, RT, KM>), dim3(1), dim3(kAlignThreads), lds, stream, logits,    \
-                     ids_in, adapter_ids, T, E, k, L, Lb, chunks, topk_ids, topk_w, sorted_slots, \
-                     offsets, status, ws_key, ws_rank)
-#define MOELORA_ALIGN_ROUTE(KL)                                      \
-  do {                                                               \
-    if (k <= 1) MOELORA_ALIGN_LAUNCH(KL, true, 1);                   \
-    else if (k <= 2) MOELORA_ALIGN_LAUNCH(KL, true, 2);              \
-    else if (k <= 4) MOELORA_ALIGN_LAUNCH(KL, true, 4);              \
-    else MOELORA_ALIGN_LAUNCH(KL, true, kMaxTopK);                   \
-  } while (0)
-  const bool route = logits != nullptr;
-  if (in_lds) {
-    if (route) MOELORA_ALIGN_ROUTE(true); else MOELORA_ALIGN_LAUNCH(true, false, 1);
-  } else {
-    if (route) MOELORA_ALIGN_ROUTE(false); else MOELORA_ALIGN_LAUNCH(false, false, 1);
+  const bool routed = logits != nullptr;
+  if (routed && T > 0) {
+    int W = 1;
+    while (W < E && W < kWave) W <<= 1;
+    const int per_wg = kRouteWaves * (kWave / W);  // tokens per workgroup
+    const dim3 grid(static_cast<unsigned>((T + per_wg - 1) / per_wg));
+#define MOELORA_ROUTE_LAUNCH(KM)                                                                 \
+  hipLaunchKernelGGL((k_route<KM>), grid, dim3(kRouteWaves * kWave), 0, stream, logits,          \
+                     adapter_ids, T, E, k, L, Lb, W, topk_ids, topk_w, ws_key)
+    if (k <= 1) MOELORA_ROUTE_LAUNCH(1);
+    else if (k <= 2) MOELORA_ROUTE_LAUNCH(2);
+    else if (k <= 4) MOELORA_ROUTE_LAUNCH(4);
+    else MOELORA_ROUTE_LAUNCH(kMaxTopK);
+#undef MOELORA_ROUTE_LAUNCH
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-#undef MOELORA_ALIGN_ROUTE
+#define MOELORA_ALIGN_LAUNCH(KL, RT)                                                               \
+  hipLaunchKernelGGL((k_align<KL, RT>), dim3(1), dim3(kAlignThreads), lds, stream, ids_in,        \
+                     adapter_ids, T, E, k, L, Lb, chunks, sorted_slots, offsets, status, ws_key, \
+                     ws_rank)
+  if (in_lds) {
+    if (routed) MOELORA_ALIGN_LAUNCH(true, true); else MOELORA_ALIGN_LAUNCH(true, false);
+  } else {
+    if (routed) MOELORA_ALIGN_LAUNCH(false, true); else MOELORA_ALIGN_LAUNCH(false, false);
+  }
 #undef MOELORA_ALIGN_LAUNCH
   return hipGetLastError();
 }

@@ -514,16 +514,15 @@ k_shrink_stream(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restr
   // time: the chunks of a tile share its activation rows and A^T block, and
   // the pipelined inner loop has no stores (a store's registers would hold up
   // the next loads behind the waits of the one in-order counter)
-  const int n = counts[1] * nkc;
-  const int i0 = static_cast<int>(static_cast<int64_t>(n) * wid / nwaves);
-  const int i1 = static_cast<int>(static_cast<int64_t>(n) * (wid + 1) / nwaves);
+  const int64_t n = static_cast<int64_t>(counts[1]) * nkc;
+  const int64_t i0 = n * wid / nwaves, i1 = n * (wid + 1) / nwaves;
   clear();
   frag_t a0[ST][RB], x0[ST], a1[ST][RB], x1[ST];
-  for (int it = i0; it < i1;) {
-    const int tl = it / nkc;
+  for (int64_t it = i0; it < i1;) {
+    const int tl = static_cast<int>(it / nkc);
     const Work w = describe(tl);
-    const int kc0 = it - tl * nkc;
-    const int kc1 = min(nkc, kc0 + (i1 - it));  // this run's chunks of the tile
+    const int kc0 = static_cast<int>(it - static_cast<int64_t>(tl) * nkc);
+    const int kc1 = static_cast<int>(min<int64_t>(nkc, kc0 + (i1 - it)));  // this run's chunks of the tile
     int kc = kc0;
     load(a0, x0, w, kc);
     for (;;) {
