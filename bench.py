@@ -16,7 +16,7 @@ library records on the launch stream around its kernels
 the per-stage breakdown; the timed K steps record only the two events around
 the dominant kernel, whose mean duration gives the roofline figure.  Also
 untimed: the per-step latency (p10/p50/p90 of event-bracketed align + forward),
-warm and cold (a 1 GiB write before each step evicts the MALL and the L2s).
+warm and cold (a 1 GiB read before each step evicts the MALL and the L2s).
 The CPU baseline times the plain C oracle on the host's cores over a bounded
 sample of the same workload.
 """
@@ -231,14 +231,15 @@ def main() -> int:
     dom_i = int(np.argmax(mean_ms))
     dom = ops.STAGES[dom_i]
 
-    # per-step latency (untimed): warm, and cold with a 1 GiB write before each
-    # step (outside its events) that evicts the MALL and the L2s
+    # per-step latency (untimed): warm, and cold with a 1 GiB read before each
+    # step (outside its events) that evicts the MALL and the L2s; a read, not a
+    # write, so that no dirty line is written back inside the timed step
     def latency(flush):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         for e0, e1 in evs:
             if flush is not None:
-                flush.zero_()
+                flush.sum()
             e0.record()
             step()
             e1.record()
@@ -246,7 +247,7 @@ def main() -> int:
         us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
         return {q: round(float(np.percentile(us, p)), 2) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
     lat_warm = latency(None)
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     lat_cold = latency(flush_buf)
     del flush_buf
 
@@ -333,7 +334,7 @@ def main() -> int:
                    "adapters": cfg.adapters, "rank": cfg.rank, "requests": cfg.requests,
                    "adapter_dist": cfg.adapter_dist, "parallelism": "single GPU"},
         "roofline": roof,
-        "latency_us": {"warm": lat_warm, "cold_1GiB_flush": lat_cold},
+        "latency_us": {"warm": lat_warm, "cold_1GiB_read_flush": lat_cold},
         "fusion": fusion,
         "deterministic": args.deterministic,
         "cpu_baseline": cpu,
