@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOELORA_ABI_VERSION 4
+#define MOELORA_ABI_VERSION 5
 
 typedef enum moelora_status {
   MOELORA_OK = 0,
@@ -76,7 +76,7 @@ typedef struct moelora_dims {
   int32_t adapters;      /* L: adapters resident at once                            */
   int32_t rank;          /* r                                                       */
   int32_t dtype;         /* moelora_dtype                                           */
-  int32_t flags;         /* 0, or MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_BASE_ONLY */
+  int32_t flags;         /* 0, or any of MOELORA_FLAG_*                              */
 } moelora_dims;
 
 /*
@@ -100,6 +100,15 @@ typedef struct moelora_dims {
  * entries (E * L + 1 without the flag), and E * Lb must stay <= 8192.
  */
 #define MOELORA_FLAG_BASE_ONLY 2
+
+/*
+ * MOELORA_FLAG_UNFUSED: moelora_forward runs every LoRA expand as a kernel of
+ * its own after the base GEMM instead of inside the GEMM's epilogue, so that
+ * the base output G is left in the workspace for layer-by-layer reconciliation
+ * (moelora_forward_workspace_layout).  The result is the same within the
+ * layer's tolerance; the fused form is faster.  Ignored by moelora_align.
+ */
+#define MOELORA_FLAG_UNFUSED 4
 
 int moelora_abi_version(void);
 
@@ -210,8 +219,8 @@ enum moelora_stage {
   MOELORA_STAGE_ZERO = 1,        /* clear the gate_up output when its GEMM is split
                                     over K (empty otherwise)                          */
   MOELORA_STAGE_SHRINK_GATE_UP = 2,
-  MOELORA_STAGE_GEMM_GATE_UP = 3,    /* with the plan of 256-row bf16 tiles and unsplit
-                                        K, also the LoRA expand and the SiLU-mul      */
+  MOELORA_STAGE_GEMM_GATE_UP = 3,    /* bf16 with unsplit K: also the LoRA expand and
+                                        the SiLU-mul (moelora_forward_fusion)         */
   MOELORA_STAGE_EXPAND_GATE_UP = 4,  /* + base add + SiLU-mul; empty when fused       */
   MOELORA_STAGE_SHRINK_DOWN = 5,
   MOELORA_STAGE_GEMM_DOWN = 6,       /* fused LoRA expand under the same condition   */
@@ -243,8 +252,8 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
  * sorted position p (row p belongs to slot sorted_slots[p]):
  *   offsets[0]  G   float [T*k][2I]  gate_up base output xW (before the LoRA add);
  *                                    not written when the gate_up GEMM fuses the
- *                                    expand (bf16, 256-row tiles, unsplit K: more
- *                                    than about 200 rows per expert)
+ *                                    expand (moelora_forward_fusion; never with
+ *                                    MOELORA_FLAG_UNFUSED)
  *   offsets[1]  Z1  float [T*k][r]   gate_up shrink xA
  *   offsets[2]  ACT dtype [T*k][I]   SiLU(gate) * up, including both LoRA terms
  *   offsets[3]  Z2  float [T*k][r]   down shrink a A
@@ -258,7 +267,10 @@ int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]
  * "Multi-LoRA", section "Implementing Multi-LoRA inference for MoE models in
  * vLLM"): *flags gets bit MOELORA_FUSED_GATE_UP (gate_up expand and SiLU-mul;
  * G is then not written) and bit MOELORA_FUSED_DOWN (down expand).  The
- * matching MOELORA_STAGE_EXPAND_* stages are then empty.  Host only; returns
+ * matching MOELORA_STAGE_EXPAND_* stages are then empty.  A projection fuses
+ * when the dtype is bf16, its base GEMM is not split over K (split K is
+ * chosen only when the output has too few tiles to fill the GPU) and
+ * MOELORA_FLAG_UNFUSED is not set.  Host only; returns
  * the validation status of dims (MOELORA_ERR_NULL for a NULL flags).
  */
 #define MOELORA_FUSED_GATE_UP 1
@@ -273,9 +285,10 @@ int moelora_forward_fusion(const moelora_dims* dims, int* flags);
  *   out[t] = x_t W + (x_t A[l]) B[l]
  * with no experts, routing or activation.  Runs the layer's own kernels with
  * one expert and k = 1: tokens bucketed by adapter, the shrink, the grouped
- * GEMM (with the LoRA expand in its epilogue for 256-row bf16 tiles), the
+ * GEMM (with the LoRA expand in its epilogue for bf16 with unsplit K), the
  * expand otherwise, and the write-back to token order in the output dtype.
- * flags as in moelora_dims (deterministic split-K, base-only adapter -1).
+ * flags as in moelora_dims (deterministic split-K, base-only adapter -1,
+ * unfused expand).
  */
 typedef struct moelora_dense_dims {
   int64_t tokens;        /* T                                                       */
@@ -284,7 +297,7 @@ typedef struct moelora_dense_dims {
   int32_t adapters;      /* L                                                       */
   int32_t rank;          /* r: 16, 32 or 64                                         */
   int32_t dtype;         /* moelora_dtype of x, weights and out                     */
-  int32_t flags;         /* MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_BASE_ONLY     */
+  int32_t flags;         /* 0, or any of MOELORA_FLAG_*                              */
 } moelora_dense_dims;
 
 int moelora_dense_workspace_size(const moelora_dense_dims* dims, size_t* bytes);

@@ -154,18 +154,84 @@ __device__ __forceinline__ uint4 masked(uint4 v, uint32_t m) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
+// Epilogues of the grouped GEMMs.  EPI_STORE writes the fp32 tile to C
+// (relaxed atomics under split K).  The two fused forms first add the LoRA
+// expand of the tile's rows to the accumulators (lora_expand_acc) and then,
+// EPI_GATE_UP, apply SiLU(gate) * up and write bf16 ACT, or, EPI_DOWN, write
+// D.  The vLLM blog page "Multi-LoRA" (section "Implementing Multi-LoRA
+// inference for MoE models in vLLM") names folding the LoRA add into the base
+// GEMM's output as the next fusion step.
+enum { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_DOWN = 2 };
+
+// acc[i][j] += z_p . B[l][e]^T for every adapter bucket (e, l) of expert e that
+// meets this wave's rows [rw0, rw1) (row block i: rows rw0 + 32 i + 0..31),
+// on the MFMA units: z (fp32, from the shrink) split into bf16 hi + lo, rows
+// outside the bucket masked to zero.  brow[j]: the B^T row of the lane's
+// output column in fragment j; col_ok[j] false: no such column.  A base-only
+// bucket, if any, comes last in the expert and is skipped.
+template <int FM, int FN>
+__device__ __forceinline__ void lora_expand_acc(f32x16_t (&acc)[FM][FN], const LoraEpilogue& lora,
+                                                int e, int rw0, int rw1, const int64_t (&brow)[FN],
+                                                const bool (&col_ok)[FN], int c32, int h) {
+  const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
+  // last bucket of expert e starting at or before rw0
+  int lb = 0, ub = lora.adapters - 1;
+  while (lb < ub) {
+    const int mid = (lb + ub + 1) >> 1;
+    if (off[mid] <= rw0) lb = mid; else ub = mid - 1;
+  }
+  const int nks = lora.rank / 16;
+  for (int l = lb; l < lora.adapters && off[l] < rw1; ++l) {
+    const int s0 = max(rw0, off[l]), s1 = min(rw1, off[l + 1]);
+    if (s0 >= s1) continue;  // uniform: an empty bucket
+    const bf16_t* Bb = lora.b + (static_cast<int64_t>(l) * lora.experts + e) * lora.b_rows * lora.rank;
+    bf16x8_t bfr[FN][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        bfr[j][q4] = (q4 < nks && col_ok[j])
+                         ? *reinterpret_cast<const bf16x8_t*>(Bb + brow[j] * lora.rank + 16 * q4 + 8 * h)
+                         : Mfma<bf16_t>::zero();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rb = rw0 + 32 * i;
+      if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
+      const int p = rb + c32;
+      const bool in = p >= s0 && p < s1;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        if (q4 >= nks) break;
+        bf16x8_t zh = Mfma<bf16_t>::zero(), zl = zh;
+        if (in) split_bf16x8(lora.z + static_cast<int64_t>(p) * lora.rank + 16 * q4 + 8 * h, zh, zl);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zh, bfr[j][q4], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zl, bfr[j][q4], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
 // ksplit > 1: workgroup (tile, s) covers the s-th of ksplit K ranges and adds
 // its partial tile to C with relaxed fp32 atomics (C must be zero before).
 // PIPE: the LDS writes of K-step kt+1 and the global loads of K-step kt+2 are
 // issued between the MFMAs of K-step kt (one barrier per K-step); requires P = 1.
+// EPI: EPI_STORE, or a fused LoRA epilogue (bf16, unsplit K).  EPI_GATE_UP
+// tiles cover BN/2 columns i of the intermediate width I = N/2 and load the
+// weight rows so that gate i and up I + i meet in the same wave: with two or
+// more 32-column fragments per wave, fragment j < FN/2 holds gate columns and
+// j + FN/2 the matching up columns (same lane); with one, lanes c < 16 hold
+// gate and lanes c + 16 the matching up columns.
 template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
-          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false>
+          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false, int EPI = EPI_STORE>
 __global__ void __launch_bounds__(WM * WN * kWave)
 k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
        const T* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
        const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
        const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, float* __restrict__ parts,
-       int64_t part_stride) {
+       int64_t part_stride, LoraEpilogue lora) {
   typedef Mfma<T> M;
   constexpr int NT_ = WM * WN * kWave;
   constexpr int ROWB = 128;                    // bytes of K per LDS row
@@ -228,12 +294,35 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   uint32_t b_mask[B_CH];
   int b_dst[B_CH];
   const T* We = Wt + static_cast<int64_t>(e) * N * K;
+  const int64_t I = N / 2;                          // EPI_GATE_UP: intermediate width
+  const int64_t it0 = static_cast<int64_t>(nt) * (BN / 2);
+  // EPI_GATE_UP: the intermediate column i and gate (0) / up (1) half of
+  // wave column group wg's fragment j, lane column c
+  auto gu_col = [&](int wg, int j, int c, int& up) -> int64_t {
+    if (FN >= 2) {
+      up = j >= FN / 2;
+      return it0 + wg * (WTN / 2) + (j % (FN / 2 > 0 ? FN / 2 : 1)) * 32 + c;
+    }
+    up = c >= 16;
+    return it0 + wg * 16 + (c & 15);
+  };
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     const int q = tid + i * NT_, row = q >> 3, ch = q & 7;
-    const int64_t n = n0 + row;
-    b_mask[i] = n < N ? 0xffffffffu : 0u;
-    b_src[i] = We + (n < N ? n : N - 1) * K + ch * VEC;
+    int64_t wrow;
+    bool ok;
+    if (EPI == EPI_GATE_UP) {
+      int up;
+      const int64_t ic = gu_col(row / WTN, (row % WTN) / 32, row & 31, up);
+      ok = ic < I;
+      wrow = up * I + (ok ? ic : I - 1);
+    } else {
+      const int64_t n = n0 + row;
+      ok = n < N;
+      wrow = ok ? n : N - 1;
+    }
+    b_mask[i] = ok ? 0xffffffffu : 0u;
+    b_src[i] = We + wrow * K + ch * VEC;
     b_dst[i] = BM * ROWB + row * ROWB + ((ch ^ swz<SWZ>(row)) << 4);
   }
 
@@ -357,6 +446,55 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   }
   }
 
+  if (EPI != EPI_STORE) {
+    static_assert(EPI == EPI_STORE || sizeof(T) == 2, "fused epilogues are bf16");
+    // output column of fragment j held by this lane, and its LoRA B row
+    int64_t col[FN], brow[FN];
+    bool col_ok[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if (EPI == EPI_GATE_UP) {
+        int up;
+        col[j] = gu_col(wn, j, c32, up);
+        col_ok[j] = col[j] < I;
+        brow[j] = up * I + col[j];
+      } else {
+        col[j] = n0 + wn * WTN + j * 32 + c32;
+        col_ok[j] = col[j] < N;
+        brow[j] = col[j];
+      }
+    }
+    const int rw0 = row0 + wm * WTM;  // this wave's rows [rw0, rw1)
+    const int rw1 = min(row_end, rw0 + WTM);
+    if (rw0 < rw1) lora_expand_acc<FM, FN>(acc, lora, e, rw0, rw1, brow, col_ok, c32, h);
+    if (EPI == EPI_GATE_UP) {
+      constexpr int FG = FN >= 2 ? FN / 2 : 1;  // gate fragments
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FG; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            // FN == 1: the up value sits 16 lanes over (every lane takes part)
+            const float g = acc[i][j][r];
+            const float u = FN >= 2 ? acc[i][FN >= 2 ? j + FG : 0][r] : __shfl_xor(g, 16);
+            const int p = rw0 + 32 * i + acc_row(r, h);
+            if ((FN >= 2 || c32 < 16) && p < row_end && col_ok[j])
+              lora.act[static_cast<int64_t>(p) * I + col[j]] = f32_to_bf16(silu(g) * u);
+          }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int p = rw0 + 32 * i + acc_row(r, h);
+            if (p < row_end && col_ok[j]) C[static_cast<int64_t>(p) * N + col[j]] = acc[i][j][r];
+          }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -395,16 +533,36 @@ struct GemmArgs {
 };
 
 template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
-          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false>
-static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, hipStream_t stream) {
-  const int n_ntiles = static_cast<int>((a.N + BN - 1) / BN);
+          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false, int EPI = EPI_STORE>
+static hipError_t lds_launch_epi(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue& lora,
+                                 hipStream_t stream) {
+  const int64_t cols = EPI == EPI_GATE_UP ? a.N / 2 : a.N;
+  const int tn = EPI == EPI_GATE_UP ? BN / 2 : BN;
+  const int n_ntiles = static_cast<int>((cols + tn - 1) / tn);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE>), dim3(static_cast<unsigned>(grid)),
-                     dim3(WM * WN * kWave), 0, stream, static_cast<const T*>(a.X), a.x_rows,
-                     a.gather_slots, a.gather_k, static_cast<const T*>(a.Wt), a.N, a.K, a.C,
-                     a.mtiles, a.counts, a.expert_tiles, n_ntiles, a.ksplit, a.parts,
-                     a.part_stride);
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE, EPI>),
+                     dim3(static_cast<unsigned>(grid)), dim3(WM * WN * kWave), 0, stream,
+                     static_cast<const T*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
+                     static_cast<const T*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
+                     a.expert_tiles, n_ntiles, a.ksplit, a.parts, a.part_stride, lora);
   return hipGetLastError();
+}
+
+// the epilogue picked by lora: none (EPI_STORE), gate_up (act set) or down
+template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
+          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false>
+static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue* lora,
+                             hipStream_t stream) {
+  if constexpr (sizeof(T) == 2) {
+    if (lora != nullptr && lora->act != nullptr)
+      return lds_launch_epi<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
+                            EPI_GATE_UP>(plan, a, *lora, stream);
+    if (lora != nullptr)
+      return lds_launch_epi<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE, EPI_DOWN>(
+          plan, a, *lora, stream);
+  }
+  return lds_launch_epi<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE>(
+      plan, a, LoraEpilogue{}, stream);
 }
 
 
@@ -442,16 +600,6 @@ __device__ __forceinline__ void dma_issue(unsigned char* smem, int slot, int64_t
         b_src[j] + ko, (lds_void_t*)(st + (kDmaTile + 32 * wave + 8 * j) * kDmaRowB), 16, 0, 0);
 }
 
-// Epilogue of the prefill GEMM.  EPI_STORE writes the fp32 tile to C
-// (relaxed atomics under split K).  The two fused forms add the LoRA expand of
-// the tile's rows to the accumulators first: for every (expert, adapter)
-// bucket that meets a wave's 128 rows, acc += z_rows . B[l][e]^T on the MFMA
-// units, z (fp32, from the shrink) split into bf16 hi + lo and the rows
-// outside the bucket masked to zero.  EPI_GATE_UP then applies SiLU(gate) * up
-// and writes bf16 ACT; EPI_DOWN writes D.  The vLLM blog page "Multi-LoRA"
-// (section "Implementing Multi-LoRA inference for MoE models in vLLM") lists
-// folding the LoRA add into the base GEMM's output as the next fusion step.
-enum { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_DOWN = 2 };
 
 template <bool GATHER, int EPI>
 __global__ void __launch_bounds__(kDmaThreads)
@@ -655,48 +803,7 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   const int rw0 = row0 + 128 * wm;                 // this wave's rows [rw0, rw1)
   const int rw1 = min(row_end, rw0 + 128);
 
-  if (EPI != EPI_STORE && rw0 < rw1) {
-    // the expert's adapter buckets (a base-only bucket, if any, comes last and is skipped)
-    const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
-    // last bucket of expert e starting at or before rw0
-    int lb = 0, ub = lora.adapters - 1;
-    while (lb < ub) {
-      const int mid = (lb + ub + 1) >> 1;
-      if (off[mid] <= rw0) lb = mid; else ub = mid - 1;
-    }
-    const int nks = lora.rank / 16;
-    for (int l = lb; l < lora.adapters && off[l] < rw1; ++l) {
-      const int s0 = max(rw0, off[l]), s1 = min(rw1, off[l + 1]);
-      if (s0 >= s1) continue;  // uniform: an empty bucket
-      const bf16_t* Bb = lora.b + (static_cast<int64_t>(l) * lora.experts + e) * lora.b_rows * lora.rank;
-      bf16x8_t bfr[2][4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          bfr[j][q4] = (q4 < nks && col_ok[j])
-                           ? *reinterpret_cast<const bf16x8_t*>(Bb + brow[j] * lora.rank + 16 * q4 + 8 * h)
-                           : Mfma<bf16_t>::zero();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rb = rw0 + 32 * i;
-        if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
-        const int p = rb + c32;
-        const bool in = p >= s0 && p < s1;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          if (q4 >= nks) break;
-          bf16x8_t zh = Mfma<bf16_t>::zero(), zl = zh;
-          if (in) split_bf16x8(lora.z + static_cast<int64_t>(p) * lora.rank + 16 * q4 + 8 * h, zh, zl);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zh, bfr[j][q4], acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zl, bfr[j][q4], acc[i][j], 0, 0, 0);
-          }
-        }
-      }
-    }
-  }
+  if (EPI != EPI_STORE && rw0 < rw1) lora_expand_acc<4, 2>(acc, lora, e, rw0, rw1, brow, col_ok, c32, h);
 
   if (EPI == EPI_GATE_UP) {
 #pragma unroll
@@ -748,19 +855,19 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const L
                                 hipStream_t stream) {
   // decode-sized M-tiles stream the weights: nontemporal loads, rotated K walk
   switch (plan.bm) {
-    case 32: return lds_launch<T, 32, 128, 1, 4, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
-    case 64: return lds_launch<T, 64, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
+    case 32: return lds_launch<T, 32, 128, 1, 4, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
+    case 64: return lds_launch<T, 64, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
     case 128:
       if (plan.stream)  // eight waves of 64 x 32
-        return lds_launch<T, 128, 128, 2, 4, 2, true, GATHER, true, false, 1, false>(plan, a, stream);
-      return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, stream);
+        return lds_launch<T, 128, 128, 2, 4, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
+      return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, lora, stream);
     case 256:  // prefill: 256x256 tiles, 8 waves of 128x64 (bf16: operands DMA'd into LDS)
       if (sizeof(T) == 2) {
         if (lora == nullptr) return dma_launch<GATHER, EPI_STORE>(plan, a, LoraEpilogue{}, stream);
         if (lora->act != nullptr) return dma_launch<GATHER, EPI_GATE_UP>(plan, a, *lora, stream);
         return dma_launch<GATHER, EPI_DOWN>(plan, a, *lora, stream);
       }
-      return lds_launch<T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, stream);
+      return lds_launch<T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, nullptr, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -775,8 +882,8 @@ hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_row
   const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts, expert_tiles,
                    ksplit, pp, c_rows * N};
   const bool gather = gather_slots != nullptr;
-  // the fused epilogues exist only in the bf16 256-row kernel, unsplit
-  if (lora != nullptr && (dtype != DT_BF16 || plan.bm != 256 || a.ksplit != 1))
+  // the fused epilogues: bf16, unsplit K
+  if (lora != nullptr && (dtype != DT_BF16 || a.ksplit != 1))
     return hipErrorInvalidValue;
   hipError_t e;
   if (dtype == DT_BF16)

@@ -28,7 +28,7 @@ int check_dims(const moelora_dims* d) {
   if (d == nullptr) return MOELORA_ERR_NULL;
   if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
   if (d->rank != 16 && d->rank != 32 && d->rank != 64) return MOELORA_ERR_UNSUPPORTED;
-  if ((d->flags & ~(MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_BASE_ONLY)) != 0)
+  if ((d->flags & ~(MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_BASE_ONLY | MOELORA_FLAG_UNFUSED)) != 0)
     return MOELORA_ERR_UNSUPPORTED;
   if (d->tokens < 0 || d->hidden <= 0 || d->intermediate <= 0) return MOELORA_ERR_DIMS;
   if (d->hidden % 64 != 0 || d->intermediate % 64 != 0) return MOELORA_ERR_DIMS;
@@ -75,8 +75,13 @@ TilePlan make_plan(const moelora_dims* d) {
   };
   p.ksplit_gu = splits(2 * d->intermediate, d->hidden);
   p.ksplit_dn = splits(d->hidden, d->intermediate);
-  // 256-row bf16 tiles run the LoRA expand in the GEMM epilogue (unsplit K)
-  const bool fusable = d->dtype == MOELORA_BF16 && p.bm == 256;
+  // bf16 GEMMs with unsplit K run the LoRA expand in their epilogue: always
+  // with 256-row tiles; with the smaller tiles only when a tile meets few
+  // adapter buckets (estimated as min(mean rows per expert, adapters) <= 8),
+  // since their epilogue takes one global round trip per bucket
+  const int64_t est_buckets = std::min<int64_t>(std::min<int64_t>(avg, p.bm), d->adapters);
+  const bool fusable = d->dtype == MOELORA_BF16 && (d->flags & MOELORA_FLAG_UNFUSED) == 0 &&
+                       (p.bm == 256 || est_buckets <= 8);
   p.fuse_gu = fusable && p.ksplit_gu == 1;
   p.fuse_dn = fusable && p.ksplit_dn == 1;
   p.det = (d->flags & MOELORA_FLAG_DETERMINISTIC) != 0;

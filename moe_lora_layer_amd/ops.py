@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmoelora.so")
 MOELORA_F32, MOELORA_BF16 = 0, 1
 MOELORA_FLAG_DETERMINISTIC = 1
 MOELORA_FLAG_BASE_ONLY = 2
+MOELORA_FLAG_UNFUSED = 4
 STAGES = ["prep", "zero", "shrink_gate_up", "gemm_gate_up", "expand_gate_up", "shrink_down",
           "gemm_down", "expand_down", "combine"]
 _TORCH_DT = {MOELORA_F32: torch.float32, MOELORA_BF16: torch.bfloat16}
@@ -84,29 +85,34 @@ def status_string(rc: int) -> str:
     return library().moelora_status_string(rc).decode()
 
 
+def _flags(deterministic, base_only, unfused) -> int:
+    return ((MOELORA_FLAG_DETERMINISTIC if deterministic else 0) |
+            (MOELORA_FLAG_BASE_ONLY if base_only else 0) |
+            (MOELORA_FLAG_UNFUSED if unfused else 0))
+
+
 def _check(rc: int, what: str):
     if rc != 0:
         raise RuntimeError(f"{what}: {status_string(rc)} (status {rc})")
 
 
 def make_dims(tokens, hidden, intermediate, experts, top_k, adapters, rank, dtype,
-              deterministic=False, base_only=False, flags=None) -> Dims:
+              deterministic=False, base_only=False, unfused=False, flags=None) -> Dims:
     if isinstance(dtype, str):
         dtype = _DT_NAME[dtype]
     elif isinstance(dtype, torch.dtype):
         dtype = MOELORA_BF16 if dtype == torch.bfloat16 else MOELORA_F32
     if flags is None:
-        flags = ((MOELORA_FLAG_DETERMINISTIC if deterministic else 0) |
-                 (MOELORA_FLAG_BASE_ONLY if base_only else 0))
+        flags = _flags(deterministic, base_only, unfused)
     return Dims(int(tokens), int(hidden), int(intermediate), int(experts), int(top_k),
                 int(adapters), int(rank), int(dtype), int(flags))
 
 
-def dims_for(cfg, tokens=None, deterministic=False, base_only=False) -> Dims:
+def dims_for(cfg, tokens=None, deterministic=False, base_only=False, unfused=False) -> Dims:
     """Dims of a workload config (moe_lora_layer_amd.synth.LayerConfig)."""
     return make_dims(cfg.tokens if tokens is None else tokens, cfg.hidden, cfg.intermediate,
                      cfg.experts, cfg.top_k, cfg.adapters, cfg.rank, cfg.dtype,
-                     deterministic=deterministic, base_only=base_only)
+                     deterministic=deterministic, base_only=base_only, unfused=unfused)
 
 
 def buckets(d: Dims) -> int:
@@ -287,11 +293,10 @@ class MoELoRALayer:
 
 
 def make_dense_dims(tokens, in_features, out_features, adapters, rank, dtype, deterministic=False,
-                    base_only=False) -> DenseDims:
+                    base_only=False, unfused=False) -> DenseDims:
     if isinstance(dtype, str):
         dtype = _DT_NAME[dtype]
-    flags = ((MOELORA_FLAG_DETERMINISTIC if deterministic else 0) |
-             (MOELORA_FLAG_BASE_ONLY if base_only else 0))
+    flags = _flags(deterministic, base_only, unfused)
     return DenseDims(int(tokens), int(in_features), int(out_features), int(adapters), int(rank),
                      int(dtype), flags)
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     assert {"moelora_align", "moelora_forward"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moelora_abi_version() == 4
+    assert lib.moelora_abi_version() == 5
 
 
 def test_status_strings():
@@ -50,8 +50,8 @@ def test_status_strings():
     (dict(hidden=100), ERR_DIMS), (dict(intermediate=96), ERR_DIMS), (dict(tokens=-1), ERR_DIMS),
     (dict(top_k=9, experts=16), ERR_DIMS), (dict(top_k=3, experts=2), ERR_DIMS), (dict(experts=0), ERR_DIMS),
     (dict(adapters=0), ERR_DIMS), (dict(experts=128, adapters=65), ERR_DIMS),
-    (dict(tokens=1 << 30, top_k=2), ERR_DIMS), (dict(flags=4), ERR_UNSUPPORTED),
-    (dict(flags=-1), ERR_UNSUPPORTED), (dict(flags=3), OK),
+    (dict(tokens=1 << 30, top_k=2), ERR_DIMS), (dict(flags=8), ERR_UNSUPPORTED),
+    (dict(flags=-1), ERR_UNSUPPORTED), (dict(flags=3), OK), (dict(flags=7), OK),
     (dict(experts=128, adapters=64), OK), (dict(experts=128, adapters=64, flags=2), ERR_DIMS),
 ])
 def test_dims_validation(kw, rc):
@@ -129,11 +129,19 @@ def test_forward_argument_errors():
 
 
 @pytest.mark.parametrize("kw,flags", [
-    (dict(), {"gate_up": False, "down": False}),                          # 16 rows per expert
+    (dict(), {"gate_up": True, "down": True}),                            # 16 rows per expert
+    (dict(unfused=True), {"gate_up": False, "down": False}),
     (dict(tokens=4096, hidden=4096, intermediate=11008, experts=16), {"gate_up": True, "down": True}),
     (dict(tokens=4096, hidden=4096, intermediate=11008, experts=16, dtype="f32"),
      {"gate_up": False, "down": False}),                                   # fused forms are bf16 only
+    (dict(tokens=4096, hidden=4096, intermediate=11008, experts=16, unfused=True),
+     {"gate_up": False, "down": False}),
     (dict(tokens=600, hidden=128, intermediate=192, experts=4), {"gate_up": True, "down": True}),
+    # 32 rows per expert over 64 adapters: too many buckets per 64-row tile
+    (dict(tokens=256, hidden=2880, intermediate=2880, experts=32, top_k=4, adapters=64, rank=64),
+     {"gate_up": False, "down": False}),
+    # one token on one expert: both GEMMs split K to fill the GPU, no fusion
+    (dict(tokens=4, hidden=4096, intermediate=1024, experts=1, top_k=1), {"gate_up": False, "down": False}),
 ])
 def test_forward_fusion_flags(kw, flags):
     assert ops.forward_fusion(good_dims(**kw)) == flags

@@ -17,12 +17,12 @@ from moe_lora_layer_amd import ops, synth
 pytestmark = pytest.mark.gpu
 
 
-def _layer(cfg, inp):
+def _layer(cfg, inp, dims=None):
     dev = device()
     dinp = device_inputs(inp, cfg, dev)
-    ids, w, ss, off, st = run_align(cfg, dinp)
+    ids, w, ss, off, st = run_align(cfg, dinp, dims)
     assert int(st[0].item()) == 0
-    out, ws = run_forward(cfg, dinp, w, ss, off)
+    out, ws = run_forward(cfg, dinp, w, ss, off, dims)
     return dinp, (ids, w, ss, off), out, ws
 
 
@@ -64,6 +64,9 @@ SMALL = [
     (300, 128, 256, 1, 1, 16, 16, "bf16"),
     # one expert, narrow output: split-K with atomics in the down GEMM
     (96, 128, 2048, 1, 1, 4, 16, "bf16"),
+    # 175 rows per expert: 128-row tiles that reuse the weight tile (four
+    # waves of 64 x 64), fused epilogues with two fragments per wave
+    (350, 192, 320, 4, 2, 3, 32, "bf16"),
     # many short adapter buckets (~2 rows each): the gate_up shrink streams
     # (tile, K chunk) items, h = 1088 ends in a half chunk
     STREAM_SHAPE,
@@ -79,6 +82,27 @@ def test_forward_small(shape):
     _, (ids, w, ss, off), out, _ = _layer(cfg, inp)
     ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
+    assert_close(to_f64(out), ref, cfg.dtype, "out")
+
+
+# bf16 shapes run again with MOELORA_FLAG_UNFUSED: the LoRA expands as
+# kernels of their own after each GEMM (one shape per GEMM tile shape)
+UNFUSED = [(64, 256, 512, 8, 2, 4, 16, "bf16"), (96, 192, 320, 5, 2, 3, 32, "bf16"),
+           (200, 320, 192, 6, 2, 3, 64, "bf16"), (350, 192, 320, 4, 2, 3, 32, "bf16"),
+           (700, 256, 320, 3, 2, 5, 32, "bf16")]
+
+
+@pytest.mark.parametrize("shape", UNFUSED, ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
+def test_forward_small_unfused(shape):
+    cfg = _small(*shape, seed=sum(shape[:7]))
+    say(f"forward small unfused {shape}")
+    inp = synth.make_inputs(cfg)
+    d = ops.dims_for(cfg, unfused=True)
+    assert ops.forward_fusion(d) == {"gate_up": False, "down": False}
+    assert ops.forward_fusion(ops.dims_for(cfg)) == {"gate_up": True, "down": True}
+    _, (ids, w, ss, off), out, _ = _layer(cfg, inp, d)
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
     ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
     assert_close(to_f64(out), ref, cfg.dtype, "out")
 
@@ -120,18 +144,20 @@ def test_forward_tile_boundaries():
     assert_close(to_f64(out), ref, cfg.dtype, "out")
 
 
-def test_forward_intermediates():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_intermediates(dtype):
     """Layer-by-layer reconciliation: G, Z1, ACT, Z2, D read from the workspace
-    against the oracle's per-slot intermediates."""
-    cfg = _small(96, 192, 320, 5, 2, 3, 32, "f32", seed=5)
+    against the oracle's per-slot intermediates (bf16: unfused, so that G is
+    written; ACT is then bf16)."""
+    cfg = _small(96, 192, 320, 5, 2, 3, 32, dtype, seed=5)
     inp = synth.make_inputs(cfg)
-    _, (ids, w, ss, off), out, ws = _layer(cfg, inp)
-    d = ops.dims_for(cfg)
+    d = ops.dims_for(cfg, unfused=True)
+    _, (ids, w, ss, off), out, ws = _layer(cfg, inp, d)
     lay = ops.forward_workspace_layout(d)
     S, I, h, r = cfg.slots, cfg.intermediate, cfg.hidden, cfg.rank
     G = to_f64(workspace_view(ws, lay["G"], (S, 2 * I), torch.float32))
     Z1 = to_f64(workspace_view(ws, lay["Z1"], (S, r), torch.float32))
-    ACT = to_f64(workspace_view(ws, lay["ACT"], (S, I), torch.float32))
+    ACT = to_f64(workspace_view(ws, lay["ACT"], (S, I), torch.float32 if dtype == "f32" else torch.bfloat16))
     Z2 = to_f64(workspace_view(ws, lay["Z2"], (S, r), torch.float32))
     D = to_f64(workspace_view(ws, lay["D"], (S, h), torch.float32))
     ss = ss.cpu().numpy()
@@ -146,9 +172,9 @@ def test_forward_intermediates():
         base = oracle.slot(base_inp, dims, t, e, l)["g"]   # xW alone
         assert_close(G[p], base, "f32", f"G p={p}")
         assert_close(Z1[p], ref["z1"], "f32", f"Z1 p={p}")
-        assert_close(ACT[p], ref["a"], "f32", f"ACT p={p}")
-        assert_close(Z2[p], ref["z2"], "f32", f"Z2 p={p}")
-        assert_close(D[p], ref["d"], "f32", f"D p={p}")
+        assert_close(ACT[p], ref["a"], dtype, f"ACT p={p}")
+        assert_close(Z2[p], ref["z2"], dtype, f"Z2 p={p}")
+        assert_close(D[p], ref["d"], dtype, f"D p={p}")
 
 
 @pytest.mark.parametrize("T", [128, 24])   # LDS-tiled GEMM / weight-streaming GEMM
@@ -162,8 +188,9 @@ def test_integer_exact_gate_up(T):
     inp = synth.make_inputs(cfg)
     for n in ["x"] + WEIGHTS:
         inp[n] = synth.from_float(rng.integers(-2, 3, inp[n].shape).astype(np.float32), "bf16")
-    _, (ids, w, ss, off), out, ws = _layer(cfg, inp)
-    lay = ops.forward_workspace_layout(ops.dims_for(cfg))
+    d = ops.dims_for(cfg, unfused=True)
+    _, (ids, w, ss, off), out, ws = _layer(cfg, inp, d)
+    lay = ops.forward_workspace_layout(d)
     S, I, r = cfg.slots, cfg.intermediate, cfg.rank
     G = to_f64(workspace_view(ws, lay["G"], (S, 2 * I), torch.float32))
     Z1 = to_f64(workspace_view(ws, lay["Z1"], (S, r), torch.float32))
