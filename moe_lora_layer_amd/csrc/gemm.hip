@@ -214,6 +214,88 @@ __device__ __forceinline__ void lora_expand_acc(f32x16_t (&acc)[FM][FN], const L
   }
 }
 
+// The same sum for waves of at most two 32-row blocks (the register-staged
+// GEMM), shaped for tiles that meet many small buckets: each row belongs to
+// one bucket, so z of the lane's rows is loaded and split once, and the B^T
+// fragments of the next bucket are loaded while the MFMAs of the current one
+// run.  Every load is unconditional (rank chunks past r and rows past the
+// wave's end reload a valid chunk or row, never used), so the compiler's
+// in-order vmcnt accounting keeps the prefetch in flight.  brow[j] must be a
+// valid B^T row for every lane (any row where the column does not exist).
+template <int FM, int FN>
+__device__ __forceinline__ void lora_expand_rows(f32x16_t (&acc)[FM][FN], const LoraEpilogue& lora,
+                                                 int e, int rw0, int rw1, const int64_t (&brow)[FN],
+                                                 int c32, int h) {
+  const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
+  const int A = lora.adapters, rk = lora.rank, nks = rk / 16;
+  int lb = 0, ub = A - 1;  // last bucket of expert e starting at or before rw0
+  while (lb < ub) {
+    const int mid = (lb + ub + 1) >> 1;
+    if (off[mid] <= rw0) lb = mid; else ub = mid - 1;
+  }
+  bf16x8_t zh[FM][4], zl[FM][4];
+  int prow[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    prow[i] = rw0 + 32 * i + c32;
+    const float* zr = lora.z + static_cast<int64_t>(min(prow[i], rw1 - 1)) * rk + 8 * h;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) split_bf16x8(zr + 16 * min(q4, nks - 1), zh[i][q4], zl[i][q4]);
+  }
+  const bf16_t* Be = lora.b + static_cast<int64_t>(e) * lora.b_rows * rk;
+  const int64_t bstride = static_cast<int64_t>(lora.experts) * lora.b_rows * rk;  // per adapter
+  auto load_b = [&](int l, bf16x8_t (&bf)[FN][4]) {
+    const bf16_t* Bb = Be + static_cast<int64_t>(l) * bstride + 8 * h;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        bf[j][q4] = *reinterpret_cast<const bf16x8_t*>(Bb + brow[j] * rk + 16 * min(q4, nks - 1));
+  };
+  auto mma_b = [&](int l, const bf16x8_t (&bf)[FN][4]) {
+    const int s0 = max(rw0, off[l]), s1 = min(rw1, off[l + 1]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rb = rw0 + 32 * i;
+      if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
+      const bool in = prow[i] >= s0 && prow[i] < s1;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        if (q4 >= nks) break;
+        const bf16x8_t a = in ? zh[i][q4] : Mfma<bf16_t>::zero();
+        const bf16x8_t b = in ? zl[i][q4] : Mfma<bf16_t>::zero();
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[j][q4], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, bf[j][q4], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // the first bucket from l on with rows in [rw0, rw1), or A
+  auto next = [&](int l) {
+    for (; l < A && off[l] < rw1; ++l)
+      if (off[l + 1] > max(off[l], rw0)) return l;
+    return A;
+  };
+  int l = next(lb);
+  if (l >= A) return;
+  bf16x8_t b0[FN][4], b1[FN][4];
+  load_b(l, b0);
+  for (;;) {  // two buckets per pass, so the two fragment sets keep fixed registers
+    int ln = next(l + 1);
+    load_b(ln < A ? ln : l, b1);  // past the last bucket: a valid reload, never used
+    mma_b(l, b0);
+    if (ln >= A) break;
+    l = ln;
+    ln = next(l + 1);
+    load_b(ln < A ? ln : l, b0);
+    mma_b(l, b1);
+    if (ln >= A) break;
+    l = ln;
+  }
+}
+
 // ksplit > 1: workgroup (tile, s) covers the s-th of ksplit K ranges and adds
 // its partial tile to C with relaxed fp32 atomics (C must be zero before).
 // PIPE: the LDS writes of K-step kt+1 and the global loads of K-step kt+2 are
@@ -448,7 +530,8 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
 
   if (EPI != EPI_STORE) {
     static_assert(EPI == EPI_STORE || sizeof(T) == 2, "fused epilogues are bf16");
-    // output column of fragment j held by this lane, and its LoRA B row
+    // output column of fragment j held by this lane, and its LoRA B row (row
+    // 0 where the column does not exist)
     int64_t col[FN], brow[FN];
     bool col_ok[FN];
 #pragma unroll
@@ -457,16 +540,24 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
         int up;
         col[j] = gu_col(wn, j, c32, up);
         col_ok[j] = col[j] < I;
-        brow[j] = up * I + col[j];
+        brow[j] = col_ok[j] ? up * I + col[j] : 0;
       } else {
         col[j] = n0 + wn * WTN + j * 32 + c32;
         col_ok[j] = col[j] < N;
-        brow[j] = col[j];
+        brow[j] = col_ok[j] ? col[j] : 0;
       }
     }
     const int rw0 = row0 + wm * WTM;  // this wave's rows [rw0, rw1)
     const int rw1 = min(row_end, rw0 + WTM);
-    if (rw0 < rw1) lora_expand_acc<FM, FN>(acc, lora, e, rw0, rw1, brow, col_ok, c32, h);
+    static_assert(EPI == EPI_STORE || FM <= 2, "lora_expand_rows keeps z of FM blocks");
+    // eight-wave tiles (two waves per SIMD per workgroup) keep the register
+    // light form: the prefetching one would cost a resident workgroup
+    if (rw0 < rw1) {
+      if constexpr (NT_ >= 512)
+        lora_expand_acc<FM, FN>(acc, lora, e, rw0, rw1, brow, col_ok, c32, h);
+      else
+        lora_expand_rows<FM, FN>(acc, lora, e, rw0, rw1, brow, c32, h);
+    }
     if (EPI == EPI_GATE_UP) {
       constexpr int FG = FN >= 2 ? FN / 2 : 1;  // gate fragments
 #pragma unroll
@@ -553,7 +644,7 @@ template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHE
           bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false>
 static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue* lora,
                              hipStream_t stream) {
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2 && BM <= 128) {  // bf16 256-row tiles run k_gemm_dma
     if (lora != nullptr && lora->act != nullptr)
       return lds_launch_epi<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
                             EPI_GATE_UP>(plan, a, *lora, stream);

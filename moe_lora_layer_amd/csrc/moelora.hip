@@ -78,7 +78,7 @@ TilePlan make_plan(const moelora_dims* d) {
   // bf16 GEMMs with unsplit K run the LoRA expand in their epilogue: always
   // with 256-row tiles; with the smaller tiles only when a tile meets few
   // adapter buckets (estimated as min(mean rows per expert, adapters) <= 8),
-  // since their epilogue takes one global round trip per bucket
+  // since their epilogue waits on about one memory round trip per bucket
   const int64_t est_buckets = std::min<int64_t>(std::min<int64_t>(avg, p.bm), d->adapters);
   const bool fusable = d->dtype == MOELORA_BF16 && (d->flags & MOELORA_FLAG_UNFUSED) == 0 &&
                        (p.bm == 256 || est_buckets <= 8);

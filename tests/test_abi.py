@@ -140,6 +140,9 @@ def test_forward_argument_errors():
     # 32 rows per expert over 64 adapters: too many buckets per 64-row tile
     (dict(tokens=256, hidden=2880, intermediate=2880, experts=32, top_k=4, adapters=64, rank=64),
      {"gate_up": False, "down": False}),
+    # 128 rows per expert over 16 adapters: too many buckets per 128-row tile
+    (dict(tokens=128, hidden=8192, intermediate=28672, experts=1, top_k=1, adapters=16),
+     {"gate_up": False, "down": False}),
     # one token on one expert: both GEMMs split K to fill the GPU, no fusion
     (dict(tokens=4, hidden=4096, intermediate=1024, experts=1, top_k=1), {"gate_up": False, "down": False}),
 ])

@@ -67,6 +67,11 @@ SMALL = [
     # 175 rows per expert: 128-row tiles that reuse the weight tile (four
     # waves of 64 x 64), fused epilogues with two fragments per wave
     (350, 192, 320, 4, 2, 3, 32, "bf16"),
+    # many one- and two-row adapter buckets per tile (the expand then runs as
+    # its own kernel): 32-, 64- and 128-row tiles, ranks 16, 64, 32
+    (48, 256, 192, 4, 2, 32, 16, "bf16"),
+    (96, 192, 320, 4, 2, 64, 64, "bf16"),
+    (350, 192, 320, 4, 2, 64, 32, "bf16"),
     # many short adapter buckets (~2 rows each): the gate_up shrink streams
     # (tile, K chunk) items, h = 1088 ends in a half chunk
     STREAM_SHAPE,
