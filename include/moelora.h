@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOELORA_ABI_VERSION 5
+#define MOELORA_ABI_VERSION 6
 
 typedef enum moelora_status {
   MOELORA_OK = 0,
@@ -59,6 +59,39 @@ typedef enum moelora_dtype {
   MOELORA_F32 = 0,   /* x, weights and out in float32                                    */
   MOELORA_BF16 = 1   /* x, weights and out in bfloat16; accumulation is always float32   */
 } moelora_dtype;
+
+/*
+ * Tile plan of moelora_forward and moelora_dense_forward: the per-shape
+ * kernel configuration (tile sizes, split-K) that the vLLM blog page
+ * "Multi-LoRA" (section "Kernel configuration tuning for Amazon SageMaker AI
+ * and Amazon Bedrock") tunes offline and lets users load from their own
+ * tuned configuration files; moe_lora_layer_amd.tune writes such a table for
+ * this library.  Every field 0
+ * means the library's automatic choice for that field; the result is the same
+ * within the layer's tolerance for any valid plan, only the speed differs.
+ *   gemm_rows       rows per M-tile of the base grouped GEMMs: 32, 64, 128, 256
+ *   gemm_form       1 weight-streaming tiles (32, 64 or 128 rows: nontemporal
+ *                   weight loads, rotated K walk), 2 weight-reuse tiles (128 or
+ *                   256 rows); needs gemm_rows set
+ *   lora_rows       rows per LoRA tile: 16 (one MFMA block, for buckets of few
+ *                   rows) or 64 (tall tiles)
+ *   ksplit_gate_up  K splits of the gate_up GEMM (fp32 atomics, or ordered
+ *                   partials with MOELORA_FLAG_DETERMINISTIC), 1..1024; rounded
+ *                   down to a count whose K ranges are all non-empty
+ *   ksplit_down     the same for the down GEMM (the dense projection's GEMM)
+ *   fuse            1: every projection whose GEMM can (bf16, unsplit K) runs
+ *                   its LoRA expand in the GEMM epilogue; 2: none does
+ * Out-of-range values make every call that takes the dims return
+ * MOELORA_ERR_UNSUPPORTED.
+ */
+typedef struct moelora_plan {
+  int32_t gemm_rows;
+  int32_t gemm_form;
+  int32_t lora_rows;
+  int32_t ksplit_gate_up;
+  int32_t ksplit_down;
+  int32_t fuse;
+} moelora_plan;
 
 /*
  * Layer dimensions.  Limits (checked, MOELORA_ERR_DIMS / _UNSUPPORTED otherwise):
@@ -77,6 +110,7 @@ typedef struct moelora_dims {
   int32_t rank;          /* r                                                       */
   int32_t dtype;         /* moelora_dtype                                           */
   int32_t flags;         /* 0, or any of MOELORA_FLAG_*                              */
+  moelora_plan plan;     /* all 0: automatic                                        */
 } moelora_dims;
 
 /*
@@ -278,6 +312,15 @@ int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]
 int moelora_forward_fusion(const moelora_dims* dims, int* flags);
 
 /*
+ * The plan moelora_forward runs for these dims: dims->plan with every
+ * automatic (0) field resolved and the split counts rounded as described at
+ * moelora_plan; fuse is 1 when at least one projection fuses, else 2.
+ * Host only; returns the validation status of dims (MOELORA_ERR_NULL for a
+ * NULL plan).
+ */
+int moelora_forward_plan(const moelora_dims* dims, moelora_plan* plan);
+
+/*
  * Dense multi-LoRA projection: the vLLM blog page "Multi-LoRA", section
  * "Implementing Multi-LoRA inference for MoE models in vLLM", notes that the
  * same multi-LoRA kernels serve dense layers (e.g. attention projections).  For
@@ -298,9 +341,15 @@ typedef struct moelora_dense_dims {
   int32_t rank;          /* r: 16, 32 or 64                                         */
   int32_t dtype;         /* moelora_dtype of x, weights and out                     */
   int32_t flags;         /* 0, or any of MOELORA_FLAG_*                              */
+  moelora_plan plan;     /* as for the layer, with the projection planned as the
+                            down GEMM: ksplit_down applies, ksplit_gate_up must
+                            be 0                                                   */
 } moelora_dense_dims;
 
 int moelora_dense_workspace_size(const moelora_dense_dims* dims, size_t* bytes);
+
+/* The resolved plan of moelora_dense_forward (as moelora_forward_plan). */
+int moelora_dense_forward_plan(const moelora_dense_dims* dims, moelora_plan* plan);
 
 /*
  *   x              in  dtype [T][K]

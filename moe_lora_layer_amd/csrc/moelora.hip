@@ -24,6 +24,22 @@ int64_t buckets_per_expert(const moelora_dims* d) {
   return static_cast<int64_t>(d->adapters) + ((d->flags & MOELORA_FLAG_BASE_ONLY) ? 1 : 0);
 }
 
+// plan fields: 0 (automatic) or a value the kernels provide
+int check_plan(const moelora_plan& o) {
+  const int rows = o.gemm_rows;
+  if (rows != 0 && rows != 32 && rows != 64 && rows != 128 && rows != 256)
+    return MOELORA_ERR_UNSUPPORTED;
+  if (o.gemm_form < 0 || o.gemm_form > 2) return MOELORA_ERR_UNSUPPORTED;
+  if (o.gemm_form != 0 && (rows == 0 || (o.gemm_form == 1 && rows == 256) ||
+                           (o.gemm_form == 2 && rows < 128)))
+    return MOELORA_ERR_UNSUPPORTED;
+  if (o.lora_rows != 0 && o.lora_rows != 16 && o.lora_rows != 64) return MOELORA_ERR_UNSUPPORTED;
+  if (o.ksplit_gate_up < 0 || o.ksplit_gate_up > 1024 || o.ksplit_down < 0 || o.ksplit_down > 1024)
+    return MOELORA_ERR_UNSUPPORTED;
+  if (o.fuse < 0 || o.fuse > 2) return MOELORA_ERR_UNSUPPORTED;
+  return MOELORA_OK;
+}
+
 int check_dims(const moelora_dims* d) {
   if (d == nullptr) return MOELORA_ERR_NULL;
   if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
@@ -38,23 +54,29 @@ int check_dims(const moelora_dims* d) {
     return MOELORA_ERR_DIMS;
   if (static_cast<int64_t>(d->experts) * buckets_per_expert(d) > 8192) return MOELORA_ERR_DIMS;
   if (d->tokens * d->top_k >= (1ll << 31)) return MOELORA_ERR_DIMS;
-  return MOELORA_OK;
+  return check_plan(d->plan);
 }
 
+// The tile plan: the automatic choice for every field of d->plan that is 0,
+// the caller's value for the others (split counts rounded so that no K range
+// is empty).
 TilePlan make_plan(const moelora_dims* d) {
+  const moelora_plan& o = d->plan;
   const int64_t S = d->tokens * d->top_k;
   const int64_t E = d->experts, nb = E * buckets_per_expert(d);
   const int64_t avg = (S + E - 1) / E;  // mean rows per expert
   TilePlan p;
   // one M-tile per expert in the common case: mean rows per expert plus 25%
   const int64_t want = (avg * 5 + 3) / 4;
-  p.bm = want <= 32 ? 32 : (want <= 64 ? 64 : (want <= 256 ? 128 : 256));
+  p.bm = o.gemm_rows != 0 ? o.gemm_rows
+                          : (want <= 32 ? 32 : (want <= 64 ? 64 : (want <= 256 ? 128 : 256)));
   // at most one 128-row M-tile per expert: nothing reuses a weight tile, so the
   // weights are streamed (nontemporal loads, rotated K walk)
-  p.stream = p.bm < 128 || want <= 160;
+  p.stream = o.gemm_form != 0 ? o.gemm_form == 1 : (p.bm < 128 || (p.bm == 128 && want <= 160));
   // LoRA tiles: 64 rows when buckets average many rows (the tall-tile kernels),
   // else one 16-row MFMA block (the weight-streaming kernels)
-  p.lora_db = S / std::max<int64_t>(1, std::min<int64_t>(nb, S)) > 16;
+  p.lora_db = o.lora_rows != 0 ? o.lora_rows == 64
+                               : S / std::max<int64_t>(1, std::min<int64_t>(nb, S)) > 16;
   p.bml = p.lora_db ? 64 : 16;
   p.max_mt = static_cast<int>(S / p.bm + (E < S ? E : S) + 1);
   p.max_lt = static_cast<int>(S / p.bml + (nb < S ? nb : S) + 1);
@@ -63,25 +85,27 @@ TilePlan make_plan(const moelora_dims* d) {
   // more splits cost more in fp32 atomics than they gain), >= 8 K-steps per
   // split.
   const int64_t est_tiles = std::max<int64_t>((S + p.bm - 1) / p.bm, std::min<int64_t>(E, S));
-  auto splits = [&](int64_t N, int64_t K) {
+  auto splits = [&](int64_t N, int64_t K, int64_t forced) {
     const int64_t wgs = std::max<int64_t>(1, est_tiles * ((N + 127) / 128));
     const int64_t steps = K / (d->dtype == MOELORA_BF16 ? 64 : 32);
-    if (wgs >= 256) return 1;
-    const int64_t want = std::max<int64_t>(1, std::min<int64_t>((512 + wgs - 1) / wgs, steps / 8));
+    if (forced == 0 && wgs >= 256) return 1;
+    const int64_t want =
+        forced != 0 ? std::min<int64_t>(forced, steps)
+                    : std::max<int64_t>(1, std::min<int64_t>((512 + wgs - 1) / wgs, steps / 8));
     // equal K ranges with none empty: every split then owns real work (and
     // writes its whole partial in deterministic mode)
     const int64_t per = (steps + want - 1) / want;
     return static_cast<int>((steps + per - 1) / per);
   };
-  p.ksplit_gu = splits(2 * d->intermediate, d->hidden);
-  p.ksplit_dn = splits(d->hidden, d->intermediate);
+  p.ksplit_gu = splits(2 * d->intermediate, d->hidden, o.ksplit_gate_up);
+  p.ksplit_dn = splits(d->hidden, d->intermediate, o.ksplit_down);
   // bf16 GEMMs with unsplit K run the LoRA expand in their epilogue: always
   // with 256-row tiles; with the smaller tiles only when a tile meets few
   // adapter buckets (estimated as min(mean rows per expert, adapters) <= 8),
   // since their epilogue waits on about one memory round trip per bucket
   const int64_t est_buckets = std::min<int64_t>(std::min<int64_t>(avg, p.bm), d->adapters);
   const bool fusable = d->dtype == MOELORA_BF16 && (d->flags & MOELORA_FLAG_UNFUSED) == 0 &&
-                       (p.bm == 256 || est_buckets <= 8);
+                       o.fuse != 2 && (o.fuse == 1 || p.bm == 256 || est_buckets <= 8);
   p.fuse_gu = fusable && p.ksplit_gu == 1;
   p.fuse_dn = fusable && p.ksplit_dn == 1;
   p.det = (d->flags & MOELORA_FLAG_DETERMINISTIC) != 0;
@@ -140,7 +164,29 @@ moelora_dims dense_as_layer(const moelora_dense_dims* d) {
   m.rank = d->rank;
   m.dtype = d->dtype;
   m.flags = d->flags;
+  m.plan = d->plan;
   return m;
+}
+
+// the dense dims as layer dims, checked (the projection is planned as the
+// layer's down GEMM, so a gate_up split count is refused)
+int dense_check(const moelora_dense_dims* d, moelora_dims* m) {
+  if (d == nullptr) return MOELORA_ERR_NULL;
+  *m = dense_as_layer(d);
+  if (d->plan.ksplit_gate_up != 0) return MOELORA_ERR_UNSUPPORTED;
+  return check_dims(m);
+}
+
+// the resolved plan in the ABI's terms
+moelora_plan plan_out(const TilePlan& p) {
+  moelora_plan o;
+  o.gemm_rows = p.bm;
+  o.gemm_form = p.bm < 128 || (p.bm == 128 && p.stream) ? 1 : 2;
+  o.lora_rows = p.bml;
+  o.ksplit_gate_up = p.ksplit_gu;
+  o.ksplit_down = p.ksplit_dn;
+  o.fuse = (p.fuse_gu || p.fuse_dn) ? 1 : 2;
+  return o;
 }
 
 struct DenseLayout {
@@ -281,6 +327,27 @@ int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]
   return MOELORA_OK;
 }
 
+int moelora_forward_plan(const moelora_dims* dims, moelora_plan* plan) {
+  if (plan == nullptr) return MOELORA_ERR_NULL;
+  const int rc = check_dims(dims);
+  if (rc != MOELORA_OK) return rc;
+  *plan = plan_out(make_plan(dims));
+  return MOELORA_OK;
+}
+
+int moelora_dense_forward_plan(const moelora_dense_dims* dims, moelora_plan* plan) {
+  moelora_dims m;
+  const int rc = dense_check(dims, &m);
+  if (rc != MOELORA_OK) return rc;
+  if (plan == nullptr) return MOELORA_ERR_NULL;
+  const TilePlan tp = make_plan(&m);
+  moelora_plan o = plan_out(tp);
+  o.ksplit_gate_up = 0;
+  o.fuse = tp.fuse_dn ? 1 : 2;
+  *plan = o;
+  return MOELORA_OK;
+}
+
 int moelora_forward_fusion(const moelora_dims* dims, int* flags) {
   if (flags == nullptr) return MOELORA_ERR_NULL;
   const int rc = check_dims(dims);
@@ -403,9 +470,8 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
 }
 
 int moelora_dense_workspace_size(const moelora_dense_dims* dims, size_t* bytes) {
-  if (dims == nullptr) return MOELORA_ERR_NULL;
-  const moelora_dims m = dense_as_layer(dims);
-  const int rc = check_dims(&m);
+  moelora_dims m;
+  const int rc = dense_check(dims, &m);
   if (rc != MOELORA_OK) return rc;
   if (bytes == nullptr) return MOELORA_ERR_NULL;
   *bytes = m.tokens == 0 ? 0 : dense_layout(&m, make_plan(&m)).total;
@@ -416,9 +482,8 @@ int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const v
                           const void* a, const void* b, const int32_t* adapter_ids, void* out,
                           int32_t* device_status, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  if (dims == nullptr) return MOELORA_ERR_NULL;
-  const moelora_dims m = dense_as_layer(dims);
-  int rc = check_dims(&m);
+  moelora_dims m;
+  int rc = dense_check(dims, &m);
   if (rc != MOELORA_OK) return rc;
   const int64_t T = m.tokens;
   if (T == 0) return MOELORA_OK;

@@ -27,22 +27,47 @@ _TORCH_DT = {MOELORA_F32: torch.float32, MOELORA_BF16: torch.bfloat16}
 _DT_NAME = {"f32": MOELORA_F32, "bf16": MOELORA_BF16}
 
 
+PLAN_FIELDS = ["gemm_rows", "gemm_form", "lora_rows", "ksplit_gate_up", "ksplit_down", "fuse"]
+
+
+class Plan(ctypes.Structure):
+    """moelora_plan: tile-plan overrides, 0 = automatic (include/moelora.h)."""
+    _fields_ = [(f, ctypes.c_int32) for f in PLAN_FIELDS]
+
+    def as_dict(self) -> dict:
+        return {f: int(getattr(self, f)) for f in PLAN_FIELDS}
+
+
+def make_plan(plan=None) -> Plan:
+    """A Plan from None (all automatic), a Plan, or a dict of some of its fields."""
+    if plan is None:
+        return Plan()
+    if isinstance(plan, Plan):
+        return plan
+    unknown = set(plan) - set(PLAN_FIELDS)
+    if unknown:
+        raise ValueError(f"unknown plan fields {sorted(unknown)}")
+    return Plan(*[int(plan.get(f, 0)) for f in PLAN_FIELDS])
+
+
 class Dims(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("intermediate", ctypes.c_int64), ("experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("adapters", ctypes.c_int32),
-                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("plan", Plan)]
 
     def __repr__(self):
-        return ("Dims(T=%d, h=%d, I=%d, E=%d, k=%d, L=%d, r=%d, dtype=%d, flags=%d)" %
+        return ("Dims(T=%d, h=%d, I=%d, E=%d, k=%d, L=%d, r=%d, dtype=%d, flags=%d, plan=%s)" %
                 (self.tokens, self.hidden, self.intermediate, self.experts, self.top_k,
-                 self.adapters, self.rank, self.dtype, self.flags))
+                 self.adapters, self.rank, self.dtype, self.flags, self.plan.as_dict()))
 
 
 class DenseDims(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("in_features", ctypes.c_int64),
                 ("out_features", ctypes.c_int64), ("adapters", ctypes.c_int32),
-                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("plan", Plan)]
 
 
 _lib = None
@@ -65,6 +90,7 @@ def library():
         L.moelora_forward_workspace_size.argtypes = [pd, ctypes.POINTER(sz)]
         L.moelora_forward_workspace_layout.argtypes = [pd, ctypes.POINTER(sz)]
         L.moelora_forward_fusion.argtypes = [pd, ctypes.POINTER(ctypes.c_int)]
+        L.moelora_forward_plan.argtypes = [pd, ctypes.POINTER(Plan)]
         L.moelora_align.argtypes = [pd] + [vp] * 8 + [sz, vp]
         L.moelora_align_topk.argtypes = [pd] + [vp] * 6 + [sz, vp]
         L.moelora_forward.argtypes = [pd] + [vp] * 12 + [sz, vp]
@@ -72,10 +98,12 @@ def library():
         pdd = ctypes.POINTER(DenseDims)
         L.moelora_dense_workspace_size.argtypes = [pdd, ctypes.POINTER(sz)]
         L.moelora_dense_forward.argtypes = [pdd] + [vp] * 8 + [sz, vp]
+        L.moelora_dense_forward_plan.argtypes = [pdd, ctypes.POINTER(Plan)]
         for f in (L.moelora_align_workspace_size, L.moelora_forward_workspace_size,
-                  L.moelora_forward_workspace_layout, L.moelora_forward_fusion, L.moelora_align,
-                  L.moelora_align_topk, L.moelora_forward, L.moelora_forward_profiled,
-                  L.moelora_dense_workspace_size, L.moelora_dense_forward):
+                  L.moelora_forward_workspace_layout, L.moelora_forward_fusion,
+                  L.moelora_forward_plan, L.moelora_align, L.moelora_align_topk,
+                  L.moelora_forward, L.moelora_forward_profiled, L.moelora_dense_workspace_size,
+                  L.moelora_dense_forward, L.moelora_dense_forward_plan):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -97,7 +125,7 @@ def _check(rc: int, what: str):
 
 
 def make_dims(tokens, hidden, intermediate, experts, top_k, adapters, rank, dtype,
-              deterministic=False, base_only=False, unfused=False, flags=None) -> Dims:
+              deterministic=False, base_only=False, unfused=False, flags=None, plan=None) -> Dims:
     if isinstance(dtype, str):
         dtype = _DT_NAME[dtype]
     elif isinstance(dtype, torch.dtype):
@@ -105,14 +133,23 @@ def make_dims(tokens, hidden, intermediate, experts, top_k, adapters, rank, dtyp
     if flags is None:
         flags = _flags(deterministic, base_only, unfused)
     return Dims(int(tokens), int(hidden), int(intermediate), int(experts), int(top_k),
-                int(adapters), int(rank), int(dtype), int(flags))
+                int(adapters), int(rank), int(dtype), int(flags), make_plan(plan))
 
 
-def dims_for(cfg, tokens=None, deterministic=False, base_only=False, unfused=False) -> Dims:
+def dims_for(cfg, tokens=None, deterministic=False, base_only=False, unfused=False,
+             plan=None) -> Dims:
     """Dims of a workload config (moe_lora_layer_amd.synth.LayerConfig)."""
     return make_dims(cfg.tokens if tokens is None else tokens, cfg.hidden, cfg.intermediate,
                      cfg.experts, cfg.top_k, cfg.adapters, cfg.rank, cfg.dtype,
-                     deterministic=deterministic, base_only=base_only, unfused=unfused)
+                     deterministic=deterministic, base_only=base_only, unfused=unfused, plan=plan)
+
+
+def forward_plan(d: Dims) -> dict:
+    """moelora_forward_plan: the plan moelora_forward runs for d, every field resolved."""
+    out = Plan()
+    _check(library().moelora_forward_plan(ctypes.byref(d), ctypes.byref(out)),
+           "moelora_forward_plan")
+    return out.as_dict()
 
 
 def buckets(d: Dims) -> int:
@@ -293,12 +330,20 @@ class MoELoRALayer:
 
 
 def make_dense_dims(tokens, in_features, out_features, adapters, rank, dtype, deterministic=False,
-                    base_only=False, unfused=False) -> DenseDims:
+                    base_only=False, unfused=False, plan=None) -> DenseDims:
     if isinstance(dtype, str):
         dtype = _DT_NAME[dtype]
     flags = _flags(deterministic, base_only, unfused)
     return DenseDims(int(tokens), int(in_features), int(out_features), int(adapters), int(rank),
-                     int(dtype), flags)
+                     int(dtype), flags, make_plan(plan))
+
+
+def dense_forward_plan(d: DenseDims) -> dict:
+    """moelora_dense_forward_plan: the resolved plan of the dense projection."""
+    out = Plan()
+    _check(library().moelora_dense_forward_plan(ctypes.byref(d), ctypes.byref(out)),
+           "moelora_dense_forward_plan")
+    return out.as_dict()
 
 
 def dense_workspace_size(d: DenseDims) -> int:

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     assert {"moelora_align", "moelora_forward"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moelora_abi_version() == 5
+    assert lib.moelora_abi_version() == 6
 
 
 def test_status_strings():
@@ -165,3 +165,96 @@ def test_deterministic_workspace_holds_the_partials(kw):
     assert lib.moelora_forward_workspace_size(ctypes.byref(good_dims(**kw)), ctypes.byref(n0)) == OK
     assert lib.moelora_forward_workspace_size(ctypes.byref(good_dims(flags=1, **kw)), ctypes.byref(n1)) == OK
     assert n1.value > n0.value
+
+
+# ---------------------------------------------------------------- tile plans
+PLAN_CASES = [
+    dict(gemm_rows=48), dict(gemm_rows=-32), dict(gemm_form=3), dict(gemm_form=1),  # form needs rows
+    dict(gemm_rows=256, gemm_form=1), dict(gemm_rows=64, gemm_form=2), dict(lora_rows=32),
+    dict(ksplit_gate_up=-1), dict(ksplit_down=1025), dict(fuse=3), dict(fuse=-1),
+]
+
+
+@pytest.mark.parametrize("plan", PLAN_CASES)
+def test_bad_plans_are_refused_everywhere(plan):
+    d = good_dims(plan=plan)
+    n = ctypes.c_size_t()
+    lib = ops.library()
+    assert lib.moelora_forward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == ERR_UNSUPPORTED
+    assert lib.moelora_align_workspace_size(ctypes.byref(d), ctypes.byref(n)) == ERR_UNSUPPORTED
+    out = ops.Plan()
+    assert lib.moelora_forward_plan(ctypes.byref(d), ctypes.byref(out)) == ERR_UNSUPPORTED
+    dd = ops.make_dense_dims(64, 256, 512, 4, 16, "bf16", plan=plan)
+    assert lib.moelora_dense_workspace_size(ctypes.byref(dd), ctypes.byref(n)) == ERR_UNSUPPORTED
+
+
+def test_plan_resolution():
+    # automatic: every field resolved; a forced field is kept, the others stay automatic
+    auto = ops.forward_plan(good_dims())
+    assert all(auto[f] != 0 for f in ops.PLAN_FIELDS)
+    assert auto == {"gemm_rows": 32, "gemm_form": 1, "lora_rows": 16, "ksplit_gate_up": 1,
+                    "ksplit_down": 1, "fuse": 1}
+    forced = ops.forward_plan(good_dims(plan=dict(gemm_rows=128, gemm_form=2, lora_rows=64)))
+    assert forced == dict(auto, gemm_rows=128, gemm_form=2, lora_rows=64)
+    # resolving a resolved plan changes nothing
+    for kw in [dict(), dict(tokens=4096, hidden=4096, intermediate=11008, experts=16),
+               dict(tokens=4, hidden=4096, intermediate=1024, experts=1, top_k=1)]:
+        p = ops.forward_plan(good_dims(**kw))
+        assert ops.forward_plan(good_dims(plan=p, **kw)) == p
+    # split counts: capped at the K-steps and rounded so that no K range is empty
+    # (h = 256: 4 steps of 64; I = 512: 8 steps)
+    p = ops.forward_plan(good_dims(plan=dict(ksplit_gate_up=3, ksplit_down=1000)))
+    assert (p["ksplit_gate_up"], p["ksplit_down"]) == (2, 8)
+    # a split GEMM cannot fuse its expand; fuse=2 turns fusion off
+    assert ops.forward_fusion(good_dims(plan=dict(ksplit_down=2))) == {"gate_up": True, "down": False}
+    assert ops.forward_fusion(good_dims(plan=dict(fuse=2))) == {"gate_up": False, "down": False}
+    many = dict(tokens=256, hidden=2880, intermediate=2880, experts=32, top_k=4, adapters=64, rank=64)
+    assert ops.forward_fusion(good_dims(plan=dict(fuse=1), **many)) == {"gate_up": True, "down": True}
+    # the workspace follows the plan (split partials in deterministic mode)
+    n1 = ops.forward_workspace_size(good_dims(flags=1))
+    n2 = ops.forward_workspace_size(good_dims(flags=1, plan=dict(ksplit_down=4)))
+    assert n2 > n1
+
+
+def test_dense_plan():
+    dd = ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16")
+    p = ops.dense_forward_plan(dd)
+    assert p["ksplit_gate_up"] == 0 and p["ksplit_down"] > 1
+    n = ctypes.c_size_t()
+    bad = ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16", plan=dict(ksplit_gate_up=2))
+    assert ops.library().moelora_dense_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == ERR_UNSUPPORTED
+    assert ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16",
+                                                      plan=dict(ksplit_down=1)))["ksplit_down"] == 1
+
+
+def test_plan_table_round_trip(tmp_path):
+    from moe_lora_layer_amd import tune
+    d = good_dims()
+    dd = ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16")
+    e1 = {"kind": "layer", "dims": {k: int(getattr(d, k)) for k in tune.LAYER_KEYS},
+          "plan": dict(ops.forward_plan(d), gemm_rows=64), "us": 1.0, "auto_us": 2.0}
+    e2 = {"kind": "dense", "dims": {k: int(getattr(dd, k)) for k in tune.DENSE_KEYS},
+          "plan": ops.dense_forward_plan(dd), "us": 1.0, "auto_us": 1.0}
+    path = str(tmp_path / "t.json")
+    tune.save_table(path, tune.merge([], [e1, e2]))
+    t = tune.load_table(path)
+    assert tune.plan_for(d, t) == e1["plan"]
+    assert tune.plan_for(dd, t) == e2["plan"]
+    assert tune.plan_for(good_dims(tokens=65), t) is None
+    # the plan field of the dims does not enter the key; a new entry replaces the old one
+    assert tune.plan_for(good_dims(plan=dict(gemm_rows=256)), t) == e1["plan"]
+    e1b = dict(e1, plan=dict(e1["plan"], gemm_rows=32))
+    assert tune.plan_for(d, tune.merge(t, [e1b])) == e1b["plan"]
+    # the packaged table's plans are all valid for their dims
+    if os.path.exists(tune.PACKAGED_TABLE):
+        for e in tune.load_table(tune.PACKAGED_TABLE):
+            if e["kind"] == "layer":
+                dims = ops.make_dims(*[e["dims"][k] for k in tune.LAYER_KEYS[:-1]],
+                                     flags=e["dims"]["flags"], plan=e["plan"])
+                assert ops.forward_plan(dims) == e["plan"]
+            else:
+                k = e["dims"]
+                dims = ops.make_dense_dims(k["tokens"], k["in_features"], k["out_features"],
+                                           k["adapters"], k["rank"], k["dtype"], plan=e["plan"])
+                dims.flags = k["flags"]
+                assert ops.dense_forward_plan(dims) == e["plan"]
