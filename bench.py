@@ -92,8 +92,14 @@ def run_dense(args, cfg) -> int:
                    else torch.from_numpy(a)).to(dev)
     x, w, a, b = t(inp["x"]), t(inp["w"]), t(inp["a"]), t(inp["b"])
     ad = torch.from_numpy(inp["adapter_ids"]).to(dev)
+    from moe_lora_layer_amd import tune
     d = ops.make_dense_dims(cfg.tokens, cfg.in_features, cfg.out_features, cfg.adapters, cfg.rank,
                             cfg.dtype, deterministic=args.deterministic)
+    plan_source = "automatic"
+    if args.plan == "tuned":
+        d, plan_source = tune.with_packaged_plan(d)
+    plan = ops.dense_forward_plan(d)
+    log(f"[bench] {cfg.name}: plan {plan} ({plan_source})")
     ws = ops.workspace(ops.dense_workspace_size(d), dev)
     out = torch.empty((cfg.tokens, cfg.out_features), dtype=x.dtype, device=dev)
     st = torch.zeros((4,), dtype=torch.int32, device=dev)
@@ -143,7 +149,8 @@ def run_dense(args, cfg) -> int:
            "data": "synthetic (seeded normal inputs, random-init weights)",
            "config": {"workload": cfg.name, "tokens": T, "in_features": K, "out_features": N,
                       "adapters": cfg.adapters, "rank": r, "parallelism": "single GPU"},
-           "roofline": roof, "cpu_baseline": cpu, "deterministic": args.deterministic}
+           "roofline": roof, "cpu_baseline": cpu, "deterministic": args.deterministic,
+           "plan": plan, "plan_source": plan_source}
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -164,6 +171,9 @@ def main() -> int:
                     help="tokens in the oracle's timed sample (default 64)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="repeat the oracle's sample for about this long (default 12 s)")
+    ap.add_argument("--plan", choices=["tuned", "auto"], default="tuned",
+                    help="tile plan: the packaged tuned table's entry for the workload when it has "
+                         "one (default), or the library's automatic plan")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -196,7 +206,13 @@ def main() -> int:
     x = dev_t(inp["x"])
     logits = torch.from_numpy(inp["logits"]).to(dev)
     adapter_ids = torch.from_numpy(inp["adapter_ids"]).to(dev)
+    from moe_lora_layer_amd import tune
     d = ops.dims_for(cfg, deterministic=args.deterministic)
+    plan_source = "automatic"
+    if args.plan == "tuned":
+        d, plan_source = tune.with_packaged_plan(d)
+    plan = ops.forward_plan(d)
+    log(f"[bench] {cfg.name}: plan {plan} ({plan_source})")
     layer = ops.MoELoRALayer(d, W, dev)
     nst = len(ops.STAGES)
 
@@ -336,6 +352,8 @@ def main() -> int:
         "roofline": roof,
         "latency_us": {"warm": lat_warm, "cold_1GiB_read_flush": lat_cold},
         "fusion": fusion,
+        "plan": plan,
+        "plan_source": plan_source,
         "deterministic": args.deterministic,
         "cpu_baseline": cpu,
         "stages": stages,

@@ -12,7 +12,7 @@ import torch
 import oracle
 from gpu_util import (WEIGHTS, assert_close, device, device_inputs, run_align, run_forward, say,
                       sample_tokens, to_f64, workspace_view)
-from moe_lora_layer_amd import ops, synth
+from moe_lora_layer_amd import ops, synth, tune
 
 pytestmark = pytest.mark.gpu
 
@@ -117,8 +117,10 @@ def test_forward_workload(name):
     cfg = synth.WORKLOADS[name]
     say(f"forward workload {name}: generating inputs")
     inp = synth.make_inputs(cfg)
-    say(f"forward workload {name}: running on GPU")
-    _, (ids, w, ss, off), out, _ = _layer(cfg, inp)
+    # the benchmark's launch configuration: the packaged tuned plan, if any
+    d, source = tune.with_packaged_plan(ops.dims_for(cfg))
+    say(f"forward workload {name}: running on GPU, plan {ops.forward_plan(d)} ({source})")
+    _, (ids, w, ss, off), out, _ = _layer(cfg, inp, d)
     ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     toks = sample_tokens(cfg.tokens, 24 if cfg.tokens > 64 else cfg.tokens)
