@@ -953,12 +953,13 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const L
         return lds_launch<T, 128, 128, 2, 4, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
       return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, lora, stream);
     case 256:  // prefill: 256x256 tiles, 8 waves of 128x64 (bf16: operands DMA'd into LDS)
-      if (sizeof(T) == 2) {
+      if constexpr (sizeof(T) == 2) {
         if (lora == nullptr) return dma_launch<GATHER, EPI_STORE>(plan, a, LoraEpilogue{}, stream);
         if (lora->act != nullptr) return dma_launch<GATHER, EPI_GATE_UP>(plan, a, *lora, stream);
         return dma_launch<GATHER, EPI_DOWN>(plan, a, *lora, stream);
+      } else {
+        return lds_launch<T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, nullptr, stream);
       }
-      return lds_launch<T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, nullptr, stream);
     default: return hipErrorInvalidValue;
   }
 }
