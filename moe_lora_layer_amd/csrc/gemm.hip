@@ -14,6 +14,8 @@
 // fragment reads (consecutive rows, same chunk) hit all banks, double
 // buffered: the next K-step's global loads are in flight while the MFMAs of
 // the current one run.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -774,18 +776,23 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   const int a_off = ((half ? 0 : wm * 128) + c32) * kDmaRowB;
   const int b_off = (kDmaTile + wn * 64 + c32) * kDmaRowB;
   bf16x8_t fa[2][4], fb[2][2];
-  auto rd = [&](int f, const unsigned char* st, int s) {
+  // Only the wave's 32-row blocks that hold rows of the tile are read and
+  // multiplied (NB of the 4; an expert's last tile is often partly empty);
+  // the K loop below is instantiated per NB.
+  auto rd = [&](int f, const unsigned char* st, int s, auto nbc) {
+    constexpr int NB = decltype(nbc)::value;
     const int ch = ((2 * s + h) ^ sw) << 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NB; ++i)
       fa[f][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * kDmaRowB + ch);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       fb[f][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * kDmaRowB + ch);
   };
-  auto mm = [&](int f) {
+  auto mm = [&](int f, auto nbc) {
+    constexpr int NB = decltype(nbc)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
@@ -806,51 +813,62 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   dma_issue(smem, 1, ko(min(1, nk - 1)), a_src, b_src, wave);
   wait_vmcnt<8>();  // this wave's loads of step 0 are in LDS
   bar();            // ... and every other wave's
-  if (!half) {
-    rd(0, smem, 0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing scalar or LDS pending into the loop
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-      const unsigned char* cur = smem + (kt & 1) * kDmaStage;
+  auto k_loop = [&](auto nbc) {
+    if (!half) {
+      rd(0, smem, 0, nbc);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing scalar or LDS pending into the loop
+      for (int kt = 0; kt + 1 < nk; ++kt) {
+        const unsigned char* cur = smem + (kt & 1) * kDmaStage;
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        rd((s + 1) & 1, cur, s + 1);
-        mm(s & 1);
+        for (int s = 0; s < 3; ++s) {
+          rd((s + 1) & 1, cur, s + 1, nbc);
+          mm(s & 1, nbc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // step kt+1 has landed and every wave has finished reading step kt
+        // (lgkmcnt(0) before the barrier): refill that stage with step kt+2
+        wait_vmcnt_lgkm0<0>();
+        bar();
+        dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
+        rd(0, smem + ((kt + 1) & 1) * kDmaStage, 0, nbc);
+        mm(1, nbc);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // step kt+1 has landed and every wave has finished reading step kt
-      // (lgkmcnt(0) before the barrier): refill that stage with step kt+2
-      wait_vmcnt_lgkm0<0>();
-      bar();
-      dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
-      rd(0, smem + ((kt + 1) & 1) * kDmaStage, 0);
-      mm(1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const unsigned char* cur = smem + ((nk - 1) & 1) * kDmaStage;
+      const unsigned char* cur = smem + ((nk - 1) & 1) * kDmaStage;
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      rd((s + 1) & 1, cur, s + 1);
-      mm(s & 1);
+      for (int s = 0; s < 3; ++s) {
+        rd((s + 1) & 1, cur, s + 1, nbc);
+        mm(s & 1, nbc);
+      }
+      mm(1, nbc);
+    } else {
+      const int s0 = 2 * wm;  // this wave row's two substeps
+      rd(0, smem, s0, nbc);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      for (int kt = 0; kt + 1 < nk; ++kt) {
+        rd(1, smem + (kt & 1) * kDmaStage, s0 + 1, nbc);
+        mm(0, nbc);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt_lgkm0<0>();
+        bar();
+        dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
+        rd(0, smem + ((kt + 1) & 1) * kDmaStage, s0, nbc);
+        mm(1, nbc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      rd(1, smem + ((nk - 1) & 1) * kDmaStage, s0 + 1, nbc);
+      mm(0, nbc);
+      mm(1, nbc);
     }
-    mm(1);
-  } else {
-    const int s0 = 2 * wm;  // this wave row's two substeps
-    rd(0, smem, s0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-      rd(1, smem + (kt & 1) * kDmaStage, s0 + 1);
-      mm(0);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt_lgkm0<0>();
-      bar();
-      dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
-      rd(0, smem + ((kt + 1) & 1) * kDmaStage, s0);
-      mm(1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    rd(1, smem + ((nk - 1) & 1) * kDmaStage, s0 + 1);
-    mm(0);
-    mm(1);
+  };
+  // 32-row blocks of this wave that hold tile rows (every wave runs the same
+  // number of K steps and barriers whatever its count)
+  const int wave_rows = half ? row_end - row0 : min(128, row_end - row0 - 128 * wm);
+  switch ((wave_rows + 31) / 32) {
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 3: k_loop(std::integral_constant<int, 3>{}); break;
+    default: k_loop(std::integral_constant<int, 4>{}); break;
   }
   wait_vmcnt<0>();  // no LDS write of this workgroup may outlive it
   if (half) {
