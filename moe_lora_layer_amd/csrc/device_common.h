@@ -30,6 +30,17 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
+// four consecutive outputs in one store (8 bytes of bf16, 16 of fp32); dst
+// 8- (bf16) or 16-byte (fp32) aligned
+__device__ __forceinline__ void store4(bf16_t* dst, float a, float b, float c, float d) {
+  const uint32_t lo = f32_to_bf16(a) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  const uint32_t hi = f32_to_bf16(c) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+}
+__device__ __forceinline__ void store4(float* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }

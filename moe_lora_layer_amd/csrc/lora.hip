@@ -646,11 +646,7 @@ k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L, in
         const float a1 = silu(gg.y + acc[0][j][1]) * (gu.y + acc[NH - 1][j][1]);
         const float a2 = silu(gg.z + acc[0][j][2]) * (gu.z + acc[NH - 1][j][2]);
         const float a3 = silu(gg.w + acc[0][j][3]) * (gu.w + acc[NH - 1][j][3]);
-        T* o = ACT + static_cast<int64_t>(p) * ncols + n;
-        o[0] = from_f32<T>(a0);
-        o[1] = from_f32<T>(a1);
-        o[2] = from_f32<T>(a2);
-        o[3] = from_f32<T>(a3);
+        store4(ACT + static_cast<int64_t>(p) * ncols + n, a0, a1, a2, a3);
       } else {
         const float4 d = blk.base[0][j];
         *reinterpret_cast<float4*>(D + static_cast<int64_t>(p) * ncols + n) =
@@ -697,11 +693,7 @@ k_combine(const float* __restrict__ D, const int32_t* __restrict__ pos, const fl
     acc.z += wj * d.z;
     acc.w += wj * d.w;
   }
-  T* o = out + static_cast<int64_t>(t) * h + c;
-  o[0] = from_f32<T>(acc.x);
-  o[1] = from_f32<T>(acc.y);
-  o[2] = from_f32<T>(acc.z);
-  o[3] = from_f32<T>(acc.w);
+  store4(out + static_cast<int64_t>(t) * h + c, acc.x, acc.y, acc.z, acc.w);
 }
 
 // -------------------------------------------------------------------- launchers
