@@ -38,6 +38,7 @@ struct TilePlan {
   bool fuse_gu;  // gate_up GEMM applies the LoRA expand and SiLU-mul in its epilogue
   bool fuse_dn;  // down GEMM applies the LoRA expand in its epilogue
   bool det;      // split-K reductions go through ordered partial sums, not atomics
+  bool shrink_partials;  // the shrinks sum per-split partials in order (det, or tall bf16 tiles)
   int nad;       // adapters; bucket index nad of an expert (base-only tokens) has no LoRA
 };
 

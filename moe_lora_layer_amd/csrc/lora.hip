@@ -315,11 +315,11 @@ __device__ __forceinline__ void shrink_dma_range(unsigned char* smem, const bf16
   wait_vmcnt<0>();  // no LDS write of this workgroup may outlive the range
 }
 
-// The wave's 32 x 32 partial of a tall tile: into Z with relaxed atomics, or,
-// deterministic, into partial slot `slot` (R > 32: the split; else split and
-// substep pair).
+// The wave's 32 x 32 partial of a tall tile into partial slot `slot` (R > 32:
+// the split; else split and substep pair); a separate pass sums the slots in
+// order into Z.
 template <int R>
-__device__ __forceinline__ void shrink_dma_emit(const f32x16_t& acc, int4 tile, float* __restrict__ Z,
+__device__ __forceinline__ void shrink_dma_emit(const f32x16_t& acc, int4 tile,
                                                 float* __restrict__ parts, int64_t part_stride,
                                                 int slot) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -331,21 +331,20 @@ __device__ __forceinline__ void shrink_dma_emit(const f32x16_t& acc, int4 tile, 
   for (int i = 0; i < 16; ++i) {
     const int p = tile.y + 32 * rh + acc_row(i, h);
     if (p >= tile.z) continue;
-    const int64_t idx = static_cast<int64_t>(p) * R + q;
-    if (parts != nullptr)
-      parts[slot * part_stride + idx] = acc[i];
-    else
-      atomic_add_relaxed(Z + idx, acc[i]);
+    parts[slot * part_stride + static_cast<int64_t>(p) * R + q] = acc[i];
   }
 }
 
-// Workgroup (tile, split): one K range of kwg_steps steps.
+// Workgroup (tile, split): one K range of kwg_steps steps, written to the
+// split's partial slots (every split owns at least one step, so every slot of
+// every LoRA row is written).  Summing the slots in order beats relaxed fp32
+// atomics into Z here, and is deterministic.
 template <int R, bool GATHER>
 __global__ void __launch_bounds__(kLoraThreads)
 k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
              int gather_k, const bf16_t* __restrict__ At, int E, int L, int nad, int64_t K, int kwg_steps,
-             int nsplit, float* __restrict__ Z, const int4* __restrict__ ltiles,
-             const int32_t* __restrict__ counts, float* __restrict__ parts, int64_t part_stride) {
+             int nsplit, const int4* __restrict__ ltiles, const int32_t* __restrict__ counts,
+             float* __restrict__ parts, int64_t part_stride) {
   typedef ShrinkDma<R> S;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kShrinkStages * S::STAGE];
   const int lt = blockIdx.x / nsplit;
@@ -359,39 +358,7 @@ k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict
   if (nk <= 0) return;  // uniform
   f32x16_t acc = zero_acc();
   shrink_dma_range<R, GATHER>(smem, X, x_rows, gather_slots, gather_k, At, E, L, K, tile, kt0, nk, acc);
-  shrink_dma_emit<R>(acc, tile, Z, parts, part_stride, R > 32 ? split : 2 * split + (threadIdx.x / kWave >> 1));
-}
-
-// Persistent form (atomics only): the work is the list of (tall tile, K step)
-// items, tile-major, and workgroup w of W takes the contiguous run
-// [n w / W, n (w+1) / W), one K range per tile it meets.  Every workgroup
-// streams the same number of steps, so the grid drains evenly, and a tile's
-// steps mostly stay in one workgroup (few atomics per Z element).
-template <int R> constexpr int shrink_run_wgs() { return R > 32 ? 2 * 256 : 3 * 256; }  // LDS-resident per CU
-
-template <int R, bool GATHER>
-__global__ void __launch_bounds__(kLoraThreads)
-k_shrink_dma_run(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
-                 int gather_k, const bf16_t* __restrict__ At, int E, int L, int nad, int64_t K,
-                 float* __restrict__ Z, const int4* __restrict__ ltiles,
-                 const int32_t* __restrict__ counts) {
-  typedef ShrinkDma<R> S;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kShrinkStages * S::STAGE];
-  const int nk_all = static_cast<int>(K / 64);
-  const int64_t n = static_cast<int64_t>(counts[1]) * nk_all;
-  const int64_t i0 = n * blockIdx.x / gridDim.x, i1 = n * (blockIdx.x + 1) / gridDim.x;
-  for (int64_t it = i0; it < i1;) {
-    const int lt = static_cast<int>(it / nk_all);
-    const int kt0 = static_cast<int>(it - static_cast<int64_t>(lt) * nk_all);
-    const int nk = static_cast<int>(min<int64_t>(nk_all - kt0, i1 - it));
-    it += nk;
-    const int4 tile = ltiles[lt];
-    if (tile.x % L >= nad) continue;  // base-only bucket: no LoRA term (uniform)
-    lds_barrier();  // every wave is done with the previous range's stages
-    f32x16_t acc = zero_acc();
-    shrink_dma_range<R, GATHER>(smem, X, x_rows, gather_slots, gather_k, At, E, L, K, tile, kt0, nk, acc);
-    shrink_dma_emit<R>(acc, tile, Z, nullptr, 0, 0);
-  }
+  shrink_dma_emit<R>(acc, tile, parts, part_stride, R > 32 ? split : 2 * split + (threadIdx.x / kWave >> 1));
 }
 
 // ------------------------------------------------------------ streaming shrink
@@ -750,12 +717,9 @@ static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
   const ShrinkSplit sp = shrink_split<T, R>(plan, K);
   const int64_t stride = static_cast<int64_t>(S) * R;
   const int64_t grid = static_cast<int64_t>(plan.max_lt) * sp.nsplit;
-  if (plan.lora_db && sizeof(T) == 2 && parts == nullptr) {
-    // tall bf16 tiles: persistent workgroups stream runs of (tile, K step) items
-    hipLaunchKernelGGL((k_shrink_dma_run<R, GATHER>), dim3(shrink_run_wgs<R>()), dim3(kLoraThreads),
-                       0, stream, static_cast<const bf16_t*>(X), x_rows, gather_slots, gather_k,
-                       static_cast<const bf16_t*>(At), E, L, plan.nad, K, Z, ltiles, counts);
-  } else if (sp.stream) {
+  if (plan.lora_db && sizeof(T) == 2 && parts == nullptr)
+    return hipErrorInvalidValue;  // tall bf16 tiles always sum partials (plan.shrink_partials)
+  if (sp.stream) {
     // many short tiles: persistent waves stream runs of (tile, K chunk) items
     constexpr int ST = ShrinkStream<R>::ST;
     const bool det = parts != nullptr;
@@ -767,11 +731,11 @@ static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
                        static_cast<const bf16_t*>(At), E, L, plan.nad, K, Z, ltiles, counts,
                        parts, stride);
   } else if (plan.lora_db && sizeof(T) == 2) {
-    // tall bf16 tiles, deterministic: DMA ring, about 1024 workgroups of (tile, K range)
+    // tall bf16 tiles: DMA ring, about 1024 workgroups of (tile, K range), partial slots
     hipLaunchKernelGGL((k_shrink_dma<R, GATHER>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const bf16_t*>(X), x_rows,
                        gather_slots, gather_k, static_cast<const bf16_t*>(At), E, L, plan.nad, K,
-                       sp.kwg_steps, sp.nsplit, Z, ltiles, counts, parts, stride);
+                       sp.kwg_steps, sp.nsplit, ltiles, counts, parts, stride);
   } else if (plan.lora_db) {
     // tall tiles: ~1024 workgroups, each wave a 16-row block over the split's K range
     constexpr int STEPS = R > 32 ? 2 : 4;

@@ -109,6 +109,9 @@ TilePlan make_plan(const moelora_dims* d) {
   p.fuse_gu = fusable && p.ksplit_gu == 1;
   p.fuse_dn = fusable && p.ksplit_dn == 1;
   p.det = (d->flags & MOELORA_FLAG_DETERMINISTIC) != 0;
+  // tall bf16 LoRA tiles: per-split partials and an ordered sum beat relaxed
+  // fp32 atomics into Z (a few hundred split tiles each adding 64 x r values)
+  p.shrink_partials = p.det || (p.lora_db && d->dtype == MOELORA_BF16);
   p.nad = d->adapters;
   return p;
 }
@@ -138,13 +141,13 @@ ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
   // deterministic mode: one region for the split-K partials of whichever
   // reduction runs (they run one after another)
   L.parts = off;
-  if (plan.det) {
+  if (plan.shrink_partials) {
     const int dt = d->dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
     size_t n = 0;
     n = std::max(n, static_cast<size_t>(moelora::shrink_parts(dt, d->rank, plan, d->hidden)) * S * r);
     n = std::max(n, static_cast<size_t>(moelora::shrink_parts(dt, d->rank, plan, d->intermediate)) * S * r);
-    if (plan.ksplit_gu > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_gu) * S * 2 * I);
-    if (plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * S * h);
+    if (plan.det && plan.ksplit_gu > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_gu) * S * 2 * I);
+    if (plan.det && plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * S * h);
     off += round_up(n * 4);
   }
   L.total = off;
@@ -211,10 +214,10 @@ DenseLayout dense_layout(const moelora_dims* m, const TilePlan& plan) {
   L.d = off + T * r * 4;
   off += round_up(T * r * 4 + T * N * 4);
   L.parts = off;
-  if (plan.det) {
+  if (plan.shrink_partials) {
     const int dt = m->dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
     size_t n = static_cast<size_t>(moelora::shrink_parts(dt, m->rank, plan, m->intermediate)) * T * r;
-    if (plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * T * N);
+    if (plan.det && plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * T * N);
     off += round_up(n * 4);
   }
   L.total = off;
@@ -423,6 +426,9 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   // the prep launch also clears Z1, Z2 (and D when the down GEMM is split)
   const int64_t nzero =
       plan.det ? 0 : 2ll * S * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * h : 0);
+  // one partials region: the shrinks' (deterministic mode or tall tiles) and,
+  // in deterministic mode, the split-K GEMMs' (they run one after another)
+  float* sparts = plan.shrink_partials ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
   float* parts = plan.det ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
   hipError_t e = mark(MOELORA_STAGE_PREP);
   if (e == hipSuccess)
@@ -435,7 +441,7 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_GATE_UP);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, x, static_cast<int>(T), sorted_slots, k, a_gate_up, E,
-                               Lad, h, Z1, S, ltiles, counts, parts, st);
+                               Lad, h, Z1, S, ltiles, counts, sparts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);
   if (e == hipSuccess) {
     const moelora::LoraEpilogue epi{Z1, static_cast<const uint16_t*>(b_gate_up), bucket_offsets,
@@ -451,7 +457,7 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_DOWN);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, ACT, S, nullptr, 1, a_down, E, Lad, I, Z2, S, ltiles,
-                               counts, parts, st);
+                               counts, sparts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
   if (e == hipSuccess) {
     const moelora::LoraEpilogue epi{Z2, static_cast<const uint16_t*>(b_down), bucket_offsets,
@@ -517,6 +523,7 @@ int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const v
   int4* ltiles = reinterpret_cast<int4*>(ws + L.ltiles);
   float* Z = reinterpret_cast<float*>(ws + L.z);
   float* D = reinterpret_cast<float*>(ws + L.d);
+  float* sparts = plan.shrink_partials ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
   float* parts = plan.det ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -530,7 +537,7 @@ int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const v
                              nzero, st);
   if (e == hipSuccess)
     e = moelora::launch_shrink(dt, r, plan, x, S, slots, 1, a, 1, Lb, K, Z, S, ltiles, counts,
-                               parts, st);
+                               sparts, st);
   if (e == hipSuccess) {
     const moelora::LoraEpilogue epi{Z, static_cast<const uint16_t*>(b), offsets, 1, nad, r, Lb, N,
                                     nullptr};

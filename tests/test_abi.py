@@ -164,7 +164,9 @@ def test_deterministic_workspace_holds_the_partials(kw):
     lib = ops.library()
     assert lib.moelora_forward_workspace_size(ctypes.byref(good_dims(**kw)), ctypes.byref(n0)) == OK
     assert lib.moelora_forward_workspace_size(ctypes.byref(good_dims(flags=1, **kw)), ctypes.byref(n1)) == OK
-    assert n1.value > n0.value
+    # tall bf16 LoRA tiles (the third shape) sum shrink partials in both modes
+    tall = ops.forward_plan(good_dims(**kw))["lora_rows"] == 64
+    assert n1.value >= n0.value if tall else n1.value > n0.value
 
 
 # ---------------------------------------------------------------- tile plans
