@@ -3,9 +3,17 @@
   python -m moe_lora_layer_amd.profiling trace  <csv_dir> <out.md> <title> <command...>
   python -m moe_lora_layer_amd.profiling traffic <out.json> <out.md> <kernel-substring>
         <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> <copy_bytes> <algo_bytes>
+  python -m moe_lora_layer_amd.profiling kernels <out.md> <title> <trace_dir> <fetch_dir>
+        <write_dir> <copy_fetch_dir> <copy_write_dir> <copy_bytes> <command...>
+  python -m moe_lora_layer_amd.profiling counters <out.md> <title> <kernel-substring>
+        <pmc_dir>... -- <command...>
 
 `trace` reads <csv_dir>/run_kernel_stats.csv (rocprofv3 --kernel-trace --stats
---output-format csv).  `traffic` reads per-dispatch FETCH_SIZE and WRITE_SIZE
+--output-format csv).  `kernels` tabulates, for every kernel of the library,
+the scaled FETCH_SIZE + WRITE_SIZE bytes per dispatch over its average
+duration in the kernel trace of the same workload (achieved HBM GB/s).
+`counters` averages raw SQ/GRBM counters per dispatch of one kernel and
+derives the engine clock and the MFMA-busy fraction from them.  `traffic` reads per-dispatch FETCH_SIZE and WRITE_SIZE
 (KiB) of the named kernel from two --pmc runs, and the same counters for a
 device copy of known size; the counters are scaled by known/counted of the
 copy.  The traffic record carries a digest of the kernel sources: bench.py
@@ -112,8 +120,82 @@ def traffic(out_json: str, out_md: str, kernel: str, fetch_dir: str, write_dir: 
         f.write("\n".join(lines) + "\n")
 
 
+def _calibration(copy_fetch_dir: str, copy_write_dir: str, copy_bytes: float):
+    _, cf = _pick(_pmc(copy_fetch_dir), "copyBuffer")
+    _, cw = _pick(_pmc(copy_write_dir), "copyBuffer")
+    return (copy_bytes / (statistics.mean(cf) * 1024.0), copy_bytes / (statistics.mean(cw) * 1024.0),
+            statistics.mean(cf), statistics.mean(cw))
+
+
+def kernels(out_md: str, title: str, trace_dir: str, fetch_dir: str, write_dir: str,
+            copy_fetch_dir: str, copy_write_dir: str, copy_bytes: float, command: str) -> None:
+    stats = {r["Name"]: r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv")))}
+    fetch, write = _pmc(fetch_dir), _pmc(write_dir)
+    fscale, wscale, cf, cw = _calibration(copy_fetch_dir, copy_write_dir, copy_bytes)
+    lines = [f"# {title}", "", "Commands (from the repository root on one MI355X; the kernel trace "
+             "of the same workload gives the durations):", "", "```", command, "```", "",
+             f"Counter scale from a {copy_bytes / 2**30:.3g} GiB device copy: FETCH_SIZE x{fscale:.4g}, "
+             f"WRITE_SIZE x{wscale:.4g} (the copy reads {cf:.6g} KiB and writes {cw:.6g} KiB as counted).",
+             "", "| kernel | dispatches | average us | read MB | written MB | achieved GB/s | of 8 TB/s |",
+             "|---|---|---|---|---|---|---|"]
+    for name in sorted(fetch, key=lambda n: -float(stats[n]["TotalDurationNs"]) if n in stats else 0):
+        if "moelora::" not in name or name not in write or name not in stats:
+            continue
+        rb = statistics.mean(fetch[name]) * 1024.0 * fscale
+        wb = statistics.mean(write[name]) * 1024.0 * wscale
+        us = float(stats[name]["AverageNs"]) / 1e3
+        gbs = (rb + wb) / (us * 1e-6) / 1e9
+        lines.append(f"| `{name[:90]}` | {len(fetch[name])} | {us:.2f} | {rb / 1e6:.1f} | "
+                     f"{wb / 1e6:.1f} | {gbs:.0f} | {gbs / 8000.0:.2f} |")
+    lines += ["", f"- kernel sources sha256: {source_digest()}"]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def counters(out_md: str, title: str, kernel: str, pmc_dirs: list[str], command: str) -> None:
+    vals, dur = {}, []
+    for d in pmc_dirs:
+        rows = [r for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
+                if kernel in r["Kernel_Name"]]
+        names = {r["Kernel_Name"] for r in rows}
+        if len(names) != 1:
+            raise SystemExit(f"kernel '{kernel}' matches {len(names)} names in {d}")
+        name = names.pop()
+        for r in rows:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dur.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    avg = {k: statistics.mean(v) for k, v in vals.items()}
+    us = statistics.mean(dur) / 1e3
+    lines = [f"# {title}", "", f"Kernel `{name[:100]}`; commands (from the repository root on one "
+             "MI355X, one counter group per run):", "", "```", command, "```", "",
+             "| counter | mean per dispatch |", "|---|---|"]
+    lines += [f"| {k} | {v:.6g} |" for k, v in sorted(avg.items())]
+    lines += ["", f"- mean dispatch duration under counter collection: {us:.1f} us"]
+    if "GRBM_GUI_ACTIVE" in avg:
+        clk = avg["GRBM_GUI_ACTIVE"] / 8 / (us * 1e-6)  # GRBM_GUI_ACTIVE sums the 8 XCDs
+        lines.append(f"- engine clock: GRBM_GUI_ACTIVE / 8 XCDs / duration = {clk / 1e9:.2f} GHz")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            simd_cycles = avg["GRBM_GUI_ACTIVE"] / 8 * 1024  # 256 CUs x 4 SIMDs
+            lines.append(f"- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) = "
+                         f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f}")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+        fl = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        lines.append(f"- bf16 MFMA work issued: 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 = {fl / 1e12:.3f} TFLOP "
+                     f"per dispatch (padding rows included)")
+    lines.append(f"- kernel sources sha256: {source_digest()}")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
-    if sys.argv[1] == "trace":
+    if sys.argv[1] == "kernels":
+        a = sys.argv
+        kernels(a[2], a[3], a[4], a[5], a[6], a[7], a[8], float(a[9]), " ".join(a[10:]))
+    elif sys.argv[1] == "counters":
+        a = sys.argv
+        sep = a.index("--")
+        counters(a[2], a[3], a[4], a[5:sep], " ".join(a[sep + 1:]))
+    elif sys.argv[1] == "trace":
         trace(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
     elif sys.argv[1] == "traffic":
         a = sys.argv
