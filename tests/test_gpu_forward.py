@@ -67,6 +67,10 @@ SMALL = [
     # 175 rows per expert: 128-row tiles that reuse the weight tile (four
     # waves of 64 x 64), fused epilogues with two fragments per wave
     (350, 192, 320, 4, 2, 3, 32, "bf16"),
+    # top-8 routing over 64 experts; and the largest bucket count (E x L =
+    # 8192) with most experts and buckets empty
+    (64, 128, 192, 64, 8, 4, 16, "bf16"),
+    (40, 128, 128, 128, 2, 64, 32, "bf16"),
     # many one- and two-row adapter buckets per tile (the expand then runs as
     # its own kernel): 32-, 64- and 128-row tiles, ranks 16, 64, 32
     (48, 256, 192, 4, 2, 32, 16, "bf16"),
