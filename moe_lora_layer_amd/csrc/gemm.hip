@@ -182,30 +182,43 @@ __device__ __forceinline__ void lora_expand_acc(f32x16_t (&acc)[FM][FN], const L
     const int mid = (lb + ub + 1) >> 1;
     if (off[mid] <= rw0) lb = mid; else ub = mid - 1;
   }
-  const int nks = lora.rank / 16;
+  const int nks = lora.rank / 16, rk = lora.rank;
+  // B^T row of every lane (row 0 where the column does not exist: loaded,
+  // never stored); all loads below are unconditional, rank chunks past r
+  // reload the last chunk, so each batch of loads costs one round trip
+  int64_t bro[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bro[j] = col_ok[j] ? brow[j] : 0;
   for (int l = lb; l < lora.adapters && off[l] < rw1; ++l) {
     const int s0 = max(rw0, off[l]), s1 = min(rw1, off[l + 1]);
     if (s0 >= s1) continue;  // uniform: an empty bucket
-    const bf16_t* Bb = lora.b + (static_cast<int64_t>(l) * lora.experts + e) * lora.b_rows * lora.rank;
+    const bf16_t* Bb = lora.b + (static_cast<int64_t>(l) * lora.experts + e) * lora.b_rows * rk + 8 * h;
     bf16x8_t bfr[FN][4];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        bfr[j][q4] = (q4 < nks && col_ok[j])
-                         ? *reinterpret_cast<const bf16x8_t*>(Bb + brow[j] * lora.rank + 16 * q4 + 8 * h)
-                         : Mfma<bf16_t>::zero();
+        bfr[j][q4] = *reinterpret_cast<const bf16x8_t*>(Bb + bro[j] * rk + 16 * min(q4, nks - 1));
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int rb = rw0 + 32 * i;
       if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
       const int p = rb + c32;
       const bool in = p >= s0 && p < s1;
+      // z of the lane's row (a row of the bucket where the lane's row is not)
+      const float* zr = lora.z + static_cast<int64_t>(min(max(p, s0), s1 - 1)) * rk + 8 * h;
+      float4 zv[4][2];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        zv[q4][0] = *reinterpret_cast<const float4*>(zr + 16 * min(q4, nks - 1));
+        zv[q4][1] = *reinterpret_cast<const float4*>(zr + 16 * min(q4, nks - 1) + 4);
+      }
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         if (q4 >= nks) break;
-        bf16x8_t zh = Mfma<bf16_t>::zero(), zl = zh;
-        if (in) split_bf16x8(lora.z + static_cast<int64_t>(p) * lora.rank + 16 * q4 + 8 * h, zh, zl);
+        bf16x8_t zh, zl;
+        split_bf16x8(zv[q4][0], zv[q4][1], zh, zl);
+        if (!in) zh = zl = Mfma<bf16_t>::zero();
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zh, bfr[j][q4], acc[i][j], 0, 0, 0);
