@@ -229,88 +229,6 @@ __device__ __forceinline__ void lora_expand_acc(f32x16_t (&acc)[FM][FN], const L
   }
 }
 
-// The same sum for waves of at most two 32-row blocks (the register-staged
-// GEMM), shaped for tiles that meet many small buckets: each row belongs to
-// one bucket, so z of the lane's rows is loaded and split once, and the B^T
-// fragments of the next bucket are loaded while the MFMAs of the current one
-// run.  Every load is unconditional (rank chunks past r and rows past the
-// wave's end reload a valid chunk or row, never used), so the compiler's
-// in-order vmcnt accounting keeps the prefetch in flight.  brow[j] must be a
-// valid B^T row for every lane (any row where the column does not exist).
-template <int FM, int FN>
-__device__ __forceinline__ void lora_expand_rows(f32x16_t (&acc)[FM][FN], const LoraEpilogue& lora,
-                                                 int e, int rw0, int rw1, const int64_t (&brow)[FN],
-                                                 int c32, int h) {
-  const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
-  const int A = lora.adapters, rk = lora.rank, nks = rk / 16;
-  int lb = 0, ub = A - 1;  // last bucket of expert e starting at or before rw0
-  while (lb < ub) {
-    const int mid = (lb + ub + 1) >> 1;
-    if (off[mid] <= rw0) lb = mid; else ub = mid - 1;
-  }
-  bf16x8_t zh[FM][4], zl[FM][4];
-  int prow[FM];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    prow[i] = rw0 + 32 * i + c32;
-    const float* zr = lora.z + static_cast<int64_t>(min(prow[i], rw1 - 1)) * rk + 8 * h;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) split_bf16x8(zr + 16 * min(q4, nks - 1), zh[i][q4], zl[i][q4]);
-  }
-  const bf16_t* Be = lora.b + static_cast<int64_t>(e) * lora.b_rows * rk;
-  const int64_t bstride = static_cast<int64_t>(lora.experts) * lora.b_rows * rk;  // per adapter
-  auto load_b = [&](int l, bf16x8_t (&bf)[FN][4]) {
-    const bf16_t* Bb = Be + static_cast<int64_t>(l) * bstride + 8 * h;
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        bf[j][q4] = *reinterpret_cast<const bf16x8_t*>(Bb + brow[j] * rk + 16 * min(q4, nks - 1));
-  };
-  auto mma_b = [&](int l, const bf16x8_t (&bf)[FN][4]) {
-    const int s0 = max(rw0, off[l]), s1 = min(rw1, off[l + 1]);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int rb = rw0 + 32 * i;
-      if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
-      const bool in = prow[i] >= s0 && prow[i] < s1;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        if (q4 >= nks) break;
-        const bf16x8_t a = in ? zh[i][q4] : Mfma<bf16_t>::zero();
-        const bf16x8_t b = in ? zl[i][q4] : Mfma<bf16_t>::zero();
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[j][q4], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, bf[j][q4], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-  };
-  // the first bucket from l on with rows in [rw0, rw1), or A
-  auto next = [&](int l) {
-    for (; l < A && off[l] < rw1; ++l)
-      if (off[l + 1] > max(off[l], rw0)) return l;
-    return A;
-  };
-  int l = next(lb);
-  if (l >= A) return;
-  bf16x8_t b0[FN][4], b1[FN][4];
-  load_b(l, b0);
-  for (;;) {  // two buckets per pass, so the two fragment sets keep fixed registers
-    int ln = next(l + 1);
-    load_b(ln < A ? ln : l, b1);  // past the last bucket: a valid reload, never used
-    mma_b(l, b0);
-    if (ln >= A) break;
-    l = ln;
-    ln = next(l + 1);
-    load_b(ln < A ? ln : l, b0);
-    mma_b(l, b1);
-    if (ln >= A) break;
-    l = ln;
-  }
-}
-
 // ksplit > 1: workgroup (tile, s) covers the s-th of ksplit K ranges and adds
 // its partial tile to C with relaxed fp32 atomics (C must be zero before).
 // PIPE: the LDS writes of K-step kt+1 and the global loads of K-step kt+2 are
@@ -564,14 +482,121 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     }
     const int rw0 = row0 + wm * WTM;  // this wave's rows [rw0, rw1)
     const int rw1 = min(row_end, rw0 + WTM);
-    static_assert(EPI == EPI_STORE || FM <= 2, "lora_expand_rows keeps z of FM blocks");
-    // eight-wave tiles (two waves per SIMD per workgroup) keep the register
-    // light form: the prefetching one would cost a resident workgroup
-    if (rw0 < rw1) {
-      if constexpr (NT_ >= 512)
-        lora_expand_acc<FM, FN>(acc, lora, e, rw0, rw1, brow, col_ok, c32, h);
-      else
-        lora_expand_rows<FM, FN>(acc, lora, e, rw0, rw1, brow, c32, h);
+    static_assert(EPI == EPI_STORE || FM <= 2, "the staged expand keeps z of FM blocks");
+    if constexpr (NT_ >= 512) {
+      // eight-wave tiles (two waves per SIMD per workgroup) keep the register
+      // light form: the staged one would cost a resident workgroup
+      if (rw0 < rw1) lora_expand_acc<FM, FN>(acc, lora, e, rw0, rw1, brow, col_ok, c32, h);
+    } else {
+      // The expand with the B^T rows staged in the (now idle) LDS stages, a
+      // group of NBUF adapter buckets per round trip: the workgroup walks the
+      // non-empty buckets meeting its rows; every thread loads its chunks of
+      // the group's B^T tiles (the tile rows of the main loop's B operand,
+      // r wide) and writes them to LDS with the main loop's swizzle; each wave
+      // then multiplies z of its rows (loaded and split once, rows outside the
+      // bucket zero) by the fragments of every bucket meeting its rows.
+      constexpr int BUCKET_BYTES = BN * ROWB;
+      constexpr int NBUF = (2 * (BM + BN) * ROWB) / BUCKET_BYTES;
+      static_assert(NBUF >= 1, "LDS holds a bucket's B^T tile");
+      unsigned char* lds = &smem[0][0];
+      const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
+      const int A = lora.adapters, rk = lora.rank, nks = rk / 16;
+      bf16x8_t zh[FM][4], zl[FM][4];
+      int prow[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        prow[i] = rw0 + 32 * i + c32;
+        const float* zr = lora.z + static_cast<int64_t>(min(prow[i], row_end - 1)) * rk + 8 * h;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) split_bf16x8(zr + 16 * min(q4, nks - 1), zh[i][q4], zl[i][q4]);
+      }
+      // this thread's B^T chunks: tile row and LDS position as in the main loop
+      int64_t b_off[B_CH];
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int q = tid + i * NT_, row = q >> 3, ch = q & 7;
+        int64_t wrow;
+        if (EPI == EPI_GATE_UP) {
+          int up;
+          const int64_t ic = gu_col(row / WTN, (row % WTN) / 32, row & 31, up);
+          wrow = up * I + (ic < I ? ic : I - 1);
+        } else {
+          const int64_t n = n0 + row;
+          wrow = n < N ? n : N - 1;
+        }
+        // chunks past r reload the last chunk of the row (never read)
+        b_off[i] = wrow * rk + 8 * min(ch, 2 * nks - 1);
+      }
+      const bf16_t* Be = lora.b + static_cast<int64_t>(e) * lora.b_rows * rk;
+      const int64_t bstride = static_cast<int64_t>(lora.experts) * lora.b_rows * rk;  // per adapter
+      // the first non-empty bucket from l on that meets [row0, row_end), or A
+      auto next = [&](int l) {
+        for (; l < A && off[l] < row_end; ++l)
+          if (off[l + 1] > max(off[l], row0)) return l;
+        return A;
+      };
+      int lb = 0, ub = A - 1;  // last bucket starting at or before row0
+      while (lb < ub) {
+        const int mid = (lb + ub + 1) >> 1;
+        if (off[mid] <= row0) lb = mid; else ub = mid - 1;
+      }
+      int l = next(lb);
+      while (l < A) {  // uniform across the workgroup
+        int grp[NBUF];
+        int ng = 0;
+#pragma unroll
+        for (int g = 0; g < NBUF; ++g) {
+          grp[g] = l;
+          if (l < A) {
+            ++ng;
+            l = next(l + 1);
+          }
+        }
+        uint4 bv[NBUF][B_CH];
+#pragma unroll
+        for (int g = 0; g < NBUF; ++g) {
+          const bf16_t* Bl = Be + static_cast<int64_t>(grp[g] < A ? grp[g] : grp[0]) * bstride;
+#pragma unroll
+          for (int i = 0; i < B_CH; ++i) bv[g][i] = *reinterpret_cast<const uint4*>(Bl + b_off[i]);
+        }
+#pragma unroll
+        for (int g = 0; g < NBUF; ++g)
+#pragma unroll
+          for (int i = 0; i < B_CH; ++i)
+            *reinterpret_cast<uint4*>(lds + g * BUCKET_BYTES + b_dst[i] - BM * ROWB) = bv[g][i];
+        __syncthreads();
+        for (int g = 0; g < ng; ++g) {
+          const int lg = grp[g];
+          const int s0 = max(rw0, off[lg]), s1 = min(rw1, off[lg + 1]);
+          if (s0 >= s1) continue;  // uniform per wave: the bucket misses its rows
+          const unsigned char* Bs = lds + g * BUCKET_BYTES;
+          bf16x8_t bfr[FN][4];
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+              bfr[j][q4] = M::load(reinterpret_cast<const T*>(
+                  Bs + frag_off(wn * WTN + j * 32 + c32, min(q4, nks - 1))));
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int rb = rw0 + 32 * i;
+            if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
+            const bool in = prow[i] >= s0 && prow[i] < s1;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              if (q4 >= nks) break;
+              const bf16x8_t zha = in ? zh[i][q4] : Mfma<bf16_t>::zero();
+              const bf16x8_t zla = in ? zl[i][q4] : Mfma<bf16_t>::zero();
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zha, bfr[j][q4], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zla, bfr[j][q4], acc[i][j], 0, 0, 0);
+              }
+            }
+          }
+        }
+        __syncthreads();  // every wave is done with the group before the next one lands
+      }
     }
     if (EPI == EPI_GATE_UP) {
       constexpr int FG = FN >= 2 ? FN / 2 : 1;  // gate fragments

@@ -71,8 +71,9 @@ SMALL = [
     # 8192) with most experts and buckets empty
     (64, 128, 192, 64, 8, 4, 16, "bf16"),
     (40, 128, 128, 128, 2, 64, 32, "bf16"),
-    # many one- and two-row adapter buckets per tile (the expand then runs as
-    # its own kernel): 32-, 64- and 128-row tiles, ranks 16, 64, 32
+    # many one- and two-row adapter buckets per tile, the expand in the GEMM
+    # epilogue with the buckets' B staged in LDS: 32-, 64- and 128-row tiles,
+    # ranks 16, 64, 32
     (48, 256, 192, 4, 2, 32, 16, "bf16"),
     (96, 192, 320, 4, 2, 64, 64, "bf16"),
     (350, 192, 320, 4, 2, 64, 32, "bf16"),
