@@ -710,10 +710,15 @@ static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, const Lora
 // a load instruction fills 8 whole rows, each lane fetching the global chunk
 // that belongs at its LDS position.
 
-constexpr int kDmaTile = 256;                   // BM = BN
-constexpr int kDmaRowB = 128;                   // bytes of K per LDS row (64 bf16)
+constexpr int kDmaTile = 256;                       // BM = BN
+constexpr int kDmaRowB = 128;                       // bytes of K per LDS row (64 bf16)
 constexpr int kDmaStage = 2 * kDmaTile * kDmaRowB;  // A and B rows of one K-step: 64 KiB
 constexpr int kDmaThreads = 512;
+
+// One lane's 16 bytes of a 1 KiB direct-to-LDS copy (lane i lands at dst + 16 i).
+__device__ __forceinline__ void dma_piece(const void* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}
 
 // The four A and four B load instructions of one wave for K-step kt into
 // stage `slot` (8 rows of 128 bytes each).
@@ -722,15 +727,99 @@ __device__ __forceinline__ void dma_issue(unsigned char* smem, int slot, int64_t
                                           int wave) {
   unsigned char* st = smem + slot * kDmaStage;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds(a_src[j] + ko,
-                                     (lds_void_t*)(st + (32 * wave + 8 * j) * kDmaRowB), 16, 0, 0);
+  for (int j = 0; j < 4; ++j) dma_piece(a_src[j] + ko, st + (32 * wave + 8 * j) * kDmaRowB);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds(
-        b_src[j] + ko, (lds_void_t*)(st + (kDmaTile + 32 * wave + 8 * j) * kDmaRowB), 16, 0, 0);
+    dma_piece(b_src[j] + ko, st + (kDmaTile + 32 * wave + 8 * j) * kDmaRowB);
 }
 
+// The fused LoRA expand of a 256 x 256 k_gemm_dma tile, with its operands
+// staged in the LDS that the K loop has finished with.  z of the
+// tile's rows (fp32, rows [row0, row_end), resident for the whole epilogue)
+// and, for a group of adapter buckets [g, g + ng) of expert e, the B^T rows of
+// the tile's columns are copied with global_load_lds in one round trip per
+// group; then each wave with rows adds z . B^T of every bucket meeting its
+// rows [rw0, rw1) to its accumulators on the MFMAs (z split into bf16 hi +
+// lo, rows outside the bucket masked to zero).  Buckets [lb, ub) are those of
+// expert e meeting the tile.  EPI_GATE_UP: the tile's columns are gate i in
+// [n0, n0 + 128) and up I + i (B^T rows of a bucket staged as the 128 gate
+// rows then the 128 up rows); EPI_DOWN: [n0, n0 + 256).
+template <int EPI>
+__device__ __forceinline__ void dma_lora_expand(f32x16_t (&acc)[4][2], const LoraEpilogue& lora,
+                                                unsigned char* smem, int e, int lb, int ub,
+                                                int row0, int row_end, int64_t n0, int64_t N,
+                                                bool active, int rw0, int rw1, int wn, int wave,
+                                                int lane, int c32, int h) {
+  constexpr int tn = kDmaTile;
+  const int rk = lora.rank, nks = rk / 16;
+  const int zbytes = kDmaTile * rk * 4;  // whole KiB
+  const int bbytes = tn * rk * 2;        // whole KiB
+  // buckets per group: 14, 6, 2 at rank 16, 32, 64
+  const int cap = (2 * kDmaStage - zbytes) / bbytes;
+  const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
+  // [src, src + bytes) to LDS dst in 1 KiB pieces over the eight waves; the
+  // lanes past the end reload the last 16 bytes (their LDS bytes stay inside
+  // the piece and are never read)
+  auto copy = [&](unsigned char* dst, const void* src, int bytes) {
+    const unsigned char* s8 = static_cast<const unsigned char*>(src);
+    for (int c = wave; c * 1024 < bytes; c += kDmaThreads / kWave)
+      dma_piece(s8 + min(c * 1024 + lane * 16, bytes - 16), dst + c * 1024);
+  };
+  for (int g = lb; g < ub; g += cap) {  // uniform
+    const int ng = min(cap, ub - g);
+    lds_barrier();  // every wave is done with what the LDS held before
+    if (g == lb) copy(smem, lora.z + static_cast<int64_t>(row0) * rk, (row_end - row0) * rk * 4);
+    for (int b = 0; b < ng; ++b) {
+      const bf16_t* Bb = lora.b + (static_cast<int64_t>(g + b) * lora.experts + e) * lora.b_rows * rk;
+      unsigned char* dst = smem + zbytes + b * bbytes;
+      if (EPI == EPI_GATE_UP) {
+        const int64_t I = N / 2;
+        const int bytes = static_cast<int>(min<int64_t>(tn / 2, I - n0)) * rk * 2;
+        copy(dst, Bb + n0 * rk, bytes);
+        copy(dst + bbytes / 2, Bb + (I + n0) * rk, bytes);
+      } else {
+        copy(dst, Bb + n0 * rk, static_cast<int>(min<int64_t>(tn, N - n0)) * rk * 2);
+      }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (!active) continue;
+    for (int b = 0; b < ng; ++b) {
+      const int s0 = max(rw0, off[g + b]), s1 = min(rw1, off[g + b + 1]);
+      if (s0 >= s1) continue;  // uniform: the bucket misses this wave's rows
+      const unsigned char* bt = smem + zbytes + b * bbytes + 16 * h;
+      bf16x8_t bfr[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int lr = EPI == EPI_GATE_UP ? j * (tn / 2) + 32 * wn + c32 : 64 * wn + 32 * j + c32;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          bfr[j][q4] = *reinterpret_cast<const bf16x8_t*>(bt + lr * rk * 2 + 32 * min(q4, nks - 1));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rb = rw0 + 32 * i;
+        if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
+        const int p = rb + c32;
+        const bool in = p >= s0 && p < s1;
+        const float* zr =
+            reinterpret_cast<const float*>(smem) + (min(max(p, s0), s1 - 1) - row0) * rk + 8 * h;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if (q4 >= nks) break;
+          bf16x8_t zh, zl;
+          split_bf16x8(zr + 16 * q4, zh, zl);
+          if (!in) zh = zl = Mfma<bf16_t>::zero();
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zh, bfr[j][q4], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zl, bfr[j][q4], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+}
 
 template <bool GATHER, int EPI>
 __global__ void __launch_bounds__(kDmaThreads)
@@ -758,20 +847,16 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   const int e = tile.x, row0 = tile.y, row_end = tile.z;
   // Output columns.  EPI_GATE_UP: the tile covers 128 columns i of the
   // intermediate width I = N/2; wave column group wn owns i in
-  // [128 nt + 32 wn, +32), as weight rows i (gate, fragment j = 0) and I + i
+  // [n0 + 32 wn, +32), as weight rows i (gate, fragment j = 0) and I + i
   // (up, j = 1), so gate and up of one output meet in the same lane.
-  // Otherwise 256 columns n of N, wave wn owning [256 nt + 64 wn, +64).
+  // Otherwise 256 columns n of N, wave wn owning [n0 + 64 wn, +64).
   const int64_t I = N / 2;
+  const int64_t cols = EPI == EPI_GATE_UP ? I : N;
   const int64_t n0 = static_cast<int64_t>(nt) * (EPI == EPI_GATE_UP ? 128 : kDmaTile);
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave >> 2, wn = wave & 3;
   const int c32 = lane & 31, h = lane >> 5;
-  // A tile of at most 128 rows (an expert's last rows) would leave half of the
-  // MFMA work on padding: both wave rows then take the same 128 rows, wave row
-  // wm doing substeps 2wm and 2wm+1 of every K-step, and the two partial
-  // tiles are summed through LDS at the end.
-  const bool half = row_end - row0 <= 128;
 
   // Load instruction j of wave w fills tile rows 32w + 8j + lane/8 (A and B);
   // the lane's LDS chunk is lane%8, so it fetches logical chunk
@@ -796,6 +881,20 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     }
     b_src[j] = We + wrow * K + lch * 8;
   }
+  // adapter buckets of expert e meeting the tile, [lb, ub) (looked up before
+  // the K loop so that the epilogue does not wait for it); a base-only
+  // bucket, if any, comes last in the expert and is skipped
+  int lb = 0, ub = 0;
+  if (EPI != EPI_STORE) {
+    const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
+    int hb = lora.adapters - 1;
+    while (lb < hb) {
+      const int mid = (lb + hb + 1) >> 1;
+      if (off[mid] <= row0) lb = mid; else hb = mid - 1;
+    }
+    ub = lb;
+    while (ub < lora.adapters && off[ub] < row_end) ++ub;
+  }
   const int nk_all = static_cast<int>(K / 64);
   const int nk_per = (nk_all + ksplit - 1) / ksplit;
   const int kbeg = min(nk_all, ks * nk_per);
@@ -811,7 +910,7 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   // fragment reads: substep s (16 of the 64 K) of row r = 128 wm + 32 i + c32;
   // (r >> 1) & 7 depends on c32 only
   const int sw = swz<1>(c32);
-  const int a_off = ((half ? 0 : wm * 128) + c32) * kDmaRowB;
+  const int a_off = (wm * 128 + c32) * kDmaRowB;
   const int b_off = (kDmaTile + wn * 64 + c32) * kDmaRowB;
   bf16x8_t fa[2][4], fb[2][2];
   // Only the wave's 32-row blocks that hold rows of the tile are read and
@@ -827,21 +926,29 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     for (int j = 0; j < 2; ++j)
       fb[f][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * kDmaRowB + ch);
   };
+  // One substep's MFMAs, with the fragment reads of the next substep (issued
+  // just before in program order) placed one after each MFMA: the reads then
+  // overlap the MFMA pipe instead of queueing as a burst, and each fragment
+  // still lands a whole substep before its use.
   auto mm = [&](int f, auto nbc) {
-    constexpr int NB = decltype(nbc)::value;
+    constexpr int NB = decltype(nbc)::value, NR = NB + 2, NM = 2 * NB;
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+    constexpr int PAIRS = NR < NM ? NR : NM;
+#pragma unroll
+    for (int q = 0; q < PAIRS; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    if constexpr (NM > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NM - PAIRS, 0);
+    if constexpr (NR > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NR - PAIRS, 0);
   };
   // workgroup barrier that orders LDS accesses only; the DMA is waited for
   // explicitly with vmcnt
-  auto bar = [&]() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  };
+  auto bar = [&]() { lds_barrier(); };
   auto ko = [&](int kt) { return static_cast<int64_t>(kbeg + kt) * 64; };
 
   // K-step kt lives in stage kt % 2.  Both stages are requested up front;
@@ -852,105 +959,63 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   wait_vmcnt<8>();  // this wave's loads of step 0 are in LDS
   bar();            // ... and every other wave's
   auto k_loop = [&](auto nbc) {
-    if (!half) {
-      rd(0, smem, 0, nbc);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing scalar or LDS pending into the loop
-      for (int kt = 0; kt + 1 < nk; ++kt) {
-        const unsigned char* cur = smem + (kt & 1) * kDmaStage;
-#pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          rd((s + 1) & 1, cur, s + 1, nbc);
-          mm(s & 1, nbc);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // step kt+1 has landed and every wave has finished reading step kt
-        // (lgkmcnt(0) before the barrier): refill that stage with step kt+2
-        wait_vmcnt_lgkm0<0>();
-        bar();
-        dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
-        rd(0, smem + ((kt + 1) & 1) * kDmaStage, 0, nbc);
-        mm(1, nbc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const unsigned char* cur = smem + ((nk - 1) & 1) * kDmaStage;
+    rd(0, smem, 0, nbc);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing scalar or LDS pending into the loop
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const unsigned char* cur = smem + (kt & 1) * kDmaStage;
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
         rd((s + 1) & 1, cur, s + 1, nbc);
         mm(s & 1, nbc);
-      }
-      mm(1, nbc);
-    } else {
-      const int s0 = 2 * wm;  // this wave row's two substeps
-      rd(0, smem, s0, nbc);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      for (int kt = 0; kt + 1 < nk; ++kt) {
-        rd(1, smem + (kt & 1) * kDmaStage, s0 + 1, nbc);
-        mm(0, nbc);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt_lgkm0<0>();
-        bar();
-        dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
-        rd(0, smem + ((kt + 1) & 1) * kDmaStage, s0, nbc);
-        mm(1, nbc);
         __builtin_amdgcn_sched_barrier(0);
       }
-      rd(1, smem + ((nk - 1) & 1) * kDmaStage, s0 + 1, nbc);
-      mm(0, nbc);
+      // step kt+1 has landed and every wave has finished reading step kt
+      // (lgkmcnt(0) before the barrier): refill that stage with step kt+2
+      wait_vmcnt_lgkm0<0>();
+      bar();
+      dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
+      rd(0, smem + ((kt + 1) & 1) * kDmaStage, 0, nbc);
       mm(1, nbc);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    const unsigned char* cur = smem + ((nk - 1) & 1) * kDmaStage;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      rd((s + 1) & 1, cur, s + 1, nbc);
+      mm(s & 1, nbc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mm(1, nbc);
+    __builtin_amdgcn_sched_barrier(0);
   };
   // 32-row blocks of this wave that hold tile rows (every wave runs the same
-  // number of K steps and barriers whatever its count)
-  const int wave_rows = half ? row_end - row0 : min(128, row_end - row0 - 128 * wm);
-  switch ((wave_rows + 31) / 32) {
+  // number of K steps and barriers whatever its count; in a tile of at most
+  // 128 rows, an expert's last, the second wave row has none and leaves its
+  // SIMD's matrix core to the first)
+  const int wave_rows = min(128, row_end - row0 - 128 * wm);
+  switch (max(0, (wave_rows + 31) / 32)) {
+    case 0: k_loop(std::integral_constant<int, 0>{}); break;
     case 1: k_loop(std::integral_constant<int, 1>{}); break;
     case 2: k_loop(std::integral_constant<int, 2>{}); break;
     case 3: k_loop(std::integral_constant<int, 3>{}); break;
     default: k_loop(std::integral_constant<int, 4>{}); break;
   }
   wait_vmcnt<0>();  // no LDS write of this workgroup may outlive it
-  if (half) {
-    // sum the two partial tiles: wave row 1 hands its accumulators over through
-    // LDS (32 KiB per wave, lane-major) and leaves; wave row 0 goes on alone
-    bar();  // every wave is done with the K stages
-    float* red = reinterpret_cast<float*>(smem) + wn * (8 * 16 * kWave);
-    if (wm == 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * kWave + lane] = acc[i][j][r];
-    }
-    bar();
-    if (wm == 1) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * kWave + lane];
-  }
 
-  // output column of fragment j held by this lane, and its LoRA B row
-  int64_t col[2], brow[2];
+  // output column of fragment j held by this lane
+  int64_t col[2];
   bool col_ok[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    if (EPI == EPI_GATE_UP) {
-      col[j] = n0 + 32 * wn + c32;
-      col_ok[j] = col[j] < I;
-      brow[j] = j * I + col[j];
-    } else {
-      col[j] = n0 + 64 * wn + 32 * j + c32;
-      col_ok[j] = col[j] < N;
-      brow[j] = col[j];
-    }
+    col[j] = EPI == EPI_GATE_UP ? n0 + 32 * wn + c32 : n0 + 64 * wn + 32 * j + c32;
+    col_ok[j] = col[j] < cols;
   }
   const int rw0 = row0 + 128 * wm;                 // this wave's rows [rw0, rw1)
   const int rw1 = min(row_end, rw0 + 128);
 
-  if (EPI != EPI_STORE && rw0 < rw1) lora_expand_acc<4, 2>(acc, lora, e, rw0, rw1, brow, col_ok, c32, h);
+  if constexpr (EPI != EPI_STORE)
+    dma_lora_expand<EPI>(acc, lora, smem, e, lb, ub, row0, row_end, n0, N, rw0 < rw1, rw0, rw1,
+                         wn, wave, lane, c32, h);
 
   if (EPI == EPI_GATE_UP) {
 #pragma unroll
