@@ -821,29 +821,23 @@ __device__ __forceinline__ void dma_lora_expand(f32x16_t (&acc)[4][2], const Lor
   }
 }
 
+// How a k_gemm_dma item writes its outputs: plain stores (the item covers the
+// whole K range), relaxed fp32 atomics into C (zero beforehand), or the
+// item's partial slot (deterministic split K).
+enum { DMA_OUT_STORE = 0, DMA_OUT_ATOMIC = 1, DMA_OUT_PART = 2 };
+
+// One item of k_gemm_dma: the K-steps [kbeg, kbeg + nk) of output tile
+// (M-tile `tile`, N-tile nt), written as `out` says; with_lora adds the fused
+// LoRA expand (exactly one item of a tile carries it).  Every wave of the
+// workgroup calls it with the same arguments.
 template <bool GATHER, int EPI>
-__global__ void __launch_bounds__(kDmaThreads)
-k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
-           int gather_k, const bf16_t* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
-           const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
-           const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, LoraEpilogue lora,
-           float* __restrict__ parts, int64_t part_stride) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDmaStage];
-  // workgroup order: as k_gemm (XCD remap over the real workgroups, then per
-  // expert N-tile by N-tile with its M-tiles innermost)
-  const int ks = static_cast<int>(blockIdx.x) % ksplit;
-  const int pid = static_cast<int>(blockIdx.x) / ksplit;
-  const int active = counts[0] * n_ntiles;
-  if (pid >= active) return;
-  const int xcd = pid % kXcds, q = active / kXcds, rem = active % kXcds;
-  const int bid = xcd * q + min(xcd, rem) + pid / kXcds;
-  const int t0 = bid / n_ntiles;
-  const int ex = mtiles[t0].x;
-  const int ta = expert_tiles[ex], tb = expert_tiles[ex + 1];
-  const int local = bid - ta * n_ntiles;
-  const int nt = local / (tb - ta);
-  const int mt = ta + local % (tb - ta);
-  const int4 tile = mtiles[mt];
+__device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __restrict__ X,
+                                         int x_rows, const int32_t* __restrict__ gather_slots,
+                                         int gather_k, const bf16_t* __restrict__ Wt, int64_t N,
+                                         int64_t K, float* __restrict__ C, int4 tile, int nt,
+                                         int kbeg, int nk, int out, bool with_lora,
+                                         const LoraEpilogue& lora, float* __restrict__ part) {
+  lds_barrier();  // every wave is done with what the LDS held for the previous item
   const int e = tile.x, row0 = tile.y, row_end = tile.z;
   // Output columns.  EPI_GATE_UP: the tile covers 128 columns i of the
   // intermediate width I = N/2; wave column group wn owns i in
@@ -885,7 +879,7 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   // the K loop so that the epilogue does not wait for it); a base-only
   // bucket, if any, comes last in the expert and is skipped
   int lb = 0, ub = 0;
-  if (EPI != EPI_STORE) {
+  if (EPI != EPI_STORE && with_lora) {
     const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
     int hb = lora.adapters - 1;
     while (lb < hb) {
@@ -895,11 +889,6 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     ub = lb;
     while (ub < lora.adapters && off[ub] < row_end) ++ub;
   }
-  const int nk_all = static_cast<int>(K / 64);
-  const int nk_per = (nk_all + ksplit - 1) / ksplit;
-  const int kbeg = min(nk_all, ks * nk_per);
-  const int nk = min(nk_all, kbeg + nk_per) - kbeg;
-  if (nk <= 0) return;  // uniform: an empty K split (only for tiny K)
 
   f32x16_t acc[4][2];
 #pragma unroll
@@ -1000,7 +989,7 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     case 3: k_loop(std::integral_constant<int, 3>{}); break;
     default: k_loop(std::integral_constant<int, 4>{}); break;
   }
-  wait_vmcnt<0>();  // no LDS write of this workgroup may outlive it
+  wait_vmcnt<0>();  // no LDS write of this item may outlive it
 
   // output column of fragment j held by this lane
   int64_t col[2];
@@ -1013,7 +1002,7 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   const int rw0 = row0 + 128 * wm;                 // this wave's rows [rw0, rw1)
   const int rw1 = min(row_end, rw0 + 128);
 
-  if constexpr (EPI != EPI_STORE)
+  if (EPI != EPI_STORE && with_lora)
     dma_lora_expand<EPI>(acc, lora, smem, e, lb, ub, row0, row_end, n0, N, rw0 < rw1, rw0, rw1,
                          wn, wave, lane, c32, h);
 
@@ -1040,14 +1029,119 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
           if (p < row_end && col_ok[j]) put(C + static_cast<int64_t>(p) * N + col[j], acc[i][j][r]);
         }
   };
-  if (ksplit == 1)
+  if (out == DMA_OUT_STORE)
     store([](float* dst, float v) { *dst = v; });
-  else if (parts != nullptr)  // deterministic: this split's partial, same index
-    store([&](float* dst, float v) { parts[ks * part_stride + (dst - C)] = v; });
+  else if (out == DMA_OUT_PART)  // deterministic split K: this split's partial, same index
+    store([&](float* dst, float v) { part[dst - C] = v; });
   else
     store([](float* dst, float v) { atomic_add_relaxed(dst, v); });
 }
 
+
+// The M-tile and N-tile of tile index bid (expert-major, per expert N-tile by
+// N-tile with its M-tiles innermost).
+__device__ __forceinline__ void dma_tile_of(int bid, int n_ntiles, const int4* __restrict__ mtiles,
+                                            const int32_t* __restrict__ expert_tiles, int4& tile,
+                                            int& nt) {
+  const int t0 = bid / n_ntiles;
+  const int ex = mtiles[t0].x;
+  const int ta = expert_tiles[ex], tb = expert_tiles[ex + 1];
+  const int local = bid - ta * n_ntiles;
+  nt = local / (tb - ta);
+  tile = mtiles[ta + local % (tb - ta)];
+}
+
+// Tiles of the data-parallel part when the last, partial round of tiles is
+// spread over `nwg` stream-K workgroups instead: whole rounds of nwg tiles,
+// when there is at least one and the remainder leaves a fifth of the
+// workgroups or more idle; else all tiles.
+__device__ __forceinline__ int dma_dp_tiles(int tiles, int nwg) {
+  const int r = tiles % nwg;
+  return tiles >= nwg && r != 0 && 5 * r <= 4 * nwg ? tiles - r : tiles;
+}
+
+// sk_mode 0: every tile, split K over ksplit workgroups per tile.
+// sk_mode 1: the data-parallel tiles only (ksplit 1), each workgroup of the
+// first r also clearing the output of one stream-K tile.
+// sk_mode 2 (grid nwg): the r = tiles - dp remaining tiles as r * nk K-steps
+// cut into nwg equal contiguous ranges, one per workgroup; a range meets at
+// most two tiles and adds each part with atomics, the part holding K-step 0
+// carrying the LoRA expand.  Used for the down projection, whose few long
+// tiles otherwise leave a last round with most CUs idle.
+template <bool GATHER, int EPI>
+__global__ void __launch_bounds__(kDmaThreads)
+k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
+           int gather_k, const bf16_t* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
+           const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
+           const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, LoraEpilogue lora,
+           float* __restrict__ parts, int64_t part_stride, int sk_mode, int nwg) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDmaStage];
+  const int tiles = counts[0] * n_ntiles;
+  const int dp = sk_mode == 0 ? tiles : dma_dp_tiles(tiles, nwg);
+  const int nk_all = static_cast<int>(K / 64);
+  // the items of this workgroup: one (tile, K split) in modes 0 and 1, the
+  // units [u, u1) in mode 2 (one call site of dma_item, so one inlined copy)
+  int64_t u = 0, u1 = 0;
+  int bid = 0, ks = 0;
+  if (sk_mode == 2) {
+    const int64_t units = static_cast<int64_t>(tiles - dp) * nk_all;
+    u = units * blockIdx.x / nwg;
+    u1 = units * (blockIdx.x + 1) / nwg;
+  } else {
+    // workgroup order: XCD remap over the real workgroups, then tile index
+    ks = static_cast<int>(blockIdx.x) % ksplit;
+    const int pid = static_cast<int>(blockIdx.x) / ksplit;
+    if (pid >= dp) return;
+    const int xcd = pid % kXcds, q = dp / kXcds, rem = dp % kXcds;
+    bid = xcd * q + min(xcd, rem) + pid / kXcds;
+    if (sk_mode == 1 && bid < tiles - dp) {
+      // clear the output of stream-K tile dp + bid (the next launch adds into it)
+      int4 st;
+      int snt;
+      dma_tile_of(dp + bid, n_ntiles, mtiles, expert_tiles, st, snt);
+      const int64_t c0 = static_cast<int64_t>(snt) * kDmaTile;
+      const int nc4 = static_cast<int>(min<int64_t>(kDmaTile, N - c0)) / 4;
+      for (int i = threadIdx.x; i < (st.z - st.y) * (kDmaTile / 4); i += kDmaThreads) {
+        const int rr = i / (kDmaTile / 4), c4 = i % (kDmaTile / 4);
+        if (c4 < nc4)
+          *reinterpret_cast<float4*>(C + static_cast<int64_t>(st.y + rr) * N + c0 + 4 * c4) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    u1 = 1;
+  }
+  while (u < u1) {  // uniform
+    int4 tile;
+    int nt, kbeg, nk, out;
+    bool with_lora;
+    float* part = nullptr;
+    if (sk_mode == 2) {
+      const int t = static_cast<int>(u / nk_all);
+      kbeg = static_cast<int>(u % nk_all);
+      nk = static_cast<int>(min<int64_t>(nk_all - kbeg, u1 - u));
+      dma_tile_of(dp + t, n_ntiles, mtiles, expert_tiles, tile, nt);
+      out = DMA_OUT_ATOMIC;
+      with_lora = kbeg == 0;
+      u += nk;
+    } else {
+      dma_tile_of(bid, n_ntiles, mtiles, expert_tiles, tile, nt);
+      const int nk_per = (nk_all + ksplit - 1) / ksplit;
+      kbeg = min(nk_all, ks * nk_per);
+      nk = min(nk_all, kbeg + nk_per) - kbeg;
+      if (nk <= 0) return;  // uniform: an empty K split (only for tiny K)
+      out = ksplit == 1 ? DMA_OUT_STORE : (parts != nullptr ? DMA_OUT_PART : DMA_OUT_ATOMIC);
+      if (parts != nullptr) part = parts + ks * part_stride;
+      with_lora = true;
+      u = u1;
+    }
+    dma_item<GATHER, EPI>(smem, X, x_rows, gather_slots, gather_k, Wt, N, K, C, tile, nt, kbeg, nk,
+                          out, with_lora, lora, part);
+  }
+}
+
+// Stream-K for the non-gate_up forms with unsplit K and no deterministic
+// partials, when the tiles exceed one round: the data-parallel launch, then
+// the stream-K launch over one workgroup per CU.
 template <bool GATHER, int EPI>
 static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue& lora,
                              hipStream_t stream) {
@@ -1055,10 +1149,26 @@ static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const Lora
   const int tn = EPI == EPI_GATE_UP ? 128 : kDmaTile;
   const int n_ntiles = static_cast<int>((cols + tn - 1) / tn);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
+  int nwg = 0;
+  if (EPI != EPI_GATE_UP && a.ksplit == 1 && !plan.det &&
+      static_cast<int64_t>(plan.max_mt) * n_ntiles >= 256) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&nwg, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+  }
+  const int mode = nwg > 0 ? 1 : 0;
   hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
-                     a.expert_tiles, n_ntiles, a.ksplit, lora, a.parts, a.part_stride);
+                     a.expert_tiles, n_ntiles, a.ksplit, lora, a.parts, a.part_stride, mode, nwg);
+  if (mode == 0) return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI>), dim3(static_cast<unsigned>(nwg)), dim3(kDmaThreads),
+                     0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
+                     static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
+                     a.expert_tiles, n_ntiles, 1, lora, a.parts, a.part_stride, 2, nwg);
   return hipGetLastError();
 }
 

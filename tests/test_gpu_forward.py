@@ -136,9 +136,9 @@ def test_forward_workload(name):
 
 def test_forward_tile_boundaries():
     """Routing crafted so that, with 256-row tiles, one expert's last tile has
-    exactly 128 rows (the largest tile computed with both wave rows splitting K),
-    another has 129 (the smallest full tile), a third exactly 256 and a fourth
-    256 + 44."""
+    exactly 128 rows (the largest tile whose second wave row has no rows),
+    another has 129 (the smallest with rows in both), a third exactly 256 and a
+    fourth 256 + 44."""
     sizes = [384, 129, 256, 300]
     cfg = _small(sum(sizes), 128, 192, len(sizes), 1, 3, 32, "bf16", seed=21)
     inp = synth.make_inputs(cfg)
@@ -154,6 +154,29 @@ def test_forward_tile_boundaries():
     assert np.array_equal(np.bincount(ref_ids.ravel(), minlength=len(sizes)), sizes)
     ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
     assert_close(to_f64(out), ref, cfg.dtype, "out")
+
+
+def test_stream_k_down_projection():
+    """The down projection's stream-K launch.  With 256-row tiles, h = 4096 (16
+    N-tiles) and 20 M-tiles, the 320 tiles exceed one round of 256 workgroups:
+    the last 64 tiles' 16 K-steps each are cut into 256 equal ranges (four
+    workgroups per tile adding their parts with atomics, the one holding K-step
+    0 adding the LoRA expand).  Full output against the oracle; the
+    deterministic mode, which has no stream-K, agrees within the same bound."""
+    cfg = _small(2048, 4096, 1024, 5, 2, 4, 16, "bf16", seed=31, requests=32)
+    inp = synth.make_inputs(cfg)
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    rows = np.bincount(ref_ids.ravel(), minlength=cfg.experts)
+    tiles = int(sum((rows + 255) // 256)) * (cfg.hidden // 256)
+    assert tiles > 256 and 0 < tiles % 256 <= 204, (rows, tiles)
+    plan = dict(gemm_rows=256, gemm_form=2)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
+    for det in (False, True):
+        d = ops.dims_for(cfg, deterministic=det, plan=plan)
+        assert ops.forward_plan(d)["ksplit_down"] == 1 and ops.forward_fusion(d)["down"]
+        say(f"stream-K shape, deterministic={det}")
+        _, _, out, _ = _layer(cfg, inp, d)
+        assert_close(to_f64(out), ref, cfg.dtype, f"out det={det}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
