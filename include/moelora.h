@@ -304,11 +304,8 @@ int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]
  * matching MOELORA_STAGE_EXPAND_* stages are then empty.  A projection can
  * fuse when the dtype is bf16 and its base GEMM is not split over K (split K
  * is chosen only when the output has too few tiles to fill the GPU); it does
- * unless MOELORA_FLAG_UNFUSED is set or dims->plan.fuse is 2, and, with the
- * automatic choice (plan.fuse 0), only when the M-tiles are 256 rows or a
- * tile meets few adapter buckets (at most about 8), since the smaller tiles'
- * epilogue waits on a memory round trip per bucket.  Host only; returns
- * the validation status of dims (MOELORA_ERR_NULL for a NULL flags).
+ * unless MOELORA_FLAG_UNFUSED is set or dims->plan.fuse is 2.  Host only;
+ * returns the validation status of dims (MOELORA_ERR_NULL for a NULL flags).
  */
 #define MOELORA_FUSED_GATE_UP 1
 #define MOELORA_FUSED_DOWN 2

@@ -229,6 +229,113 @@ __device__ __forceinline__ void lora_expand_acc(f32x16_t (&acc)[FM][FN], const L
   }
 }
 
+// One lane's 16 bytes of a 1 KiB direct-to-LDS copy (lane i lands at dst + 16 i).
+__device__ __forceinline__ void dma_piece(const void* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}
+
+// The fused LoRA expand of a tile with its operands staged in `lds_bytes` of
+// LDS that the K loop has finished with (whole KiB).  z of the tile's rows
+// (fp32, rows [row0, row_end), at most tm of them, resident for the whole
+// epilogue) and, for a group of adapter buckets, the B^T rows of the tile's tn
+// columns are copied with global_load_lds (1 KiB pieces spread over the
+// workgroup's nwaves waves) in one round trip per group; then each wave with
+// rows adds z . B^T of every bucket meeting its rows [rw0, rw1) (FM blocks of
+// 32) to its accumulators on the MFMAs (z split into bf16 hi + lo, rows
+// outside the bucket masked to zero).  Buckets [lb, ub) of expert e are those
+// meeting the tile.  EPI_GATE_UP: the tile's columns are gate i in
+// [n0, n0 + tn/2) and up I + i, staged as the tn/2 gate rows then the tn/2 up
+// rows; EPI_DOWN: [n0, n0 + tn).  lrow[j]: the staged row of the lane's
+// column in fragment j.
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void staged_lora_expand(f32x16_t (&acc)[FM][FN], const LoraEpilogue& lora,
+                                                   unsigned char* lds, int lds_bytes, int nwaves,
+                                                   int e, int lb, int ub, int row0, int row_end,
+                                                   int tm, int tn, int64_t n0, int64_t N,
+                                                   const int (&lrow)[FN], bool active, int rw0,
+                                                   int rw1, int wave, int lane, int c32, int h) {
+  const int rk = lora.rank, nks = rk / 16;
+  const int zbytes = tm * rk * 4;
+  const int bbytes = tn * rk * 2;
+  const int cap = (lds_bytes - zbytes) / bbytes;
+  const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
+  // [src, src + bytes) to LDS dst in 1 KiB pieces; the lanes past the end
+  // reload the last 16 bytes (their LDS bytes stay inside the piece and are
+  // never read)
+  auto copy = [&](unsigned char* dst, const void* src, int bytes) {
+    const unsigned char* s8 = static_cast<const unsigned char*>(src);
+    for (int c = wave; c * 1024 < bytes; c += nwaves)
+      dma_piece(s8 + min(c * 1024 + lane * 16, bytes - 16), dst + c * 1024);
+  };
+  for (int g = lb; g < ub; g += cap) {  // uniform
+    const int ng = min(cap, ub - g);
+    lds_barrier();  // every wave is done with what the LDS held before
+    if (g == lb) copy(lds, lora.z + static_cast<int64_t>(row0) * rk, (row_end - row0) * rk * 4);
+    for (int b = 0; b < ng; ++b) {
+      const bf16_t* Bb = lora.b + (static_cast<int64_t>(g + b) * lora.experts + e) * lora.b_rows * rk;
+      unsigned char* dst = lds + zbytes + b * bbytes;
+      if (EPI == EPI_GATE_UP) {
+        const int64_t I = N / 2;
+        const int bytes = static_cast<int>(min<int64_t>(tn / 2, I - n0)) * rk * 2;
+        copy(dst, Bb + n0 * rk, bytes);
+        copy(dst + bbytes / 2, Bb + (I + n0) * rk, bytes);
+      } else {
+        copy(dst, Bb + n0 * rk, static_cast<int>(min<int64_t>(tn, N - n0)) * rk * 2);
+      }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (!active) continue;
+    for (int b = 0; b < ng; ++b) {
+      const int s0 = max(rw0, off[g + b]), s1 = min(rw1, off[g + b + 1]);
+      if (s0 >= s1) continue;  // uniform: the bucket misses this wave's rows
+      const unsigned char* bt = lds + zbytes + b * bbytes + 16 * h;
+      bf16x8_t bfr[FN][4];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          bfr[j][q4] = *reinterpret_cast<const bf16x8_t*>(bt + lrow[j] * rk * 2 + 32 * min(q4, nks - 1));
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int rb = rw0 + 32 * i;
+        if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
+        const int p = rb + c32;
+        const bool in = p >= s0 && p < s1;
+        const float* zr =
+            reinterpret_cast<const float*>(lds) + (min(max(p, s0), s1 - 1) - row0) * rk + 8 * h;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if (q4 >= nks) break;
+          bf16x8_t zh, zl;
+          split_bf16x8(zr + 16 * q4, zh, zl);
+          if (!in) zh = zl = Mfma<bf16_t>::zero();
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zh, bfr[j][q4], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zl, bfr[j][q4], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Adapter buckets of expert e meeting rows [row0, row_end), as [lb, ub); a
+// base-only bucket, if any, comes last in the expert and is left out.
+__device__ __forceinline__ void lora_buckets(const LoraEpilogue& lora, int e, int row0, int row_end,
+                                             int& lb, int& ub) {
+  const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
+  lb = 0;
+  int hb = lora.adapters - 1;
+  while (lb < hb) {
+    const int mid = (lb + hb + 1) >> 1;
+    if (off[mid] <= row0) lb = mid; else hb = mid - 1;
+  }
+  ub = lb;
+  while (ub < lora.adapters && off[ub] < row_end) ++ub;
+}
+
 // ksplit > 1: workgroup (tile, s) covers the s-th of ksplit K ranges and adds
 // its partial tile to C with relaxed fp32 atomics (C must be zero before).
 // PIPE: the LDS writes of K-step kt+1 and the global loads of K-step kt+2 are
@@ -484,9 +591,25 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     const int rw1 = min(row_end, rw0 + WTM);
     static_assert(EPI == EPI_STORE || FM <= 2, "the staged expand keeps z of FM blocks");
     if constexpr (NT_ >= 512) {
-      // eight-wave tiles (two waves per SIMD per workgroup) keep the register
-      // light form: the staged one would cost a resident workgroup
-      if (rw0 < rw1) lora_expand_acc<FM, FN>(acc, lora, e, rw0, rw1, brow, col_ok, c32, h);
+      // eight-wave tiles (two waves per SIMD per workgroup): the operands are
+      // copied straight into the idle LDS stages, which costs no registers
+      int lrow[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if (EPI == EPI_GATE_UP) {
+          int up;
+          const int64_t ic = gu_col(wn, j, c32, up);
+          lrow[j] = up * (BN / 2) + static_cast<int>(ic - it0);
+        } else {
+          lrow[j] = wn * WTN + j * 32 + c32;
+        }
+      }
+      int lb, ub;
+      lora_buckets(lora, e, row0, row_end, lb, ub);
+      staged_lora_expand<EPI, FM, FN>(acc, lora, &smem[0][0], 2 * (BM + BN) * ROWB, NT_ / kWave, e, lb,
+                                      ub, row0, row_end, BM, BN,
+                                      EPI == EPI_GATE_UP ? it0 : n0, N, lrow, rw0 < rw1, rw0, rw1,
+                                      wave, lane, c32, h);
     } else {
       // The expand with the B^T rows staged in the (now idle) LDS stages, a
       // group of NBUF adapter buckets per round trip: the workgroup walks the
@@ -715,11 +838,6 @@ constexpr int kDmaRowB = 128;                       // bytes of K per LDS row (6
 constexpr int kDmaStage = 2 * kDmaTile * kDmaRowB;  // A and B rows of one K-step: 64 KiB
 constexpr int kDmaThreads = 512;
 
-// One lane's 16 bytes of a 1 KiB direct-to-LDS copy (lane i lands at dst + 16 i).
-__device__ __forceinline__ void dma_piece(const void* src, unsigned char* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
-}
-
 // The four A and four B load instructions of one wave for K-step kt into
 // stage `slot` (8 rows of 128 bytes each).
 __device__ __forceinline__ void dma_issue(unsigned char* smem, int slot, int64_t ko,
@@ -731,94 +849,6 @@ __device__ __forceinline__ void dma_issue(unsigned char* smem, int slot, int64_t
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     dma_piece(b_src[j] + ko, st + (kDmaTile + 32 * wave + 8 * j) * kDmaRowB);
-}
-
-// The fused LoRA expand of a 256 x 256 k_gemm_dma tile, with its operands
-// staged in the LDS that the K loop has finished with.  z of the
-// tile's rows (fp32, rows [row0, row_end), resident for the whole epilogue)
-// and, for a group of adapter buckets [g, g + ng) of expert e, the B^T rows of
-// the tile's columns are copied with global_load_lds in one round trip per
-// group; then each wave with rows adds z . B^T of every bucket meeting its
-// rows [rw0, rw1) to its accumulators on the MFMAs (z split into bf16 hi +
-// lo, rows outside the bucket masked to zero).  Buckets [lb, ub) are those of
-// expert e meeting the tile.  EPI_GATE_UP: the tile's columns are gate i in
-// [n0, n0 + 128) and up I + i (B^T rows of a bucket staged as the 128 gate
-// rows then the 128 up rows); EPI_DOWN: [n0, n0 + 256).
-template <int EPI>
-__device__ __forceinline__ void dma_lora_expand(f32x16_t (&acc)[4][2], const LoraEpilogue& lora,
-                                                unsigned char* smem, int e, int lb, int ub,
-                                                int row0, int row_end, int64_t n0, int64_t N,
-                                                bool active, int rw0, int rw1, int wn, int wave,
-                                                int lane, int c32, int h) {
-  constexpr int tn = kDmaTile;
-  const int rk = lora.rank, nks = rk / 16;
-  const int zbytes = kDmaTile * rk * 4;  // whole KiB
-  const int bbytes = tn * rk * 2;        // whole KiB
-  // buckets per group: 14, 6, 2 at rank 16, 32, 64
-  const int cap = (2 * kDmaStage - zbytes) / bbytes;
-  const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
-  // [src, src + bytes) to LDS dst in 1 KiB pieces over the eight waves; the
-  // lanes past the end reload the last 16 bytes (their LDS bytes stay inside
-  // the piece and are never read)
-  auto copy = [&](unsigned char* dst, const void* src, int bytes) {
-    const unsigned char* s8 = static_cast<const unsigned char*>(src);
-    for (int c = wave; c * 1024 < bytes; c += kDmaThreads / kWave)
-      dma_piece(s8 + min(c * 1024 + lane * 16, bytes - 16), dst + c * 1024);
-  };
-  for (int g = lb; g < ub; g += cap) {  // uniform
-    const int ng = min(cap, ub - g);
-    lds_barrier();  // every wave is done with what the LDS held before
-    if (g == lb) copy(smem, lora.z + static_cast<int64_t>(row0) * rk, (row_end - row0) * rk * 4);
-    for (int b = 0; b < ng; ++b) {
-      const bf16_t* Bb = lora.b + (static_cast<int64_t>(g + b) * lora.experts + e) * lora.b_rows * rk;
-      unsigned char* dst = smem + zbytes + b * bbytes;
-      if (EPI == EPI_GATE_UP) {
-        const int64_t I = N / 2;
-        const int bytes = static_cast<int>(min<int64_t>(tn / 2, I - n0)) * rk * 2;
-        copy(dst, Bb + n0 * rk, bytes);
-        copy(dst + bbytes / 2, Bb + (I + n0) * rk, bytes);
-      } else {
-        copy(dst, Bb + n0 * rk, static_cast<int>(min<int64_t>(tn, N - n0)) * rk * 2);
-      }
-    }
-    wait_vmcnt<0>();
-    lds_barrier();
-    if (!active) continue;
-    for (int b = 0; b < ng; ++b) {
-      const int s0 = max(rw0, off[g + b]), s1 = min(rw1, off[g + b + 1]);
-      if (s0 >= s1) continue;  // uniform: the bucket misses this wave's rows
-      const unsigned char* bt = smem + zbytes + b * bbytes + 16 * h;
-      bf16x8_t bfr[2][4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int lr = EPI == EPI_GATE_UP ? j * (tn / 2) + 32 * wn + c32 : 64 * wn + 32 * j + c32;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          bfr[j][q4] = *reinterpret_cast<const bf16x8_t*>(bt + lr * rk * 2 + 32 * min(q4, nks - 1));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rb = rw0 + 32 * i;
-        if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
-        const int p = rb + c32;
-        const bool in = p >= s0 && p < s1;
-        const float* zr =
-            reinterpret_cast<const float*>(smem) + (min(max(p, s0), s1 - 1) - row0) * rk + 8 * h;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          if (q4 >= nks) break;
-          bf16x8_t zh, zl;
-          split_bf16x8(zr + 16 * q4, zh, zl);
-          if (!in) zh = zl = Mfma<bf16_t>::zero();
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zh, bfr[j][q4], acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zl, bfr[j][q4], acc[i][j], 0, 0, 0);
-          }
-        }
-      }
-    }
-  }
 }
 
 // How a k_gemm_dma item writes its outputs: plain stores (the item covers the
@@ -879,16 +909,7 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
   // the K loop so that the epilogue does not wait for it); a base-only
   // bucket, if any, comes last in the expert and is skipped
   int lb = 0, ub = 0;
-  if (EPI != EPI_STORE && with_lora) {
-    const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
-    int hb = lora.adapters - 1;
-    while (lb < hb) {
-      const int mid = (lb + hb + 1) >> 1;
-      if (off[mid] <= row0) lb = mid; else hb = mid - 1;
-    }
-    ub = lb;
-    while (ub < lora.adapters && off[ub] < row_end) ++ub;
-  }
+  if (EPI != EPI_STORE && with_lora) lora_buckets(lora, e, row0, row_end, lb, ub);
 
   f32x16_t acc[4][2];
 #pragma unroll
@@ -1002,9 +1023,17 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
   const int rw0 = row0 + 128 * wm;                 // this wave's rows [rw0, rw1)
   const int rw1 = min(row_end, rw0 + 128);
 
-  if (EPI != EPI_STORE && with_lora)
-    dma_lora_expand<EPI>(acc, lora, smem, e, lb, ub, row0, row_end, n0, N, rw0 < rw1, rw0, rw1,
-                         wn, wave, lane, c32, h);
+  if (EPI != EPI_STORE && with_lora) {
+    // operands staged in the idle K stages: up to 14, 6, 2 buckets per round
+    // trip at rank 16, 32, 64
+    int lrow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      lrow[j] = EPI == EPI_GATE_UP ? j * (kDmaTile / 2) + 32 * wn + c32 : 64 * wn + 32 * j + c32;
+    staged_lora_expand<EPI, 4, 2>(acc, lora, smem, 2 * kDmaStage, kDmaThreads / kWave, e, lb, ub,
+                                  row0, row_end, kDmaTile, kDmaTile, n0, N, lrow, rw0 < rw1, rw0,
+                                  rw1, wave, lane, c32, h);
+  }
 
   if (EPI == EPI_GATE_UP) {
 #pragma unroll

@@ -99,15 +99,11 @@ TilePlan make_plan(const moelora_dims* d) {
   };
   p.ksplit_gu = splits(2 * d->intermediate, d->hidden, o.ksplit_gate_up);
   p.ksplit_dn = splits(d->hidden, d->intermediate, o.ksplit_down);
-  // bf16 GEMMs with unsplit K run the LoRA expand in their epilogue.  The
-  // eight-wave 128-row weight-streaming tile has the register-light epilogue
-  // (one memory round trip per adapter bucket), so with the automatic choice
-  // it fuses only when a tile meets few buckets (estimated as min(mean rows
-  // per expert, adapters) <= 8); the other tiles always fuse.
-  const int64_t est_buckets = std::min<int64_t>(std::min<int64_t>(avg, p.bm), d->adapters);
-  const bool light_epilogue = p.bm == 128 && p.stream;
+  // bf16 GEMMs with unsplit K run the LoRA expand in their epilogue (every
+  // tile family stages the expand's operands in its idle LDS, a group of
+  // adapter buckets per memory round trip)
   const bool fusable = d->dtype == MOELORA_BF16 && (d->flags & MOELORA_FLAG_UNFUSED) == 0 &&
-                       o.fuse != 2 && (o.fuse == 1 || !light_epilogue || est_buckets <= 8);
+                       o.fuse != 2;
   p.fuse_gu = fusable && p.ksplit_gu == 1;
   p.fuse_dn = fusable && p.ksplit_dn == 1;
   p.det = (d->flags & MOELORA_FLAG_DETERMINISTIC) != 0;
