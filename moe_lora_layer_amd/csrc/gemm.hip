@@ -158,76 +158,12 @@ __device__ __forceinline__ uint4 masked(uint4 v, uint32_t m) {
 
 // Epilogues of the grouped GEMMs.  EPI_STORE writes the fp32 tile to C
 // (relaxed atomics under split K).  The two fused forms first add the LoRA
-// expand of the tile's rows to the accumulators (lora_expand_acc) and then,
+// expand of the tile's rows to the accumulators and then,
 // EPI_GATE_UP, apply SiLU(gate) * up and write bf16 ACT, or, EPI_DOWN, write
 // D.  The vLLM blog page "Multi-LoRA" (section "Implementing Multi-LoRA
 // inference for MoE models in vLLM") names folding the LoRA add into the base
 // GEMM's output as the next fusion step.
 enum { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_DOWN = 2 };
-
-// acc[i][j] += z_p . B[l][e]^T for every adapter bucket (e, l) of expert e that
-// meets this wave's rows [rw0, rw1) (row block i: rows rw0 + 32 i + 0..31),
-// on the MFMA units: z (fp32, from the shrink) split into bf16 hi + lo, rows
-// outside the bucket masked to zero.  brow[j]: the B^T row of the lane's
-// output column in fragment j; col_ok[j] false: no such column.  A base-only
-// bucket, if any, comes last in the expert and is skipped.
-template <int FM, int FN>
-__device__ __forceinline__ void lora_expand_acc(f32x16_t (&acc)[FM][FN], const LoraEpilogue& lora,
-                                                int e, int rw0, int rw1, const int64_t (&brow)[FN],
-                                                const bool (&col_ok)[FN], int c32, int h) {
-  const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
-  // last bucket of expert e starting at or before rw0
-  int lb = 0, ub = lora.adapters - 1;
-  while (lb < ub) {
-    const int mid = (lb + ub + 1) >> 1;
-    if (off[mid] <= rw0) lb = mid; else ub = mid - 1;
-  }
-  const int nks = lora.rank / 16, rk = lora.rank;
-  // B^T row of every lane (row 0 where the column does not exist: loaded,
-  // never stored); all loads below are unconditional, rank chunks past r
-  // reload the last chunk, so each batch of loads costs one round trip
-  int64_t bro[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) bro[j] = col_ok[j] ? brow[j] : 0;
-  for (int l = lb; l < lora.adapters && off[l] < rw1; ++l) {
-    const int s0 = max(rw0, off[l]), s1 = min(rw1, off[l + 1]);
-    if (s0 >= s1) continue;  // uniform: an empty bucket
-    const bf16_t* Bb = lora.b + (static_cast<int64_t>(l) * lora.experts + e) * lora.b_rows * rk + 8 * h;
-    bf16x8_t bfr[FN][4];
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        bfr[j][q4] = *reinterpret_cast<const bf16x8_t*>(Bb + bro[j] * rk + 16 * min(q4, nks - 1));
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int rb = rw0 + 32 * i;
-      if (rb >= s1 || rb + 32 <= s0) continue;  // uniform: block outside the bucket
-      const int p = rb + c32;
-      const bool in = p >= s0 && p < s1;
-      // z of the lane's row (a row of the bucket where the lane's row is not)
-      const float* zr = lora.z + static_cast<int64_t>(min(max(p, s0), s1 - 1)) * rk + 8 * h;
-      float4 zv[4][2];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        zv[q4][0] = *reinterpret_cast<const float4*>(zr + 16 * min(q4, nks - 1));
-        zv[q4][1] = *reinterpret_cast<const float4*>(zr + 16 * min(q4, nks - 1) + 4);
-      }
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        if (q4 >= nks) break;
-        bf16x8_t zh, zl;
-        split_bf16x8(zv[q4][0], zv[q4][1], zh, zl);
-        if (!in) zh = zl = Mfma<bf16_t>::zero();
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zh, bfr[j][q4], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zl, bfr[j][q4], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-  }
-}
 
 // One lane's 16 bytes of a 1 KiB direct-to-LDS copy (lane i lands at dst + 16 i).
 __device__ __forceinline__ void dma_piece(const void* src, unsigned char* dst) {
@@ -570,9 +506,8 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
 
   if (EPI != EPI_STORE) {
     static_assert(EPI == EPI_STORE || sizeof(T) == 2, "fused epilogues are bf16");
-    // output column of fragment j held by this lane, and its LoRA B row (row
-    // 0 where the column does not exist)
-    int64_t col[FN], brow[FN];
+    // output column of fragment j held by this lane
+    int64_t col[FN];
     bool col_ok[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -580,11 +515,9 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
         int up;
         col[j] = gu_col(wn, j, c32, up);
         col_ok[j] = col[j] < I;
-        brow[j] = col_ok[j] ? up * I + col[j] : 0;
       } else {
         col[j] = n0 + wn * WTN + j * 32 + c32;
         col_ok[j] = col[j] < N;
-        brow[j] = col_ok[j] ? col[j] : 0;
       }
     }
     const int rw0 = row0 + wm * WTM;  // this wave's rows [rw0, rw1)
@@ -1110,12 +1043,12 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   const int nk_all = static_cast<int>(K / 64);
   // the items of this workgroup: one (tile, K split) in modes 0 and 1, the
   // units [u, u1) in mode 2 (one call site of dma_item, so one inlined copy)
-  int64_t u = 0, u1 = 0;
+  int u = 0, u1 = 0;  // at most 255 tiles x 16384 K-steps
   int bid = 0, ks = 0;
   if (sk_mode == 2) {
     const int64_t units = static_cast<int64_t>(tiles - dp) * nk_all;
-    u = units * blockIdx.x / nwg;
-    u1 = units * (blockIdx.x + 1) / nwg;
+    u = static_cast<int>(units * blockIdx.x / nwg);
+    u1 = static_cast<int>(units * (blockIdx.x + 1) / nwg);
   } else {
     // workgroup order: XCD remap over the real workgroups, then tile index
     ks = static_cast<int>(blockIdx.x) % ksplit;
@@ -1145,9 +1078,9 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     bool with_lora;
     float* part = nullptr;
     if (sk_mode == 2) {
-      const int t = static_cast<int>(u / nk_all);
-      kbeg = static_cast<int>(u % nk_all);
-      nk = static_cast<int>(min<int64_t>(nk_all - kbeg, u1 - u));
+      const int t = u / nk_all;
+      kbeg = u % nk_all;
+      nk = min(nk_all - kbeg, u1 - u);
       dma_tile_of(dp + t, n_ntiles, mtiles, expert_tiles, tile, nt);
       out = DMA_OUT_ATOMIC;
       with_lora = kbeg == 0;
