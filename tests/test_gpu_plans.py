@@ -20,9 +20,11 @@ PLANS = [dict(gemm_rows=r, gemm_form=f, lora_rows=lr, ksplit_gate_up=kg, ksplit_
                                                            (1, 2))]
 
 # (T, h, I, E, k, L, r, dtype): rows per expert 38 (many buckets of a few rows),
-# 150, and a fp32 layer; h and 2I tails against every tile width
+# 150, and a fp32 layer; h and 2I tails against every tile width; 300 rows per
+# expert over 16 adapters at rank 32 (a 256-row tile meets more buckets than
+# one LDS group of the staged expand holds)
 SHAPES = [(96, 192, 320, 5, 2, 3, 32, "bf16"), (300, 320, 192, 4, 2, 6, 64, "bf16"),
-          (96, 192, 320, 5, 2, 3, 16, "f32")]
+          (96, 192, 320, 5, 2, 3, 16, "f32"), (300, 256, 192, 2, 2, 16, 32, "bf16")]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
