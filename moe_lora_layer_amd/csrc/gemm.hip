@@ -193,6 +193,8 @@ __device__ __forceinline__ void staged_lora_expand(f32x16_t (&acc)[FM][FN], cons
   const int rk = lora.rank, nks = rk / 16;
   const int zbytes = tm * rk * 4;
   const int bbytes = tn * rk * 2;
+  // buckets per group, >= 2 for the tiles that call this (128 x 128 in
+  // 64 KiB, 256 x 256 in 128 KiB) at every supported rank
   const int cap = (lds_bytes - zbytes) / bbytes;
   const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
   // [src, src + bytes) to LDS dst in 1 KiB pieces; the lanes past the end
@@ -1111,15 +1113,15 @@ static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const Lora
   const int tn = EPI == EPI_GATE_UP ? 128 : kDmaTile;
   const int n_ntiles = static_cast<int>((cols + tn - 1) / tn);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
-  int nwg = 0;
-  if (EPI != EPI_GATE_UP && a.ksplit == 1 && !plan.det &&
-      static_cast<int64_t>(plan.max_mt) * n_ntiles >= 256) {
+  int nwg = 0;  // CUs: one stream-K workgroup each
+  if (EPI != EPI_GATE_UP && a.ksplit == 1 && !plan.det) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&nwg, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorInvalidDevice;
   }
-  const int mode = nwg > 0 ? 1 : 0;
+  // the tiles' upper bound must reach a round for the device to pick stream-K
+  const int mode = nwg > 0 && static_cast<int64_t>(plan.max_mt) * n_ntiles >= nwg ? 1 : 0;
   hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
