@@ -161,8 +161,10 @@ def test_stream_k_down_projection():
     N-tiles) and 20 M-tiles, the 320 tiles exceed one round of 256 workgroups:
     the last 64 tiles' 16 K-steps each are cut into 256 equal ranges (four
     workgroups per tile adding their parts with atomics, the one holding K-step
-    0 adding the LoRA expand).  Full output against the oracle; the
-    deterministic mode, which has no stream-K, agrees within the same bound."""
+    0 adding the LoRA expand).  Full output against the oracle, with the
+    workspace filled with NaN first (the data-parallel launch must clear every
+    stream-K tile), also with base-only tokens; the deterministic mode, which
+    has no stream-K, agrees within the same bound."""
     cfg = _small(2048, 4096, 1024, 5, 2, 4, 16, "bf16", seed=31, requests=32)
     inp = synth.make_inputs(cfg)
     ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
@@ -170,13 +172,24 @@ def test_stream_k_down_projection():
     tiles = int(sum((rows + 255) // 256)) * (cfg.hidden // 256)
     assert tiles > 256 and 0 < tiles % 256 <= 204, (rows, tiles)
     plan = dict(gemm_rows=256, gemm_form=2)
-    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
-    for det in (False, True):
-        d = ops.dims_for(cfg, deterministic=det, plan=plan)
+    dev = device()
+    for det, base_only in [(False, False), (True, False), (False, True)]:
+        case = dict(inp)
+        if base_only:
+            rng = np.random.default_rng(5)
+            case["adapter_ids"] = np.where(rng.random(cfg.tokens) < 0.3, -1,
+                                           inp["adapter_ids"]).astype(np.int32)
+        d = ops.dims_for(cfg, deterministic=det, base_only=base_only, plan=plan)
         assert ops.forward_plan(d)["ksplit_down"] == 1 and ops.forward_fusion(d)["down"]
-        say(f"stream-K shape, deterministic={det}")
-        _, _, out, _ = _layer(cfg, inp, d)
-        assert_close(to_f64(out), ref, cfg.dtype, f"out det={det}")
+        say(f"stream-K shape, deterministic={det}, base_only={base_only}")
+        dinp = device_inputs(case, cfg, dev)
+        ids, w, ss, off, st = run_align(cfg, dinp, dims=d)
+        assert int(st[0].item()) == 0
+        ws = ops.workspace(ops.forward_workspace_size(d), dev)
+        ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+        out, _ = run_forward(cfg, dinp, w, ss, off, dims=d, workspace_buf=ws)
+        ref = oracle.forward(case, oracle.dims_of(cfg), ref_ids, ref_w)
+        assert_close(to_f64(out), ref, cfg.dtype, f"out det={det} base_only={base_only}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
