@@ -178,6 +178,17 @@ def counters(out_md: str, title: str, kernel: str, pmc_dirs: list[str], command:
             simd_cycles = avg["GRBM_GUI_ACTIVE"] / 8 * 1024  # 256 CUs x 4 SIMDs
             lines.append(f"- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) = "
                          f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f}")
+    if "SQ_INSTS_LDS_LOAD_BANDWIDTH" in avg and "GRBM_GUI_ACTIVE" in avg:
+        # the counter counts 64-byte units of LDS reads, summed over the CUs
+        per_cu_clk = avg["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64 / 256 / (avg["GRBM_GUI_ACTIVE"] / 8)
+        lines.append(f"- LDS reads: 64 x SQ_INSTS_LDS_LOAD_BANDWIDTH = "
+                     f"{avg['SQ_INSTS_LDS_LOAD_BANDWIDTH'] * 64 / 1e9:.1f} GB per dispatch, "
+                     f"{per_cu_clk:.0f} bytes per clock per CU")
+    if "SQ_WAVE_CYCLES" in avg:
+        for k, what in (("SQ_WAIT_ANY", "at s_waitcnt"), ("SQ_WAIT_INST_ANY", "for an instruction to issue")):
+            if k in avg:
+                lines.append(f"- waves waiting {what}: {k} / SQ_WAVE_CYCLES = "
+                             f"{avg[k] / avg['SQ_WAVE_CYCLES']:.2f}")
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
         fl = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
         lines.append(f"- bf16 MFMA work issued: 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 = {fl / 1e12:.3f} TFLOP "
