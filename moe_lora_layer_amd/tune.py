@@ -42,7 +42,7 @@ DENSE_KEYS = ["tokens", "in_features", "out_features", "adapters", "rank", "dtyp
 
 # values tried per field (gemm_rows and gemm_form move together)
 GEMM_SHAPES = [(32, 1), (64, 1), (128, 1), (128, 2), (256, 2)]
-SPLITS = [1, 2, 4, 8, 16]
+SPLITS = [1, 2, 3, 4, 5, 6, 8, 12, 16]
 
 
 def _key(d) -> tuple:
