@@ -117,7 +117,9 @@ typedef struct moelora_dims {
  * MOELORA_FLAG_DETERMINISTIC: every split-K reduction (the LoRA shrinks, and
  * the base GEMMs when their K is split because the output is narrow) writes
  * one fp32 partial per split to the forward workspace and a separate pass sums
- * the partials in split order, instead of relaxed fp32 atomics.  The output is
+ * the partials in split order, instead of relaxed fp32 atomics; and the
+ * 256-row down GEMM gives up its stream-K pass (the last, partial round of
+ * tiles cut into K ranges whose parts are added with atomics).  The output is
  * then bit-identical from run to run for the same inputs and dims (without the
  * flag the atomics' order varies, within the layer's tolerance).  The forward
  * workspace grows by the partials (moelora_forward_workspace_size accounts for
