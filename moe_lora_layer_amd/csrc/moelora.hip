@@ -170,12 +170,28 @@ moelora_dims dense_as_layer(const moelora_dense_dims* d) {
 }
 
 // the dense dims as layer dims, checked (the projection is planned as the
-// layer's down GEMM, so a gate_up split count is refused)
+// layer's down GEMM, so a gate_up split count is refused).  Automatic tiles of
+// the projection: when its rows would get the 128-row weight-streaming tiles
+// and those tiles fall short of one round of the MI355X's 256 CUs, the
+// four-wave weight-reuse tiles split over K into about one round instead (q/k/v
+// projection 128 x 8192 -> 10240: 74 against 97 us per call).
 int dense_check(const moelora_dense_dims* d, moelora_dims* m) {
   if (d == nullptr) return MOELORA_ERR_NULL;
   *m = dense_as_layer(d);
   if (d->plan.ksplit_gate_up != 0) return MOELORA_ERR_UNSUPPORTED;
-  return check_dims(m);
+  const int rc = check_dims(m);
+  if (rc != MOELORA_OK) return rc;
+  moelora_plan& p = m->plan;
+  const int64_t want = (d->tokens * 5 + 3) / 4;  // the layer's automatic rule, one expert
+  if (p.gemm_rows == 0 && p.gemm_form == 0 && p.ksplit_down == 0 && want > 64 && want <= 256) {
+    const int64_t tiles = ((d->tokens + 127) / 128) * ((d->out_features + 127) / 128);
+    if (tiles < 256) {
+      p.gemm_rows = 128;
+      p.gemm_form = 2;
+      p.ksplit_down = static_cast<int32_t>(std::max<int64_t>(1, (256 + tiles / 2) / tiles));
+    }
+  }
+  return MOELORA_OK;
 }
 
 // the resolved plan in the ABI's terms
