@@ -230,6 +230,21 @@ def test_dense_plan():
                                                       plan=dict(ksplit_down=1)))["ksplit_down"] == 1
 
 
+def test_dense_automatic_plan_fills_one_round():
+    # 128 rows: the 128-row weight-streaming tiles would make 80 workgroups for
+    # 10240 outputs; the automatic plan takes weight-reuse tiles split over K
+    # into about one round of 256 instead (3 splits), and keeps the streaming
+    # tiles when they fill a round by themselves (65536 outputs: 512 tiles)
+    p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16"))
+    assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 2, 3)
+    p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 65536, 16, 16, "bf16"))
+    assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 1, 1)
+    # decode-sized rows keep their own tiles; an explicit field is respected
+    assert ops.dense_forward_plan(ops.make_dense_dims(16, 8192, 10240, 16, 16, "bf16"))["gemm_rows"] == 32
+    p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16", plan=dict(gemm_form=1)))
+    assert p["gemm_form"] == 1
+
+
 def test_plan_table_round_trip(tmp_path):
     from moe_lora_layer_amd import tune
     d = good_dims()
