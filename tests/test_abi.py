@@ -241,8 +241,9 @@ def test_dense_automatic_plan_fills_one_round():
     assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 1, 1)
     # decode-sized rows keep their own tiles; an explicit field is respected
     assert ops.dense_forward_plan(ops.make_dense_dims(16, 8192, 10240, 16, 16, "bf16"))["gemm_rows"] == 32
-    p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16", plan=dict(gemm_form=1)))
-    assert p["gemm_form"] == 1
+    p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16",
+                                                   plan=dict(gemm_rows=128, gemm_form=1)))
+    assert p["gemm_form"] == 1 and p["ksplit_down"] > 3  # the streaming rule: ~512 workgroups
 
 
 def test_plan_table_round_trip(tmp_path):
