@@ -9,8 +9,10 @@ go to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Default workload: decode_h4096 (64 tokens, h 4096, I 11008, 16 experts top-2,
-8 adapters rank 32, bf16).  Kernel durations come from HIP events that the
+Default workload: prefill_h4096 (4096 tokens as 8 requests of 512, h 4096,
+I 11008, 16 experts top-2 with a per-expert logit bias, 8 adapters rank 32,
+bf16), the largest configuration, where the base grouped GEMMs are bound by the
+matrix cores.  Kernel durations come from HIP events that the
 library records on the launch stream around its kernels
 (moelora_forward_profiled): an untimed pass records every stage boundary for
 the per-stage breakdown; the timed K steps record only the two events around
@@ -39,6 +41,18 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA bf16; fp32 (vec
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def stage_work(cfg, offsets, fusion):
@@ -139,7 +153,7 @@ def run_dense(args, cfg) -> int:
             reps += 1
         tcpu = time.perf_counter() - tc
         cpu = {"value": round(reps * n / tcpu, 3), "unit": "tokens/s", "cores": oracle.max_threads(),
-               "kind": "oracle",
+               "kind": "oracle", "cpu": cpu_model(), "host_cpus": os.cpu_count(),
                "sample": f"{reps} passes over {n} of {T} tokens, fp64 C oracle, {tcpu:.1f} s wall"}
     log(f"[bench] {cfg.name}: {value:.1f} tokens/s, call {call_ms * 1e3:.1f} us, "
         f"{roof['achieved']:.0f} GB/s")
@@ -162,7 +176,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_h4096",
+    ap.add_argument("--workload", default="prefill_h4096",
                     choices=synth.WORKLOAD_ORDER + list(synth.DENSE_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true",
@@ -225,7 +239,7 @@ def main() -> int:
     def step(evs=None):
         ids, w, ss, off, _ = ops.align(d, logits, adapter_ids, out=layer.routing,
                                        workspace_buf=layer.ws_align, status=layer.status)
-        return ops.forward(d, x, *[W[n] for n in names], w, ss, off, out=layer.out,
+        return ops.forward(d, x, *[W[n] for n in names], w, ss, off, topk_ids=ids, out=layer.out,
                            workspace_buf=layer.ws_fwd, stage_events=evs)
 
     for _ in range(args.warmup):
@@ -317,6 +331,15 @@ def main() -> int:
     roof["algorithmic_bytes"] = by
     roof["kernel"] = dom
     roof["kernel_us"] = round(dom_s * 1e6, 2)
+    # the two base grouped GEMMs together (gate_up and down, each with its fused
+    # LoRA expand when fused) against the bf16 matrix-core peak
+    gemm_us = (mean_ms[ops.STAGES.index("gemm_gate_up")] + mean_ms[ops.STAGES.index("gemm_down")]) * 1e3
+    gemm_fl = work["gemm_gate_up"][1] + work["gemm_down"][1]
+    base_fl = 2 * cfg.tokens * cfg.top_k * cfg.hidden * cfg.intermediate * 3
+    gemms = {"us": round(gemm_us, 2), "flops": gemm_fl, "TFLOP/s": round(gemm_fl / gemm_us / 1e6, 2),
+             "frac": round(gemm_fl / gemm_us / 1e6 / peak_f, 4),
+             "us_at_half_peak": round(base_fl / (0.5 * peak_f * 1e12) * 1e6, 2)}
+    log(f"[bench] base GEMMs (gate_up + down): {gemms}")
     log(f"[bench] latency per step (us): warm {lat_warm}, cold {lat_cold}")
     log(f"[bench] {cfg.name}: {value:.1f} tokens/s, {ms_per_step:.3f} ms/step, "
         f"sum of stages {mean_ms.sum():.3f} ms, active experts {Eact}, active buckets {P}")
@@ -336,6 +359,7 @@ def main() -> int:
             reps += 1
         tcpu = time.perf_counter() - tc
         cpu = {"value": round(reps * n / tcpu, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "cpu": cpu_model(), "host_cpus": os.cpu_count(),
                "sample": f"{reps} passes over {n} of {cfg.tokens} tokens (routing and permutation of "
                          f"all {cfg.tokens} each pass), fp64 C oracle, {tcpu:.1f} s wall"}
         log(f"[bench] cpu oracle: {reps} x {n} tokens in {tcpu:.1f}s on {threads} threads")
@@ -350,7 +374,9 @@ def main() -> int:
                    "adapters": cfg.adapters, "rank": cfg.rank, "requests": cfg.requests,
                    "adapter_dist": cfg.adapter_dist, "parallelism": "single GPU"},
         "roofline": roof,
+        "value_cold_p50": round(cfg.tokens / (lat_cold["p50"] * 1e-6), 2),
         "latency_us": {"warm": lat_warm, "cold_1GiB_read_flush": lat_cold},
+        "gemms": gemms,
         "fusion": fusion,
         "plan": plan,
         "plan_source": plan_source,

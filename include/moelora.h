@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOELORA_ABI_VERSION 6
+#define MOELORA_ABI_VERSION 7
 
 typedef enum moelora_status {
   MOELORA_OK = 0,
@@ -97,7 +97,7 @@ typedef struct moelora_plan {
  * Layer dimensions.  Limits (checked, MOELORA_ERR_DIMS / _UNSUPPORTED otherwise):
  *   tokens T >= 0 (T == 0 is a no-op), T * top_k < 2^31
  *   hidden h and intermediate I: positive multiples of 64
- *   experts E >= 1, 1 <= top_k <= min(E, 8), adapters L >= 1, E * L <= 8192
+ *   experts E >= 1, 1 <= top_k <= min(E, 8), adapters L >= 1, E * L <= 65536
  *   rank r in {16, 32, 64}
  */
 typedef struct moelora_dims {
@@ -133,7 +133,7 @@ typedef struct moelora_dims {
  * reading taken is that such a token has no LoRA term in either projection,
  * exactly as if its B were zero).  Every expert then has Lb = L + 1 buckets,
  * its base-only slots in the last one: bucket_offsets has E * (L + 1) + 1
- * entries (E * L + 1 without the flag), and E * Lb must stay <= 8192.
+ * entries (E * L + 1 without the flag); E * L <= 65536 still holds.
  */
 #define MOELORA_FLAG_BASE_ONLY 2
 
@@ -233,6 +233,12 @@ int moelora_forward_workspace_size(const moelora_dims* dims, size_t* bytes);
  *   b_gate_up  in  [L][E][2I][r]   (B_gu^T)
  *   a_down     in  [L][E][r][I]    (A_dn^T)
  *   b_down     in  [L][E][h][r]    (B_dn^T)
+ *   topk_ids   in  int32 [T][k] as produced by moelora_align (or the caller's own
+ *              ids given to moelora_align_topk), or NULL: the ids the
+ *              permutation was built from.  No kernel reads them: every
+ *              sorted row takes the expert (and adapter) of its bucket in
+ *              bucket_offsets.  Passing align's outputs unchanged is the
+ *              intended use.
  *   topk_weights, sorted_slots, bucket_offsets: as produced by moelora_align
  *              (any stable bucketed permutation of the same keys is valid)
  *   out        out [T][h], fully overwritten
@@ -242,9 +248,10 @@ int moelora_forward_workspace_size(const moelora_dims* dims, size_t* bytes);
  */
 int moelora_forward(const moelora_dims* dims, const void* x, const void* w_gate_up,
                     const void* w_down, const void* a_gate_up, const void* b_gate_up,
-                    const void* a_down, const void* b_down, const float* topk_weights,
-                    const int32_t* sorted_slots, const int32_t* bucket_offsets, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                    const void* a_down, const void* b_down, const int32_t* topk_ids,
+                    const float* topk_weights, const int32_t* sorted_slots,
+                    const int32_t* bucket_offsets, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /*
  * Stages of moelora_forward, in launch order (one kernel each).
@@ -277,20 +284,24 @@ enum moelora_stage {
  */
 int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void* w_gate_up,
                              const void* w_down, const void* a_gate_up, const void* b_gate_up,
-                             const void* a_down, const void* b_down, const float* topk_weights,
-                             const int32_t* sorted_slots, const int32_t* bucket_offsets,
-                             void* out, void* workspace, size_t workspace_bytes, void* stream,
-                             void* const* stage_events);
+                             const void* a_down, const void* b_down, const int32_t* topk_ids,
+                             const float* topk_weights, const int32_t* sorted_slots,
+                             const int32_t* bucket_offsets, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream, void* const* stage_events);
 
 /*
  * Debug aid for layer-by-layer reconciliation: byte offsets, inside the forward
  * workspace, of the intermediates left there by moelora_forward, all indexed by
  * sorted position p (row p belongs to slot sorted_slots[p]):
  *   offsets[0]  G   float [T*k][2I]  gate_up base output xW (before the LoRA add);
- *                                    not written when the gate_up GEMM fuses the
- *                                    expand (moelora_forward_fusion; never with
- *                                    MOELORA_FLAG_UNFUSED)
- *   offsets[1]  Z1  float [T*k][r]   gate_up shrink xA
+ *                                    when the gate_up GEMM fuses the expand
+ *                                    (moelora_forward_fusion; never with
+ *                                    MOELORA_FLAG_UNFUSED) G is neither written
+ *                                    nor given any workspace bytes
+ *   offsets[1]  Z1  float [T*k][r]   gate_up shrink xA (the rows of base-only
+ *                                    slots, MOELORA_FLAG_BASE_ONLY, are
+ *                                    unspecified, as are those of Z2: no LoRA
+ *                                    term reads them)
  *   offsets[2]  ACT dtype [T*k][I]   SiLU(gate) * up, including both LoRA terms
  *   offsets[3]  Z2  float [T*k][r]   down shrink a A
  *   offsets[4]  D   float [T*k][h]   down output including its LoRA term

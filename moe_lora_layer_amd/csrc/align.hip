@@ -26,6 +26,8 @@
 // device_status: 0 ok, 1 an adapter id outside [0, L), 2 internal
 // inconsistency, 3 a given expert id outside [0, E) (the largest code wins).
 // No step depends on atomic ordering, so the result is bit-exact and stable.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -37,7 +39,7 @@ constexpr int kMaxTopK = 8;
 // KEYS_LDS: the per-slot keys and ranks live in LDS after the counters (small
 // batches); otherwise in the workspace.
 // Set in a routed key whose token had an adapter id outside [0, L) (keys stay
-// below 2^13 by the bucket limit).
+// below 2^18 by the bucket limit).
 constexpr int kKeyBadAdapter = 1 << 30;
 
 // Routing.  A segment of W lanes (the smallest power of two >= E, at most 64)
@@ -62,11 +64,14 @@ k_route(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
   const int t = (blockIdx.x * kRouteWaves + wave) * (kWave / W) + seg;
   const bool tok = t < T;
   const float* lg = logits + static_cast<int64_t>(tok ? t : 0) * E;
+  // a NaN logit ranks as -infinity (below every number), so every token still
+  // gets k distinct experts in range
+  auto rank_value = [](float v) { return v != v ? -INFINITY : v; };
   float lv[kRouteCached];
 #pragma unroll
   for (int j = 0; j < kRouteCached; ++j) {
     const int e = sl + W * j;
-    lv[j] = (tok && e < E) ? lg[e] : -INFINITY;
+    lv[j] = (tok && e < E) ? rank_value(lg[e]) : -INFINITY;
   }
   float win_v[KMAX];
   int win_id[KMAX];
@@ -91,7 +96,7 @@ k_route(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
       const int e = sl + W * j;
       if (e < E) consider(lv[j], e);
     }
-    for (int e = sl + W * kRouteCached; tok && e < E; e += W) consider(lg[e], e);  // E > 256
+    for (int e = sl + W * kRouteCached; tok && e < E; e += W) consider(rank_value(lg[e]), e);  // E > 256
     // segmented arg-max over aligned groups of W lanes
     for (int d = 1; d < W; d <<= 1) {
       const float ov = __shfl_xor(bv, d, kWave);
@@ -132,13 +137,15 @@ k_route(const float* __restrict__ logits, const int32_t* __restrict__ adapter_id
   }
 }
 
-template <bool KEYS_LDS, bool ROUTED>
+// CNT_LDS: the per-chunk bucket counters live in LDS (up to kAlignLdsInts of
+// them); otherwise (very many buckets) in the workspace, updated with atomics.
+template <bool KEYS_LDS, bool ROUTED, bool CNT_LDS>
 __global__ void __launch_bounds__(kAlignThreads)
 k_align(const int32_t* __restrict__ ids_in, const int32_t* __restrict__ adapter_ids, int T, int E,
         int k, int L, int Lb, int chunks, int32_t* __restrict__ sorted_slots,
         int32_t* __restrict__ offsets, int32_t* __restrict__ status, int32_t* __restrict__ ws_key,
-        int32_t* __restrict__ ws_rank) {
-  extern __shared__ int cnt[];  // [chunks][nb], then (KEYS_LDS) key[S], rank[S]
+        int32_t* __restrict__ ws_rank, int32_t* __restrict__ ws_cnt) {
+  extern __shared__ int lds[];  // (CNT_LDS) cnt[chunks][nb], then (KEYS_LDS) key[S], rank[S]
   __shared__ int wave_tmp[16];
   __shared__ int bad;
 
@@ -148,8 +155,10 @@ k_align(const int32_t* __restrict__ ids_in, const int32_t* __restrict__ adapter_
   const int nb = E * Lb;
   const int S = T * k;
 
-  int* key_buf = KEYS_LDS ? cnt + chunks * nb : ws_key;
-  int* rank_buf = KEYS_LDS ? cnt + chunks * nb + S : ws_rank;
+  int* cnt = CNT_LDS ? lds : ws_cnt;
+  int* const keys_base = CNT_LDS ? lds + chunks * nb : lds;
+  int* key_buf = KEYS_LDS ? keys_base : ws_key;
+  int* rank_buf = KEYS_LDS ? keys_base + S : ws_rank;
   for (int i = tid; i < chunks * nb; i += kAlignThreads) cnt[i] = 0;
   if (tid == 0) bad = 0;
   __syncthreads();
@@ -162,6 +171,10 @@ k_align(const int32_t* __restrict__ ids_in, const int32_t* __restrict__ adapter_
       if (key & kKeyBadAdapter) {
         atomicMax(&bad, 1);
         key &= ~kKeyBadAdapter;
+      }
+      if (key < 0 || key >= nb) {  // cannot happen for routed keys; never index with it
+        atomicMax(&bad, 2);
+        key = 0;
       }
       key_buf[s] = key;
     }
@@ -203,7 +216,7 @@ k_align(const int32_t* __restrict__ ids_in, const int32_t* __restrict__ adapter_
       const int s = base + lane;
       const bool valid = s < c1;
       const int key = valid ? key_buf[s] : nb;  // invalid lanes sort last
-      // packed (key, lane): keys < 2^24 / 64 by the bucket limit
+      // packed (key, lane): keys <= 2^18 by the bucket limit, far below 2^25
       int v = (key << 6) | lane;
 #pragma unroll
       for (int kk = 2; kk <= kWave; kk <<= 1) {
@@ -228,13 +241,29 @@ k_align(const int32_t* __restrict__ ids_in, const int32_t* __restrict__ adapter_
         if (lane >= d) first = max(first, y);
       }
       const int rank = lane - first;
-      const int before = skey < nb ? my_cnt[skey] : 0;
+      int before;
+      if (CNT_LDS) {
+        before = skey < nb ? my_cnt[skey] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (tail && skey < nb) my_cnt[skey] = before + rank + 1;
+        __builtin_amdgcn_wave_barrier();
+      } else {
+        // counters in global memory: the key's last lane adds the key's count
+        // with one returning atomic, and every lane of the key takes the old
+        // value from that lane (the nearest tail at or after it)
+        int old = 0;
+        if (tail && skey < nb) old = atomicAdd(my_cnt + skey, rank + 1);
+        int last = tail ? lane : kWave;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+          const int y = __shfl_down(last, d, kWave);
+          if (lane + d < kWave) last = min(last, y);
+        }
+        before = __shfl(old, last, kWave);
+      }
       // back to the slot's own lane
       const int r_src = __builtin_amdgcn_ds_permute(src << 2, before + rank);
       if (valid) rank_buf[s] = r_src;
-      __builtin_amdgcn_wave_barrier();
-      if (tail && skey < nb) my_cnt[skey] = before + rank + 1;
-      __builtin_amdgcn_wave_barrier();
     }
   }
   __syncthreads();
@@ -272,27 +301,36 @@ k_align(const int32_t* __restrict__ ids_in, const int32_t* __restrict__ adapter_
   if (tid == 0 && status != nullptr) *status = bad;
 }
 
-// Per-slot keys and ranks go to LDS when they fit beside at least one
-// chunk of counters.
-static bool keys_in_lds(int S, int nb) { return 2ll * S + nb <= kAlignLdsInts; }
-
-int align_chunks(int nb, int S) {
-  const int budget = keys_in_lds(S, nb) ? kAlignLdsInts - 2 * S : kAlignLdsInts;
-  int c = budget / nb;
-  if (c > 16) c = 16;
-  if (c < 1) c = 1;
-  return c;
+AlignLayout align_layout(int nb, int S) {
+  AlignLayout a;
+  a.cnt_lds = nb <= kAlignLdsInts;
+  if (a.cnt_lds) {
+    // keys and ranks go to LDS when they fit beside at least one chunk of counters
+    a.keys_lds = 2ll * S + nb <= kAlignLdsInts;
+    const int budget = a.keys_lds ? kAlignLdsInts - 2 * S : kAlignLdsInts;
+    a.chunks = std::max(1, std::min(16, budget / nb));
+    a.cnt_ints = 0;
+  } else {
+    // more buckets than LDS holds counters: counters in the workspace, one
+    // chunk per 1024 slots (every chunk's counters are cleared by the kernel)
+    a.keys_lds = 2ll * S <= kAlignLdsInts;
+    a.chunks = std::max(1, std::min(16, S / 1024));
+    a.cnt_ints = static_cast<int64_t>(a.chunks) * nb;
+  }
+  return a;
 }
 
 hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_t* adapter_ids,
                         int T, int E, int k, int L, int Lb, int32_t* topk_ids, float* topk_w,
                         int32_t* sorted_slots, int32_t* offsets, int32_t* status, int32_t* ws_key,
-                        int32_t* ws_rank, hipStream_t stream) {
+                        int32_t* ws_rank, int32_t* ws_cnt, hipStream_t stream) {
   const int nb = E * Lb;
   const int S = T * k;
-  const int chunks = align_chunks(nb, S);
-  const bool in_lds = keys_in_lds(S, nb);
-  const size_t lds = (static_cast<size_t>(chunks) * nb + (in_lds ? 2 * S : 0)) * sizeof(int);
+  const AlignLayout al = align_layout(nb, S);
+  const int chunks = al.chunks;
+  const bool in_lds = al.keys_lds;
+  const size_t lds =
+      ((al.cnt_lds ? static_cast<size_t>(chunks) * nb : 0) + (in_lds ? 2 * S : 0)) * sizeof(int);
   const bool routed = logits != nullptr;
   if (routed && T > 0) {
     int W = 1;
@@ -310,15 +348,19 @@ hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#define MOELORA_ALIGN_LAUNCH(KL, RT)                                                               \
-  hipLaunchKernelGGL((k_align<KL, RT>), dim3(1), dim3(kAlignThreads), lds, stream, ids_in,        \
+#define MOELORA_ALIGN_LAUNCH(KL, RT, CL)                                                           \
+  hipLaunchKernelGGL((k_align<KL, RT, CL>), dim3(1), dim3(kAlignThreads), lds, stream, ids_in,    \
                      adapter_ids, T, E, k, L, Lb, chunks, sorted_slots, offsets, status, ws_key, \
-                     ws_rank)
-  if (in_lds) {
-    if (routed) MOELORA_ALIGN_LAUNCH(true, true); else MOELORA_ALIGN_LAUNCH(true, false);
+                     ws_rank, ws_cnt)
+#define MOELORA_ALIGN_LAUNCH2(KL, CL)                                                              \
+  if (routed) MOELORA_ALIGN_LAUNCH(KL, true, CL); else MOELORA_ALIGN_LAUNCH(KL, false, CL)
+  if (!al.cnt_lds && ws_cnt == nullptr) return hipErrorInvalidValue;
+  if (al.cnt_lds) {
+    if (in_lds) { MOELORA_ALIGN_LAUNCH2(true, true); } else { MOELORA_ALIGN_LAUNCH2(false, true); }
   } else {
-    if (routed) MOELORA_ALIGN_LAUNCH(false, true); else MOELORA_ALIGN_LAUNCH(false, false);
+    if (in_lds) { MOELORA_ALIGN_LAUNCH2(true, false); } else { MOELORA_ALIGN_LAUNCH2(false, false); }
   }
+#undef MOELORA_ALIGN_LAUNCH2
 #undef MOELORA_ALIGN_LAUNCH
   return hipGetLastError();
 }

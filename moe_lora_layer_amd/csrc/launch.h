@@ -13,16 +13,26 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 // when they fit, the per-slot keys and ranks (144 KiB of the 160 KiB a gfx950
 // workgroup may use).
 constexpr int kAlignLdsInts = 36864;
-int align_chunks(int nb, int S);
+// Where the align kernel keeps its per-chunk bucket counters and per-slot
+// keys and ranks for nb buckets and S slots; cnt_ints = counters it needs in
+// the workspace (0 when they live in LDS).
+struct AlignLayout {
+  bool cnt_lds, keys_lds;
+  int chunks;
+  int64_t cnt_ints;
+};
+AlignLayout align_layout(int nb, int S);
 
 // logits == nullptr: the expert ids come from ids_in (no routing, topk_ids and
 // topk_w untouched); ids_in == nullptr too: every slot goes to expert 0.
 // L adapters; Lb buckets per expert (L, or L + 1 when adapter id -1 marks a
 // base-only token, keyed to bucket L of its expert).
+// ws_key and ws_rank hold S ints each; ws_cnt align_layout(E * Lb, T * k).cnt_ints
+// (may be nullptr when that is 0).
 hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_t* adapter_ids,
                         int T, int E, int k, int L, int Lb, int32_t* topk_ids, float* topk_w,
                         int32_t* sorted_slots, int32_t* offsets, int32_t* status, int32_t* ws_key,
-                        int32_t* ws_rank, hipStream_t stream);
+                        int32_t* ws_rank, int32_t* ws_cnt, hipStream_t stream);
 
 // Tile descriptor: x = expert (M-tiles) or bucket (LoRA tiles), y = first
 // sorted row, z = end row (exclusive), w unused.

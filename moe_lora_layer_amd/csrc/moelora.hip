@@ -13,6 +13,7 @@ using moelora::TilePlan;
 namespace {
 
 constexpr size_t kSectionAlign = 256;
+constexpr int64_t kMaxExpertAdapters = 65536;  // E * L
 constexpr int64_t kMaxGrid = (1ll << 31) - 1;
 
 size_t round_up(size_t x) { return (x + kSectionAlign - 1) / kSectionAlign * kSectionAlign; }
@@ -52,7 +53,10 @@ int check_dims(const moelora_dims* d) {
   if (d->experts < 1 || d->adapters < 1 || d->top_k < 1 || d->top_k > 8 ||
       d->top_k > d->experts)
     return MOELORA_ERR_DIMS;
-  if (static_cast<int64_t>(d->experts) * buckets_per_expert(d) > 8192) return MOELORA_ERR_DIMS;
+  // E * L <= 65536 adapters x experts (plus one base-only bucket per expert)
+  if (static_cast<int64_t>(d->experts) * d->adapters > kMaxExpertAdapters ||
+      static_cast<int64_t>(d->experts) * buckets_per_expert(d) > 2 * kMaxExpertAdapters)
+    return MOELORA_ERR_DIMS;
   if (d->tokens * d->top_k >= (1ll << 31)) return MOELORA_ERR_DIMS;
   return check_plan(d->plan);
 }
@@ -130,7 +134,8 @@ ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
   L.etiles = off; off += round_up((static_cast<size_t>(d->experts) + 1) * 4);
   L.mtiles = off; off += round_up(static_cast<size_t>(plan.max_mt) * 16);
   L.ltiles = off; off += round_up(static_cast<size_t>(plan.max_lt) * 16);
-  L.g = off;      off += round_up(S * 2 * I * 4);
+  // G is written only when the gate_up expand runs as a kernel of its own
+  L.g = off;      off += plan.fuse_gu ? 0 : round_up(S * 2 * I * 4);
   L.act = off;    off += round_up(S * I * esz);
   L.z1 = off;     // Z1, Z2 and D are adjacent: one fill clears Z1 and Z2, and D
   L.z2 = off + S * r * 4;  // too when the down GEMM accumulates with atomics
@@ -174,7 +179,8 @@ moelora_dims dense_as_layer(const moelora_dense_dims* d) {
 // the projection: when its rows would get the 128-row weight-streaming tiles
 // and those tiles fall short of one round of the MI355X's 256 CUs, the
 // four-wave weight-reuse tiles split over K into about one round instead (q/k/v
-// projection 128 x 8192 -> 10240: 74 against 97 us per call).
+// projection 128 x 8192 -> 10240: 76-80 against 97-100 us per call), with at
+// least 8 K-steps per split as in the layer's own rule.
 int dense_check(const moelora_dense_dims* d, moelora_dims* m) {
   if (d == nullptr) return MOELORA_ERR_NULL;
   *m = dense_as_layer(d);
@@ -188,7 +194,9 @@ int dense_check(const moelora_dense_dims* d, moelora_dims* m) {
     if (tiles < 256) {
       p.gemm_rows = 128;
       p.gemm_form = 2;
-      p.ksplit_down = static_cast<int32_t>(std::max<int64_t>(1, (256 + tiles / 2) / tiles));
+      const int64_t steps = d->in_features / (d->dtype == MOELORA_BF16 ? 64 : 32);
+      p.ksplit_down = static_cast<int32_t>(std::max<int64_t>(
+          1, std::min<int64_t>((256 + tiles / 2) / tiles, steps / 8)));
     }
   }
   return MOELORA_OK;
@@ -207,7 +215,7 @@ moelora_plan plan_out(const TilePlan& p) {
 }
 
 struct DenseLayout {
-  size_t key, rank, slots, offsets, pos, counts, etiles, mtiles, ltiles, z, d, parts, total;
+  size_t key, rank, cnt, slots, offsets, pos, counts, etiles, mtiles, ltiles, z, d, parts, total;
 };
 
 DenseLayout dense_layout(const moelora_dims* m, const TilePlan& plan) {
@@ -217,6 +225,8 @@ DenseLayout dense_layout(const moelora_dims* m, const TilePlan& plan) {
   size_t off = 0;
   L.key = off;     off += round_up(T * 4);
   L.rank = off;    off += round_up(T * 4);
+  L.cnt = off;
+  off += round_up(static_cast<size_t>(moelora::align_layout(static_cast<int>(Lb), static_cast<int>(T)).cnt_ints) * 4);
   L.slots = off;   off += round_up(T * 4);
   L.offsets = off; off += round_up((Lb + 1) * 4);
   L.pos = off;     off += round_up(T * 4);
@@ -239,6 +249,27 @@ DenseLayout dense_layout(const moelora_dims* m, const TilePlan& plan) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOELORA_OK : MOELORA_ERR_HIP; }
+
+// Align workspace: per-slot keys and ranks, and the bucket counters when the
+// buckets are too many for LDS.
+struct AlignWs {
+  size_t key, rank, cnt, total;
+};
+
+AlignWs align_ws_for(int64_t nb, int64_t S) {
+  const moelora::AlignLayout al = moelora::align_layout(static_cast<int>(nb), static_cast<int>(S));
+  AlignWs w;
+  w.key = 0;
+  w.rank = round_up(static_cast<size_t>(S) * 4);
+  w.cnt = 2 * w.rank;
+  w.total = w.cnt + round_up(static_cast<size_t>(al.cnt_ints) * 4);
+  return w;
+}
+
+AlignWs align_ws(const moelora_dims* d) {
+  return align_ws_for(static_cast<int64_t>(d->experts) * buckets_per_expert(d),
+                      d->tokens * d->top_k);
+}
 
 }  // namespace
 
@@ -263,8 +294,7 @@ int moelora_align_workspace_size(const moelora_dims* dims, size_t* bytes) {
   const int rc = check_dims(dims);
   if (rc != MOELORA_OK) return rc;
   if (bytes == nullptr) return MOELORA_ERR_NULL;
-  const size_t S = static_cast<size_t>(dims->tokens * dims->top_k);
-  *bytes = 2 * round_up(S * 4);
+  *bytes = align_ws(dims).total;
   return MOELORA_OK;
 }
 
@@ -286,15 +316,14 @@ int moelora_align(const moelora_dims* dims, const float* router_logits,
                         bucket_offsets, workspace};
   for (const void* p : ptrs)
     if (p != nullptr && !aligned16(p)) return MOELORA_ERR_ALIGNMENT;
-  const size_t S = static_cast<size_t>(T * dims->top_k);
-  int32_t* ws_key = static_cast<int32_t*>(workspace);
-  int32_t* ws_rank = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + round_up(S * 4));
-  return hip_status(moelora::launch_align(router_logits, nullptr, adapter_ids,
-                                          static_cast<int>(T), dims->experts, dims->top_k,
-                                          dims->adapters, static_cast<int>(buckets_per_expert(dims)),
-                                          topk_ids, topk_weights, sorted_slots,
-                                          bucket_offsets, device_status, ws_key, ws_rank,
-                                          static_cast<hipStream_t>(stream)));
+  const AlignWs aw = align_ws(dims);
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(moelora::launch_align(
+      router_logits, nullptr, adapter_ids, static_cast<int>(T), dims->experts, dims->top_k,
+      dims->adapters, static_cast<int>(buckets_per_expert(dims)), topk_ids, topk_weights,
+      sorted_slots, bucket_offsets, device_status, reinterpret_cast<int32_t*>(ws + aw.key),
+      reinterpret_cast<int32_t*>(ws + aw.rank), reinterpret_cast<int32_t*>(ws + aw.cnt),
+      static_cast<hipStream_t>(stream)));
 }
 
 int moelora_align_topk(const moelora_dims* dims, const int32_t* topk_ids,
@@ -313,14 +342,14 @@ int moelora_align_topk(const moelora_dims* dims, const int32_t* topk_ids,
   const void* ptrs[] = {topk_ids, adapter_ids, sorted_slots, bucket_offsets, workspace};
   for (const void* p : ptrs)
     if (p != nullptr && !aligned16(p)) return MOELORA_ERR_ALIGNMENT;
-  const size_t S = static_cast<size_t>(T * dims->top_k);
-  int32_t* ws_key = static_cast<int32_t*>(workspace);
-  int32_t* ws_rank = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + round_up(S * 4));
-  return hip_status(moelora::launch_align(nullptr, topk_ids, adapter_ids, static_cast<int>(T),
-                                          dims->experts, dims->top_k, dims->adapters,
-                                          static_cast<int>(buckets_per_expert(dims)), nullptr,
-                                          nullptr, sorted_slots, bucket_offsets, device_status,
-                                          ws_key, ws_rank, static_cast<hipStream_t>(stream)));
+  const AlignWs aw = align_ws(dims);
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(moelora::launch_align(
+      nullptr, topk_ids, adapter_ids, static_cast<int>(T), dims->experts, dims->top_k,
+      dims->adapters, static_cast<int>(buckets_per_expert(dims)), nullptr, nullptr, sorted_slots,
+      bucket_offsets, device_status, reinterpret_cast<int32_t*>(ws + aw.key),
+      reinterpret_cast<int32_t*>(ws + aw.rank), reinterpret_cast<int32_t*>(ws + aw.cnt),
+      static_cast<hipStream_t>(stream)));
 }
 
 int moelora_forward_workspace_size(const moelora_dims* dims, size_t* bytes) {
@@ -376,20 +405,23 @@ int moelora_forward_fusion(const moelora_dims* dims, int* flags) {
 
 int moelora_forward(const moelora_dims* dims, const void* x, const void* w_gate_up,
                     const void* w_down, const void* a_gate_up, const void* b_gate_up,
-                    const void* a_down, const void* b_down, const float* topk_weights,
-                    const int32_t* sorted_slots, const int32_t* bucket_offsets, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    const void* a_down, const void* b_down, const int32_t* topk_ids,
+                    const float* topk_weights, const int32_t* sorted_slots,
+                    const int32_t* bucket_offsets, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   return moelora_forward_profiled(dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down,
-                                  b_down, topk_weights, sorted_slots, bucket_offsets, out,
-                                  workspace, workspace_bytes, stream, nullptr);
+                                  b_down, topk_ids, topk_weights, sorted_slots, bucket_offsets,
+                                  out, workspace, workspace_bytes, stream, nullptr);
 }
 
 int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void* w_gate_up,
                              const void* w_down, const void* a_gate_up, const void* b_gate_up,
-                             const void* a_down, const void* b_down, const float* topk_weights,
-                             const int32_t* sorted_slots, const int32_t* bucket_offsets,
-                             void* out, void* workspace, size_t workspace_bytes, void* stream,
-                             void* const* stage_events) {
+                             const void* a_down, const void* b_down, const int32_t* topk_ids,
+                             const float* topk_weights, const int32_t* sorted_slots,
+                             const int32_t* bucket_offsets, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream, void* const* stage_events) {
+  // every sorted row's expert is that of its bucket: topk_ids is not read
+  (void)topk_ids;
   int rc = check_dims(dims);
   if (rc != MOELORA_OK) return rc;
   const int64_t T = dims->tokens;
@@ -528,6 +560,7 @@ int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const v
   char* ws = static_cast<char*>(workspace);
   int32_t* ws_key = reinterpret_cast<int32_t*>(ws + L.key);
   int32_t* ws_rank = reinterpret_cast<int32_t*>(ws + L.rank);
+  int32_t* ws_cnt = reinterpret_cast<int32_t*>(ws + L.cnt);
   int32_t* slots = reinterpret_cast<int32_t*>(ws + L.slots);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
@@ -543,7 +576,8 @@ int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const v
 
   // tokens bucketed by adapter (one expert, k = 1)
   hipError_t e = moelora::launch_align(nullptr, nullptr, adapter_ids, S, 1, 1, nad, Lb, nullptr,
-                                       nullptr, slots, offsets, device_status, ws_key, ws_rank, st);
+                                       nullptr, slots, offsets, device_status, ws_key, ws_rank,
+                                       ws_cnt, st);
   const int64_t nzero =
       plan.det ? 0 : static_cast<int64_t>(S) * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * N : 0);
   if (e == hipSuccess)

@@ -93,8 +93,8 @@ def library():
         L.moelora_forward_plan.argtypes = [pd, ctypes.POINTER(Plan)]
         L.moelora_align.argtypes = [pd] + [vp] * 8 + [sz, vp]
         L.moelora_align_topk.argtypes = [pd] + [vp] * 6 + [sz, vp]
-        L.moelora_forward.argtypes = [pd] + [vp] * 12 + [sz, vp]
-        L.moelora_forward_profiled.argtypes = [pd] + [vp] * 12 + [sz, vp, vp]
+        L.moelora_forward.argtypes = [pd] + [vp] * 13 + [sz, vp]
+        L.moelora_forward_profiled.argtypes = [pd] + [vp] * 13 + [sz, vp, vp]
         pdd = ctypes.POINTER(DenseDims)
         L.moelora_dense_workspace_size.argtypes = [pdd, ctypes.POINTER(sz)]
         L.moelora_dense_forward.argtypes = [pdd] + [vp] * 8 + [sz, vp]
@@ -261,11 +261,12 @@ def align_topk(d: Dims, topk_ids: torch.Tensor, adapter_ids: torch.Tensor, *, ou
 
 
 def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down, topk_weights,
-            sorted_slots, bucket_offsets, *, out=None, workspace_buf=None, stream=None,
-            stage_events=None):
+            sorted_slots, bucket_offsets, *, topk_ids=None, out=None, workspace_buf=None,
+            stream=None, stage_events=None):
     """moelora_forward (moelora_forward_profiled when stage_events, a list of
     len(STAGES) + 1 recorded-once torch.cuda.Event(enable_timing=True) or None,
-    is given).  Returns out [T][h]."""
+    is given).  topk_ids: align's expert ids, or None (the library does not
+    read them).  Returns out [T][h]."""
     dev = x.device
     T, h, I, E, k, L, r = d.tokens, d.hidden, d.intermediate, d.experts, d.top_k, d.adapters, d.rank
     dt = _TORCH_DT[d.dtype]
@@ -276,6 +277,8 @@ def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
     _expect(b_gate_up, "b_gate_up", (L, E, 2 * I, r), dt, dev)
     _expect(a_down, "a_down", (L, E, r, I), dt, dev)
     _expect(b_down, "b_down", (L, E, h, r), dt, dev)
+    if topk_ids is not None:
+        _expect(topk_ids, "topk_ids", (T, k), torch.int32, dev)
     _expect(topk_weights, "topk_weights", (T, k), torch.float32, dev)
     _expect(sorted_slots, "sorted_slots", (T * k,), torch.int32, dev)
     _expect(bucket_offsets, "bucket_offsets", (buckets(d) + 1,), torch.int32, dev)
@@ -285,9 +288,9 @@ def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
     if workspace_buf is None:
         workspace_buf = workspace(forward_workspace_size(d), dev)
     args = [ctypes.byref(d), _ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(a_gate_up),
-            _ptr(b_gate_up), _ptr(a_down), _ptr(b_down), _ptr(topk_weights), _ptr(sorted_slots),
-            _ptr(bucket_offsets), _ptr(out), _ptr(workspace_buf), workspace_buf.numel(),
-            _stream(stream)]
+            _ptr(b_gate_up), _ptr(a_down), _ptr(b_down), _ptr(topk_ids), _ptr(topk_weights),
+            _ptr(sorted_slots), _ptr(bucket_offsets), _ptr(out), _ptr(workspace_buf),
+            workspace_buf.numel(), _stream(stream)]
     if stage_events is None:
         _check(library().moelora_forward(*args), "moelora_forward")
     else:
@@ -325,7 +328,7 @@ class MoELoRALayer:
                                    workspace_buf=self.ws_align, status=self.status, stream=stream)
         W = self.w
         return forward(self.d, x, W["w_gate_up"], W["w_down"], W["a_gate_up"], W["b_gate_up"],
-                       W["a_down"], W["b_down"], w, ss, off, out=self.out,
+                       W["a_down"], W["b_down"], w, ss, off, topk_ids=ids, out=self.out,
                        workspace_buf=self.ws_fwd, stream=stream)
 
 

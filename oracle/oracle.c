@@ -100,7 +100,11 @@ static double dot(const double* v, const void* M, int64_t off, int64_t n, int dt
  * their softmax probabilities renormalised over the k kept experts.  With
  * m = the largest logit, w_j = exp(l_j - m) / sum_i exp(l_i - m); this is the
  * full softmax restricted to the kept experts and rescaled to sum to one.
+ * A NaN logit (the page never meets one) ranks as -infinity, below every
+ * number, so every token still gets k distinct experts.
  */
+static float rank_value(float v) { return isnan(v) ? -INFINITY : v; }
+
 int oracle_route(int64_t T, int32_t E, int32_t k, const float* logits,
                  int32_t* topk_ids, double* topk_w) {
   if (T < 0 || E < 1 || k < 1 || k > E) return ORC_EARG;
@@ -114,15 +118,15 @@ int oracle_route(int64_t T, int32_t E, int32_t k, const float* logits,
       int32_t best = -1;
       for (int32_t e = 0; e < E; ++e) {
         if (taken[e]) continue;
-        if (best < 0 || lg[e] > lg[best]) best = e;
+        if (best < 0 || rank_value(lg[e]) > rank_value(lg[best])) best = e;
       }
       taken[best] = 1;
       topk_ids[t * k + j] = best;
     }
-    double m = (double)lg[topk_ids[t * k]];
+    double m = (double)rank_value(lg[topk_ids[t * k]]);
     double sum = 0.0;
     for (int32_t j = 0; j < k; ++j) {
-      ex[j] = exp((double)lg[topk_ids[t * k + j]] - m);
+      ex[j] = exp((double)rank_value(lg[topk_ids[t * k + j]]) - m);
       sum += ex[j];
     }
     for (int32_t j = 0; j < k; ++j) topk_w[t * k + j] = ex[j] / sum;
@@ -247,6 +251,10 @@ int oracle_forward(int64_t T, int64_t h, int64_t I, int32_t E, int32_t k, int32_
     if (sel[i] < 0 || sel[i] >= T) return ORC_EARG;
     int32_t l = adapter_ids[sel[i]];
     if (l < -1 || l >= L) return ORC_EADAPTER;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t e = topk_ids[sel[i] * k + j];
+      if (e < 0 || e >= E) return ORC_EARG;  /* an expert id outside [0, E) */
+    }
   }
   int status = ORC_OK;
 #ifdef _OPENMP
@@ -269,8 +277,15 @@ int oracle_forward(int64_t T, int64_t h, int64_t I, int32_t E, int32_t k, int32_
       for (int64_t n = 0; n < h; ++n) o[n] = 0.0;
       for (int32_t j = 0; j < k; ++j) {
         int32_t e = topk_ids[t * k + j];
-        oracle_slot(T, h, I, E, L, r, dtype, x, w_gu, w_dn, a_gu, b_gu, a_dn, b_dn, t, e,
-                    adapter_ids[t], g, z, a, z + r, d);
+        int rc = oracle_slot(T, h, I, E, L, r, dtype, x, w_gu, w_dn, a_gu, b_gu, a_dn, b_dn, t,
+                             e, adapter_ids[t], g, z, a, z + r, d);
+        if (rc != ORC_OK) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+          status = rc;
+          break;
+        }
         double w = topk_w[t * k + j];
         for (int64_t n = 0; n < h; ++n) o[n] += w * d[n];
       }

@@ -102,6 +102,50 @@ def check_route_weights_softmax():
         assert np.all(w1 == 1.0)
 
 
+def check_route_nan_ranks_last():
+    """A NaN router logit ranks below every number (the reading taken for a
+    case the page never meets): ids against a stable argsort of the logits
+    with NaN replaced by -inf; an all-NaN row takes experts 0..k-1; rows
+    without NaN keep their weights."""
+    rng = np.random.default_rng(4)
+    T, E = 24, 8
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[3, :] = np.nan
+    logits[5, 2] = np.nan
+    logits[7, [0, 6]] = np.nan
+    logits[9, :5] = np.nan
+    ranked = np.where(np.isnan(logits), -np.inf, logits)
+    for k in (1, 2, 4, 8):
+        ids, w = oracle.route(logits, k)
+        assert np.array_equal(ids, np.argsort(-ranked, axis=1, kind="stable")[:, :k]), k
+        clean = ~np.isnan(logits).any(axis=1)
+        _, w_ref = oracle.route(np.where(clean[:, None], logits, 0).astype(np.float32), k)
+        assert np.array_equal(w[clean], w_ref[clean]), k
+    ids, _ = oracle.route(logits, 3)
+    assert ids[3].tolist() == [0, 1, 2]
+
+
+def check_forward_rejects_bad_expert_id():
+    """An expert id outside [0, E) is refused, not read as some other expert."""
+    cfg = tiny_cfg()
+    inp = synth.make_inputs(cfg)
+    ids, w = oracle.route(inp["logits"], cfg.top_k)
+    for bad in (-1, cfg.experts):
+        bad_ids = ids.copy()
+        bad_ids[2, 1] = bad
+        try:
+            oracle.forward(inp, oracle.dims_of(cfg), bad_ids, w)
+        except ValueError:
+            continue
+        raise AssertionError(f"expert id {bad} was accepted")
+    # the same id on an unselected token is not looked at
+    bad_ids = ids.copy()
+    bad_ids[2, 1] = cfg.experts
+    sel = np.array([0, 1, 3])
+    assert _rel_err(oracle.forward(inp, oracle.dims_of(cfg), bad_ids, w, tokens=sel),
+                    oracle.forward(inp, oracle.dims_of(cfg), ids, w, tokens=sel)) == 0.0
+
+
 # ----------------------------------------------------------------------------- permutation
 
 def check_align_stable_argsort():
@@ -300,7 +344,8 @@ def check_dense_projection():
         assert np.array_equal(got[base], zb[base])
 
 
-ALL_CHECKS = [check_route_ids_stable_argsort, check_route_weights_softmax, check_align_stable_argsort,
+ALL_CHECKS = [check_route_ids_stable_argsort, check_route_weights_softmax, check_route_nan_ranks_last,
+              check_forward_rejects_bad_expert_id, check_align_stable_argsort,
               check_align_base_only_argsort, check_forward_dense_formulation,
               check_gate_up_integer_exact, check_lora_zero_is_base_moe, check_base_only_is_base_moe,
               check_merged_weight_identity, check_dense_case_torch, check_token_permutation_invariance,

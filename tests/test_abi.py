@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     assert {"moelora_align", "moelora_forward"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moelora_abi_version() == 6
+    assert lib.moelora_abi_version() == 7
 
 
 def test_status_strings():
@@ -49,10 +49,12 @@ def test_status_strings():
     (dict(dtype=7), ERR_UNSUPPORTED), (dict(rank=8), ERR_UNSUPPORTED), (dict(rank=128), ERR_UNSUPPORTED),
     (dict(hidden=100), ERR_DIMS), (dict(intermediate=96), ERR_DIMS), (dict(tokens=-1), ERR_DIMS),
     (dict(top_k=9, experts=16), ERR_DIMS), (dict(top_k=3, experts=2), ERR_DIMS), (dict(experts=0), ERR_DIMS),
-    (dict(adapters=0), ERR_DIMS), (dict(experts=128, adapters=65), ERR_DIMS),
+    (dict(adapters=0), ERR_DIMS), (dict(experts=256, adapters=257), ERR_DIMS),
+    (dict(experts=1, top_k=1, adapters=65537), ERR_DIMS), (dict(experts=1, top_k=1, adapters=65536), OK),
+    (dict(experts=256, adapters=256), OK), (dict(experts=256, adapters=256, flags=2), OK),
     (dict(tokens=1 << 30, top_k=2), ERR_DIMS), (dict(flags=8), ERR_UNSUPPORTED),
     (dict(flags=-1), ERR_UNSUPPORTED), (dict(flags=3), OK), (dict(flags=7), OK),
-    (dict(experts=128, adapters=64), OK), (dict(experts=128, adapters=64, flags=2), ERR_DIMS),
+    (dict(experts=128, adapters=64), OK), (dict(experts=128, adapters=64, flags=2), OK),
 ])
 def test_dims_validation(kw, rc):
     d = good_dims(**kw)
@@ -71,7 +73,11 @@ def test_null_dims_and_outputs():
 
 
 def test_workspace_sizes_and_layout():
-    d = good_dims(tokens=100, hidden=320, intermediate=192, experts=5, top_k=2, adapters=3, rank=32)
+    d = good_dims(tokens=100, hidden=320, intermediate=192, experts=5, top_k=2, adapters=3, rank=32,
+                  unfused=True)
+    fused = good_dims(tokens=100, hidden=320, intermediate=192, experts=5, top_k=2, adapters=3, rank=32)
+    # the fused gate_up GEMM never writes G: the workspace holds no bytes for it
+    assert ops.forward_workspace_size(fused) <= ops.forward_workspace_size(d) - 200 * 2 * 192 * 4
     size = ops.forward_workspace_size(d)
     lay = ops.forward_workspace_layout(d)
     S, I, h, r = 200, 192, 320, 32
@@ -115,7 +121,7 @@ def test_forward_argument_errors():
     d = good_dims()
     fake = 1 << 20
     ws = ops.forward_workspace_size(d)
-    ptrs = [_vp(fake)] * 11
+    ptrs = [_vp(fake)] * 12
     p = list(ptrs); p[3] = None
     assert lib.moelora_forward(ctypes.byref(d), *p, _vp(fake), ws, None) == ERR_NULL
     assert lib.moelora_forward(ctypes.byref(d), *ptrs, _vp(fake), ws - 1, None) == ERR_WORKSPACE
@@ -125,7 +131,10 @@ def test_forward_argument_errors():
     assert lib.moelora_forward(ctypes.byref(d), *ptrs, _vp(fake + 8), ws, None) == ERR_ALIGNMENT
     # T == 0 is a no-op that touches nothing
     z = good_dims(tokens=0)
-    assert lib.moelora_forward(ctypes.byref(z), *([None] * 11), None, 0, None) == OK
+    assert lib.moelora_forward(ctypes.byref(z), *([None] * 12), None, 0, None) == OK
+    # topk_ids (argument 8) may be NULL: not read by any kernel
+    p = list(ptrs); p[7] = None
+    assert lib.moelora_forward(ctypes.byref(d), *p, _vp(fake), ws - 1, None) == ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("kw,flags", [
@@ -244,6 +253,10 @@ def test_dense_automatic_plan_fills_one_round():
     p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16",
                                                    plan=dict(gemm_rows=128, gemm_form=1)))
     assert p["gemm_form"] == 1 and p["ksplit_down"] > 3  # the streaming rule: ~512 workgroups
+    # a narrow output over a short K: the forced split keeps >= 8 K-steps per
+    # split (96 rows, K 2048 = 32 steps, N 128: 4 splits, not 256 / 1)
+    p = ops.dense_forward_plan(ops.make_dense_dims(96, 2048, 128, 4, 16, "bf16"))
+    assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 2, 4)
 
 
 def test_plan_table_round_trip(tmp_path):

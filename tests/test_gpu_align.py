@@ -48,7 +48,10 @@ def _cfg(T, E, k, L, seed=1, **kw):
 
 @pytest.mark.parametrize("T,E,k,L", [(1, 8, 2, 4), (1, 1, 1, 1), (3, 4, 4, 2), (1000, 32, 8, 16),
                                      (5000, 16, 2, 8), (257, 256, 8, 32), (70, 8192, 1, 1),
-                                     (4096, 64, 6, 128), (20000, 2, 2, 3)])
+                                     (4096, 64, 6, 128), (20000, 2, 2, 3),
+                                     # E * L = 65536 buckets, more than LDS holds
+                                     # counters for: counters in the workspace
+                                     (2048, 64, 4, 1024), (300, 256, 2, 256), (9000, 1, 1, 65536)])
 def test_align_shapes(T, E, k, L):
     cfg = _cfg(T, E, k, L)
     say(f"align shape T={T} E={E} k={k} L={L}")
@@ -140,7 +143,8 @@ def test_align_topk_reports_bad_ids():
     assert _topk(cfg, bad_e, bad_l)[2] == 3      # the larger code is reported
 
 
-@pytest.mark.parametrize("T,E,k,L", [(50, 8, 2, 4), (1000, 32, 8, 16), (5000, 16, 2, 8), (300, 64, 4, 1)])
+@pytest.mark.parametrize("T,E,k,L", [(50, 8, 2, 4), (1000, 32, 8, 16), (5000, 16, 2, 8), (300, 64, 4, 1),
+                                     (2000, 256, 2, 256)])
 def test_align_base_only_tokens(T, E, k, L):
     """MOELORA_FLAG_BASE_ONLY: adapter id -1 goes to each expert's extra last
     bucket; routing and permutation equal the oracle's bit for bit, for
@@ -173,3 +177,32 @@ def test_align_minus_one_needs_the_flag():
                                 torch.from_numpy(r["adapter_ids"]).to(dev))
     torch.cuda.synchronize()
     assert int(st[0].item()) == 1 and sorted(ss.cpu().numpy().tolist()) == list(range(40))
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (16, 4), (300, 8)])
+def test_align_nan_logits(E, k):
+    """NaN router logits rank below every number, as in the oracle: an all-NaN
+    row takes experts 0..k-1, a row with some NaN keeps its numeric experts
+    first; every id stays in range, so the other tokens' slots and the whole
+    permutation are bit-exact; weights match on the rows without NaN."""
+    T, L = 96, 4
+    cfg = _cfg(T, E, k, L, seed=E)
+    rinp = synth.make_routing_inputs(cfg)
+    logits = rinp["logits"].copy()
+    logits[0, :] = np.nan
+    logits[17, 1] = np.nan
+    logits[40, : E // 2] = np.nan
+    logits[95, :] = np.nan
+    say(f"align NaN logits E={E} k={k}")
+    dev = device()
+    ids, w, ss, off, st = run_align(cfg, {"logits": torch.from_numpy(logits).to(dev),
+                                          "adapter_ids": torch.from_numpy(rinp["adapter_ids"]).to(dev)})
+    ref_ids, ref_w = oracle.route(logits, k)
+    ref_ss, ref_off = oracle.align(ref_ids, rinp["adapter_ids"], E, L)
+    assert int(st[0].item()) == 0
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert ref_ids[0].tolist() == list(range(k))
+    assert np.array_equal(ss.cpu().numpy(), ref_ss)
+    assert np.array_equal(off.cpu().numpy(), ref_off)
+    clean = ~np.isnan(logits).any(axis=1)
+    assert np.max(np.abs(w.cpu().numpy()[clean].astype(np.float64) - ref_w[clean])) <= 1e-6

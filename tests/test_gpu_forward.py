@@ -81,6 +81,8 @@ SMALL = [
     # (tile, K chunk) items, h = 1088 ends in a half chunk
     STREAM_SHAPE,
     *STREAM_SHAPES_R32_R16,
+    # E * L = 65536 (expert, adapter) buckets, the largest the layer takes
+    (300, 64, 64, 16, 2, 4096, 16, "bf16"),
 ]
 
 

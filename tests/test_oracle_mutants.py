@@ -14,7 +14,8 @@ MUTANTS = {
     "lora_term_dropped": ("? base + dot(z, Bt, b_off + n * r, r, dtype) : base", "? base : base"),
     "silu_sign": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
     "gate_up_swapped": ("a[i] = silu(g[i]) * g[I + i];", "a[i] = silu(g[I + i]) * g[i];"),
-    "tie_to_higher_id": ("lg[e] > lg[best]", "lg[e] >= lg[best]"),
+    "tie_to_higher_id": ("rank_value(lg[e]) > rank_value(lg[best])", "rank_value(lg[e]) >= rank_value(lg[best])"),
+    "nan_not_ranked_last": ("return isnan(v) ? -INFINITY : v;", "return v;"),
     "b_stride": ("b_off + n * r", "b_off + n"),
     "w_stride": ("w_off + n * K", "w_off + n"),
     "adapter_expert_index": ("(int64_t)(l < 0 ? 0 : l) * E + e;", "(int64_t)e * L + (l < 0 ? 0 : l);"),
