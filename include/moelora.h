@@ -28,7 +28,8 @@
  *     device memory.  The caller keeps every buffer alive until the stream has
  *     executed the work.  Calls are reentrant; concurrent calls need distinct
  *     outputs and workspaces.
- *   - Inputs are never written.  The library keeps no state between calls.
+ *   - Inputs are never written.  The library keeps no state between calls,
+ *     except the static scratch of moelora_forward_noalloc (see there).
  *   - Errors are returned as a moelora_status code before anything is
  *     enqueued (argument errors) or right after the launches (MOELORA_ERR_HIP).
  *     No C++ exception crosses this boundary.
@@ -52,7 +53,9 @@ typedef enum moelora_status {
   MOELORA_ERR_UNSUPPORTED = 3,  /* dtype or rank not supported                           */
   MOELORA_ERR_ALIGNMENT = 4,    /* a tensor pointer is not 16-byte aligned               */
   MOELORA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than *_workspace_size       */
-  MOELORA_ERR_HIP = 6           /* the HIP runtime reported an error at launch           */
+  MOELORA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch           */
+  MOELORA_ERR_TOO_LARGE = 7     /* moelora_forward_noalloc: the call needs more than its
+                                   static scratch (MOELORA_NOALLOC_SCRATCH_BYTES)         */
 } moelora_status;
 
 typedef enum moelora_dtype {
@@ -252,6 +255,33 @@ int moelora_forward(const moelora_dims* dims, const void* x, const void* w_gate_
                     const float* topk_weights, const int32_t* sorted_slots,
                     const int32_t* bucket_offsets, void* out, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * moelora_forward_noalloc -- moelora_forward for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The arguments and the result are those of
+ * moelora_forward without the workspace: the call runs in a static device
+ * array of MOELORA_NOALLOC_SCRATCH_BYTES that the library holds, one per GPU
+ * it runs on, from the first call on that GPU until the process ends.  It
+ * calls no hipMalloc, hipFree or other allocating routine.
+ *   - Dims whose moelora_forward_workspace_size exceeds the scratch are refused
+ *     with MOELORA_ERR_TOO_LARGE before anything is enqueued (64 MiB holds every
+ *     decode-sized batch, e.g. 64 tokens at h 4096, I 11008, or 256 tokens at
+ *     h 2880, I 2880 over 32 experts top-4; a 4096-token prefill at h 4096,
+ *     I 11008 needs ~0.35 GiB and goes through moelora_forward).
+ *   - Every call on one GPU shares that GPU's scratch and finds in it what the
+ *     previous call left (the kernels clear what must start at zero), so calls
+ *     that overlap on one GPU (other streams, other threads) race: the caller
+ *     serialises them.
+ *   - The first call on a GPU looks up the scratch's device address with
+ *     hipGetSymbolAddress (MOELORA_ERR_HIP if that fails) and keeps it.
+ */
+#define MOELORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moelora_forward_noalloc(const moelora_dims* dims, const void* x, const void* w_gate_up,
+                            const void* w_down, const void* a_gate_up, const void* b_gate_up,
+                            const void* a_down, const void* b_down, const int32_t* topk_ids,
+                            const float* topk_weights, const int32_t* sorted_slots,
+                            const int32_t* bucket_offsets, void* out, void* stream);
 
 /*
  * Stages of moelora_forward, in launch order (one kernel each).

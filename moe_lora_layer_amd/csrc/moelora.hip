@@ -4,9 +4,16 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "launch.h"
 #include "moelora.h"
+
+// Device scratch of moelora_forward_noalloc: one copy per GPU the library runs
+// on, held until the process ends.  Host code never passes the array's name to
+// a kernel or a copy (on the host it is only a stand-in for the symbol): it
+// uses the device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MOELORA_NOALLOC_SCRATCH_BYTES];
 
 using moelora::TilePlan;
 
@@ -250,6 +257,29 @@ DenseLayout dense_layout(const moelora_dims* m, const TilePlan& plan) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOELORA_OK : MOELORA_ERR_HIP; }
 
+// Device address of `scratch` on the current device, looked up once per device
+// (hipGetSymbolAddress with that device current) and kept for later calls.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // Align workspace: per-slot keys and ranks, and the bucket counters when the
 // buckets are too many for LDS.
 struct AlignWs {
@@ -286,6 +316,9 @@ const char* moelora_status_string(int status) {
     case MOELORA_ERR_ALIGNMENT: return "moelora: a tensor pointer is not 16-byte aligned";
     case MOELORA_ERR_WORKSPACE: return "moelora: workspace missing or too small";
     case MOELORA_ERR_HIP: return "moelora: HIP launch error";
+    case MOELORA_ERR_TOO_LARGE:
+      return "moelora: the call needs more workspace than the static scratch of "
+             "moelora_forward_noalloc holds";
     default: return "moelora: unknown status";
   }
 }
@@ -412,6 +445,27 @@ int moelora_forward(const moelora_dims* dims, const void* x, const void* w_gate_
   return moelora_forward_profiled(dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down,
                                   b_down, topk_ids, topk_weights, sorted_slots, bucket_offsets,
                                   out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moelora_forward_noalloc(const moelora_dims* dims, const void* x, const void* w_gate_up,
+                            const void* w_down, const void* a_gate_up, const void* b_gate_up,
+                            const void* a_down, const void* b_down, const int32_t* topk_ids,
+                            const float* topk_weights, const int32_t* sorted_slots,
+                            const int32_t* bucket_offsets, void* out, void* stream) {
+  size_t need = 0;
+  const int rc = moelora_forward_workspace_size(dims, &need);
+  if (rc != MOELORA_OK) return rc;
+  if (dims->tokens == 0) return MOELORA_OK;
+  if (need > MOELORA_NOALLOC_SCRATCH_BYTES) return MOELORA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return MOELORA_ERR_HIP;
+  // the same launch sequence as moelora_forward; every accumulator it needs
+  // cleared is cleared by its own kernels, so whatever the previous call left
+  // in the scratch does not matter
+  return moelora_forward_profiled(dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down,
+                                  b_down, topk_ids, topk_weights, sorted_slots, bucket_offsets,
+                                  out, ws, MOELORA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void* w_gate_up,

@@ -95,6 +95,7 @@ def library():
         L.moelora_align_topk.argtypes = [pd] + [vp] * 6 + [sz, vp]
         L.moelora_forward.argtypes = [pd] + [vp] * 13 + [sz, vp]
         L.moelora_forward_profiled.argtypes = [pd] + [vp] * 13 + [sz, vp, vp]
+        L.moelora_forward_noalloc.argtypes = [pd] + [vp] * 13
         pdd = ctypes.POINTER(DenseDims)
         L.moelora_dense_workspace_size.argtypes = [pdd, ctypes.POINTER(sz)]
         L.moelora_dense_forward.argtypes = [pdd] + [vp] * 8 + [sz, vp]
@@ -102,7 +103,8 @@ def library():
         for f in (L.moelora_align_workspace_size, L.moelora_forward_workspace_size,
                   L.moelora_forward_workspace_layout, L.moelora_forward_fusion,
                   L.moelora_forward_plan, L.moelora_align, L.moelora_align_topk,
-                  L.moelora_forward, L.moelora_forward_profiled, L.moelora_dense_workspace_size,
+                  L.moelora_forward, L.moelora_forward_profiled, L.moelora_forward_noalloc,
+                  L.moelora_dense_workspace_size,
                   L.moelora_dense_forward, L.moelora_dense_forward_plan):
             f.restype = ctypes.c_int
         _lib = L
@@ -301,6 +303,40 @@ def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
             raise ValueError("record every event once before passing it (creates the handle)")
         handles = (ctypes.c_void_p * len(hs))(*hs)
         _check(library().moelora_forward_profiled(*args, handles), "moelora_forward_profiled")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_noalloc(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
+                    topk_weights, sorted_slots, bucket_offsets, *, topk_ids=None, out=None,
+                    stream=None):
+    """moelora_forward_noalloc: moelora_forward in the library's static device
+    scratch (no workspace argument).  out must be given when the caller cannot
+    allocate; with out=None one is allocated here.  Returns out [T][h]."""
+    dev = x.device
+    T, h, I, E, k, L, r = d.tokens, d.hidden, d.intermediate, d.experts, d.top_k, d.adapters, d.rank
+    dt = _TORCH_DT[d.dtype]
+    _expect(x, "x", (T, h), dt, dev)
+    _expect(w_gate_up, "w_gate_up", (E, 2 * I, h), dt, dev)
+    _expect(w_down, "w_down", (E, h, I), dt, dev)
+    _expect(a_gate_up, "a_gate_up", (L, E, r, h), dt, dev)
+    _expect(b_gate_up, "b_gate_up", (L, E, 2 * I, r), dt, dev)
+    _expect(a_down, "a_down", (L, E, r, I), dt, dev)
+    _expect(b_down, "b_down", (L, E, h, r), dt, dev)
+    if topk_ids is not None:
+        _expect(topk_ids, "topk_ids", (T, k), torch.int32, dev)
+    _expect(topk_weights, "topk_weights", (T, k), torch.float32, dev)
+    _expect(sorted_slots, "sorted_slots", (T * k,), torch.int32, dev)
+    _expect(bucket_offsets, "bucket_offsets", (buckets(d) + 1,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((T, h), dtype=dt, device=dev)
+    _expect(out, "out", (T, h), dt, dev)
+    _check(library().moelora_forward_noalloc(
+        ctypes.byref(d), _ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(a_gate_up), _ptr(b_gate_up),
+        _ptr(a_down), _ptr(b_down), _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_slots),
+        _ptr(bucket_offsets), _ptr(out), _stream(stream)), "moelora_forward_noalloc")
     return out
 
 

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for rc in range(7):
+    for rc in range(8):
         s = ops.status_string(rc)
         assert s.startswith("moelora:")
     assert "unknown" in ops.status_string(99)
@@ -290,3 +290,17 @@ def test_plan_table_round_trip(tmp_path):
                                            k["adapters"], k["rank"], k["dtype"], plan=e["plan"])
                 dims.flags = k["flags"]
                 assert ops.dense_forward_plan(dims) == e["plan"]
+
+
+def test_noalloc_refuses_before_touching_the_gpu():
+    """moelora_forward_noalloc checks the dims and the static scratch's size on
+    the host: a batch beyond the scratch (4096-token prefill) is refused with
+    status 7, bad dims with their own status, T == 0 is a no-op."""
+    lib = ops.library()
+    fake = [_vp(1 << 20)] * 12
+    big = good_dims(tokens=4096, hidden=4096, intermediate=11008, experts=16)
+    assert ops.forward_workspace_size(big) > ops.NOALLOC_SCRATCH_BYTES
+    assert lib.moelora_forward_noalloc(ctypes.byref(big), *fake, None) == 7
+    assert lib.moelora_forward_noalloc(ctypes.byref(good_dims(rank=8)), *fake, None) == ERR_UNSUPPORTED
+    assert lib.moelora_forward_noalloc(ctypes.byref(good_dims(tokens=0)), *([None] * 12), None) == OK
+    assert "static scratch" in ops.status_string(7)
