@@ -119,19 +119,57 @@ def test_forward_small_unfused(shape):
     assert_close(to_f64(out), ref, cfg.dtype, "out")
 
 
+def mtile_cover(off, experts, buckets, rows, ss, top_k, toks):
+    """The M-tiles of the base GEMMs (each expert's sorted rows cut into tiles of
+    `rows`, the last one partial) and the fraction of them holding a slot of a
+    token in `toks`; plus one token per tile (the tile's last row), so that a
+    sample can be completed to cover every tile."""
+    have = set(int(t) for t in toks)
+    covered, tiles, extra = 0, 0, []
+    for e in range(experts):
+        r0, r1 = int(off[e * buckets]), int(off[(e + 1) * buckets])
+        for a in range(r0, r1, rows):
+            b = min(r1, a + rows)
+            tiles += 1
+            tile_toks = {int(ss[p]) // top_k for p in range(a, b)}
+            if tile_toks & have:
+                covered += 1
+            extra.append(int(ss[b - 1]) // top_k)
+    return covered, tiles, extra
+
+
 @pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
 def test_forward_workload(name):
+    """Every workload at full size in the benchmark's launch configuration.
+    The compared tokens are a random sample completed so that every M-tile of
+    the base GEMMs (every expert's first and last, partial, tile included;
+    with the 256-row plan also the down GEMM's stream-K tiles, which are M x N
+    tiles of the same M-tiles) holds a compared row: the test asserts 100 %
+    M-tile coverage.  The dense 70B-MLP workload (128 tokens) is compared in
+    full."""
     cfg = synth.WORKLOADS[name]
     say(f"forward workload {name}: generating inputs")
     inp = synth.make_inputs(cfg)
     # the benchmark's launch configuration: the packaged tuned plan, if any
     d, source = tune.with_packaged_plan(ops.dims_for(cfg))
-    say(f"forward workload {name}: running on GPU, plan {ops.forward_plan(d)} ({source})")
+    plan = ops.forward_plan(d)
+    say(f"forward workload {name}: running on GPU, plan {plan} ({source})")
     _, (ids, w, ss, off), out, _ = _layer(cfg, inp, d)
     ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
-    toks = sample_tokens(cfg.tokens, 24 if cfg.tokens > 64 else cfg.tokens)
-    say(f"forward workload {name}: oracle on {len(toks)} tokens")
+    ss_h, off_h = ss.cpu().numpy(), off.cpu().numpy()
+    if name == "dense_h8192":
+        toks = np.arange(cfg.tokens)
+    else:
+        toks = sample_tokens(cfg.tokens, 24 if cfg.tokens > 64 else cfg.tokens)
+        _, _, extra = mtile_cover(off_h, cfg.experts, cfg.adapters, plan["gemm_rows"], ss_h,
+                                  cfg.top_k, toks)
+        toks = np.unique(np.concatenate([toks, np.array(extra, np.int64)]))
+    covered, tiles, _ = mtile_cover(off_h, cfg.experts, cfg.adapters, plan["gemm_rows"], ss_h,
+                                    cfg.top_k, toks)
+    say(f"forward workload {name}: oracle on {len(toks)} tokens, M-tile coverage "
+        f"{covered}/{tiles} ({plan['gemm_rows']}-row tiles)")
+    assert covered == tiles
     ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w, tokens=toks)
     assert_close(to_f64(out)[toks], ref, cfg.dtype, f"{name} out")
 
