@@ -104,11 +104,15 @@ def run_dense(args, cfg) -> int:
     inp = synth.make_dense_inputs(cfg)
     t = lambda a: (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16
                    else torch.from_numpy(a)).to(dev)
-    x, w, a, b = t(inp["x"]), t(inp["w"]), t(inp["a"]), t(inp["b"])
+    if args.in_out:
+        x, w = t(inp["x"]), t(np.ascontiguousarray(inp["w"].T))
+        a, b = (t(np.ascontiguousarray(np.swapaxes(inp[n], 1, 2))) for n in ("a", "b"))
+    else:
+        x, w, a, b = t(inp["x"]), t(inp["w"]), t(inp["a"]), t(inp["b"])
     ad = torch.from_numpy(inp["adapter_ids"]).to(dev)
     from moe_lora_layer_amd import tune
     d = ops.make_dense_dims(cfg.tokens, cfg.in_features, cfg.out_features, cfg.adapters, cfg.rank,
-                            cfg.dtype, deterministic=args.deterministic)
+                            cfg.dtype, deterministic=args.deterministic, in_out=args.in_out)
     plan_source = "automatic"
     if args.plan == "tuned":
         d, plan_source = tune.with_packaged_plan(d)
@@ -185,6 +189,9 @@ def main() -> int:
                     help="tokens in the oracle's timed sample (default 64)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="repeat the oracle's sample for about this long (default 12 s)")
+    ap.add_argument("--in-out", action="store_true",
+                    help="MOELORA_FLAG_IN_OUT: pass every weight h_in x h_out as the page writes "
+                         "it (default: K-contiguous, i.e. transposed)")
     ap.add_argument("--plan", choices=["tuned", "auto"], default="tuned",
                     help="tile plan: the packaged tuned table's entry for the workload when it has "
                          "one (default), or the library's automatic plan")
@@ -216,12 +223,14 @@ def main() -> int:
         return torch.from_numpy(a).to(dev)
 
     names = ["w_gate_up", "w_down", "a_gate_up", "b_gate_up", "a_down", "b_down"]
-    W = {n: dev_t(inp[n]) for n in names}
+    # h_in x h_out weights: the K-contiguous arrays transposed in their last two axes
+    W = {n: dev_t(np.ascontiguousarray(np.swapaxes(inp[n], -1, -2)) if args.in_out else inp[n])
+         for n in names}
     x = dev_t(inp["x"])
     logits = torch.from_numpy(inp["logits"]).to(dev)
     adapter_ids = torch.from_numpy(inp["adapter_ids"]).to(dev)
     from moe_lora_layer_amd import tune
-    d = ops.dims_for(cfg, deterministic=args.deterministic)
+    d = ops.dims_for(cfg, deterministic=args.deterministic, in_out=args.in_out)
     plan_source = "automatic"
     if args.plan == "tuned":
         d, plan_source = tune.with_packaged_plan(d)
@@ -381,6 +390,7 @@ def main() -> int:
         "plan": plan,
         "plan_source": plan_source,
         "deterministic": args.deterministic,
+        "weights": "h_in x h_out" if args.in_out else "K-contiguous",
         "cpu_baseline": cpu,
         "stages": stages,
     }

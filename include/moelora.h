@@ -21,8 +21,10 @@
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers (hipMalloc / torch allocations on the
  *     current device), row-major, contiguous, 16-byte aligned.
- *   - Weights are K-contiguous: each array holds its matrix TRANSPOSED, i.e.
- *     row n of the array is column n of the page's h_in x h_out matrix.
+ *   - Weights are K-contiguous by default: each array holds its matrix
+ *     TRANSPOSED, i.e. row n of the array is column n of the page's h_in x h_out
+ *     matrix.  With MOELORA_FLAG_IN_OUT they are h_in x h_out as the page writes
+ *     them (see there).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     work on it: no host synchronisation, no allocation, no host reads of
  *     device memory.  The caller keeps every buffer alive until the stream has
@@ -149,6 +151,21 @@ typedef struct moelora_dims {
  */
 #define MOELORA_FLAG_UNFUSED 4
 
+/*
+ * MOELORA_FLAG_IN_OUT: every weight is stored as the Multi-LoRA page writes it
+ * (section "Implementing Multi-LoRA inference for MoE models in vLLM": W is
+ * h_in x h_out, A is h_in x r, B is r x h_out), row-major:
+ *   moelora_forward:        w_gate_up [E][h][2I]   w_down [E][I][h]
+ *                           a_gate_up [L][E][h][r] b_gate_up [L][E][r][2I]
+ *                           a_down    [L][E][I][r] b_down    [L][E][r][h]
+ *   moelora_dense_forward:  w [K][N], a [L][K][r], b [L][r][N]
+ * instead of the default K-contiguous (transposed) arrays.  Same result within
+ * the layer's tolerance.  The kernels read these arrays as they are: operands
+ * loaded through registers are transposed across lanes in registers, operands
+ * copied straight into LDS are read with the transposing LDS loads of gfx950.
+ */
+#define MOELORA_FLAG_IN_OUT 8
+
 int moelora_abi_version(void);
 
 /* Static string for a status code (never NULL). */
@@ -236,6 +253,9 @@ int moelora_forward_workspace_size(const moelora_dims* dims, size_t* bytes);
  *   b_gate_up  in  [L][E][2I][r]   (B_gu^T)
  *   a_down     in  [L][E][r][I]    (A_dn^T)
  *   b_down     in  [L][E][h][r]    (B_dn^T)
+ *              (with MOELORA_FLAG_IN_OUT the untransposed matrices:
+ *              [E][h][2I], [E][I][h], [L][E][h][r], [L][E][r][2I],
+ *              [L][E][I][r], [L][E][r][h]; columns [0,I) of W_gu and B_gu gate)
  *   topk_ids   in  int32 [T][k] as produced by moelora_align (or the caller's own
  *              ids given to moelora_align_topk), or NULL: the ids the
  *              permutation was built from.  No kernel reads them: every
@@ -396,9 +416,9 @@ int moelora_dense_forward_plan(const moelora_dense_dims* dims, moelora_plan* pla
 
 /*
  *   x              in  dtype [T][K]
- *   w              in  dtype [N][K]      (W^T rows)
- *   a              in  dtype [L][r][K]   (A^T rows per adapter)
- *   b              in  dtype [L][N][r]   (B^T rows per adapter)
+ *   w              in  dtype [N][K]      (W^T rows; [K][N] with MOELORA_FLAG_IN_OUT)
+ *   a              in  dtype [L][r][K]   (A^T rows per adapter; [L][K][r] with the flag)
+ *   b              in  dtype [L][N][r]   (B^T rows per adapter; [L][r][N] with the flag)
  *   adapter_ids    in  int32 [T], in [0, L) (or -1 with MOELORA_FLAG_BASE_ONLY)
  *   out            out dtype [T][N], fully overwritten
  *   device_status  out int32 [1] or NULL: 0 ok, 1 an adapter id out of range

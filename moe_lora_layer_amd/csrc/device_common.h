@@ -180,6 +180,95 @@ __device__ __forceinline__ void atomic_add_relaxed(float* p, float v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// Weights stored k-major ([K][N], N contiguous: the page's h_in x h_out
+// orientation).  MFMA fragments take K-contiguous runs per lane, so a k-major
+// operand is turned around on its way in:
+//   - loaded through registers: each aligned group of 8 lanes (bf16) or 4
+//     lanes (fp32) loads a square block, lane m holding k-row m of 8 (4)
+//     consecutive columns; transpose8/transpose4 leave lane m holding column m
+//     of 8 (4) consecutive k, i.e. exactly the 16-byte chunk the K-contiguous
+//     layout would have given it;
+//   - staged in LDS by direct-to-LDS copies: the tile stays k-major in LDS and
+//     the fragments are read with ds_read_b64_tr_b16 (tr16_frag).
+// Every lane of a group must execute the transposes (no divergence).
+// ---------------------------------------------------------------------------
+template <int MASK>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), MASK, kWave));
+}
+
+// 8 x 8 bf16 transpose across the aligned 8-lane group of this lane: on entry
+// lane m holds row m (columns 0..7, two per dword, low half first); on exit it
+// holds column m (rows 0..7).  Three exchange steps swap the row and column
+// bits 2, 1, 0 of every element.
+__device__ __forceinline__ uint4 transpose8(uint4 v) {
+  const int m = threadIdx.x & 7;
+  {  // bit 2: dwords {0,1} hold columns 0-3, {2,3} columns 4-7
+    const bool hi = (m & 4) != 0;
+    const uint32_t s0 = xor_lane<4>(hi ? v.x : v.z), s1 = xor_lane<4>(hi ? v.y : v.w);
+    if (hi) { v.x = s0; v.y = s1; } else { v.z = s0; v.w = s1; }
+  }
+  {  // bit 1: dwords {0,2} hold columns with bit 1 clear, {1,3} set
+    const bool hi = (m & 2) != 0;
+    const uint32_t s0 = xor_lane<2>(hi ? v.x : v.y), s1 = xor_lane<2>(hi ? v.z : v.w);
+    if (hi) { v.x = s0; v.z = s1; } else { v.y = s0; v.w = s1; }
+  }
+  {  // bit 0: the low half of each dword holds the even column, the high half the odd
+    const bool hi = (m & 1) != 0;
+    // send the halves the partner keeps: odd columns from an even lane, even from an odd one
+    const uint32_t p0 = hi ? ((v.x & 0xffffu) | (v.y << 16)) : ((v.x >> 16) | (v.y & 0xffff0000u));
+    const uint32_t p1 = hi ? ((v.z & 0xffffu) | (v.w << 16)) : ((v.z >> 16) | (v.w & 0xffff0000u));
+    const uint32_t r0 = xor_lane<1>(p0), r1 = xor_lane<1>(p1);
+    if (hi) {  // keep the high halves, take the partner's high halves (its odd columns) as low
+      v.x = (v.x & 0xffff0000u) | (r0 & 0xffffu);
+      v.y = (v.y & 0xffff0000u) | (r0 >> 16);
+      v.z = (v.z & 0xffff0000u) | (r1 & 0xffffu);
+      v.w = (v.w & 0xffff0000u) | (r1 >> 16);
+    } else {   // keep the low halves, take the partner's low halves (its even columns) as high
+      v.x = (v.x & 0xffffu) | (r0 << 16);
+      v.y = (v.y & 0xffffu) | (r0 & 0xffff0000u);
+      v.z = (v.z & 0xffffu) | (r1 << 16);
+      v.w = (v.w & 0xffffu) | (r1 & 0xffff0000u);
+    }
+  }
+  return v;
+}
+
+// 4 x 4 fp32 transpose across the aligned 4-lane group (lane m: row m on
+// entry, column m on exit).
+__device__ __forceinline__ uint4 transpose4(uint4 v) {
+  const int m = threadIdx.x & 3;
+  {  // bit 1: x, y hold columns 0-1, z, w columns 2-3
+    const bool hi = (m & 2) != 0;
+    const uint32_t s0 = xor_lane<2>(hi ? v.x : v.z), s1 = xor_lane<2>(hi ? v.y : v.w);
+    if (hi) { v.x = s0; v.y = s1; } else { v.z = s0; v.w = s1; }
+  }
+  {  // bit 0: x, z even columns, y, w odd
+    const bool hi = (m & 1) != 0;
+    const uint32_t s0 = xor_lane<1>(hi ? v.x : v.y), s1 = xor_lane<1>(hi ? v.z : v.w);
+    if (hi) { v.x = s0; v.z = s1; } else { v.y = s0; v.w = s1; }
+  }
+  return v;
+}
+
+// The transpose for the element type of a 16-byte chunk.
+template <typename T> __device__ __forceinline__ uint4 transpose_chunk(uint4 v);
+template <> __device__ __forceinline__ uint4 transpose_chunk<bf16_t>(uint4 v) { return transpose8(v); }
+template <> __device__ __forceinline__ uint4 transpose_chunk<float>(uint4 v) { return transpose4(v); }
+
+// ds_read_b64_tr_b16: within each aligned 16-lane group, lane i supplies the
+// LDS address of 4 consecutive bf16 of a k-major tile, namely row kb + i/4,
+// columns cb + 4 (i % 4) .. + 3; lane i receives column cb + i of rows
+// kb .. kb + 3 (element j = row kb + j).
+typedef short tr_v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ds_read_tr16(const unsigned char* lds_byte_addr) {
+  typedef __attribute__((address_space(3))) tr_v4i16 lds_v4i16;
+  const tr_v4i16 v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<unsigned char*>(lds_byte_addr)));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // Inclusive scan of one int across the 64 lanes of a wave.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
   const int lane = threadIdx.x & (kWave - 1);

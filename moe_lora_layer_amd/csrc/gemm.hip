@@ -170,6 +170,28 @@ __device__ __forceinline__ void dma_piece(const void* src, unsigned char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
 }
 
+// Byte offset of (row, col) in a k-major LDS tile with rows of `pitch` bytes
+// (at least 16 chunks of 16 bytes): the 64-byte groups of a row are XORed with
+// row % 4, so that the four rows of a transposed read fall on different banks.
+__device__ __forceinline__ int kn_lds_off(int row, int col, int pitch) {
+  return row * pitch + ((((col >> 3) ^ ((row & 3) << 2))) << 4) + ((col & 7) << 1);
+}
+
+// The 32x32x16 bf16 B fragment of a k-major LDS tile (rows = k, `pitch` bytes
+// per row, kn_lds_off layout) for the lane's column: two transposed reads of
+// four k each.  cbase: the tile column of lane c32 & ~15 (the lane's column
+// is cbase + (c32 & 15), consecutive over its 16-lane group); k0: the first of
+// the fragment's 16 k (the lane takes k0 + 8h .. + 7).
+__device__ __forceinline__ bf16x8_t kn_frag(const unsigned char* tile, int pitch, int cbase, int k0,
+                                            int lane) {
+  const int i = lane & 15, h = lane >> 5;
+  const int col = cbase + 4 * (i & 3);
+  const int r = k0 + 8 * h + (i >> 2);
+  const uint2 a = ds_read_tr16(tile + kn_lds_off(r, col, pitch));
+  const uint2 b = ds_read_tr16(tile + kn_lds_off(r + 4, col, pitch));
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+
 // The fused LoRA expand of a tile with its operands staged in `lds_bytes` of
 // LDS that the K loop has finished with (whole KiB).  z of the tile's rows
 // (fp32, rows [row0, row_end), at most tm of them, resident for the whole
@@ -182,8 +204,10 @@ __device__ __forceinline__ void dma_piece(const void* src, unsigned char* dst) {
 // meeting the tile.  EPI_GATE_UP: the tile's columns are gate i in
 // [n0, n0 + tn/2) and up I + i, staged as the tn/2 gate rows then the tn/2 up
 // rows; EPI_DOWN: [n0, n0 + tn).  lrow[j]: the staged row of the lane's
-// column in fragment j.
-template <int EPI, int FM, int FN>
+// column in fragment j.  KN (k-major B, [r][columns]): a bucket's tile is
+// staged as r rows of tn columns (kn_lds_off layout, the same bytes) and read
+// with transposed reads.
+template <int EPI, int FM, int FN, bool KN = false>
 __device__ __forceinline__ void staged_lora_expand(f32x16_t (&acc)[FM][FN], const LoraEpilogue& lora,
                                                    unsigned char* lds, int lds_bytes, int nwaves,
                                                    int e, int lb, int ub, int row0, int row_end,
@@ -205,6 +229,29 @@ __device__ __forceinline__ void staged_lora_expand(f32x16_t (&acc)[FM][FN], cons
     for (int c = wave; c * 1024 < bytes; c += nwaves)
       dma_piece(s8 + min(c * 1024 + lane * 16, bytes - 16), dst + c * 1024);
   };
+  // k-major B block Bb ([rk][b_rows]): staged row q holds the tile's tn
+  // columns; each lane fetches the logical chunk that belongs at its LDS
+  // position (columns past the end fetch the segment's first chunk: never read)
+  const int64_t I = N / 2;
+  const int pitch = tn * 2;
+  const int valid_cols = static_cast<int>(EPI == EPI_GATE_UP ? min<int64_t>(tn / 2, I - n0)
+                                                             : min<int64_t>(tn, N - n0));
+  auto copy_kn = [&](unsigned char* dst, const bf16_t* Bb) {
+    for (int c = wave; c * 1024 < bbytes; c += nwaves) {
+      const int o = c * 1024 + lane * 16;
+      const int q = o / pitch, lc = ((o % pitch) >> 4) ^ ((q & 3) << 2);
+      int col = lc * 8;
+      int64_t g;
+      if (EPI == EPI_GATE_UP) {
+        const int up = col >= tn / 2;
+        const int ci = col - up * (tn / 2);
+        g = up * I + n0 + (ci < valid_cols ? ci : 0);
+      } else {
+        g = n0 + (col < valid_cols ? col : 0);
+      }
+      dma_piece(Bb + static_cast<int64_t>(q) * lora.b_rows + g, dst + c * 1024);
+    }
+  };
   for (int g = lb; g < ub; g += cap) {  // uniform
     const int ng = min(cap, ub - g);
     lds_barrier();  // every wave is done with what the LDS held before
@@ -212,13 +259,14 @@ __device__ __forceinline__ void staged_lora_expand(f32x16_t (&acc)[FM][FN], cons
     for (int b = 0; b < ng; ++b) {
       const bf16_t* Bb = lora.b + (static_cast<int64_t>(g + b) * lora.experts + e) * lora.b_rows * rk;
       unsigned char* dst = lds + zbytes + b * bbytes;
-      if (EPI == EPI_GATE_UP) {
-        const int64_t I = N / 2;
-        const int bytes = static_cast<int>(min<int64_t>(tn / 2, I - n0)) * rk * 2;
+      if (KN) {
+        copy_kn(dst, Bb);
+      } else if (EPI == EPI_GATE_UP) {
+        const int bytes = valid_cols * rk * 2;
         copy(dst, Bb + n0 * rk, bytes);
         copy(dst + bbytes / 2, Bb + (I + n0) * rk, bytes);
       } else {
-        copy(dst, Bb + n0 * rk, static_cast<int>(min<int64_t>(tn, N - n0)) * rk * 2);
+        copy(dst, Bb + n0 * rk, valid_cols * rk * 2);
       }
     }
     wait_vmcnt<0>();
@@ -227,13 +275,22 @@ __device__ __forceinline__ void staged_lora_expand(f32x16_t (&acc)[FM][FN], cons
     for (int b = 0; b < ng; ++b) {
       const int s0 = max(rw0, off[g + b]), s1 = min(rw1, off[g + b + 1]);
       if (s0 >= s1) continue;  // uniform: the bucket misses this wave's rows
-      const unsigned char* bt = lds + zbytes + b * bbytes + 16 * h;
       bf16x8_t bfr[FN][4];
+      if (KN) {
+        const unsigned char* bt = lds + zbytes + b * bbytes;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          bfr[j][q4] = *reinterpret_cast<const bf16x8_t*>(bt + lrow[j] * rk * 2 + 32 * min(q4, nks - 1));
+          for (int q4 = 0; q4 < 4; ++q4)
+            bfr[j][q4] = kn_frag(bt, pitch, lrow[j] - (c32 & 15), 16 * min(q4, nks - 1), lane);
+      } else {
+        const unsigned char* bt = lds + zbytes + b * bbytes + 16 * h;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            bfr[j][q4] = *reinterpret_cast<const bf16x8_t*>(bt + lrow[j] * rk * 2 + 32 * min(q4, nks - 1));
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int rb = rw0 + 32 * i;
@@ -284,8 +341,12 @@ __device__ __forceinline__ void lora_buckets(const LoraEpilogue& lora, int e, in
 // more 32-column fragments per wave, fragment j < FN/2 holds gate columns and
 // j + FN/2 the matching up columns (same lane); with one, lanes c < 16 hold
 // gate and lanes c + 16 the matching up columns.
+// KN: the weights are k-major ([K][N]); each aligned group of VEC lanes loads
+// VEC k-rows of VEC consecutive columns and transposes them in registers, so
+// the LDS tile and the fragment reads are those of the K-contiguous layout.
 template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
-          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false, int EPI = EPI_STORE>
+          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false, int EPI = EPI_STORE,
+          bool KN = false>
 __global__ void __launch_bounds__(WM * WN * kWave)
 k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
        const T* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
@@ -366,25 +427,42 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     up = c >= 16;
     return it0 + wg * 16 + (c & 15);
   };
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int q = tid + i * NT_, row = q >> 3, ch = q & 7;
-    int64_t wrow;
-    bool ok;
+  // the weight column (gate_up: up * I + intermediate column) of tile row
+  // `row`, clamped to a valid one when it is past the end (ok = false)
+  auto w_col = [&](int row, bool& ok) -> int64_t {
     if (EPI == EPI_GATE_UP) {
       int up;
       const int64_t ic = gu_col(row / WTN, (row % WTN) / 32, row & 31, up);
       ok = ic < I;
-      wrow = up * I + (ok ? ic : I - 1);
+      return up * I + (ok ? ic : I - 1);
+    }
+    const int64_t n = n0 + row;
+    ok = n < N;
+    return ok ? n : N - 1;
+  };
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int q = tid + i * NT_;
+    bool ok;
+    if (!KN) {
+      const int row = q >> 3, ch = q & 7;
+      b_src[i] = We + w_col(row, ok) * K + ch * VEC;
+      b_dst[i] = BM * ROWB + row * ROWB + ((ch ^ swz<SWZ>(row)) << 4);
     } else {
-      const int64_t n = n0 + row;
-      ok = n < N;
-      wrow = ok ? n : N - 1;
+      // block q / VEC: k-group kg (VEC k-rows) x column group cg (VEC tile
+      // rows); lane m of the block loads k-row kg * VEC + m of the group's
+      // columns and, after the transpose, holds tile row cg * VEC + m, chunk kg
+      const int blk = q / VEC, m = q % VEC, ncg = BN / VEC;
+      const int cg = blk % ncg, kg = blk / ncg;
+      int64_t col0 = w_col(cg * VEC, ok);  // VEC consecutive columns, all valid or none
+      if (!ok) col0 = 0;                   // masked: any VEC columns inside the row
+      b_src[i] = We + static_cast<int64_t>(kg * VEC + m) * N + col0;
+      const int row = cg * VEC + m;
+      b_dst[i] = BM * ROWB + row * ROWB + ((kg ^ swz<SWZ>(row)) << 4);
     }
     b_mask[i] = ok ? 0xffffffffu : 0u;
-    b_src[i] = We + wrow * K + ch * VEC;
-    b_dst[i] = BM * ROWB + row * ROWB + ((ch ^ swz<SWZ>(row)) << 4);
   }
+  const int64_t b_kmul = KN ? N : 1;  // elements of B per unit of K
 
   // ROT: every workgroup starts its K walk at a different step, so that
   // workgroups resident together do not all read the same K columns at once
@@ -401,15 +479,17 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) a_reg[slot][i] = load16<false>(a_src[i] + ko);
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) b_reg[slot][i] = load16<NT>(b_src[i] + ko);
+    for (int i = 0; i < B_CH; ++i) b_reg[slot][i] = load16<NT>(b_src[i] + ko * b_kmul);
   };
   auto sstore = [&](int slot, int buf) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i)
       *reinterpret_cast<uint4*>(&smem[buf][a_dst[i]]) = masked(a_reg[slot][i], a_mask[i]);
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      *reinterpret_cast<uint4*>(&smem[buf][b_dst[i]]) = masked(b_reg[slot][i], b_mask[i]);
+    for (int i = 0; i < B_CH; ++i) {
+      const uint4 v = KN ? transpose_chunk<T>(b_reg[slot][i]) : b_reg[slot][i];
+      *reinterpret_cast<uint4*>(&smem[buf][b_dst[i]]) = masked(v, b_mask[i]);
+    }
   };
 
   f32x16_t acc[FM][FN];
@@ -541,7 +621,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
       }
       int lb, ub;
       lora_buckets(lora, e, row0, row_end, lb, ub);
-      staged_lora_expand<EPI, FM, FN>(acc, lora, &smem[0][0], 2 * (BM + BN) * ROWB, NT_ / kWave, e, lb,
+      staged_lora_expand<EPI, FM, FN, KN>(acc, lora, &smem[0][0], 2 * (BM + BN) * ROWB, NT_ / kWave, e, lb,
                                       ub, row0, row_end, BM, BN,
                                       EPI == EPI_GATE_UP ? it0 : n0, N, lrow, rw0 < rw1, rw0, rw1,
                                       wave, lane, c32, h);
@@ -569,21 +649,25 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
         for (int q4 = 0; q4 < 4; ++q4) split_bf16x8(zr + 16 * min(q4, nks - 1), zh[i][q4], zl[i][q4]);
       }
       // this thread's B^T chunks: tile row and LDS position as in the main loop
+      // (k-major B: the block of rank rows x columns this lane's group loads,
+      // transposed before the LDS store)
       int64_t b_off[B_CH];
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
-        const int q = tid + i * NT_, row = q >> 3, ch = q & 7;
-        int64_t wrow;
-        if (EPI == EPI_GATE_UP) {
-          int up;
-          const int64_t ic = gu_col(row / WTN, (row % WTN) / 32, row & 31, up);
-          wrow = up * I + (ic < I ? ic : I - 1);
+        const int q = tid + i * NT_;
+        bool ok;
+        if (!KN) {
+          const int row = q >> 3, ch = q & 7;
+          // chunks past r reload the last chunk of the row (never read)
+          b_off[i] = w_col(row, ok) * rk + 8 * min(ch, 2 * nks - 1);
         } else {
-          const int64_t n = n0 + row;
-          wrow = n < N ? n : N - 1;
+          const int blk = q / 8, m = q % 8, ncg = BN / 8;
+          const int cg = blk % ncg, kg = blk / ncg;
+          int64_t col0 = w_col(cg * 8, ok);
+          if (!ok) col0 = 0;
+          // rank groups past r reload the last group (never read)
+          b_off[i] = static_cast<int64_t>(min(kg, 2 * nks - 1) * 8 + m) * lora.b_rows + col0;
         }
-        // chunks past r reload the last chunk of the row (never read)
-        b_off[i] = wrow * rk + 8 * min(ch, 2 * nks - 1);
       }
       const bf16_t* Be = lora.b + static_cast<int64_t>(e) * lora.b_rows * rk;
       const int64_t bstride = static_cast<int64_t>(lora.experts) * lora.b_rows * rk;  // per adapter
@@ -621,7 +705,8 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
         for (int g = 0; g < NBUF; ++g)
 #pragma unroll
           for (int i = 0; i < B_CH; ++i)
-            *reinterpret_cast<uint4*>(lds + g * BUCKET_BYTES + b_dst[i] - BM * ROWB) = bv[g][i];
+            *reinterpret_cast<uint4*>(lds + g * BUCKET_BYTES + b_dst[i] - BM * ROWB) =
+                KN ? transpose8(bv[g][i]) : bv[g][i];
         __syncthreads();
         for (int g = 0; g < ng; ++g) {
           const int lg = grp[g];
@@ -721,15 +806,16 @@ struct GemmArgs {
   int64_t part_stride;  // elements per partial (rows of C times N)
 };
 
-template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
-          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false, int EPI = EPI_STORE>
+template <bool KN, typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER,
+          bool ROT = false, bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false,
+          int EPI = EPI_STORE>
 static hipError_t lds_launch_epi(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue& lora,
                                  hipStream_t stream) {
   const int64_t cols = EPI == EPI_GATE_UP ? a.N / 2 : a.N;
   const int tn = EPI == EPI_GATE_UP ? BN / 2 : BN;
   const int n_ntiles = static_cast<int>((cols + tn - 1) / tn);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE, EPI>),
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE, EPI, KN>),
                      dim3(static_cast<unsigned>(grid)), dim3(WM * WN * kWave), 0, stream,
                      static_cast<const T*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const T*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
@@ -738,19 +824,19 @@ static hipError_t lds_launch_epi(const TilePlan& plan, const GemmArgs& a, const 
 }
 
 // the epilogue picked by lora: none (EPI_STORE), gate_up (act set) or down
-template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
-          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false>
+template <bool KN, typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER,
+          bool ROT = false, bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false>
 static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue* lora,
                              hipStream_t stream) {
   if constexpr (sizeof(T) == 2 && BM <= 128) {  // bf16 256-row tiles run k_gemm_dma
     if (lora != nullptr && lora->act != nullptr)
-      return lds_launch_epi<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
+      return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
                             EPI_GATE_UP>(plan, a, *lora, stream);
     if (lora != nullptr)
-      return lds_launch_epi<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE, EPI_DOWN>(
-          plan, a, *lora, stream);
+      return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
+                            EPI_DOWN>(plan, a, *lora, stream);
   }
-  return lds_launch_epi<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE>(
+  return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE>(
       plan, a, LoraEpilogue{}, stream);
 }
 
@@ -773,17 +859,24 @@ constexpr int kDmaRowB = 128;                       // bytes of K per LDS row (6
 constexpr int kDmaStage = 2 * kDmaTile * kDmaRowB;  // A and B rows of one K-step: 64 KiB
 constexpr int kDmaThreads = 512;
 
-// The four A and four B load instructions of one wave for K-step kt into
-// stage `slot` (8 rows of 128 bytes each).
-__device__ __forceinline__ void dma_issue(unsigned char* smem, int slot, int64_t ko,
+// The four A and four B load instructions of one wave for the K-step at
+// element offset ko into stage `slot` (8 rows of 128 bytes each; KN, k-major
+// weights: the B tile is 64 k-rows of 512 bytes, 2 rows per instruction, and
+// the step advances the weight rows by ko * N).
+template <bool KN>
+__device__ __forceinline__ void dma_issue(unsigned char* smem, int slot, int64_t ko, int64_t N,
                                           const bf16_t* const* a_src, const bf16_t* const* b_src,
                                           int wave) {
   unsigned char* st = smem + slot * kDmaStage;
 #pragma unroll
   for (int j = 0; j < 4; ++j) dma_piece(a_src[j] + ko, st + (32 * wave + 8 * j) * kDmaRowB);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    dma_piece(b_src[j] + ko, st + (kDmaTile + 32 * wave + 8 * j) * kDmaRowB);
+  for (int j = 0; j < 4; ++j) {
+    if (KN)
+      dma_piece(b_src[j] + ko * N, st + kDmaTile * kDmaRowB + (8 * wave + 2 * j) * (2 * kDmaTile));
+    else
+      dma_piece(b_src[j] + ko, st + (kDmaTile + 32 * wave + 8 * j) * kDmaRowB);
+  }
 }
 
 // How a k_gemm_dma item writes its outputs: plain stores (the item covers the
@@ -795,7 +888,7 @@ enum { DMA_OUT_STORE = 0, DMA_OUT_ATOMIC = 1, DMA_OUT_PART = 2 };
 // (M-tile `tile`, N-tile nt), written as `out` says; with_lora adds the fused
 // LoRA expand (exactly one item of a tile carries it).  Every wave of the
 // workgroup calls it with the same arguments.
-template <bool GATHER, int EPI>
+template <bool GATHER, int EPI, bool KN>
 __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __restrict__ X,
                                          int x_rows, const int32_t* __restrict__ gather_slots,
                                          int gather_k, const bf16_t* __restrict__ Wt, int64_t N,
@@ -831,14 +924,30 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
     const int p = min(row0 + rt, row_end - 1);
     const int r = GATHER ? gather_slots[p] / gather_k : p;
     a_src[j] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + lch * 8;
-    int64_t wrow;
-    if (EPI == EPI_GATE_UP) {  // B tile row rt = 64 wn' + 32 half + c
-      const int64_t i = min(n0 + 32 * (rt >> 6) + (rt & 31), I - 1);
-      wrow = ((rt >> 5) & 1) * I + i;
+    if (!KN) {
+      int64_t wrow;
+      if (EPI == EPI_GATE_UP) {  // B tile row rt = 64 wn' + 32 half + c
+        const int64_t i = min(n0 + 32 * (rt >> 6) + (rt & 31), I - 1);
+        wrow = ((rt >> 5) & 1) * I + i;
+      } else {
+        wrow = min(n0 + rt, N - 1);
+      }
+      b_src[j] = We + wrow * K + lch * 8;
     } else {
-      wrow = min(n0 + rt, N - 1);
+      // k-row kr of the B tile, LDS chunk lane % 32 holding the logical
+      // chunk (tile columns) of the kn_lds_off layout; columns past the end
+      // fetch the first chunk of their half (never stored)
+      const int kr = 8 * wave + 2 * j + (lane >> 5);
+      const int t = 8 * ((lane & 31) ^ ((kr & 3) << 2));
+      int64_t col;
+      if (EPI == EPI_GATE_UP) {
+        const int64_t i = n0 + 32 * (t >> 6) + (t & 31);
+        col = ((t >> 5) & 1) * I + (i < I ? i : 0);
+      } else {
+        col = n0 + t < N ? n0 + t : 0;
+      }
+      b_src[j] = We + static_cast<int64_t>(kr) * N + col;
     }
-    b_src[j] = We + wrow * K + lch * 8;
   }
   // adapter buckets of expert e meeting the tile, [lb, ub) (looked up before
   // the K loop so that the epilogue does not wait for it); a base-only
@@ -868,15 +977,20 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
     for (int i = 0; i < NB; ++i)
       fa[f][i] = *reinterpret_cast<const bf16x8_t*>(st + a_off + i * 32 * kDmaRowB + ch);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      fb[f][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * kDmaRowB + ch);
+    for (int j = 0; j < 2; ++j) {
+      if (KN)
+        fb[f][j] = kn_frag(st + kDmaTile * kDmaRowB, 2 * kDmaTile, wn * 64 + 32 * j + (c32 & 16),
+                           16 * s, lane);
+      else
+        fb[f][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * kDmaRowB + ch);
+    }
   };
   // One substep's MFMAs, with the fragment reads of the next substep (issued
   // just before in program order) placed one after each MFMA: the reads then
   // overlap the MFMA pipe instead of queueing as a burst, and each fragment
   // still lands a whole substep before its use.
   auto mm = [&](int f, auto nbc) {
-    constexpr int NB = decltype(nbc)::value, NR = NB + 2, NM = 2 * NB;
+    constexpr int NB = decltype(nbc)::value, NR = NB + (KN ? 4 : 2), NM = 2 * NB;
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -899,8 +1013,8 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
   // K-step kt lives in stage kt % 2.  Both stages are requested up front;
   // steps past the end repeat the last one (never read), which keeps the
   // vmcnt accounting the same in every iteration.
-  dma_issue(smem, 0, ko(0), a_src, b_src, wave);
-  dma_issue(smem, 1, ko(min(1, nk - 1)), a_src, b_src, wave);
+  dma_issue<KN>(smem, 0, ko(0), N, a_src, b_src, wave);
+  dma_issue<KN>(smem, 1, ko(min(1, nk - 1)), N, a_src, b_src, wave);
   wait_vmcnt<8>();  // this wave's loads of step 0 are in LDS
   bar();            // ... and every other wave's
   auto k_loop = [&](auto nbc) {
@@ -918,7 +1032,7 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
       // (lgkmcnt(0) before the barrier): refill that stage with step kt+2
       wait_vmcnt_lgkm0<0>();
       bar();
-      dma_issue(smem, kt & 1, ko(min(kt + 2, nk - 1)), a_src, b_src, wave);
+      dma_issue<KN>(smem, kt & 1, ko(min(kt + 2, nk - 1)), N, a_src, b_src, wave);
       rd(0, smem + ((kt + 1) & 1) * kDmaStage, 0, nbc);
       mm(1, nbc);
       __builtin_amdgcn_sched_barrier(0);
@@ -965,7 +1079,7 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       lrow[j] = EPI == EPI_GATE_UP ? j * (kDmaTile / 2) + 32 * wn + c32 : 64 * wn + 32 * j + c32;
-    staged_lora_expand<EPI, 4, 2>(acc, lora, smem, 2 * kDmaStage, kDmaThreads / kWave, e, lb, ub,
+    staged_lora_expand<EPI, 4, 2, KN>(acc, lora, smem, 2 * kDmaStage, kDmaThreads / kWave, e, lb, ub,
                                   row0, row_end, kDmaTile, kDmaTile, n0, N, lrow, rw0 < rw1, rw0,
                                   rw1, wave, lane, c32, h);
   }
@@ -1032,7 +1146,7 @@ __device__ __forceinline__ int dma_dp_tiles(int tiles, int nwg) {
 // most two tiles and adds each part with atomics, the part holding K-step 0
 // carrying the LoRA expand.  Used for the down projection, whose few long
 // tiles otherwise leave a last round with most CUs idle.
-template <bool GATHER, int EPI>
+template <bool GATHER, int EPI, bool KN>
 __global__ void __launch_bounds__(kDmaThreads)
 k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
            int gather_k, const bf16_t* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
@@ -1098,15 +1212,15 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
       with_lora = true;
       u = u1;
     }
-    dma_item<GATHER, EPI>(smem, X, x_rows, gather_slots, gather_k, Wt, N, K, C, tile, nt, kbeg, nk,
-                          out, with_lora, lora, part);
+    dma_item<GATHER, EPI, KN>(smem, X, x_rows, gather_slots, gather_k, Wt, N, K, C, tile, nt, kbeg,
+                              nk, out, with_lora, lora, part);
   }
 }
 
 // Stream-K for the non-gate_up forms with unsplit K and no deterministic
 // partials, when the tiles exceed one round: the data-parallel launch, then
 // the stream-K launch over one workgroup per CU.
-template <bool GATHER, int EPI>
+template <bool GATHER, int EPI, bool KN>
 static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue& lora,
                              hipStream_t stream) {
   const int64_t cols = EPI == EPI_GATE_UP ? a.N / 2 : a.N;
@@ -1122,41 +1236,48 @@ static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const Lora
   }
   // the tiles' upper bound must reach a round for the device to pick stream-K
   const int mode = nwg > 0 && static_cast<int64_t>(plan.max_mt) * n_ntiles >= nwg ? 1 : 0;
-  hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
+  hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI, KN>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
                      a.expert_tiles, n_ntiles, a.ksplit, lora, a.parts, a.part_stride, mode, nwg);
   if (mode == 0) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI>), dim3(static_cast<unsigned>(nwg)), dim3(kDmaThreads),
+  hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI, KN>), dim3(static_cast<unsigned>(nwg)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
                      a.expert_tiles, n_ntiles, 1, lora, a.parts, a.part_stride, 2, nwg);
   return hipGetLastError();
 }
 
-template <typename T, bool GATHER>
+template <typename T, bool GATHER, bool KN>
 static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue* lora,
                                 hipStream_t stream) {
   // decode-sized M-tiles stream the weights: nontemporal loads, rotated K walk
   switch (plan.bm) {
-    case 32: return lds_launch<T, 32, 128, 1, 4, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
-    case 64: return lds_launch<T, 64, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
+    case 32: return lds_launch<KN, T, 32, 128, 1, 4, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
+    case 64: return lds_launch<KN, T, 64, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
     case 128:
       if (plan.stream)  // eight waves of 64 x 32
-        return lds_launch<T, 128, 128, 2, 4, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
-      return lds_launch<T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, lora, stream);
+        return lds_launch<KN, T, 128, 128, 2, 4, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
+      return lds_launch<KN, T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, lora, stream);
     case 256:  // prefill: 256x256 tiles, 8 waves of 128x64 (bf16: operands DMA'd into LDS)
       if constexpr (sizeof(T) == 2) {
-        if (lora == nullptr) return dma_launch<GATHER, EPI_STORE>(plan, a, LoraEpilogue{}, stream);
-        if (lora->act != nullptr) return dma_launch<GATHER, EPI_GATE_UP>(plan, a, *lora, stream);
-        return dma_launch<GATHER, EPI_DOWN>(plan, a, *lora, stream);
+        if (lora == nullptr) return dma_launch<GATHER, EPI_STORE, KN>(plan, a, LoraEpilogue{}, stream);
+        if (lora->act != nullptr) return dma_launch<GATHER, EPI_GATE_UP, KN>(plan, a, *lora, stream);
+        return dma_launch<GATHER, EPI_DOWN, KN>(plan, a, *lora, stream);
       } else {
-        return lds_launch<T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, nullptr, stream);
+        return lds_launch<KN, T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, nullptr, stream);
       }
     default: return hipErrorInvalidValue;
   }
+}
+
+template <typename T, bool KN>
+static hipError_t gemm_dispatch_g(bool gather, const TilePlan& plan, const GemmArgs& a,
+                                  const LoraEpilogue* lora, hipStream_t stream) {
+  return gather ? gemm_dispatch<T, true, KN>(plan, a, lora, stream)
+                : gemm_dispatch<T, false, KN>(plan, a, lora, stream);
 }
 
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
@@ -1174,11 +1295,11 @@ hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_row
     return hipErrorInvalidValue;
   hipError_t e;
   if (dtype == DT_BF16)
-    e = gather ? gemm_dispatch<bf16_t, true>(plan, a, lora, stream)
-               : gemm_dispatch<bf16_t, false>(plan, a, lora, stream);
+    e = plan.kn ? gemm_dispatch_g<bf16_t, true>(gather, plan, a, lora, stream)
+                : gemm_dispatch_g<bf16_t, false>(gather, plan, a, lora, stream);
   else
-    e = gather ? gemm_dispatch<float, true>(plan, a, nullptr, stream)
-               : gemm_dispatch<float, false>(plan, a, nullptr, stream);
+    e = plan.kn ? gemm_dispatch_g<float, true>(gather, plan, a, nullptr, stream)
+                : gemm_dispatch_g<float, false>(gather, plan, a, nullptr, stream);
   if (e == hipSuccess && pp != nullptr) e = launch_reduce_parts(pp, ksplit, c_rows * N, C, stream);
   return e;
 }

@@ -50,6 +50,7 @@ struct TilePlan {
   bool det;      // split-K reductions go through ordered partial sums, not atomics
   bool shrink_partials;  // the shrinks sum per-split partials in order (det, or tall bf16 tiles)
   int nad;       // adapters; bucket index nad of an expert (base-only tokens) has no LoRA
+  bool kn;       // every weight is k-major ([K][N], the h_in x h_out orientation)
 };
 
 // Operands of the LoRA expand fused into a base GEMM's epilogue:

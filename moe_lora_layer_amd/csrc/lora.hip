@@ -48,13 +48,37 @@ template <> struct ZFrag<float> {
   __device__ __forceinline__ void mma(f32x4_t& acc, float a) const { Mfma16<float>::run(acc, a, v); }
 };
 
+// The MFMA 16x16 fragment (lane (g, c): row rb + c, the KPACK elements
+// k0 + g * KPACK ..) of a k-major matrix M[k][row] with ld elements per k-row
+// (LoRA weights stored h_in x r or r x h_out).  bf16: the lane's aligned
+// 8-lane group loads 8 k-rows of 8 consecutive rows and transposes them;
+// fp32: one element.  ok (uniform per group) false: zero, and row 0 of k-row 0
+// is read instead (always in range).  Every lane of the wave must call it.
+template <typename T> struct KnFrag;
+template <> struct KnFrag<bf16_t> {
+  __device__ __forceinline__ static bf16x8_t load(const bf16_t* M, int64_t ld, int64_t rb, int64_t k0,
+                                                  bool ok) {
+    const int lane = threadIdx.x & (kWave - 1), g = lane >> 4, c = lane & 15;
+    const int64_t kk = ok ? k0 + 8 * g + (c & 7) : 0, rr = ok ? rb + (c & 8) : 0;
+    const uint4 v = transpose8(*reinterpret_cast<const uint4*>(M + kk * ld + rr));
+    return ok ? __builtin_bit_cast(bf16x8_t, v) : Mfma16<bf16_t>::zero();
+  }
+};
+template <> struct KnFrag<float> {
+  __device__ __forceinline__ static float load(const float* M, int64_t ld, int64_t rb, int64_t k0,
+                                               bool ok) {
+    const int lane = threadIdx.x & (kWave - 1), g = lane >> 4, c = lane & 15;
+    return ok ? M[(k0 + g) * ld + rb + c] : 0.0f;
+  }
+};
+
 // --------------------------------------------------------------------- shrink
 // Workgroup (tile, split): four waves take consecutive K ranges of STEPS
 // MFMA steps each.  For every 16-row block of the tile a wave issues all its
 // loads (weights A^T and the gathered activation rows) up front, multiplies,
 // and the four partial z blocks are summed through LDS; the sum goes to Z with
 // one relaxed fp32 atomic per element.
-template <typename T, int R, int STEPS, bool GATHER>
+template <typename T, int R, int STEPS, bool GATHER, bool KN>
 __global__ void __launch_bounds__(kLoraThreads)
 k_shrink(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
          const T* __restrict__ At, int E, int L, int nad, int64_t K, int nsplit,
@@ -94,8 +118,12 @@ k_shrink(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather
       const int64_t k = k0 + s * M::KSTEP;
       const bool in = k < K;
 #pragma unroll
-      for (int j = 0; j < RB; ++j)
-        af[s][j] = in ? M::load(Ab + static_cast<int64_t>(16 * j + c) * K + g * M::KPACK + k) : M::zero();
+      for (int j = 0; j < RB; ++j) {
+        if (KN)
+          af[s][j] = KnFrag<T>::load(Ab, R, 16 * j, k, in);
+        else
+          af[s][j] = in ? M::load(Ab + static_cast<int64_t>(16 * j + c) * K + g * M::KPACK + k) : M::zero();
+      }
       xf[s] = (in && xp) ? M::load(xp + k) : M::zero();
     }
     f32x4_t acc[RB];
@@ -134,7 +162,7 @@ k_shrink(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather
 // tile and walks the workgroup's whole K range, STEPS MFMA steps at a time
 // with the next STEPS in flight; no cross-wave reduction is needed, and each
 // wave adds its z block to Z with one relaxed atomic per element.
-template <typename T, int R, int STEPS, bool GATHER>
+template <typename T, int R, int STEPS, bool GATHER, bool KN>
 __global__ void __launch_bounds__(kLoraThreads)
 k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
               int gather_k, const T* __restrict__ At, int E, int L, int nad, int64_t K, int64_t kwg,
@@ -157,7 +185,8 @@ k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ g
   const int c = lane & 15, g = lane >> 4;
   const int64_t kb0 = static_cast<int64_t>(split) * kwg;
   const int64_t kb1 = kb0 + kwg < K ? kb0 + kwg : K;
-  const T* Ab = At + (static_cast<int64_t>(l) * E + e) * R * K + g * M::KPACK;
+  const T* Ablk = At + (static_cast<int64_t>(l) * E + e) * R * K;
+  const T* Ab = Ablk + g * M::KPACK;
 
   for (int m0 = row0 + 16 * wave; m0 < row_end; m0 += 16 * kLoraWaves) {
     const int p = m0 + c;
@@ -175,8 +204,12 @@ k_shrink_tall(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ g
         const int64_t k = k0 + s2 * M::KSTEP;
         const bool in = k < kb1;
 #pragma unroll
-        for (int j = 0; j < RB; ++j)
-          af[s2][j] = in ? M::load(Ab + static_cast<int64_t>(16 * j + c) * K + k) : M::zero();
+        for (int j = 0; j < RB; ++j) {
+          if (KN)
+            af[s2][j] = KnFrag<T>::load(Ablk, R, 16 * j, k, in);
+          else
+            af[s2][j] = in ? M::load(Ab + static_cast<int64_t>(16 * j + c) * K + k) : M::zero();
+        }
         xf[s2] = (in && ok) ? M::load(xp + k) : M::zero();
       }
     };
@@ -234,7 +267,21 @@ template <int R> struct ShrinkDma {
   static constexpr int LPW = XI + AI;               // loads per wave per stage
 };
 
+// KN (k-major A, [K][R]): the A part of a stage holds the step's 64 k-rows of
+// R ranks (R * 2 bytes each, 64-byte halves XORed with bit 1 of the row at
+// R = 64), copied as R / 8 pieces of 1 KiB; with R = 16 the last two waves
+// repeat the first two waves' pieces.
 template <int R>
+__device__ __forceinline__ int shrink_kn_piece(int wave, int j) {
+  return min(ShrinkDma<R>::AI * wave + j, R / 8 - 1);
+}
+template <int R>
+__device__ __forceinline__ int shrink_kn_off(int row, int col) {
+  const int sw = R == 64 ? ((row >> 1) & 1) << 2 : 0;
+  return row * (R * 2) + ((((col >> 3) ^ sw)) << 4) + ((col & 7) << 1);
+}
+
+template <int R, bool KN>
 __device__ __forceinline__ void shrink_issue(unsigned char* smem, int slot, int64_t ko,
                                              const bf16_t* const* x_src, const bf16_t* const* a_src,
                                              int wave) {
@@ -245,16 +292,22 @@ __device__ __forceinline__ void shrink_issue(unsigned char* smem, int slot, int6
     __builtin_amdgcn_global_load_lds(x_src[j] + ko, (lds_void_t*)(st + (16 * wave + 8 * j) * 128),
                                      16, 0, 0);
 #pragma unroll
-  for (int j = 0; j < S::AI; ++j)
-    __builtin_amdgcn_global_load_lds(a_src[j] + ko,
-                                     (lds_void_t*)(st + (64 + 8 * (S::AI * wave + j)) * 128), 16, 0, 0);
+  for (int j = 0; j < S::AI; ++j) {
+    if (KN)
+      __builtin_amdgcn_global_load_lds(a_src[j] + ko * R,
+                                       (lds_void_t*)(st + 64 * 128 + shrink_kn_piece<R>(wave, j) * 1024),
+                                       16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(a_src[j] + ko,
+                                       (lds_void_t*)(st + (64 + 8 * (S::AI * wave + j)) * 128), 16, 0, 0);
+  }
 }
 
 // One K range [kt0, kt0 + nk) (in 64-wide steps) of one tall LoRA tile through
 // the ring; the wave's 32 x 32 partial is left in acc.  `tile` is the tile's
 // (bucket, row0, row_end); the caller has checked that its bucket has an
 // adapter.
-template <int R, bool GATHER>
+template <int R, bool GATHER, bool KN>
 __device__ __forceinline__ void shrink_dma_range(unsigned char* smem, const bf16_t* __restrict__ X,
                                                  int x_rows, const int32_t* __restrict__ gather_slots,
                                                  int gather_k, const bf16_t* __restrict__ At, int E,
@@ -280,9 +333,19 @@ __device__ __forceinline__ void shrink_dma_range(unsigned char* smem, const bf16
   const bf16_t* Ab = At + (static_cast<int64_t>(l) * E + e) * R * K;
 #pragma unroll
   for (int j = 0; j < S::AI; ++j) {
-    const int rt = 8 * (S::AI * wave + j) + (lane >> 3);
-    const int lch = (lane & 7) ^ ((rt >> 1) & 7);
-    a_src[j] = Ab + static_cast<int64_t>(min(rt, R - 1)) * K + kt0 * 64ll + lch * 8;
+    if (KN) {
+      // byte o of the step's A part: k-row o / (2R), the logical chunk that
+      // belongs at its physical position
+      const int o = shrink_kn_piece<R>(wave, j) * 1024 + lane * 16;
+      const int kr = o / (2 * R);
+      const int sw = R == 64 ? ((kr >> 1) & 1) << 2 : 0;
+      const int lch = ((o % (2 * R)) >> 4) ^ sw;
+      a_src[j] = Ab + (kt0 * 64ll + kr) * R + lch * 8;
+    } else {
+      const int rt = 8 * (S::AI * wave + j) + (lane >> 3);
+      const int lch = (lane & 7) ^ ((rt >> 1) & 7);
+      a_src[j] = Ab + static_cast<int64_t>(min(rt, R - 1)) * K + kt0 * 64ll + lch * 8;
+    }
   }
 
   const int rh = wave & 1;
@@ -293,22 +356,35 @@ __device__ __forceinline__ void shrink_dma_range(unsigned char* smem, const bf16
   const int a_off = (64 + q0 + c32) * 128;
 
   for (int s = 0; s + 1 < kShrinkStages; ++s)
-    shrink_issue<R>(smem, s, static_cast<int64_t>(min(s, nk - 1)) * 64, x_src, a_src, wave);
+    shrink_issue<R, KN>(smem, s, static_cast<int64_t>(min(s, nk - 1)) * 64, x_src, a_src, wave);
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt landed (two newer stages may still fly) and this wave's reads of
     // stage kt-1 are done; after the barrier its slot takes stage kt+3 (steps
     // past the end repeat the last one and are never read)
     wait_vmcnt_lgkm0<S::LPW * (kShrinkStages - 2)>();
     lds_barrier();
-    shrink_issue<R>(smem, (kt + kShrinkStages - 1) % kShrinkStages,
-                    static_cast<int64_t>(min(kt + kShrinkStages - 1, nk - 1)) * 64, x_src, a_src, wave);
+    shrink_issue<R, KN>(smem, (kt + kShrinkStages - 1) % kShrinkStages,
+                        static_cast<int64_t>(min(kt + kShrinkStages - 1, nk - 1)) * 64, x_src, a_src,
+                        wave);
     const unsigned char* st = smem + (kt % kShrinkStages) * S::STAGE;
 #pragma unroll
     for (int u = 0; u < (R > 32 ? 4 : 2); ++u) {
       const int sub = R > 32 ? u : 2 * sel + u;
       const int ch = ((2 * sub + h) ^ sw) << 4;
       const bf16x8_t fx = *reinterpret_cast<const bf16x8_t*>(st + x_off + ch);
-      const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(st + a_off + ch);
+      bf16x8_t fa;
+      if (KN) {
+        // rank columns q0 + c32 (a 16-lane group past R = 16 repeats the first 16)
+        const int i = lane & 15;
+        const int cb = min(q0 + (c32 & 16), R - 16);
+        const int col = cb + 4 * (i & 3), r = 16 * sub + 8 * h + (i >> 2);
+        const unsigned char* ap = st + 64 * 128;
+        const uint2 lo = ds_read_tr16(ap + shrink_kn_off<R>(r, col));
+        const uint2 hi = ds_read_tr16(ap + shrink_kn_off<R>(r + 4, col));
+        fa = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      } else {
+        fa = *reinterpret_cast<const bf16x8_t*>(st + a_off + ch);
+      }
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx, fa, acc, 0, 0, 0);
     }
   }
@@ -339,7 +415,7 @@ __device__ __forceinline__ void shrink_dma_emit(const f32x16_t& acc, int4 tile,
 // split's partial slots (every split owns at least one step, so every slot of
 // every LoRA row is written).  Summing the slots in order beats relaxed fp32
 // atomics into Z here, and is deterministic.
-template <int R, bool GATHER>
+template <int R, bool GATHER, bool KN>
 __global__ void __launch_bounds__(kLoraThreads)
 k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
              int gather_k, const bf16_t* __restrict__ At, int E, int L, int nad, int64_t K, int kwg_steps,
@@ -357,7 +433,8 @@ k_shrink_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict
   const int nk = min(nk_all, kt0 + kwg_steps) - kt0;
   if (nk <= 0) return;  // uniform
   f32x16_t acc = zero_acc();
-  shrink_dma_range<R, GATHER>(smem, X, x_rows, gather_slots, gather_k, At, E, L, K, tile, kt0, nk, acc);
+  shrink_dma_range<R, GATHER, KN>(smem, X, x_rows, gather_slots, gather_k, At, E, L, K, tile, kt0, nk,
+                                  acc);
   shrink_dma_emit<R>(acc, tile, parts, part_stride, R > 32 ? split : 2 * split + (threadIdx.x / kWave >> 1));
 }
 
@@ -407,7 +484,7 @@ __device__ __forceinline__ int64_t stream_x_row(const int32_t* __restrict__ gath
   return min(max(r, 0), x_rows - 1);
 }
 
-template <int R, int ST, bool GATHER, bool DET>
+template <int R, int ST, bool GATHER, bool DET, bool KN>
 __global__ void __launch_bounds__(kLoraThreads, 2)
 k_shrink_stream(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
                 int gather_k, const bf16_t* __restrict__ At, int E, int L, int nad, int64_t K,
@@ -466,7 +543,13 @@ k_shrink_stream(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restr
     for (int s = 0; s < ST; ++s) {
       const int64_t k = static_cast<int64_t>(kc) * KC + s * M::KSTEP + g * M::KPACK;
 #pragma unroll
-      for (int j = 0; j < RB; ++j) af[s][j] = M::load(ab + static_cast<int64_t>(16 * j + c) * K + k);
+      for (int j = 0; j < RB; ++j) {
+        if (KN)
+          af[s][j] = KnFrag<bf16_t>::load(ab, R, 16 * j, static_cast<int64_t>(kc) * KC + s * M::KSTEP,
+                                          true);
+        else
+          af[s][j] = M::load(ab + static_cast<int64_t>(16 * j + c) * K + k);
+      }
       xf[s] = M::load(w.xp + k);
     }
   };
@@ -522,7 +605,7 @@ k_shrink_stream(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restr
 // down:    D[p][n] += z_p.B[n] (ncols = h)
 // DB: double-buffer the row blocks (tiles of many rows); otherwise one block
 // buffer, whose first fetch still overlaps the weight loads.
-template <typename T, int R, int NB, bool GATE_UP, bool DB>
+template <typename T, int R, int NB, bool GATE_UP, bool DB, bool KN>
 __global__ void __launch_bounds__(kLoraThreads)
 k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L, int nad,
          const float* __restrict__ G, T* __restrict__ ACT, float* __restrict__ D, int64_t ncols,
@@ -561,7 +644,11 @@ k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L, in
       for (int ks = 0; ks < KS; ++ks) {
         const int q = ks * M::KSTEP + g * M::KPACK;
         const int64_t n = hh * ncols + c0 + 16 * j + c;
-        bf[hh][j][ks] = (lora && q < R && nb_ok[j]) ? M::load(Bb + n * R + q) : M::zero();
+        if (KN)  // B [R][nfull]: the rank is the k of the fragment
+          bf[hh][j][ks] = KnFrag<T>::load(Bb, nfull, hh * ncols + c0 + 16 * j, ks * M::KSTEP,
+                                          lora && q < R && nb_ok[j]);
+        else
+          bf[hh][j][ks] = (lora && q < R && nb_ok[j]) ? M::load(Bb + n * R + q) : M::zero();
       }
 
   // per 16-row block: z fragments and the four base values per column block
@@ -709,7 +796,7 @@ static ShrinkSplit shrink_split(const TilePlan& plan, int64_t K) {
   return sp;
 }
 
-template <typename T, int R, bool GATHER>
+template <typename T, int R, bool GATHER, bool KN>
 static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
                                 const int32_t* gather_slots, int gather_k, const void* At, int E,
                                 int L, int64_t K, float* Z, int S, const int4* ltiles,
@@ -724,28 +811,28 @@ static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
     constexpr int ST = ShrinkStream<R>::ST;
     const bool det = parts != nullptr;
     auto kern = ShrinkStream<R>::steps(K) == ST
-                    ? (det ? k_shrink_stream<R, ST, GATHER, true> : k_shrink_stream<R, ST, GATHER, false>)
-                    : (det ? k_shrink_stream<R, 2, GATHER, true> : k_shrink_stream<R, 2, GATHER, false>);
+                    ? (det ? k_shrink_stream<R, ST, GATHER, true, KN> : k_shrink_stream<R, ST, GATHER, false, KN>)
+                    : (det ? k_shrink_stream<R, 2, GATHER, true, KN> : k_shrink_stream<R, 2, GATHER, false, KN>);
     hipLaunchKernelGGL(kern, dim3(kStreamWgs), dim3(kLoraThreads), 0, stream,
                        static_cast<const bf16_t*>(X), x_rows, gather_slots, gather_k,
                        static_cast<const bf16_t*>(At), E, L, plan.nad, K, Z, ltiles, counts,
                        parts, stride);
   } else if (plan.lora_db && sizeof(T) == 2) {
     // tall bf16 tiles: DMA ring, about 1024 workgroups of (tile, K range), partial slots
-    hipLaunchKernelGGL((k_shrink_dma<R, GATHER>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((k_shrink_dma<R, GATHER, KN>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const bf16_t*>(X), x_rows,
                        gather_slots, gather_k, static_cast<const bf16_t*>(At), E, L, plan.nad, K,
                        sp.kwg_steps, sp.nsplit, ltiles, counts, parts, stride);
   } else if (plan.lora_db) {
     // tall tiles: ~1024 workgroups, each wave a 16-row block over the split's K range
     constexpr int STEPS = R > 32 ? 2 : 4;
-    hipLaunchKernelGGL((k_shrink_tall<T, R, STEPS, GATHER>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((k_shrink_tall<T, R, STEPS, GATHER, KN>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const T*>(X), x_rows,
                        gather_slots, gather_k, static_cast<const T*>(At), E, L, plan.nad, K, sp.kwg,
                        sp.nsplit, Z, ltiles, counts, parts, stride);
   } else {
     constexpr int STEPS = R <= 32 ? 8 : 4;
-    hipLaunchKernelGGL((k_shrink<T, R, STEPS, GATHER>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((k_shrink<T, R, STEPS, GATHER, KN>), dim3(static_cast<unsigned>(grid)),
                        dim3(kLoraThreads), 0, stream, static_cast<const T*>(X), x_rows, gather_slots,
                        gather_k, static_cast<const T*>(At), E, L, plan.nad, K, sp.nsplit, Z, ltiles,
                        counts, parts, stride);
@@ -755,17 +842,28 @@ static hipError_t shrink_launch(const TilePlan& plan, const void* X, int x_rows,
   return e;
 }
 
+template <typename T, bool GATHER, bool KN>
+static hipError_t shrink_dispatch_kn(int rank, const TilePlan& plan, const void* X, int x_rows,
+                                     const int32_t* gather_slots, int gather_k, const void* At, int E,
+                                     int L, int64_t K, float* Z, int S, const int4* ltiles,
+                                     const int32_t* counts, float* parts, hipStream_t stream) {
+  switch (rank) {
+    case 16: return shrink_launch<T, 16, GATHER, KN>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
+    case 32: return shrink_launch<T, 32, GATHER, KN>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
+    case 64: return shrink_launch<T, 64, GATHER, KN>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, bool GATHER>
 static hipError_t shrink_dispatch(int rank, const TilePlan& plan, const void* X, int x_rows,
                                   const int32_t* gather_slots, int gather_k, const void* At, int E,
                                   int L, int64_t K, float* Z, int S, const int4* ltiles,
                                   const int32_t* counts, float* parts, hipStream_t stream) {
-  switch (rank) {
-    case 16: return shrink_launch<T, 16, GATHER>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
-    case 32: return shrink_launch<T, 32, GATHER>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
-    case 64: return shrink_launch<T, 64, GATHER>(plan, X, x_rows, gather_slots, gather_k, At, E, L, K, Z, S, ltiles, counts, parts, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return plan.kn ? shrink_dispatch_kn<T, GATHER, true>(rank, plan, X, x_rows, gather_slots, gather_k, At,
+                                                       E, L, K, Z, S, ltiles, counts, parts, stream)
+                 : shrink_dispatch_kn<T, GATHER, false>(rank, plan, X, x_rows, gather_slots, gather_k,
+                                                        At, E, L, K, Z, S, ltiles, counts, parts, stream);
 }
 
 hipError_t launch_shrink(int dtype, int rank, const TilePlan& plan, const void* X, int x_rows,
@@ -800,14 +898,11 @@ static hipError_t expand_launch(const TilePlan& plan, const float* Z, const void
   constexpr int COLS = kLoraWaves * 16 * NB;
   const int n_chunks = static_cast<int>((ncols + COLS - 1) / COLS);
   const int64_t grid = static_cast<int64_t>(plan.max_lt) * n_chunks;
-  if (plan.lora_db)
-    hipLaunchKernelGGL((k_expand<T, R, NB, GU, true>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kLoraThreads), 0, stream, Z, static_cast<const T*>(Bt), E, L, plan.nad, G,
-                       static_cast<T*>(ACT), D, ncols, ltiles, counts, n_chunks);
-  else
-    hipLaunchKernelGGL((k_expand<T, R, NB, GU, false>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kLoraThreads), 0, stream, Z, static_cast<const T*>(Bt), E, L, plan.nad, G,
-                       static_cast<T*>(ACT), D, ncols, ltiles, counts, n_chunks);
+  auto kern = plan.lora_db ? (plan.kn ? k_expand<T, R, NB, GU, true, true> : k_expand<T, R, NB, GU, true, false>)
+                           : (plan.kn ? k_expand<T, R, NB, GU, false, true> : k_expand<T, R, NB, GU, false, false>);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kLoraThreads), 0, stream, Z,
+                     static_cast<const T*>(Bt), E, L, plan.nad, G, static_cast<T*>(ACT), D, ncols,
+                     ltiles, counts, n_chunks);
   return hipGetLastError();
 }
 

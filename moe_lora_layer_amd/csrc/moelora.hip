@@ -52,7 +52,8 @@ int check_dims(const moelora_dims* d) {
   if (d == nullptr) return MOELORA_ERR_NULL;
   if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
   if (d->rank != 16 && d->rank != 32 && d->rank != 64) return MOELORA_ERR_UNSUPPORTED;
-  if ((d->flags & ~(MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_BASE_ONLY | MOELORA_FLAG_UNFUSED)) != 0)
+  if ((d->flags & ~(MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_BASE_ONLY | MOELORA_FLAG_UNFUSED |
+                    MOELORA_FLAG_IN_OUT)) != 0)
     return MOELORA_ERR_UNSUPPORTED;
   if (d->tokens < 0 || d->hidden <= 0 || d->intermediate <= 0) return MOELORA_ERR_DIMS;
   if (d->hidden % 64 != 0 || d->intermediate % 64 != 0) return MOELORA_ERR_DIMS;
@@ -122,6 +123,7 @@ TilePlan make_plan(const moelora_dims* d) {
   // fp32 atomics into Z (a few hundred split tiles each adding 64 x r values)
   p.shrink_partials = p.det || (p.lora_db && d->dtype == MOELORA_BF16);
   p.nad = d->adapters;
+  p.kn = (d->flags & MOELORA_FLAG_IN_OUT) != 0;
   return p;
 }
 

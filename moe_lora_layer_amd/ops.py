@@ -21,6 +21,7 @@ MOELORA_F32, MOELORA_BF16 = 0, 1
 MOELORA_FLAG_DETERMINISTIC = 1
 MOELORA_FLAG_BASE_ONLY = 2
 MOELORA_FLAG_UNFUSED = 4
+MOELORA_FLAG_IN_OUT = 8
 STAGES = ["prep", "zero", "shrink_gate_up", "gemm_gate_up", "expand_gate_up", "shrink_down",
           "gemm_down", "expand_down", "combine"]
 _TORCH_DT = {MOELORA_F32: torch.float32, MOELORA_BF16: torch.bfloat16}
@@ -115,10 +116,27 @@ def status_string(rc: int) -> str:
     return library().moelora_status_string(rc).decode()
 
 
-def _flags(deterministic, base_only, unfused) -> int:
+def _flags(deterministic, base_only, unfused, in_out=False) -> int:
     return ((MOELORA_FLAG_DETERMINISTIC if deterministic else 0) |
             (MOELORA_FLAG_BASE_ONLY if base_only else 0) |
-            (MOELORA_FLAG_UNFUSED if unfused else 0))
+            (MOELORA_FLAG_UNFUSED if unfused else 0) |
+            (MOELORA_FLAG_IN_OUT if in_out else 0))
+
+
+def weight_shapes(d) -> dict:
+    """Shapes of the weight arrays the library expects for dims d: K-contiguous
+    (transposed) by default, h_in x h_out with MOELORA_FLAG_IN_OUT."""
+    io = bool(d.flags & MOELORA_FLAG_IN_OUT)
+    if isinstance(d, DenseDims):
+        K, N, L, r = d.in_features, d.out_features, d.adapters, d.rank
+        return ({"w": (K, N), "a": (L, K, r), "b": (L, r, N)} if io else
+                {"w": (N, K), "a": (L, r, K), "b": (L, N, r)})
+    h, I, E, L, r = d.hidden, d.intermediate, d.experts, d.adapters, d.rank
+    if io:
+        return {"w_gate_up": (E, h, 2 * I), "w_down": (E, I, h), "a_gate_up": (L, E, h, r),
+                "b_gate_up": (L, E, r, 2 * I), "a_down": (L, E, I, r), "b_down": (L, E, r, h)}
+    return {"w_gate_up": (E, 2 * I, h), "w_down": (E, h, I), "a_gate_up": (L, E, r, h),
+            "b_gate_up": (L, E, 2 * I, r), "a_down": (L, E, r, I), "b_down": (L, E, h, r)}
 
 
 def _check(rc: int, what: str):
@@ -127,23 +145,25 @@ def _check(rc: int, what: str):
 
 
 def make_dims(tokens, hidden, intermediate, experts, top_k, adapters, rank, dtype,
-              deterministic=False, base_only=False, unfused=False, flags=None, plan=None) -> Dims:
+              deterministic=False, base_only=False, unfused=False, in_out=False, flags=None,
+              plan=None) -> Dims:
     if isinstance(dtype, str):
         dtype = _DT_NAME[dtype]
     elif isinstance(dtype, torch.dtype):
         dtype = MOELORA_BF16 if dtype == torch.bfloat16 else MOELORA_F32
     if flags is None:
-        flags = _flags(deterministic, base_only, unfused)
+        flags = _flags(deterministic, base_only, unfused, in_out)
     return Dims(int(tokens), int(hidden), int(intermediate), int(experts), int(top_k),
                 int(adapters), int(rank), int(dtype), int(flags), make_plan(plan))
 
 
 def dims_for(cfg, tokens=None, deterministic=False, base_only=False, unfused=False,
-             plan=None) -> Dims:
+             in_out=False, plan=None) -> Dims:
     """Dims of a workload config (moe_lora_layer_amd.synth.LayerConfig)."""
     return make_dims(cfg.tokens if tokens is None else tokens, cfg.hidden, cfg.intermediate,
                      cfg.experts, cfg.top_k, cfg.adapters, cfg.rank, cfg.dtype,
-                     deterministic=deterministic, base_only=base_only, unfused=unfused, plan=plan)
+                     deterministic=deterministic, base_only=base_only, unfused=unfused,
+                     in_out=in_out, plan=plan)
 
 
 def forward_plan(d: Dims) -> dict:
@@ -273,12 +293,10 @@ def forward(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down, b_down,
     T, h, I, E, k, L, r = d.tokens, d.hidden, d.intermediate, d.experts, d.top_k, d.adapters, d.rank
     dt = _TORCH_DT[d.dtype]
     _expect(x, "x", (T, h), dt, dev)
-    _expect(w_gate_up, "w_gate_up", (E, 2 * I, h), dt, dev)
-    _expect(w_down, "w_down", (E, h, I), dt, dev)
-    _expect(a_gate_up, "a_gate_up", (L, E, r, h), dt, dev)
-    _expect(b_gate_up, "b_gate_up", (L, E, 2 * I, r), dt, dev)
-    _expect(a_down, "a_down", (L, E, r, I), dt, dev)
-    _expect(b_down, "b_down", (L, E, h, r), dt, dev)
+    ws = weight_shapes(d)
+    for name, t in (("w_gate_up", w_gate_up), ("w_down", w_down), ("a_gate_up", a_gate_up),
+                    ("b_gate_up", b_gate_up), ("a_down", a_down), ("b_down", b_down)):
+        _expect(t, name, ws[name], dt, dev)
     if topk_ids is not None:
         _expect(topk_ids, "topk_ids", (T, k), torch.int32, dev)
     _expect(topk_weights, "topk_weights", (T, k), torch.float32, dev)
@@ -319,12 +337,10 @@ def forward_noalloc(d: Dims, x, w_gate_up, w_down, a_gate_up, b_gate_up, a_down,
     T, h, I, E, k, L, r = d.tokens, d.hidden, d.intermediate, d.experts, d.top_k, d.adapters, d.rank
     dt = _TORCH_DT[d.dtype]
     _expect(x, "x", (T, h), dt, dev)
-    _expect(w_gate_up, "w_gate_up", (E, 2 * I, h), dt, dev)
-    _expect(w_down, "w_down", (E, h, I), dt, dev)
-    _expect(a_gate_up, "a_gate_up", (L, E, r, h), dt, dev)
-    _expect(b_gate_up, "b_gate_up", (L, E, 2 * I, r), dt, dev)
-    _expect(a_down, "a_down", (L, E, r, I), dt, dev)
-    _expect(b_down, "b_down", (L, E, h, r), dt, dev)
+    ws = weight_shapes(d)
+    for name, t in (("w_gate_up", w_gate_up), ("w_down", w_down), ("a_gate_up", a_gate_up),
+                    ("b_gate_up", b_gate_up), ("a_down", a_down), ("b_down", b_down)):
+        _expect(t, name, ws[name], dt, dev)
     if topk_ids is not None:
         _expect(topk_ids, "topk_ids", (T, k), torch.int32, dev)
     _expect(topk_weights, "topk_weights", (T, k), torch.float32, dev)
@@ -369,10 +385,10 @@ class MoELoRALayer:
 
 
 def make_dense_dims(tokens, in_features, out_features, adapters, rank, dtype, deterministic=False,
-                    base_only=False, unfused=False, plan=None) -> DenseDims:
+                    base_only=False, unfused=False, in_out=False, plan=None) -> DenseDims:
     if isinstance(dtype, str):
         dtype = _DT_NAME[dtype]
-    flags = _flags(deterministic, base_only, unfused)
+    flags = _flags(deterministic, base_only, unfused, in_out)
     return DenseDims(int(tokens), int(in_features), int(out_features), int(adapters), int(rank),
                      int(dtype), flags, make_plan(plan))
 
@@ -399,9 +415,10 @@ def dense_forward(d: DenseDims, x, w, a, b, adapter_ids, *, out=None, workspace_
     T, K, N, L, r = d.tokens, d.in_features, d.out_features, d.adapters, d.rank
     dt = _TORCH_DT[d.dtype]
     _expect(x, "x", (T, K), dt, dev)
-    _expect(w, "w", (N, K), dt, dev)
-    _expect(a, "a", (L, r, K), dt, dev)
-    _expect(b, "b", (L, N, r), dt, dev)
+    ws = weight_shapes(d)
+    _expect(w, "w", ws["w"], dt, dev)
+    _expect(a, "a", ws["a"], dt, dev)
+    _expect(b, "b", ws["b"], dt, dev)
     _expect(adapter_ids, "adapter_ids", (T,), torch.int32, dev)
     if out is None:
         out = torch.empty((T, N), dtype=dt, device=dev)

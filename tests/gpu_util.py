@@ -31,6 +31,16 @@ def to_dev(a: np.ndarray, dtype: str, dev) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
+def in_out(inp: dict) -> dict:
+    """The weights of a workload in the page's h_in x h_out orientation (the
+    layout of MOELORA_FLAG_IN_OUT): every K-contiguous weight array transposed
+    in its last two axes.  The oracle keeps taking the K-contiguous arrays."""
+    out = dict(inp)
+    for n in WEIGHTS:
+        out[n] = np.ascontiguousarray(np.swapaxes(inp[n], -1, -2))
+    return out
+
+
 def device_inputs(inp: dict, cfg, dev) -> dict:
     d = {n: to_dev(inp[n], cfg.dtype, dev) for n in ["x"] + WEIGHTS if n in inp}
     d["logits"] = torch.from_numpy(inp["logits"]).to(dev)

@@ -52,7 +52,8 @@ def test_status_strings():
     (dict(adapters=0), ERR_DIMS), (dict(experts=256, adapters=257), ERR_DIMS),
     (dict(experts=1, top_k=1, adapters=65537), ERR_DIMS), (dict(experts=1, top_k=1, adapters=65536), OK),
     (dict(experts=256, adapters=256), OK), (dict(experts=256, adapters=256, flags=2), OK),
-    (dict(tokens=1 << 30, top_k=2), ERR_DIMS), (dict(flags=8), ERR_UNSUPPORTED),
+    (dict(tokens=1 << 30, top_k=2), ERR_DIMS), (dict(flags=8), OK), (dict(flags=16), ERR_UNSUPPORTED),
+    (dict(flags=15), OK),
     (dict(flags=-1), ERR_UNSUPPORTED), (dict(flags=3), OK), (dict(flags=7), OK),
     (dict(experts=128, adapters=64), OK), (dict(experts=128, adapters=64, flags=2), OK),
 ])
