@@ -85,7 +85,11 @@ typedef enum moelora_dtype {
  *                   down to a count whose K ranges are all non-empty
  *   ksplit_down     the same for the down GEMM (the dense projection's GEMM)
  *   fuse            1: every projection whose GEMM can (bf16, unsplit K) runs
- *                   its LoRA expand in the GEMM epilogue; 2: none does
+ *                   its LoRA expand in the GEMM epilogue; 2: none does; 3: as
+ *                   1, and the fused gate_up epilogue also computes the down
+ *                   projection's LoRA shrink (MOELORA_FUSED_DOWN_SHRINK; never
+ *                   the automatic choice: slower on MI355X at every shape
+ *                   measured, kept for callers whose ACT re-read costs more)
  * Out-of-range values make every call that takes the dims return
  * MOELORA_ERR_UNSUPPORTED.
  */
@@ -372,6 +376,13 @@ int moelora_forward_workspace_layout(const moelora_dims* dims, size_t offsets[5]
  */
 #define MOELORA_FUSED_GATE_UP 1
 #define MOELORA_FUSED_DOWN 2
+/* MOELORA_FUSED_DOWN_SHRINK: the fused gate_up epilogue also computes the down
+ * projection's LoRA shrink (z2 = a A_dn, summed over its columns with relaxed
+ * fp32 atomics, or per-N-tile partials summed in order with
+ * MOELORA_FLAG_DETERMINISTIC); the MOELORA_STAGE_SHRINK_DOWN stage is then
+ * empty (deterministic: only the ordered sum).  Set when the gate_up
+ * expand is fused and dims->plan.fuse is 3. */
+#define MOELORA_FUSED_DOWN_SHRINK 4
 int moelora_forward_fusion(const moelora_dims* dims, int* flags);
 
 /*

@@ -193,9 +193,18 @@ __device__ __forceinline__ void atomic_add_relaxed(float* p, float v) {
 //     the fragments are read with ds_read_b64_tr_b16 (tr16_frag).
 // Every lane of a group must execute the transposes (no divergence).
 // ---------------------------------------------------------------------------
+// v of lane ^ MASK (MASK 1, 2, 4), with DPP moves on the vector ALU: quad
+// permutations for 1 and 2, and for 4 a row shift by 4 towards or away from
+// lane 0 (lanes with bit 2 clear read lane + 4, the others lane - 4).
 template <int MASK>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-  return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), MASK, kWave));
+  static_assert(MASK == 1 || MASK == 2 || MASK == 4, "xor_lane: 1, 2 or 4");
+  const int x = static_cast<int>(v);
+  if (MASK == 1) return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+  if (MASK == 2) return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+  const int up = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);    // row_shl:4, lane + 4
+  const int down = __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, true);  // row_shr:4, lane - 4
+  return static_cast<uint32_t>((threadIdx.x & 4) ? down : up);
 }
 
 // 8 x 8 bf16 transpose across the aligned 8-lane group of this lane: on entry

@@ -163,7 +163,11 @@ __device__ __forceinline__ uint4 masked(uint4 v, uint32_t m) {
 // D.  The vLLM blog page "Multi-LoRA" (section "Implementing Multi-LoRA
 // inference for MoE models in vLLM") names folding the LoRA add into the base
 // GEMM's output as the next fusion step.
-enum { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_DOWN = 2 };
+// EPI_GATE_UP_FOLD: EPI_GATE_UP plus the down projection's shrink folded in
+// (an instantiation of its own, so that the other kernels carry none of it).
+enum { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_DOWN = 2, EPI_GATE_UP_FOLD = 3 };
+__host__ __device__ constexpr bool is_gu(int epi) { return epi == EPI_GATE_UP || epi == EPI_GATE_UP_FOLD; }
+__host__ __device__ constexpr int expand_form(int epi) { return is_gu(epi) ? EPI_GATE_UP : epi; }
 
 // One lane's 16 bytes of a 1 KiB direct-to-LDS copy (lane i lands at dst + 16 i).
 __device__ __forceinline__ void dma_piece(const void* src, unsigned char* dst) {
@@ -316,6 +320,133 @@ __device__ __forceinline__ void staged_lora_expand(f32x16_t (&acc)[FM][FN], cons
   }
 }
 
+// The down projection's LoRA shrink folded into the fused gate_up epilogue:
+// once a tile has its activation a = SiLU(gate) * up (rounded to bf16, the
+// values it stores), it adds its tn columns' share of z2[p] = a[p] . A_dn[l][e]
+// (the sum over the intermediate columns, section "Implementing Multi-LoRA
+// inference for MoE models in vLLM" of the Multi-LoRA page: the shrink of the
+// down projection) for each of its rows, so that no pass re-reads ACT.
+// acc[i][j][r], j < FG: the lane's activation values (accumulator layout:
+// block i of 32 rows from rw0, element r at row acc_row(r, h), intermediate
+// column col[j]; wr[j]: this lane owns that column, i.e. when a wave holds one
+// 32-column fragment the lane holds the gate half; col_ok[j]: the column is
+// below I).  The tile's rows [row0, row_end) (at most tm) x columns
+// [it0, it0 + tn) go to LDS column-major (a column's tm rows contiguous, four
+// rows per 8-byte write), the layout of a k-major operand, and are read back as
+// MFMA row fragments with transposed reads; each wave takes (32-row block,
+// 32-rank block) items and, per adapter bucket meeting a block, loads all of
+// the bucket's A_dn fragments for the tile's columns, then multiplies (rows
+// outside the bucket zero, K = tn) and adds the results to Z2 (atomics, or the
+// N-tile's partial slot).
+__device__ __forceinline__ int fold_off(int row, int col, int pitch) {
+  // 64-byte groups of a row XORed so that four consecutive rows of a
+  // transposed read sit on different banks
+  const int x = pitch >= 256 ? (row & 3) << 2 : (pitch == 128 ? ((row >> 1) & 1) << 2 : 0);
+  return row * pitch + (((col >> 3) ^ x) << 4) + ((col & 7) << 1);
+}
+
+template <int FM, int FN, int FG, bool KN>
+__device__ __forceinline__ void folded_down_shrink(const f32x16_t (&acc)[FM][FN],
+                                                   const int64_t (&col)[FN], const bool (&wr)[FN],
+                                                   const bool (&col_ok)[FN], int rw0,
+                                                   const LoraEpilogue& lora, unsigned char* lds,
+                                                   int nwaves, int e, int row0, int row_end, int tm,
+                                                   int tn, int64_t it0, int64_t I, int nt, int wave,
+                                                   int lane) {
+  const int c32 = lane & 31, h = lane >> 5;
+  const int rk = lora.rank, pitch = tm * 2;
+  lds_barrier();  // the epilogue before this one is done with the LDS
+  // every (row < row_end, column) of the tile is written: past I with zeros
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jg = 0; jg < FG; ++jg) {
+      if (!wr[jg]) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int p = rw0 + 32 * i + 8 * g + 4 * h;  // rows p .. p + 3
+        if (p >= row_end) continue;
+        const f32x16_t& a = acc[i][jg];
+        const uint32_t lo = col_ok[jg] ? (f32_to_bf16(a[4 * g]) | (static_cast<uint32_t>(f32_to_bf16(a[4 * g + 1])) << 16)) : 0u;
+        const uint32_t hi = col_ok[jg] ? (f32_to_bf16(a[4 * g + 2]) | (static_cast<uint32_t>(f32_to_bf16(a[4 * g + 3])) << 16)) : 0u;
+        *reinterpret_cast<uint2*>(lds + fold_off(static_cast<int>(col[jg] - it0), p - row0, pitch)) =
+            make_uint2(lo, hi);
+      }
+    }
+  lds_barrier();
+  const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
+  const int nblk = (min(row_end - row0, tm) + 31) / 32;
+  const int nqb = (rk + 31) / 32;
+  const int nks = tn / 16;  // 4 or 8
+  for (int b = wave; b < nblk * nqb; b += nwaves) {  // (row block, rank block) items
+    const int rb = row0 + 32 * (b / nqb), qb = b % nqb;
+    const int rb1 = min(row_end, rb + 32);
+    f32x16_t z = zero_acc();
+    bool any = false;
+    // adapter buckets meeting rows [rb, rb1); a base-only bucket has no LoRA
+    int l = 0, hi_l = lora.adapters - 1;
+    while (l < hi_l) {
+      const int mid = (l + hi_l + 1) >> 1;
+      if (off[mid] <= rb) l = mid; else hi_l = mid - 1;
+    }
+    for (; l < lora.adapters && off[l] < rb1; ++l) {
+      const int s0 = max(rb, off[l]), s1 = min(rb1, off[l + 1]);
+      if (s0 >= s1) continue;  // uniform
+      any = true;
+      const bf16_t* A = lora.dn_a + (static_cast<int64_t>(l) * lora.experts + e) * rk * I;
+      // all the bucket's A_dn fragments for the tile's columns first
+      bf16x8_t fb[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks >= nks) break;
+        const int64_t k = it0 + 16 * ks + 8 * h;  // this lane's 8 columns
+        if (KN) {
+          // A_dn [I][r]: the lane's aligned 8-lane group loads 8 columns (k-rows)
+          // of 8 ranks and transposes them
+          const int qc = 32 * qb + (c32 & 24);
+          const bool ok = qc < rk && k < I;
+          const uint4 v = transpose8(*reinterpret_cast<const uint4*>(
+              A + (ok ? (k + (c32 & 7)) * rk + qc : 0)));
+          fb[ks] = ok ? __builtin_bit_cast(bf16x8_t, v) : Mfma<bf16_t>::zero();
+        } else {
+          const int q = 32 * qb + c32;
+          const bool ok = q < rk && k < I;
+          fb[ks] = ok ? *reinterpret_cast<const bf16x8_t*>(A + static_cast<int64_t>(q) * I + k)
+                      : Mfma<bf16_t>::zero();
+        }
+      }
+      const int p = rb + c32;
+      const bool in = p >= s0 && p < s1;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks >= nks) break;
+        // rows rb .. rb + 31 (the lane's row c32), columns 16 ks + 8 h ..
+        const int i = lane & 15;
+        const int pl = rb - row0 + (c32 & 16) + 4 * (i & 3);
+        const int cl = 16 * ks + 8 * h + (i >> 2);
+        const uint2 u0 = ds_read_tr16(lds + fold_off(cl, pl, pitch));
+        const uint2 u1 = ds_read_tr16(lds + fold_off(cl + 4, pl, pitch));
+        bf16x8_t fa = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+        if (!in) fa = Mfma<bf16_t>::zero();
+        z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[ks], z, 0, 0, 0);
+      }
+    }
+    if (!any) continue;  // uniform
+    const int q = 32 * qb + c32;
+    if (q >= rk) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int p = rb + acc_row(r, h);
+      if (p >= rb1) continue;
+      const int64_t idx = static_cast<int64_t>(p) * rk + q;
+      if (lora.dn_parts != nullptr)
+        lora.dn_parts[nt * lora.dn_part_stride + idx] = z[r];
+      else
+        atomic_add_relaxed(lora.dn_z + idx, z[r]);
+    }
+  }
+}
+
 // Adapter buckets of expert e meeting rows [row0, row_end), as [lb, ub); a
 // base-only bucket, if any, comes last in the expert and is left out.
 __device__ __forceinline__ void lora_buckets(const LoraEpilogue& lora, int e, int row0, int row_end,
@@ -430,7 +561,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   // the weight column (gate_up: up * I + intermediate column) of tile row
   // `row`, clamped to a valid one when it is past the end (ok = false)
   auto w_col = [&](int row, bool& ok) -> int64_t {
-    if (EPI == EPI_GATE_UP) {
+    if (is_gu(EPI)) {
       int up;
       const int64_t ic = gu_col(row / WTN, (row % WTN) / 32, row & 31, up);
       ok = ic < I;
@@ -470,7 +601,10 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   const int nk_per = (nk_all + ksplit - 1) / ksplit;
   const int kbeg = min(nk_all, ks * nk_per);
   const int nk = min(nk_all, kbeg + nk_per) - kbeg;  // K-steps of this workgroup
-  const int kstart = (ROT && nk > 0) ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk) : 0;
+  // (not for k-major weights: there the workgroups of neighbouring N-tiles
+  // read neighbouring pieces of the same k-rows, best at the same time)
+  const int kstart =
+      (ROT && !KN && nk > 0) ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk) : 0;
   uint4 a_reg[P][A_CH], b_reg[P][B_CH];
   auto gload = [&](int slot, int kt) {
     int kk = kt + kstart;
@@ -593,7 +727,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     bool col_ok[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      if (EPI == EPI_GATE_UP) {
+      if (is_gu(EPI)) {
         int up;
         col[j] = gu_col(wn, j, c32, up);
         col_ok[j] = col[j] < I;
@@ -611,7 +745,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
       int lrow[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        if (EPI == EPI_GATE_UP) {
+        if (is_gu(EPI)) {
           int up;
           const int64_t ic = gu_col(wn, j, c32, up);
           lrow[j] = up * (BN / 2) + static_cast<int>(ic - it0);
@@ -621,9 +755,9 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
       }
       int lb, ub;
       lora_buckets(lora, e, row0, row_end, lb, ub);
-      staged_lora_expand<EPI, FM, FN, KN>(acc, lora, &smem[0][0], 2 * (BM + BN) * ROWB, NT_ / kWave, e, lb,
+      staged_lora_expand<expand_form(EPI), FM, FN, KN>(acc, lora, &smem[0][0], 2 * (BM + BN) * ROWB, NT_ / kWave, e, lb,
                                       ub, row0, row_end, BM, BN,
-                                      EPI == EPI_GATE_UP ? it0 : n0, N, lrow, rw0 < rw1, rw0, rw1,
+                                      is_gu(EPI) ? it0 : n0, N, lrow, rw0 < rw1, rw0, rw1,
                                       wave, lane, c32, h);
     } else {
       // The expand with the B^T rows staged in the (now idle) LDS stages, a
@@ -741,8 +875,11 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
         __syncthreads();  // every wave is done with the group before the next one lands
       }
     }
-    if (EPI == EPI_GATE_UP) {
+    if (is_gu(EPI)) {
       constexpr int FG = FN >= 2 ? FN / 2 : 1;  // gate fragments
+      bool wr[FN];  // the lane owns column col[j] (gate half of the wave's fragment)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) wr[j] = j < FG && (FN >= 2 || c32 < 16);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -752,10 +889,14 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
             // FN == 1: the up value sits 16 lanes over (every lane takes part)
             const float g = acc[i][j][r];
             const float u = FN >= 2 ? acc[i][FN >= 2 ? j + FG : 0][r] : __shfl_xor(g, 16);
+            acc[i][j][r] = silu(g) * u;  // the activation, in place of gate
             const int p = rw0 + 32 * i + acc_row(r, h);
-            if ((FN >= 2 || c32 < 16) && p < row_end && col_ok[j])
-              lora.act[static_cast<int64_t>(p) * I + col[j]] = f32_to_bf16(silu(g) * u);
+            if (wr[j] && col_ok[j] && p < row_end)
+              lora.act[static_cast<int64_t>(p) * I + col[j]] = f32_to_bf16(acc[i][j][r]);
           }
+      if constexpr (EPI == EPI_GATE_UP_FOLD)
+        folded_down_shrink<FM, FN, FG, KN>(acc, col, wr, col_ok, rw0, lora, &smem[0][0], NT_ / kWave,
+                                           e, row0, row_end, BM, BN / 2, it0, I, nt, wave, lane);
     } else {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -811,8 +952,8 @@ template <bool KN, typename T, int BM, int BN, int WM, int WN, int P, bool NT, b
           int EPI = EPI_STORE>
 static hipError_t lds_launch_epi(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue& lora,
                                  hipStream_t stream) {
-  const int64_t cols = EPI == EPI_GATE_UP ? a.N / 2 : a.N;
-  const int tn = EPI == EPI_GATE_UP ? BN / 2 : BN;
+  const int64_t cols = is_gu(EPI) ? a.N / 2 : a.N;
+  const int tn = is_gu(EPI) ? BN / 2 : BN;
   const int n_ntiles = static_cast<int>((cols + tn - 1) / tn);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
   hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE, EPI, KN>),
@@ -829,6 +970,9 @@ template <bool KN, typename T, int BM, int BN, int WM, int WN, int P, bool NT, b
 static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue* lora,
                              hipStream_t stream) {
   if constexpr (sizeof(T) == 2 && BM <= 128) {  // bf16 256-row tiles run k_gemm_dma
+    if (lora != nullptr && lora->act != nullptr && lora->dn_a != nullptr)
+      return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
+                            EPI_GATE_UP_FOLD>(plan, a, *lora, stream);
     if (lora != nullptr && lora->act != nullptr)
       return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
                             EPI_GATE_UP>(plan, a, *lora, stream);
@@ -903,8 +1047,8 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
   // (up, j = 1), so gate and up of one output meet in the same lane.
   // Otherwise 256 columns n of N, wave wn owning [n0 + 64 wn, +64).
   const int64_t I = N / 2;
-  const int64_t cols = EPI == EPI_GATE_UP ? I : N;
-  const int64_t n0 = static_cast<int64_t>(nt) * (EPI == EPI_GATE_UP ? 128 : kDmaTile);
+  const int64_t cols = is_gu(EPI) ? I : N;
+  const int64_t n0 = static_cast<int64_t>(nt) * (is_gu(EPI) ? 128 : kDmaTile);
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave >> 2, wn = wave & 3;
@@ -926,7 +1070,7 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
     a_src[j] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + lch * 8;
     if (!KN) {
       int64_t wrow;
-      if (EPI == EPI_GATE_UP) {  // B tile row rt = 64 wn' + 32 half + c
+      if (is_gu(EPI)) {  // B tile row rt = 64 wn' + 32 half + c
         const int64_t i = min(n0 + 32 * (rt >> 6) + (rt & 31), I - 1);
         wrow = ((rt >> 5) & 1) * I + i;
       } else {
@@ -940,7 +1084,7 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
       const int kr = 8 * wave + 2 * j + (lane >> 5);
       const int t = 8 * ((lane & 31) ^ ((kr & 3) << 2));
       int64_t col;
-      if (EPI == EPI_GATE_UP) {
+      if (is_gu(EPI)) {
         const int64_t i = n0 + 32 * (t >> 6) + (t & 31);
         col = ((t >> 5) & 1) * I + (i < I ? i : 0);
       } else {
@@ -1066,7 +1210,7 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
   bool col_ok[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    col[j] = EPI == EPI_GATE_UP ? n0 + 32 * wn + c32 : n0 + 64 * wn + 32 * j + c32;
+    col[j] = is_gu(EPI) ? n0 + 32 * wn + c32 : n0 + 64 * wn + 32 * j + c32;
     col_ok[j] = col[j] < cols;
   }
   const int rw0 = row0 + 128 * wm;                 // this wave's rows [rw0, rw1)
@@ -1078,22 +1222,27 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
     int lrow[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      lrow[j] = EPI == EPI_GATE_UP ? j * (kDmaTile / 2) + 32 * wn + c32 : 64 * wn + 32 * j + c32;
-    staged_lora_expand<EPI, 4, 2, KN>(acc, lora, smem, 2 * kDmaStage, kDmaThreads / kWave, e, lb, ub,
+      lrow[j] = is_gu(EPI) ? j * (kDmaTile / 2) + 32 * wn + c32 : 64 * wn + 32 * j + c32;
+    staged_lora_expand<expand_form(EPI), 4, 2, KN>(acc, lora, smem, 2 * kDmaStage, kDmaThreads / kWave, e, lb, ub,
                                   row0, row_end, kDmaTile, kDmaTile, n0, N, lrow, rw0 < rw1, rw0,
                                   rw1, wave, lane, c32, h);
   }
 
-  if (EPI == EPI_GATE_UP) {
+  if (is_gu(EPI)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        acc[i][0][r] = silu(acc[i][0][r]) * acc[i][1][r];  // the activation, in place of gate
         const int p = rw0 + 32 * i + acc_row(r, h);
         if (p < row_end && col_ok[0])
-          lora.act[static_cast<int64_t>(p) * I + col[0]] =
-              f32_to_bf16(silu(acc[i][0][r]) * acc[i][1][r]);
+          lora.act[static_cast<int64_t>(p) * I + col[0]] = f32_to_bf16(acc[i][0][r]);
       }
+    if constexpr (EPI == EPI_GATE_UP_FOLD) {
+      const bool wr[2] = {true, false};
+      folded_down_shrink<4, 2, 1, KN>(acc, col, wr, col_ok, rw0, lora, smem, kDmaThreads / kWave, e,
+                                      row0, row_end, kDmaTile, 128, n0, I, nt, wave, lane);
+    }
     return;
   }
   auto store = [&](auto&& put) {
@@ -1223,12 +1372,12 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
 template <bool GATHER, int EPI, bool KN>
 static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue& lora,
                              hipStream_t stream) {
-  const int64_t cols = EPI == EPI_GATE_UP ? a.N / 2 : a.N;
-  const int tn = EPI == EPI_GATE_UP ? 128 : kDmaTile;
+  const int64_t cols = is_gu(EPI) ? a.N / 2 : a.N;
+  const int tn = is_gu(EPI) ? 128 : kDmaTile;
   const int n_ntiles = static_cast<int>((cols + tn - 1) / tn);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
   int nwg = 0;  // CUs: one stream-K workgroup each
-  if (EPI != EPI_GATE_UP && a.ksplit == 1 && !plan.det) {
+  if (!is_gu(EPI) && a.ksplit == 1 && !plan.det) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&nwg, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -1264,6 +1413,8 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const L
     case 256:  // prefill: 256x256 tiles, 8 waves of 128x64 (bf16: operands DMA'd into LDS)
       if constexpr (sizeof(T) == 2) {
         if (lora == nullptr) return dma_launch<GATHER, EPI_STORE, KN>(plan, a, LoraEpilogue{}, stream);
+        if (lora->act != nullptr && lora->dn_a != nullptr)
+          return dma_launch<GATHER, EPI_GATE_UP_FOLD, KN>(plan, a, *lora, stream);
         if (lora->act != nullptr) return dma_launch<GATHER, EPI_GATE_UP, KN>(plan, a, *lora, stream);
         return dma_launch<GATHER, EPI_DOWN, KN>(plan, a, *lora, stream);
       } else {

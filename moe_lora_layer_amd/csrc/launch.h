@@ -51,6 +51,7 @@ struct TilePlan {
   bool shrink_partials;  // the shrinks sum per-split partials in order (det, or tall bf16 tiles)
   int nad;       // adapters; bucket index nad of an expert (base-only tokens) has no LoRA
   bool kn;       // every weight is k-major ([K][N], the h_in x h_out orientation)
+  bool fold_dn;  // the down shrink runs in the fused gate_up GEMM's epilogue
 };
 
 // Operands of the LoRA expand fused into a base GEMM's epilogue:
@@ -65,6 +66,15 @@ struct LoraEpilogue {
   int buckets;              // buckets per expert (adapters, + 1 with base-only tokens)
   int64_t b_rows;           // rows of each B block (2I for gate_up, h for down)
   uint16_t* act;            // bf16 [S][I] output of the gate_up form, else nullptr
+  // gate_up form only: the down projection's shrink z2 = act . A_dn folded
+  // into the epilogue (dn_a == nullptr: not folded).  Each tile adds its
+  // columns' share of z2 to dn_z with relaxed fp32 atomics (dn_z zero
+  // beforehand), or, dn_parts != nullptr (deterministic), writes it to
+  // partial slot nt (its N-tile) at dn_parts + nt * dn_part_stride.
+  const uint16_t* dn_a;     // A_dn [L][E][r][I] bf16 (k-major: [L][E][I][r])
+  float* dn_z;              // [S][rank] fp32
+  float* dn_parts;
+  int64_t dn_part_stride;
 };
 
 // Inverse permutation pos[slot] = sorted position, the M-tile list (tiles of

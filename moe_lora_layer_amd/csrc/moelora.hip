@@ -44,7 +44,7 @@ int check_plan(const moelora_plan& o) {
   if (o.lora_rows != 0 && o.lora_rows != 16 && o.lora_rows != 64) return MOELORA_ERR_UNSUPPORTED;
   if (o.ksplit_gate_up < 0 || o.ksplit_gate_up > 1024 || o.ksplit_down < 0 || o.ksplit_down > 1024)
     return MOELORA_ERR_UNSUPPORTED;
-  if (o.fuse < 0 || o.fuse > 2) return MOELORA_ERR_UNSUPPORTED;
+  if (o.fuse < 0 || o.fuse > 3) return MOELORA_ERR_UNSUPPORTED;
   return MOELORA_OK;
 }
 
@@ -118,6 +118,13 @@ TilePlan make_plan(const moelora_dims* d) {
                        o.fuse != 2;
   p.fuse_gu = fusable && p.ksplit_gu == 1;
   p.fuse_dn = fusable && p.ksplit_dn == 1;
+  // plan.fuse 3: the fused gate_up epilogue also adds its columns' share of
+  // the down projection's shrink (no separate pass over ACT).  Not the
+  // automatic choice: on MI355X the epilogue work (an LDS round trip of the
+  // activation tile and a load round trip per adapter bucket, with the matrix
+  // cores idle) costs more than the separate shrink's pass over ACT (prefill
+  // gate_up GEMM +180 us against a 57 us shrink, decode +25 against 16 us).
+  p.fold_dn = p.fuse_gu && o.fuse == 3;
   p.det = (d->flags & MOELORA_FLAG_DETERMINISTIC) != 0;
   // tall bf16 LoRA tiles: per-split partials and an ordered sum beat relaxed
   // fp32 atomics into Z (a few hundred split tiles each adding 64 x r values)
@@ -125,6 +132,14 @@ TilePlan make_plan(const moelora_dims* d) {
   p.nad = d->adapters;
   p.kn = (d->flags & MOELORA_FLAG_IN_OUT) != 0;
   return p;
+}
+
+// N-tiles of the gate_up GEMM (each covers 128 intermediate columns in the
+// 256-row bf16 tiles, 64 in the others): the partial slots of the folded
+// down shrink in deterministic mode.
+int64_t gate_up_ntiles(const moelora_dims* d, const TilePlan& plan) {
+  const int64_t tn = (plan.bm == 256 && d->dtype == MOELORA_BF16) ? 128 : 64;
+  return (d->intermediate + tn - 1) / tn;
 }
 
 struct ForwardLayout {
@@ -153,12 +168,13 @@ ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
   // deterministic mode: one region for the split-K partials of whichever
   // reduction runs (they run one after another)
   L.parts = off;
-  if (plan.shrink_partials) {
+  if (plan.shrink_partials || (plan.det && plan.fold_dn)) {
     const int dt = d->dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
     size_t n = 0;
     n = std::max(n, static_cast<size_t>(moelora::shrink_parts(dt, d->rank, plan, d->hidden)) * S * r);
     n = std::max(n, static_cast<size_t>(moelora::shrink_parts(dt, d->rank, plan, d->intermediate)) * S * r);
     if (plan.det && plan.ksplit_gu > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_gu) * S * 2 * I);
+    if (plan.det && plan.fold_dn) n = std::max(n, static_cast<size_t>(gate_up_ntiles(d, plan)) * S * r);
     if (plan.det && plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * S * h);
     off += round_up(n * 4);
   }
@@ -219,7 +235,7 @@ moelora_plan plan_out(const TilePlan& p) {
   o.lora_rows = p.bml;
   o.ksplit_gate_up = p.ksplit_gu;
   o.ksplit_down = p.ksplit_dn;
-  o.fuse = (p.fuse_gu || p.fuse_dn) ? 1 : 2;
+  o.fuse = p.fold_dn ? 3 : ((p.fuse_gu || p.fuse_dn) ? 1 : 2);
   return o;
 }
 
@@ -434,7 +450,8 @@ int moelora_forward_fusion(const moelora_dims* dims, int* flags) {
   const int rc = check_dims(dims);
   if (rc != MOELORA_OK) return rc;
   const TilePlan plan = make_plan(dims);
-  *flags = (plan.fuse_gu ? MOELORA_FUSED_GATE_UP : 0) | (plan.fuse_dn ? MOELORA_FUSED_DOWN : 0);
+  *flags = (plan.fuse_gu ? MOELORA_FUSED_GATE_UP : 0) | (plan.fuse_dn ? MOELORA_FUSED_DOWN : 0) |
+           (plan.fold_dn ? MOELORA_FUSED_DOWN_SHRINK : 0);
   return MOELORA_OK;
 }
 
@@ -546,8 +563,13 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
                                Lad, h, Z1, S, ltiles, counts, sparts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_GATE_UP);
   if (e == hipSuccess) {
+    // the folded down shrink adds into Z2 (cleared by prep), or, deterministic,
+    // writes per-N-tile partials that the down-shrink stage sums in order
     const moelora::LoraEpilogue epi{Z1, static_cast<const uint16_t*>(b_gate_up), bucket_offsets,
-                                    E, dims->adapters, r, Lad, 2 * I, static_cast<uint16_t*>(ACT)};
+                                    E, dims->adapters, r, Lad, 2 * I, static_cast<uint16_t*>(ACT),
+                                    plan.fold_dn ? static_cast<const uint16_t*>(a_down) : nullptr,
+                                    Z2, plan.fold_dn ? parts : nullptr,
+                                    static_cast<int64_t>(S) * r};
     e = moelora::launch_gemm(dt, plan, x, static_cast<int>(T), sorted_slots, k, w_gate_up, 2 * I,
                              h, G, S, mtiles, counts, etiles, plan.ksplit_gu,
                              plan.fuse_gu ? &epi : nullptr, parts, st);
@@ -557,9 +579,12 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
     e = moelora::launch_expand_gate_up(dt, r, plan, Z1, b_gate_up, E, Lad, G, ACT, I, ltiles,
                                        counts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_SHRINK_DOWN);
-  if (e == hipSuccess)
+  if (e == hipSuccess && !plan.fold_dn)
     e = moelora::launch_shrink(dt, r, plan, ACT, S, nullptr, 1, a_down, E, Lad, I, Z2, S, ltiles,
                                counts, sparts, st);
+  if (e == hipSuccess && plan.fold_dn && plan.det)
+    e = moelora::launch_reduce_parts(parts, static_cast<int>(gate_up_ntiles(dims, plan)),
+                                     static_cast<int64_t>(S) * r, Z2, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
   if (e == hipSuccess) {
     const moelora::LoraEpilogue epi{Z2, static_cast<const uint16_t*>(b_down), bucket_offsets,

@@ -205,7 +205,8 @@ def forward_fusion(d: Dims) -> dict:
     flags = ctypes.c_int()
     _check(library().moelora_forward_fusion(ctypes.byref(d), ctypes.byref(flags)),
            "moelora_forward_fusion")
-    return {"gate_up": bool(flags.value & 1), "down": bool(flags.value & 2)}
+    return {"gate_up": bool(flags.value & 1), "down": bool(flags.value & 2),
+            "down_shrink": bool(flags.value & 4)}
 
 
 def _ptr(t):

@@ -203,7 +203,7 @@ def _search(d, run, fields: list, steps: int, rounds: int, log):
             elif field == "lora_rows":
                 options = [{"lora_rows": v} for v in (16, 64)]
             elif field == "fuse":
-                options = [{"fuse": v} for v in (1, 2)]
+                options = [{"fuse": v} for v in (1, 2, 3)]
             else:
                 options = [{field: v} for v in SPLITS]
             for opt in options:

@@ -139,23 +139,23 @@ def test_forward_argument_errors():
 
 
 @pytest.mark.parametrize("kw,flags", [
-    (dict(), {"gate_up": True, "down": True}),                            # 16 rows per expert
-    (dict(unfused=True), {"gate_up": False, "down": False}),
-    (dict(tokens=4096, hidden=4096, intermediate=11008, experts=16), {"gate_up": True, "down": True}),
+    (dict(), {"gate_up": True, "down": True, "down_shrink": False}),                            # 16 rows per expert
+    (dict(unfused=True), {"gate_up": False, "down": False, "down_shrink": False}),
+    (dict(tokens=4096, hidden=4096, intermediate=11008, experts=16), {"gate_up": True, "down": True, "down_shrink": False}),
     (dict(tokens=4096, hidden=4096, intermediate=11008, experts=16, dtype="f32"),
-     {"gate_up": False, "down": False}),                                   # fused forms are bf16 only
+     {"gate_up": False, "down": False, "down_shrink": False}),                                   # fused forms are bf16 only
     (dict(tokens=4096, hidden=4096, intermediate=11008, experts=16, unfused=True),
-     {"gate_up": False, "down": False}),
-    (dict(tokens=600, hidden=128, intermediate=192, experts=4), {"gate_up": True, "down": True}),
+     {"gate_up": False, "down": False, "down_shrink": False}),
+    (dict(tokens=600, hidden=128, intermediate=192, experts=4), {"gate_up": True, "down": True, "down_shrink": False}),
     # 32 rows per expert over 64 adapters: 64-row tiles stage the buckets' B in LDS
     (dict(tokens=256, hidden=2880, intermediate=2880, experts=32, top_k=4, adapters=64, rank=64),
-     {"gate_up": True, "down": True}),
+     {"gate_up": True, "down": True, "down_shrink": False}),
     # 128 rows per expert over 16 adapters (eight-wave tiles): the gate_up GEMM
     # fuses; the down GEMM (N = 8192, one M-tile) splits K and does not
     (dict(tokens=128, hidden=8192, intermediate=28672, experts=1, top_k=1, adapters=16),
-     {"gate_up": True, "down": False}),
+     {"gate_up": True, "down": False, "down_shrink": False}),
     # one token on one expert: both GEMMs split K to fill the GPU, no fusion
-    (dict(tokens=4, hidden=4096, intermediate=1024, experts=1, top_k=1), {"gate_up": False, "down": False}),
+    (dict(tokens=4, hidden=4096, intermediate=1024, experts=1, top_k=1), {"gate_up": False, "down": False, "down_shrink": False}),
 ])
 def test_forward_fusion_flags(kw, flags):
     assert ops.forward_fusion(good_dims(**kw)) == flags
@@ -184,7 +184,7 @@ def test_deterministic_workspace_holds_the_partials(kw):
 PLAN_CASES = [
     dict(gemm_rows=48), dict(gemm_rows=-32), dict(gemm_form=3), dict(gemm_form=1),  # form needs rows
     dict(gemm_rows=256, gemm_form=1), dict(gemm_rows=64, gemm_form=2), dict(lora_rows=32),
-    dict(ksplit_gate_up=-1), dict(ksplit_down=1025), dict(fuse=3), dict(fuse=-1),
+    dict(ksplit_gate_up=-1), dict(ksplit_down=1025), dict(fuse=4), dict(fuse=-1),
 ]
 
 
@@ -219,10 +219,10 @@ def test_plan_resolution():
     p = ops.forward_plan(good_dims(plan=dict(ksplit_gate_up=3, ksplit_down=1000)))
     assert (p["ksplit_gate_up"], p["ksplit_down"]) == (2, 8)
     # a split GEMM cannot fuse its expand; fuse=2 turns fusion off
-    assert ops.forward_fusion(good_dims(plan=dict(ksplit_down=2))) == {"gate_up": True, "down": False}
-    assert ops.forward_fusion(good_dims(plan=dict(fuse=2))) == {"gate_up": False, "down": False}
+    assert ops.forward_fusion(good_dims(plan=dict(ksplit_down=2))) == {"gate_up": True, "down": False, "down_shrink": False}
+    assert ops.forward_fusion(good_dims(plan=dict(fuse=2))) == {"gate_up": False, "down": False, "down_shrink": False}
     many = dict(tokens=256, hidden=2880, intermediate=2880, experts=32, top_k=4, adapters=64, rank=64)
-    assert ops.forward_fusion(good_dims(plan=dict(fuse=1), **many)) == {"gate_up": True, "down": True}
+    assert ops.forward_fusion(good_dims(plan=dict(fuse=1), **many)) == {"gate_up": True, "down": True, "down_shrink": False}
     # the workspace follows the plan (split partials in deterministic mode)
     n1 = ops.forward_workspace_size(good_dims(flags=1))
     n2 = ops.forward_workspace_size(good_dims(flags=1, plan=dict(ksplit_down=4)))

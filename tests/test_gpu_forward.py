@@ -111,8 +111,8 @@ def test_forward_small_unfused(shape):
     say(f"forward small unfused {shape}")
     inp = synth.make_inputs(cfg)
     d = ops.dims_for(cfg, unfused=True)
-    assert ops.forward_fusion(d) == {"gate_up": False, "down": False}
-    assert ops.forward_fusion(ops.dims_for(cfg)) == {"gate_up": True, "down": True}
+    assert ops.forward_fusion(d) == {"gate_up": False, "down": False, "down_shrink": False}
+    assert ops.forward_fusion(ops.dims_for(cfg)) == {"gate_up": True, "down": True, "down_shrink": False}
     _, (ids, w, ss, off), out, _ = _layer(cfg, inp, d)
     ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
     ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
@@ -187,7 +187,7 @@ def test_forward_tile_boundaries():
     logits = np.zeros((cfg.tokens, len(sizes)), np.float32)
     logits[np.arange(cfg.tokens), owner] = 4.0
     inp["logits"] = logits
-    assert ops.forward_fusion(ops.dims_for(cfg)) == {"gate_up": True, "down": True}
+    assert ops.forward_fusion(ops.dims_for(cfg)) == {"gate_up": True, "down": True, "down_shrink": False}
     _, (ids, w, ss, off), out, _ = _layer(cfg, inp)
     ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
@@ -494,3 +494,38 @@ def test_forward_base_only_tokens(shape, det):
     ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
     ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
     assert_close(to_f64(out), ref, cfg.dtype, "out")
+
+
+FOLD_SHAPES = [(64, 256, 512, 8, 2, 4, 16, "bf16"), (96, 192, 320, 5, 2, 3, 32, "bf16"),
+               (200, 320, 192, 6, 2, 3, 64, "bf16"), (350, 192, 320, 4, 2, 3, 32, "bf16"),
+               (600, 128, 192, 4, 2, 3, 16, "bf16"), (700, 256, 320, 3, 2, 5, 32, "bf16")]
+
+
+@pytest.mark.parametrize("in_out", [False, True], ids=["k_contig", "in_out"])
+@pytest.mark.parametrize("det", [False, True], ids=["atomics", "deterministic"])
+@pytest.mark.parametrize("shape", FOLD_SHAPES, ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
+def test_folded_down_shrink_z2(shape, det, in_out):
+    """Plan fuse = 3: the down projection's shrink folded into the fused
+    gate_up epilogue (every fused tile family: 32-, 64-row, 128-row streaming
+    and reuse, 256-row; both weight layouts): Z2 read back from the workspace
+    against the oracle's z2 = a A_dn per slot, and the layer output against
+    the oracle."""
+    from gpu_util import in_out as to_in_out
+    cfg = _small(*shape, seed=sum(shape[:7]) + 11)
+    inp = synth.make_inputs(cfg)
+    d = ops.dims_for(cfg, deterministic=det, in_out=in_out, plan=dict(fuse=3))
+    assert ops.forward_fusion(d)["down_shrink"] and ops.forward_plan(d)["fuse"] == 3
+    assert not ops.forward_fusion(ops.dims_for(cfg))["down_shrink"]   # never automatic
+    _, (ids, w, ss, off), out, ws = _layer(cfg, to_in_out(inp) if in_out else inp, d)
+    lay = ops.forward_workspace_layout(d)
+    S, r = cfg.slots, cfg.rank
+    Z2 = to_f64(workspace_view(ws, lay["Z2"], (S, r), torch.float32))
+    ss, ids_h = ss.cpu().numpy(), ids.cpu().numpy()
+    dims = oracle.dims_of(cfg)
+    ref_z2 = np.stack([oracle.slot(inp, dims, int(ss[p]) // cfg.top_k,
+                                   int(ids_h[int(ss[p]) // cfg.top_k, int(ss[p]) % cfg.top_k]),
+                                   int(inp["adapter_ids"][int(ss[p]) // cfg.top_k]))["z2"]
+                       for p in range(S)])
+    assert_close(Z2, ref_z2, "bf16", "Z2")
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    assert_close(to_f64(out), oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w), "bf16", "out")
