@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOELORA_ABI_VERSION 7
+#define MOELORA_ABI_VERSION 8
 
 typedef enum moelora_status {
   MOELORA_OK = 0,
@@ -90,6 +90,18 @@ typedef enum moelora_dtype {
  *                   projection's LoRA shrink (MOELORA_FUSED_DOWN_SHRINK; never
  *                   the automatic choice: slower on MI355X at every shape
  *                   measured, kept for callers whose ACT re-read costs more)
+ *   order           workgroup order of the base GEMMs (the page's CTA
+ *                   swizzling for L2 reuse, section "Kernel optimisation"):
+ *                   1 launch order; 2 each expert's tiles N-tile by N-tile,
+ *                   M-tiles innermost, remapped so that every XCD (one L2)
+ *                   runs a contiguous run of them; 3 launch order with every
+ *                   workgroup's K walk starting at its own step (rotated), so
+ *                   that resident workgroups stream different K columns; 4 both
+ *                   (automatic: 2 for the weight-reuse tiles, 3 for the
+ *                   weight-streaming ones, 1 for them over MOELORA_FLAG_IN_OUT
+ *                   weights)
+ * The K step of every GEMM tile is fixed at 64 bf16 / 32 fp32 elements (one
+ * 128-byte LDS row); it is not a plan field.
  * Out-of-range values make every call that takes the dims return
  * MOELORA_ERR_UNSUPPORTED.
  */
@@ -100,6 +112,7 @@ typedef struct moelora_plan {
   int32_t ksplit_gate_up;
   int32_t ksplit_down;
   int32_t fuse;
+  int32_t order;
 } moelora_plan;
 
 /*

@@ -475,15 +475,14 @@ __device__ __forceinline__ void lora_buckets(const LoraEpilogue& lora, int e, in
 // KN: the weights are k-major ([K][N]); each aligned group of VEC lanes loads
 // VEC k-rows of VEC consecutive columns and transposes them in registers, so
 // the LDS tile and the fragment reads are those of the K-contiguous layout.
-template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool ROT = false,
-          bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false, int EPI = EPI_STORE,
-          bool KN = false>
+template <typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER, bool SCHED = false,
+          int SWZ = 1, bool PIPE = false, int EPI = EPI_STORE, bool KN = false>
 __global__ void __launch_bounds__(WM * WN * kWave)
 k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots, int gather_k,
        const T* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
        const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
        const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, float* __restrict__ parts,
-       int64_t part_stride, LoraEpilogue lora) {
+       int64_t part_stride, LoraEpilogue lora, int order) {
   typedef Mfma<T> M;
   constexpr int NT_ = WM * WN * kWave;
   constexpr int ROWB = 128;                    // bytes of K per LDS row
@@ -499,7 +498,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
 
   // Workgroup order.  The grid is sized from a host-side bound; the first
   // counts[0] * n_ntiles workgroups are the real ones.  Hardware hands
-  // consecutive workgroup ids to the 8 XCDs in turn; XCDMAP remaps the real
+  // consecutive workgroup ids to the 8 XCDs in turn; ORDER_XCD remaps the real
   // ones so that consecutive logical ids run on the same XCD (each XCD gets
   // an equal share), then each expert's tiles are walked N-tile by N-tile with
   // its M-tiles innermost, so M-tiles sharing one weight tile run together on
@@ -509,7 +508,8 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   const int active = counts[0] * n_ntiles;
   if (pid >= active) return;
   const int xcd = pid % kXcds, q = active / kXcds, rem = active % kXcds;
-  const int bid = XCDMAP ? xcd * q + min(xcd, rem) + pid / kXcds : pid;
+  const bool xcd_grouped = order == ORDER_XCD || order == ORDER_XCD_ROTATED;
+  const int bid = xcd_grouped ? xcd * q + min(xcd, rem) + pid / kXcds : pid;
   const int t0 = bid / n_ntiles;
   const int ex = mtiles[t0].x;
   const int ta = expert_tiles[ex], tb = expert_tiles[ex + 1];
@@ -595,20 +595,19 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   }
   const int64_t b_kmul = KN ? N : 1;  // elements of B per unit of K
 
-  // ROT: every workgroup starts its K walk at a different step, so that
+  // ORDER_ROTATED: every workgroup starts its K walk at a different step, so that
   // workgroups resident together do not all read the same K columns at once
   const int nk_all = static_cast<int>(K / BK);
   const int nk_per = (nk_all + ksplit - 1) / ksplit;
   const int kbeg = min(nk_all, ks * nk_per);
   const int nk = min(nk_all, kbeg + nk_per) - kbeg;  // K-steps of this workgroup
-  // (not for k-major weights: there the workgroups of neighbouring N-tiles
-  // read neighbouring pieces of the same k-rows, best at the same time)
+  const bool rot = order == ORDER_ROTATED || order == ORDER_XCD_ROTATED;
   const int kstart =
-      (ROT && !KN && nk > 0) ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk) : 0;
+      (rot && nk > 0) ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk) : 0;
   uint4 a_reg[P][A_CH], b_reg[P][B_CH];
   auto gload = [&](int slot, int kt) {
     int kk = kt + kstart;
-    if (ROT && kk >= nk) kk -= nk;
+    if (kk >= nk) kk -= nk;
     const int64_t ko = static_cast<int64_t>(kbeg + kk) * BK;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) a_reg[slot][i] = load16<false>(a_src[i] + ko);
@@ -948,39 +947,38 @@ struct GemmArgs {
 };
 
 template <bool KN, typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER,
-          bool ROT = false, bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false,
-          int EPI = EPI_STORE>
+          bool SCHED = false, int SWZ = 1, bool PIPE = false, int EPI = EPI_STORE>
 static hipError_t lds_launch_epi(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue& lora,
                                  hipStream_t stream) {
   const int64_t cols = is_gu(EPI) ? a.N / 2 : a.N;
   const int tn = is_gu(EPI) ? BN / 2 : BN;
   const int n_ntiles = static_cast<int>((cols + tn - 1) / tn);
   const int64_t grid = static_cast<int64_t>(plan.max_mt) * n_ntiles * a.ksplit;
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE, EPI, KN>),
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WM, WN, P, NT, GATHER, SCHED, SWZ, PIPE, EPI, KN>),
                      dim3(static_cast<unsigned>(grid)), dim3(WM * WN * kWave), 0, stream,
                      static_cast<const T*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const T*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
-                     a.expert_tiles, n_ntiles, a.ksplit, a.parts, a.part_stride, lora);
+                     a.expert_tiles, n_ntiles, a.ksplit, a.parts, a.part_stride, lora, plan.order);
   return hipGetLastError();
 }
 
 // the epilogue picked by lora: none (EPI_STORE), gate_up (act set) or down
 template <bool KN, typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER,
-          bool ROT = false, bool SCHED = false, int SWZ = 1, bool XCDMAP = true, bool PIPE = false>
+          bool SCHED = false, int SWZ = 1, bool PIPE = false>
 static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue* lora,
                              hipStream_t stream) {
   if constexpr (sizeof(T) == 2 && BM <= 128) {  // bf16 256-row tiles run k_gemm_dma
     if (lora != nullptr && lora->act != nullptr && lora->dn_a != nullptr)
-      return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
+      return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, SCHED, SWZ, PIPE,
                             EPI_GATE_UP_FOLD>(plan, a, *lora, stream);
     if (lora != nullptr && lora->act != nullptr)
-      return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
+      return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, SCHED, SWZ, PIPE,
                             EPI_GATE_UP>(plan, a, *lora, stream);
     if (lora != nullptr)
-      return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE,
+      return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, SCHED, SWZ, PIPE,
                             EPI_DOWN>(plan, a, *lora, stream);
   }
-  return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, ROT, SCHED, SWZ, XCDMAP, PIPE>(
+  return lds_launch_epi<KN, T, BM, BN, WM, WN, P, NT, GATHER, SCHED, SWZ, PIPE>(
       plan, a, LoraEpilogue{}, stream);
 }
 
@@ -1038,7 +1036,8 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
                                          int gather_k, const bf16_t* __restrict__ Wt, int64_t N,
                                          int64_t K, float* __restrict__ C, int4 tile, int nt,
                                          int kbeg, int nk, int out, bool with_lora,
-                                         const LoraEpilogue& lora, float* __restrict__ part) {
+                                         const LoraEpilogue& lora, float* __restrict__ part,
+                                         int kstart) {
   lds_barrier();  // every wave is done with what the LDS held for the previous item
   const int e = tile.x, row0 = tile.y, row_end = tile.z;
   // Output columns.  EPI_GATE_UP: the tile covers 128 columns i of the
@@ -1152,7 +1151,10 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
   // workgroup barrier that orders LDS accesses only; the DMA is waited for
   // explicitly with vmcnt
   auto bar = [&]() { lds_barrier(); };
-  auto ko = [&](int kt) { return static_cast<int64_t>(kbeg + kt) * 64; };
+  auto ko = [&](int kt) {
+    const int kk = kt + kstart;
+    return static_cast<int64_t>(kbeg + (kk >= nk ? kk - nk : kk)) * 64;
+  };
 
   // K-step kt lives in stage kt % 2.  Both stages are requested up front;
   // steps past the end repeat the last one (never read), which keeps the
@@ -1301,7 +1303,7 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
            int gather_k, const bf16_t* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
            const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
            const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, LoraEpilogue lora,
-           float* __restrict__ parts, int64_t part_stride, int sk_mode, int nwg) {
+           float* __restrict__ parts, int64_t part_stride, int sk_mode, int nwg, int order) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDmaStage];
   const int tiles = counts[0] * n_ntiles;
   const int dp = sk_mode == 0 ? tiles : dma_dp_tiles(tiles, nwg);
@@ -1320,7 +1322,8 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     const int pid = static_cast<int>(blockIdx.x) / ksplit;
     if (pid >= dp) return;
     const int xcd = pid % kXcds, q = dp / kXcds, rem = dp % kXcds;
-    bid = xcd * q + min(xcd, rem) + pid / kXcds;
+    bid = (order == ORDER_XCD || order == ORDER_XCD_ROTATED) ? xcd * q + min(xcd, rem) + pid / kXcds
+                                                             : pid;
     if (sk_mode == 1 && bid < tiles - dp) {
       // clear the output of stream-K tile dp + bid (the next launch adds into it)
       int4 st;
@@ -1361,8 +1364,12 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
       with_lora = true;
       u = u1;
     }
+    // rotated K walk (data-parallel items only): this workgroup starts at step kstart
+    const int kstart = (sk_mode != 2 && (order == ORDER_ROTATED || order == ORDER_XCD_ROTATED) && nk > 0)
+                           ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk)
+                           : 0;
     dma_item<GATHER, EPI, KN>(smem, X, x_rows, gather_slots, gather_k, Wt, N, K, C, tile, nt, kbeg,
-                              nk, out, with_lora, lora, part);
+                              nk, out, with_lora, lora, part, kstart);
   }
 }
 
@@ -1388,14 +1395,15 @@ static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const Lora
   hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI, KN>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
-                     a.expert_tiles, n_ntiles, a.ksplit, lora, a.parts, a.part_stride, mode, nwg);
+                     a.expert_tiles, n_ntiles, a.ksplit, lora, a.parts, a.part_stride, mode, nwg,
+                     plan.order);
   if (mode == 0) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI, KN>), dim3(static_cast<unsigned>(nwg)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
-                     a.expert_tiles, n_ntiles, 1, lora, a.parts, a.part_stride, 2, nwg);
+                     a.expert_tiles, n_ntiles, 1, lora, a.parts, a.part_stride, 2, nwg, plan.order);
   return hipGetLastError();
 }
 
@@ -1404,12 +1412,12 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const L
                                 hipStream_t stream) {
   // decode-sized M-tiles stream the weights: nontemporal loads, rotated K walk
   switch (plan.bm) {
-    case 32: return lds_launch<KN, T, 32, 128, 1, 4, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
-    case 64: return lds_launch<KN, T, 64, 128, 2, 2, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
+    case 32: return lds_launch<KN, T, 32, 128, 1, 4, 2, true, GATHER>(plan, a, lora, stream);
+    case 64: return lds_launch<KN, T, 64, 128, 2, 2, 2, true, GATHER>(plan, a, lora, stream);
     case 128:
       if (plan.stream)  // eight waves of 64 x 32
-        return lds_launch<KN, T, 128, 128, 2, 4, 2, true, GATHER, true, false, 1, false>(plan, a, lora, stream);
-      return lds_launch<KN, T, 128, 128, 2, 2, 1, false, GATHER, false, false, 1, true, true>(plan, a, lora, stream);
+        return lds_launch<KN, T, 128, 128, 2, 4, 2, true, GATHER>(plan, a, lora, stream);
+      return lds_launch<KN, T, 128, 128, 2, 2, 1, false, GATHER, false, 1, true>(plan, a, lora, stream);
     case 256:  // prefill: 256x256 tiles, 8 waves of 128x64 (bf16: operands DMA'd into LDS)
       if constexpr (sizeof(T) == 2) {
         if (lora == nullptr) return dma_launch<GATHER, EPI_STORE, KN>(plan, a, LoraEpilogue{}, stream);
@@ -1418,7 +1426,7 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const L
         if (lora->act != nullptr) return dma_launch<GATHER, EPI_GATE_UP, KN>(plan, a, *lora, stream);
         return dma_launch<GATHER, EPI_DOWN, KN>(plan, a, *lora, stream);
       } else {
-        return lds_launch<KN, T, 256, 256, 2, 4, 1, false, GATHER, false, false, 1, true, true>(plan, a, nullptr, stream);
+        return lds_launch<KN, T, 256, 256, 2, 4, 1, false, GATHER, false, 1, true>(plan, a, nullptr, stream);
       }
     default: return hipErrorInvalidValue;
   }

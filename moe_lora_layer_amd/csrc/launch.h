@@ -34,6 +34,10 @@ hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_
                         int32_t* sorted_slots, int32_t* offsets, int32_t* status, int32_t* ws_key,
                         int32_t* ws_rank, int32_t* ws_cnt, hipStream_t stream);
 
+// Workgroup order of the base GEMMs (moelora_plan.order): launch order, the
+// expert's tiles grouped per XCD, every workgroup's K walk rotated, or both.
+enum { ORDER_LAUNCH = 1, ORDER_XCD = 2, ORDER_ROTATED = 3, ORDER_XCD_ROTATED = 4 };
+
 // Tile descriptor: x = expert (M-tiles) or bucket (LoRA tiles), y = first
 // sorted row, z = end row (exclusive), w unused.
 struct TilePlan {
@@ -52,6 +56,7 @@ struct TilePlan {
   int nad;       // adapters; bucket index nad of an expert (base-only tokens) has no LoRA
   bool kn;       // every weight is k-major ([K][N], the h_in x h_out orientation)
   bool fold_dn;  // the down shrink runs in the fused gate_up GEMM's epilogue
+  int order;     // ORDER_*: workgroup order of the base GEMMs
 };
 
 // Operands of the LoRA expand fused into a base GEMM's epilogue:

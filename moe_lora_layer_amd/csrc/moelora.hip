@@ -45,6 +45,7 @@ int check_plan(const moelora_plan& o) {
   if (o.ksplit_gate_up < 0 || o.ksplit_gate_up > 1024 || o.ksplit_down < 0 || o.ksplit_down > 1024)
     return MOELORA_ERR_UNSUPPORTED;
   if (o.fuse < 0 || o.fuse > 3) return MOELORA_ERR_UNSUPPORTED;
+  if (o.order < 0 || o.order > 4) return MOELORA_ERR_UNSUPPORTED;
   return MOELORA_OK;
 }
 
@@ -131,6 +132,13 @@ TilePlan make_plan(const moelora_dims* d) {
   p.shrink_partials = p.det || (p.lora_db && d->dtype == MOELORA_BF16);
   p.nad = d->adapters;
   p.kn = (d->flags & MOELORA_FLAG_IN_OUT) != 0;
+  // workgroup order: tiles that reuse their weight tile (256 rows, 128-row
+  // reuse) run each expert's tiles together per XCD (one L2); weight-streaming
+  // tiles rotate every workgroup's K walk, except over k-major weights, whose
+  // neighbouring N-tiles read neighbouring pieces of the same k-rows
+  const bool reuse = p.bm == 256 || (p.bm == 128 && !p.stream);
+  p.order = o.order != 0 ? o.order
+                         : (reuse ? moelora::ORDER_XCD : (p.kn ? moelora::ORDER_LAUNCH : moelora::ORDER_ROTATED));
   return p;
 }
 
@@ -236,6 +244,7 @@ moelora_plan plan_out(const TilePlan& p) {
   o.ksplit_gate_up = p.ksplit_gu;
   o.ksplit_down = p.ksplit_dn;
   o.fuse = p.fold_dn ? 3 : ((p.fuse_gu || p.fuse_dn) ? 1 : 2);
+  o.order = p.order;
   return o;
 }
 

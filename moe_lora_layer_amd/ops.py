@@ -28,7 +28,8 @@ _TORCH_DT = {MOELORA_F32: torch.float32, MOELORA_BF16: torch.bfloat16}
 _DT_NAME = {"f32": MOELORA_F32, "bf16": MOELORA_BF16}
 
 
-PLAN_FIELDS = ["gemm_rows", "gemm_form", "lora_rows", "ksplit_gate_up", "ksplit_down", "fuse"]
+PLAN_FIELDS = ["gemm_rows", "gemm_form", "lora_rows", "ksplit_gate_up", "ksplit_down", "fuse",
+               "order"]
 
 
 class Plan(ctypes.Structure):

@@ -204,6 +204,8 @@ def _search(d, run, fields: list, steps: int, rounds: int, log):
                 options = [{"lora_rows": v} for v in (16, 64)]
             elif field == "fuse":
                 options = [{"fuse": v} for v in (1, 2, 3)]
+            elif field == "order":
+                options = [{"order": v} for v in (1, 2, 3, 4)]
             else:
                 options = [{field: v} for v in SPLITS]
             for opt in options:
@@ -253,7 +255,7 @@ def tune_layer(cfg, steps: int = 10, rounds: int = 2, log=print) -> dict:
 
     log(f"tuning {cfg.name}")
     plan, us, auto_us = _search(d, run, ["gemm", "lora_rows", "ksplit_gate_up", "ksplit_down",
-                                         "fuse"], steps, rounds, log)
+                                         "fuse", "order"], steps, rounds, log)
     return {"kind": "layer", "name": cfg.name, "dims": {k: int(getattr(d, k)) for k in LAYER_KEYS},
             "plan": plan, "us": round(us, 2), "auto_us": round(auto_us, 2)}
 
@@ -277,7 +279,7 @@ def tune_dense(cfg, steps: int = 10, rounds: int = 2, log=print) -> dict:
         return out
 
     log(f"tuning {cfg.name}")
-    plan, us, auto_us = _search(d, run, ["gemm", "lora_rows", "ksplit_down", "fuse"], steps,
+    plan, us, auto_us = _search(d, run, ["gemm", "lora_rows", "ksplit_down", "fuse", "order"], steps,
                                 rounds, log)
     return {"kind": "dense", "name": cfg.name, "dims": {k: int(getattr(d, k)) for k in DENSE_KEYS},
             "plan": plan, "us": round(us, 2), "auto_us": round(auto_us, 2)}

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     assert {"moelora_align", "moelora_forward"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.moelora_abi_version() == 7
+    assert lib.moelora_abi_version() == 8
 
 
 def test_status_strings():
@@ -184,7 +184,8 @@ def test_deterministic_workspace_holds_the_partials(kw):
 PLAN_CASES = [
     dict(gemm_rows=48), dict(gemm_rows=-32), dict(gemm_form=3), dict(gemm_form=1),  # form needs rows
     dict(gemm_rows=256, gemm_form=1), dict(gemm_rows=64, gemm_form=2), dict(lora_rows=32),
-    dict(ksplit_gate_up=-1), dict(ksplit_down=1025), dict(fuse=4), dict(fuse=-1),
+    dict(ksplit_gate_up=-1), dict(ksplit_down=1025), dict(fuse=4), dict(fuse=-1), dict(order=5),
+    dict(order=-1),
 ]
 
 
@@ -206,9 +207,12 @@ def test_plan_resolution():
     auto = ops.forward_plan(good_dims())
     assert all(auto[f] != 0 for f in ops.PLAN_FIELDS)
     assert auto == {"gemm_rows": 32, "gemm_form": 1, "lora_rows": 16, "ksplit_gate_up": 1,
-                    "ksplit_down": 1, "fuse": 1}
+                    "ksplit_down": 1, "fuse": 1, "order": 3}
     forced = ops.forward_plan(good_dims(plan=dict(gemm_rows=128, gemm_form=2, lora_rows=64)))
-    assert forced == dict(auto, gemm_rows=128, gemm_form=2, lora_rows=64)
+    # weight-reuse tiles default to the XCD-grouped order
+    assert forced == dict(auto, gemm_rows=128, gemm_form=2, lora_rows=64, order=2)
+    assert ops.forward_plan(good_dims(in_out=True))["order"] == 1
+    assert ops.forward_plan(good_dims(plan=dict(order=4)))["order"] == 4
     # resolving a resolved plan changes nothing
     for kw in [dict(), dict(tokens=4096, hidden=4096, intermediate=11008, experts=16),
                dict(tokens=4, hidden=4096, intermediate=1024, experts=1, top_k=1)]:

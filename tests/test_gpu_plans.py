@@ -79,3 +79,32 @@ def test_dense_every_plan():
         assert int(st[0].item()) == 0
         assert_close(to_f64(out), ref, cfg.dtype, f"dense plan {eff}")
     assert len(seen) >= 15
+
+
+@pytest.mark.parametrize("shape", SHAPES[:2] + SHAPES[2:3], ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
+def test_forward_every_workgroup_order(shape):
+    """plan.order 1-4 (launch order, XCD-grouped, rotated K walk, both) on every
+    GEMM tile family, split-K included, for both weight layouts: the oracle's
+    result within tolerance."""
+    from gpu_util import in_out
+    cfg = synth.LayerConfig("orders", *shape, requests=shape[0], seed=sum(shape[:7]) + 9)
+    inp = synth.make_inputs(cfg)
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
+    for io in (False, True):
+        dinp = device_inputs(in_out(inp) if io else inp, cfg, device())
+        ids, w, ss, off, st = run_align(cfg, dinp)
+        assert int(st[0].item()) == 0
+        seen = set()
+        for (r, f), (kg, kd), order in itertools.product(GEMM_SHAPES, ((0, 0), (3, 2)), (1, 2, 3, 4)):
+            d = ops.dims_for(cfg, in_out=io, plan=dict(gemm_rows=r, gemm_form=f, ksplit_gate_up=kg,
+                                                       ksplit_down=kd, order=order))
+            eff = ops.forward_plan(d)
+            assert eff["order"] == order
+            key = tuple(sorted(eff.items()))
+            if key in seen:
+                continue
+            seen.add(key)
+            say(f"forward {shape} in_out={io} plan {eff}")
+            out, _ = run_forward(cfg, dinp, w, ss, off, dims=d)
+            assert_close(to_f64(out), ref, cfg.dtype, f"plan {eff}")
