@@ -184,13 +184,15 @@ __device__ __forceinline__ void atomic_add_relaxed(float* p, float v) {
 // Weights stored k-major ([K][N], N contiguous: the page's h_in x h_out
 // orientation).  MFMA fragments take K-contiguous runs per lane, so a k-major
 // operand is turned around on its way in:
-//   - loaded through registers: each aligned group of 8 lanes (bf16) or 4
-//     lanes (fp32) loads a square block, lane m holding k-row m of 8 (4)
-//     consecutive columns; transpose8/transpose4 leave lane m holding column m
-//     of 8 (4) consecutive k, i.e. exactly the 16-byte chunk the K-contiguous
-//     layout would have given it;
-//   - staged in LDS by direct-to-LDS copies: the tile stays k-major in LDS and
-//     the fragments are read with ds_read_b64_tr_b16 (tr16_frag).
+//   - loaded through registers straight into MFMA fragments (the LoRA
+//     kernels, and fp32 tiles on their way to LDS): each aligned group of 8
+//     lanes (bf16) or 4 lanes (fp32) loads a square block, lane m holding
+//     k-row m of 8 (4) consecutive columns; transpose8/transpose4 leave lane m
+//     holding column m of 8 (4) consecutive k, i.e. exactly the 16-byte chunk
+//     the K-contiguous layout would have given it;
+//   - staged in LDS (direct-to-LDS copies, and bf16 GEMM tiles stored from
+//     registers as loaded): the tile stays k-major in LDS and the fragments
+//     are read with ds_read_b64_tr_b16 (kn_frag).
 // Every lane of a group must execute the transposes (no divergence).
 // ---------------------------------------------------------------------------
 // v of lane ^ MASK (MASK 1, 2, 4), with DPP moves on the vector ALU: quad

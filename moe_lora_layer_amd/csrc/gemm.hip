@@ -494,6 +494,10 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(A_CH >= 1 && B_CH >= 1 && BM * 8 % NT_ == 0 && BN * 8 % NT_ == 0, "tile/threads");
   static_assert(FM >= 1 && FN >= 1 && P >= 1, "wave tile");
+  // k-major bf16 weights stay k-major in LDS (a K-step's 64 k-rows of BN
+  // columns, the same bytes as BN rows of 128) and are read transposed
+  constexpr bool KNL = KN && sizeof(T) == 2;
+  static_assert(!KNL || BN >= 128, "kn_lds_off needs rows of 16 chunks");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2][(BM + BN) * ROWB];
 
   // Workgroup order.  The grid is sized from a host-side bound; the first
@@ -582,14 +586,18 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     } else {
       // block q / VEC: k-group kg (VEC k-rows) x column group cg (VEC tile
       // rows); lane m of the block loads k-row kg * VEC + m of the group's
-      // columns and, after the transpose, holds tile row cg * VEC + m, chunk kg
+      // columns.  bf16: the chunk is stored as loaded into a k-major LDS tile
+      // (k-rows of BN columns, kn_lds_off layout) and the fragments are read
+      // with transposed reads; fp32: the block is transposed across its lanes,
+      // after which lane m holds tile row cg * VEC + m, chunk kg
       const int blk = q / VEC, m = q % VEC, ncg = BN / VEC;
       const int cg = blk % ncg, kg = blk / ncg;
       int64_t col0 = w_col(cg * VEC, ok);  // VEC consecutive columns, all valid or none
       if (!ok) col0 = 0;                   // masked: any VEC columns inside the row
       b_src[i] = We + static_cast<int64_t>(kg * VEC + m) * N + col0;
       const int row = cg * VEC + m;
-      b_dst[i] = BM * ROWB + row * ROWB + ((kg ^ swz<SWZ>(row)) << 4);
+      b_dst[i] = KNL ? BM * ROWB + kn_lds_off(kg * VEC + m, cg * VEC, BN * 2)
+                     : BM * ROWB + row * ROWB + ((kg ^ swz<SWZ>(row)) << 4);
     }
     b_mask[i] = ok ? 0xffffffffu : 0u;
   }
@@ -620,7 +628,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
       *reinterpret_cast<uint4*>(&smem[buf][a_dst[i]]) = masked(a_reg[slot][i], a_mask[i]);
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      const uint4 v = KN ? transpose_chunk<T>(b_reg[slot][i]) : b_reg[slot][i];
+      const uint4 v = (KN && !KNL) ? transpose_chunk<T>(b_reg[slot][i]) : b_reg[slot][i];
       *reinterpret_cast<uint4*>(&smem[buf][b_dst[i]]) = masked(v, b_mask[i]);
     }
   };
@@ -649,8 +657,12 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
     for (int i = 0; i < FM; ++i)
       af[i] = M::load(reinterpret_cast<const T*>(As + frag_off(wm * WTM + i * 32 + c32, ks)));
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bfr[j] = M::load(reinterpret_cast<const T*>(Bs + frag_off(wn * WTN + j * 32 + c32, ks)));
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (KNL)
+        bfr[j] = kn_frag(Bs, BN * 2, wn * WTN + j * 32 + (c32 & 16), ks * M::KSTEP, lane);
+      else
+        bfr[j] = M::load(reinterpret_cast<const T*>(Bs + frag_off(wn * WTN + j * 32 + c32, ks)));
+    }
   };
   auto mma = [&](const frag_t (&af)[FM], const frag_t (&bfr)[FN]) {
 #pragma unroll
@@ -783,7 +795,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
       }
       // this thread's B^T chunks: tile row and LDS position as in the main loop
       // (k-major B: the block of rank rows x columns this lane's group loads,
-      // transposed before the LDS store)
+      // stored k-major as in the main loop and read transposed)
       int64_t b_off[B_CH];
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
@@ -838,8 +850,7 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
         for (int g = 0; g < NBUF; ++g)
 #pragma unroll
           for (int i = 0; i < B_CH; ++i)
-            *reinterpret_cast<uint4*>(lds + g * BUCKET_BYTES + b_dst[i] - BM * ROWB) =
-                KN ? transpose8(bv[g][i]) : bv[g][i];
+            *reinterpret_cast<uint4*>(lds + g * BUCKET_BYTES + b_dst[i] - BM * ROWB) = bv[g][i];
         __syncthreads();
         for (int g = 0; g < ng; ++g) {
           const int lg = grp[g];
@@ -850,9 +861,13 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
 #pragma unroll
           for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-              bfr[j][q4] = M::load(reinterpret_cast<const T*>(
-                  Bs + frag_off(wn * WTN + j * 32 + c32, min(q4, nks - 1))));
+            for (int q4 = 0; q4 < 4; ++q4) {
+              if constexpr (KNL)
+                bfr[j][q4] = kn_frag(Bs, BN * 2, wn * WTN + j * 32 + (c32 & 16), 16 * min(q4, nks - 1), lane);
+              else
+                bfr[j][q4] = M::load(reinterpret_cast<const T*>(
+                    Bs + frag_off(wn * WTN + j * 32 + c32, min(q4, nks - 1))));
+            }
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
             const int rb = rw0 + 32 * i;
