@@ -311,6 +311,25 @@ def main() -> int:
     # --------------------------------------------------------------------------
     dom_ms = float(np.mean([ev[dom_i].elapsed_time(ev[dom_i + 1]) for ev in dom_events]))
 
+    # the same K steps replayed from a HIP graph of the step (align + forward
+    # captured once; no host launch cost per kernel), for context
+    try:
+        cs = ops.CapturedStep(ops.MoELoRALayer(d, W, dev), x, logits, adapter_ids)
+        for _ in range(args.warmup):
+            cs.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(args.steps):
+            cs.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter() - tg
+        graph = {"value": round(cfg.tokens * args.steps / tg, 2),
+                 "ms_per_step": round(tg * 1e3 / args.steps, 4)}
+        del cs
+    except Exception as exc:  # reported, not fatal: the eager line above is the measurement
+        graph = {"error": str(exc)[:200]}
+    log(f"[bench] HIP graph replay: {graph}")
+
     offsets = layer.routing[3].cpu().numpy()
     fusion = ops.forward_fusion(d)
     work, Eact, P = stage_work(cfg, offsets, fusion)
@@ -390,6 +409,7 @@ def main() -> int:
                    "adapter_dist": cfg.adapter_dist, "parallelism": "single GPU"},
         "roofline": roof,
         "value_cold_p50": round(cfg.tokens / (lat_cold["p50"] * 1e-6), 2),
+        "graph_replay": graph,
         "latency_us": {"warm": lat_warm, "cold_1GiB_read_flush": lat_cold},
         "gemms": gemms,
         "fusion": fusion,

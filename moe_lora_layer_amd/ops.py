@@ -386,6 +386,31 @@ class MoELoRALayer:
                        workspace_buf=self.ws_fwd, stream=stream)
 
 
+class CapturedStep:
+    """A MoELoRALayer step (moelora_align then moelora_forward) captured once
+    into a HIP graph over fixed input buffers x [T][h], logits [T][E] and
+    adapter_ids [T]; replay() runs it again on whatever those buffers hold
+    and returns the layer's output buffer.  Nothing is allocated or
+    synchronised inside the step and the library clears its memory with fill
+    kernels, so the graph holds kernel launches only.  One warm-up call runs
+    outside the capture (the library's first-call lookups)."""
+
+    def __init__(self, layer: MoELoRALayer, x, logits, adapter_ids):
+        self.layer, self.x, self.logits, self.adapter_ids = layer, x, logits, adapter_ids
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer(x, logits, adapter_ids)
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.out = layer(x, logits, adapter_ids)
+
+    def replay(self):
+        self.graph.replay()
+        return self.out
+
+
 def make_dense_dims(tokens, in_features, out_features, adapters, rank, dtype, deterministic=False,
                     base_only=False, unfused=False, in_out=False, plan=None) -> DenseDims:
     if isinstance(dtype, str):
