@@ -13,10 +13,11 @@
 //   1. keys: read the routed keys (or, without routing, form them from the
 //      caller's expert ids) into LDS when they fit;
 //   2. chunk ranks: the S slots are cut into C contiguous chunks, one per wave.
-//      A wave walks its chunk 64 slots at a time; lanes with equal keys find
-//      each other with ballots, so every slot gets its rank among equal keys of
-//      lower index inside the chunk, and the chunk's per-bucket counts live in
-//      LDS (cnt[c][b]); keys and ranks stay in LDS too when the batch is small;
+//      A wave walks its chunk 64 slots at a time; a bitonic sort of (key, lane)
+//      across the wave brings equal keys together, so every slot gets its rank
+//      among equal keys of lower index inside the chunk, and the chunk's
+//      per-bucket counts live in LDS (cnt[c][b]), or in the workspace when
+//      there are very many buckets; keys and ranks stay in LDS when they fit;
 //   3. scan: bucket totals, a wavefront-level exclusive prefix scan over the
 //      buckets gives bucket_offsets, and cnt[c][b] becomes the first output
 //      position of chunk c's slots in bucket b;
@@ -35,6 +36,7 @@ namespace moelora {
 
 constexpr int kAlignThreads = 1024;
 constexpr int kMaxTopK = 8;
+constexpr int kKeyBatch = 8;  // slot keys loaded per thread before any is used
 
 // KEYS_LDS: the per-slot keys and ranks live in LDS after the counters (small
 // batches); otherwise in the workspace.
@@ -165,18 +167,31 @@ k_align(const int32_t* __restrict__ ids_in, const int32_t* __restrict__ adapter_
 
   // ---- 1. keys -----------------------------------------------------------------
   if (ROUTED) {
-    // keys from k_route; a flagged key marks a token whose adapter id was out of range
-    for (int s = tid; s < S; s += kAlignThreads) {
-      int key = ws_key[s];
-      if (key & kKeyBadAdapter) {
-        atomicMax(&bad, 1);
-        key &= ~kKeyBadAdapter;
+    // keys from k_route; a flagged key marks a token whose adapter id was out of range.
+    // kKeyBatch keys per thread are loaded before any is used, so their
+    // latencies overlap (the loop would otherwise wait for each load in turn)
+    for (int s0 = tid; s0 < S; s0 += kKeyBatch * kAlignThreads) {
+      int kv[kKeyBatch];
+#pragma unroll
+      for (int u = 0; u < kKeyBatch; ++u) {
+        const int s = s0 + u * kAlignThreads;
+        kv[u] = s < S ? ws_key[s] : 0;
       }
-      if (key < 0 || key >= nb) {  // cannot happen for routed keys; never index with it
-        atomicMax(&bad, 2);
-        key = 0;
+#pragma unroll
+      for (int u = 0; u < kKeyBatch; ++u) {
+        const int s = s0 + u * kAlignThreads;
+        if (s >= S) break;
+        int key = kv[u];
+        if (key & kKeyBadAdapter) {
+          atomicMax(&bad, 1);
+          key &= ~kKeyBadAdapter;
+        }
+        if (key < 0 || key >= nb) {  // cannot happen for routed keys; never index with it
+          atomicMax(&bad, 2);
+          key = 0;
+        }
+        key_buf[s] = key;
       }
-      key_buf[s] = key;
     }
   } else {
     for (int t = tid; t < T; t += kAlignThreads) {
