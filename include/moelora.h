@@ -177,9 +177,13 @@ typedef struct moelora_dims {
  *                           a_down    [L][E][I][r] b_down    [L][E][r][h]
  *   moelora_dense_forward:  w [K][N], a [L][K][r], b [L][r][N]
  * instead of the default K-contiguous (transposed) arrays.  Same result within
- * the layer's tolerance.  The kernels read these arrays as they are: operands
- * loaded through registers are transposed across lanes in registers, operands
- * copied straight into LDS are read with the transposing LDS loads of gfx950.
+ * the layer's tolerance.  The kernels read these arrays as they are: bf16
+ * operands that pass through LDS (copied straight in, or stored from
+ * registers as loaded) stay k-major there and are read with the transposing
+ * LDS loads of gfx950; operands loaded straight into MFMA fragments (the LoRA
+ * shrink and expand kernels) and fp32 tiles are transposed across lanes in
+ * registers.  The default layout is the faster one for weight-streaming
+ * (decode-sized) batches.
  */
 #define MOELORA_FLAG_IN_OUT 8
 

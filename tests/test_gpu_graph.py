@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import WEIGHTS, assert_close, device, device_inputs, say, to_f64
+from gpu_util import WEIGHTS, assert_close, device, device_inputs, in_out, say, to_f64
 from moe_lora_layer_amd import ops, synth
 
 pytestmark = pytest.mark.gpu
@@ -16,6 +16,8 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("bf16_decode", lambda seed: synth.LayerConfig("graph", 64, 512, 1024, 8, 2, 4, 32, "bf16",
                                                    requests=64, seed=seed)),
+    ("bf16_decode_in_out", lambda seed: synth.LayerConfig("graph_io", 64, 512, 1024, 8, 2, 4, 32, "bf16",
+                                                          requests=64, seed=seed)),
     ("bf16_ragged", lambda seed: synth.LayerConfig("graph", 37, 256, 768, 6, 3, 5, 16, "bf16",
                                                    requests=37, seed=seed)),
     ("f32_tiny", lambda seed: synth.LayerConfig("graph", 64, 256, 512, 8, 2, 4, 16, "f32",
@@ -29,8 +31,9 @@ def test_graph_replays_match_eager(name, make, det):
     dev = device()
     cfgs = [make(seed) for seed in (11, 12, 13, 14)]
     inps = [synth.make_inputs(c) for c in cfgs]
-    dinps = [device_inputs(i, c, dev) for i, c in zip(inps, cfgs)]
-    d = ops.dims_for(cfgs[0], deterministic=det)
+    kn = name.endswith("in_out")  # weights h_in x h_out (MOELORA_FLAG_IN_OUT); the oracle keeps inps
+    dinps = [device_inputs(in_out(i) if kn else i, c, dev) for i, c in zip(inps, cfgs)]
+    d = ops.dims_for(cfgs[0], deterministic=det, in_out=kn)
     W = {n: dinps[0][n] for n in WEIGHTS}  # one layer's weights (seed 11) for every input set
     eager = ops.MoELoRALayer(d, W, dev)
     refs = [eager(di["x"], di["logits"], di["adapter_ids"]).clone() for di in dinps]
