@@ -189,6 +189,14 @@ def counters(out_md: str, title: str, kernel: str, pmc_dirs: list[str], command:
             if k in avg:
                 lines.append(f"- waves waiting {what}: {k} / SQ_WAVE_CYCLES = "
                              f"{avg[k] / avg['SQ_WAVE_CYCLES']:.2f}")
+    if "TCC_EA0_RDREQ_LEVEL_sum" in avg and avg.get("TCC_EA0_RDREQ_sum", 0) > 0:
+        # reads in flight summed over cycles, over reads: the mean L2-miss read latency
+        lines.append(f"- L2-miss read latency: TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum = "
+                     f"{avg['TCC_EA0_RDREQ_LEVEL_sum'] / avg['TCC_EA0_RDREQ_sum']:.0f} cycles")
+    if "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum" in avg and "GRBM_GUI_ACTIVE" in avg:
+        lines.append(f"- DRAM credit stalls: TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum / cycles = "
+                     f"{avg['TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum'] / (avg['GRBM_GUI_ACTIVE'] / 8):.3f} "
+                     f"(summed over the L2 channels)")
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
         fl = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
         lines.append(f"- bf16 MFMA work issued: 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 = {fl / 1e12:.3f} TFLOP "
