@@ -96,7 +96,10 @@ typedef enum moelora_dtype {
  *                   M-tiles innermost, remapped so that every XCD (one L2)
  *                   runs a contiguous run of them; 3 launch order with every
  *                   workgroup's K walk starting at its own step (rotated), so
- *                   that resident workgroups stream different K columns; 4 both
+ *                   that resident workgroups stream different K columns; 4 both;
+ *                   5 as 2, with the M-tiles of an expert starting their K walks
+ *                   2 steps apart per M-tile (the tiles sharing a weight tile
+ *                   then read each weight step from L2 after the first)
  *                   (automatic: 2 for the weight-reuse tiles, 3 for the
  *                   weight-streaming ones, 1 for them over MOELORA_FLAG_IN_OUT
  *                   weights)

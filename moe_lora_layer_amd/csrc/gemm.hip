@@ -512,14 +512,15 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   const int active = counts[0] * n_ntiles;
   if (pid >= active) return;
   const int xcd = pid % kXcds, q = active / kXcds, rem = active % kXcds;
-  const bool xcd_grouped = order == ORDER_XCD || order == ORDER_XCD_ROTATED;
+  const bool xcd_grouped = order_xcd(order);
   const int bid = xcd_grouped ? xcd * q + min(xcd, rem) + pid / kXcds : pid;
   const int t0 = bid / n_ntiles;
   const int ex = mtiles[t0].x;
   const int ta = expert_tiles[ex], tb = expert_tiles[ex + 1];
   const int local = bid - ta * n_ntiles;
   const int nt = local / (tb - ta);
-  const int mt = ta + local % (tb - ta);
+  const int m_local = local % (tb - ta);  // M-tile of the expert, from its first
+  const int mt = ta + m_local;
   const int4 tile = mtiles[mt];
   const int e = tile.x, row0 = tile.y, row_end = tile.z;
   const int64_t n0 = static_cast<int64_t>(nt) * BN;
@@ -604,14 +605,20 @@ k_gemm(const T* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_s
   const int64_t b_kmul = KN ? N : 1;  // elements of B per unit of K
 
   // ORDER_ROTATED: every workgroup starts its K walk at a different step, so that
-  // workgroups resident together do not all read the same K columns at once
+  // workgroups resident together do not all read the same K columns at once.
+  // ORDER_XCD_STAGGERED: the M-tiles sharing a weight tile start kOrderStagger
+  // steps apart (those sharing activation rows together), so that one of them
+  // brings each weight step into L2 a little before the others read it
   const int nk_all = static_cast<int>(K / BK);
   const int nk_per = (nk_all + ksplit - 1) / ksplit;
   const int kbeg = min(nk_all, ks * nk_per);
   const int nk = min(nk_all, kbeg + nk_per) - kbeg;  // K-steps of this workgroup
   const bool rot = order == ORDER_ROTATED || order == ORDER_XCD_ROTATED;
   const int kstart =
-      (rot && nk > 0) ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk) : 0;
+      nk <= 0 ? 0
+      : rot   ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk)
+      : order == ORDER_XCD_STAGGERED ? (kOrderStagger * m_local) % nk
+              : 0;
   uint4 a_reg[P][A_CH], b_reg[P][B_CH];
   auto gload = [&](int slot, int kt) {
     int kk = kt + kstart;
@@ -1283,16 +1290,18 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
 
 
 // The M-tile and N-tile of tile index bid (expert-major, per expert N-tile by
-// N-tile with its M-tiles innermost).
+// N-tile with its M-tiles innermost); m_local: the M-tile's index inside its
+// expert.
 __device__ __forceinline__ void dma_tile_of(int bid, int n_ntiles, const int4* __restrict__ mtiles,
                                             const int32_t* __restrict__ expert_tiles, int4& tile,
-                                            int& nt) {
+                                            int& nt, int& m_local) {
   const int t0 = bid / n_ntiles;
   const int ex = mtiles[t0].x;
   const int ta = expert_tiles[ex], tb = expert_tiles[ex + 1];
   const int local = bid - ta * n_ntiles;
   nt = local / (tb - ta);
-  tile = mtiles[ta + local % (tb - ta)];
+  m_local = local % (tb - ta);
+  tile = mtiles[ta + m_local];
 }
 
 // Tiles of the data-parallel part when the last, partial round of tiles is
@@ -1337,13 +1346,12 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     const int pid = static_cast<int>(blockIdx.x) / ksplit;
     if (pid >= dp) return;
     const int xcd = pid % kXcds, q = dp / kXcds, rem = dp % kXcds;
-    bid = (order == ORDER_XCD || order == ORDER_XCD_ROTATED) ? xcd * q + min(xcd, rem) + pid / kXcds
-                                                             : pid;
+    bid = order_xcd(order) ? xcd * q + min(xcd, rem) + pid / kXcds : pid;
     if (sk_mode == 1 && bid < tiles - dp) {
       // clear the output of stream-K tile dp + bid (the next launch adds into it)
       int4 st;
-      int snt;
-      dma_tile_of(dp + bid, n_ntiles, mtiles, expert_tiles, st, snt);
+      int snt, sml;
+      dma_tile_of(dp + bid, n_ntiles, mtiles, expert_tiles, st, snt, sml);
       const int64_t c0 = static_cast<int64_t>(snt) * kDmaTile;
       const int nc4 = static_cast<int>(min<int64_t>(kDmaTile, N - c0)) / 4;
       for (int i = threadIdx.x; i < (st.z - st.y) * (kDmaTile / 4); i += kDmaThreads) {
@@ -1357,19 +1365,19 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
   }
   while (u < u1) {  // uniform
     int4 tile;
-    int nt, kbeg, nk, out;
+    int nt, m_local, kbeg, nk, out;
     bool with_lora;
     float* part = nullptr;
     if (sk_mode == 2) {
       const int t = u / nk_all;
       kbeg = u % nk_all;
       nk = min(nk_all - kbeg, u1 - u);
-      dma_tile_of(dp + t, n_ntiles, mtiles, expert_tiles, tile, nt);
+      dma_tile_of(dp + t, n_ntiles, mtiles, expert_tiles, tile, nt, m_local);
       out = DMA_OUT_ATOMIC;
       with_lora = kbeg == 0;
       u += nk;
     } else {
-      dma_tile_of(bid, n_ntiles, mtiles, expert_tiles, tile, nt);
+      dma_tile_of(bid, n_ntiles, mtiles, expert_tiles, tile, nt, m_local);
       const int nk_per = (nk_all + ksplit - 1) / ksplit;
       kbeg = min(nk_all, ks * nk_per);
       nk = min(nk_all, kbeg + nk_per) - kbeg;
@@ -1379,10 +1387,15 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
       with_lora = true;
       u = u1;
     }
-    // rotated K walk (data-parallel items only): this workgroup starts at step kstart
-    const int kstart = (sk_mode != 2 && (order == ORDER_ROTATED || order == ORDER_XCD_ROTATED) && nk > 0)
-                           ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk)
-                           : 0;
+    // rotated or staggered K walk (data-parallel items only, as in k_gemm):
+    // this workgroup starts at step kstart
+    int kstart = 0;
+    if (sk_mode != 2 && nk > 0) {
+      if (order == ORDER_ROTATED || order == ORDER_XCD_ROTATED)
+        kstart = static_cast<int>((static_cast<int64_t>(blockIdx.x) * 37) % nk);
+      else if (order == ORDER_XCD_STAGGERED)
+        kstart = (kOrderStagger * m_local) % nk;
+    }
     dma_item<GATHER, EPI, KN>(smem, X, x_rows, gather_slots, gather_k, Wt, N, K, C, tile, nt, kbeg,
                               nk, out, with_lora, lora, part, kstart);
   }

@@ -36,7 +36,13 @@ hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_
 
 // Workgroup order of the base GEMMs (moelora_plan.order): launch order, the
 // expert's tiles grouped per XCD, every workgroup's K walk rotated, or both.
-enum { ORDER_LAUNCH = 1, ORDER_XCD = 2, ORDER_ROTATED = 3, ORDER_XCD_ROTATED = 4 };
+enum { ORDER_LAUNCH = 1, ORDER_XCD = 2, ORDER_ROTATED = 3, ORDER_XCD_ROTATED = 4, ORDER_XCD_STAGGERED = 5 };
+// ORDER_XCD_STAGGERED: M-tile m of an expert (counted from the expert's first)
+// starts its K walk kOrderStagger * m steps in
+constexpr int kOrderStagger = 2;
+__host__ __device__ constexpr bool order_xcd(int order) {
+  return order == ORDER_XCD || order == ORDER_XCD_ROTATED || order == ORDER_XCD_STAGGERED;
+}
 
 // Tile descriptor: x = expert (M-tiles) or bucket (LoRA tiles), y = first
 // sorted row, z = end row (exclusive), w unused.

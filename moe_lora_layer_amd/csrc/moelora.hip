@@ -45,7 +45,7 @@ int check_plan(const moelora_plan& o) {
   if (o.ksplit_gate_up < 0 || o.ksplit_gate_up > 1024 || o.ksplit_down < 0 || o.ksplit_down > 1024)
     return MOELORA_ERR_UNSUPPORTED;
   if (o.fuse < 0 || o.fuse > 3) return MOELORA_ERR_UNSUPPORTED;
-  if (o.order < 0 || o.order > 4) return MOELORA_ERR_UNSUPPORTED;
+  if (o.order < 0 || o.order > 5) return MOELORA_ERR_UNSUPPORTED;
   return MOELORA_OK;
 }
 

@@ -205,7 +205,7 @@ def _search(d, run, fields: list, steps: int, rounds: int, log):
             elif field == "fuse":
                 options = [{"fuse": v} for v in (1, 2, 3)]
             elif field == "order":
-                options = [{"order": v} for v in (1, 2, 3, 4)]
+                options = [{"order": v} for v in (1, 2, 3, 4, 5)]
             else:
                 options = [{field: v} for v in SPLITS]
             for opt in options:

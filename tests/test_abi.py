@@ -184,7 +184,7 @@ def test_deterministic_workspace_holds_the_partials(kw):
 PLAN_CASES = [
     dict(gemm_rows=48), dict(gemm_rows=-32), dict(gemm_form=3), dict(gemm_form=1),  # form needs rows
     dict(gemm_rows=256, gemm_form=1), dict(gemm_rows=64, gemm_form=2), dict(lora_rows=32),
-    dict(ksplit_gate_up=-1), dict(ksplit_down=1025), dict(fuse=4), dict(fuse=-1), dict(order=5),
+    dict(ksplit_gate_up=-1), dict(ksplit_down=1025), dict(fuse=4), dict(fuse=-1), dict(order=6),
     dict(order=-1),
 ]
 

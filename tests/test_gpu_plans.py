@@ -83,7 +83,8 @@ def test_dense_every_plan():
 
 @pytest.mark.parametrize("shape", SHAPES[:2] + SHAPES[2:3], ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
 def test_forward_every_workgroup_order(shape):
-    """plan.order 1-4 (launch order, XCD-grouped, rotated K walk, both) on every
+    """plan.order 1-5 (launch order, XCD-grouped, rotated K walk, both, XCD-grouped
+    with staggered K walks) on every
     GEMM tile family, split-K included, for both weight layouts: the oracle's
     result within tolerance."""
     from gpu_util import in_out
@@ -96,7 +97,7 @@ def test_forward_every_workgroup_order(shape):
         ids, w, ss, off, st = run_align(cfg, dinp)
         assert int(st[0].item()) == 0
         seen = set()
-        for (r, f), (kg, kd), order in itertools.product(GEMM_SHAPES, ((0, 0), (3, 2)), (1, 2, 3, 4)):
+        for (r, f), (kg, kd), order in itertools.product(GEMM_SHAPES, ((0, 0), (3, 2)), (1, 2, 3, 4, 5)):
             d = ops.dims_for(cfg, in_out=io, plan=dict(gemm_rows=r, gemm_form=f, ksplit_gate_up=kg,
                                                        ksplit_down=kd, order=order))
             eff = ops.forward_plan(d)
