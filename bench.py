@@ -44,15 +44,24 @@ def log(*a):
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    """The host CPU as /proc/cpuinfo names it (model name, with the family /
+    model / stepping numbers, which identify the core generation when a
+    virtualised host reports a generic name), or "unknown"."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if info:
+                        break  # first processor only
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                info.setdefault(k, v)
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def stage_work(cfg, offsets, fusion):
