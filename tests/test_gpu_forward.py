@@ -368,43 +368,6 @@ def test_canaries_and_second_stream():
     assert_close(to_f64(out2), ref, "bf16", "stream 2")
 
 
-def test_graph_capture_replays_match_eager():
-    """align + forward captured in a HIP graph (the library only enqueues
-    kernels and event-free launches, no memsets); every replay, with eager work
-    and synchronisations between replays, matches the eager run: routing and
-    permutation bit for bit, the output within the parity tolerance."""
-    cfg = _small(96, 192, 320, 5, 2, 3, 32, "bf16", seed=23)
-    inp = synth.make_inputs(cfg)
-    dev = device()
-    dinp = device_inputs(inp, cfg, dev)
-    d = ops.dims_for(cfg)
-    layer = ops.MoELoRALayer(d, {n: dinp[n] for n in WEIGHTS}, dev)
-    eager = layer(dinp["x"], dinp["logits"], dinp["adapter_ids"]).clone()
-    eager_routing = [t.clone() for t in layer.routing]
-    torch.cuda.synchronize()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        layer(dinp["x"], dinp["logits"], dinp["adapter_ids"])   # warm-up on the side stream
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        layer(dinp["x"], dinp["logits"], dinp["adapter_ids"])
-    for rep in range(3):
-        layer.out.fill_(-1.0)
-        for t in layer.routing:
-            t.fill_(-7)
-        torch.cuda.synchronize()
-        g.replay()
-        junk = torch.randn(1 << 16, device=dev).sum()      # eager work between replays
-        torch.cuda.synchronize()
-        for a, b in zip(layer.routing, eager_routing):
-            assert torch.equal(a, b), rep
-        assert_close(to_f64(layer.out), to_f64(eager), "bf16", f"replay {rep}")
-        del junk
-
-
 DET_SHAPES = [
     (96, 128, 2048, 1, 1, 4, 16, "bf16"),    # down GEMM split over K
     (64, 256, 512, 8, 2, 4, 16, "f32"),      # short buckets: k_shrink

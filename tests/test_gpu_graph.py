@@ -1,9 +1,10 @@
 """A layer step (moelora_align then moelora_forward, through the C ABI)
 captured into a HIP graph and replayed: every replay, on new inputs copied
-into the captured buffers with eager work and synchronisations in between,
-against the eager step on the same inputs (bit-identical in deterministic
-mode, within the layer's tolerance with atomics) and, for one replay, against
-the oracle."""
+into the captured buffers and with its outputs clobbered beforehand, with
+eager work and synchronisations in between, against the eager step on the
+same inputs (routing and permutation bit for bit; the output bit-identical in
+deterministic mode, within the layer's tolerance with atomics) and, for one
+replay, against the oracle."""
 import pytest
 import torch
 
@@ -36,7 +37,10 @@ def test_graph_replays_match_eager(name, make, det):
     d = ops.dims_for(cfgs[0], deterministic=det, in_out=kn)
     W = {n: dinps[0][n] for n in WEIGHTS}  # one layer's weights (seed 11) for every input set
     eager = ops.MoELoRALayer(d, W, dev)
-    refs = [eager(di["x"], di["logits"], di["adapter_ids"]).clone() for di in dinps]
+    refs, routings = [], []
+    for di in dinps:
+        refs.append(eager(di["x"], di["logits"], di["adapter_ids"]).clone())
+        routings.append([t.clone() for t in eager.routing])
     torch.cuda.synchronize()
     assert int(eager.status[0].item()) == 0
 
@@ -51,10 +55,15 @@ def test_graph_replays_match_eager(name, make, det):
             x.copy_(di["x"])
             logits.copy_(di["logits"])
             aid.copy_(di["adapter_ids"])
+            graphed.out.fill_(-1.0)           # every output is rewritten by the replay
+            for t in graphed.routing:
+                t.fill_(-7)
             torch.cuda.synchronize()
             out = step.replay()
             torch.cuda.synchronize()
             assert int(graphed.status[0].item()) == 0
+            for a, b in zip(graphed.routing, routings[i]):  # routing and permutation bit for bit
+                assert torch.equal(a, b), (rep, i)
             if det:
                 assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
                                    refs[i].view(torch.int16) if out.dtype == torch.bfloat16 else refs[i])
