@@ -77,13 +77,18 @@ typedef enum moelora_dtype {
  *   gemm_rows       rows per M-tile of the base grouped GEMMs: 32, 64, 128, 256
  *   gemm_form       1 weight-streaming tiles (32, 64 or 128 rows: nontemporal
  *                   weight loads, rotated K walk), 2 weight-reuse tiles (128 or
- *                   256 rows); needs gemm_rows set
+ *                   256 rows), 3 (bf16, 128 rows) weight-streaming tiles of
+ *                   128 x 256 outputs whose operands go straight into three LDS
+ *                   stages; needs gemm_rows set
+ *                   (MOELORA_ERR_UNSUPPORTED otherwise, and for 3 with fp32)
  *   lora_rows       rows per LoRA tile: 16 (one MFMA block, for buckets of few
  *                   rows) or 64 (tall tiles)
  *   ksplit_gate_up  K splits of the gate_up GEMM (fp32 atomics, or ordered
  *                   partials with MOELORA_FLAG_DETERMINISTIC), 1..1024; rounded
  *                   down to a count whose K ranges are all non-empty
- *   ksplit_down     the same for the down GEMM (the dense projection's GEMM)
+ *   ksplit_down     the same for the down GEMM (the dense projection's GEMM),
+ *                   whose splits always store partials that the combine pass
+ *                   sums in split order (deterministic with or without the flag)
  *   fuse            1: every projection whose GEMM can (bf16, unsplit K) runs
  *                   its LoRA expand in the GEMM epilogue; 2: none does; 3: as
  *                   1, and the fused gate_up epilogue also computes the down
@@ -100,9 +105,9 @@ typedef enum moelora_dtype {
  *                   5 as 2, with the M-tiles of an expert starting their K walks
  *                   2 steps apart per M-tile (the tiles sharing a weight tile
  *                   then read each weight step from L2 after the first)
- *                   (automatic: 2 for the weight-reuse tiles, 3 for the
- *                   weight-streaming ones, 1 for them over MOELORA_FLAG_IN_OUT
- *                   weights)
+ *                   (automatic: 2 for the weight-reuse tiles and form 3, 3
+ *                   for the other weight-streaming ones, 1 for those over
+ *                   MOELORA_FLAG_IN_OUT weights)
  * The K step of every GEMM tile is fixed at 64 bf16 / 32 fp32 elements (one
  * 128-byte LDS row); it is not a plan field.
  * Out-of-range values make every call that takes the dims return
@@ -140,9 +145,10 @@ typedef struct moelora_dims {
 
 /*
  * MOELORA_FLAG_DETERMINISTIC: every split-K reduction (the LoRA shrinks, and
- * the base GEMMs when their K is split because the output is narrow) writes
+ * the gate_up GEMM when its K is split because the output is narrow) writes
  * one fp32 partial per split to the forward workspace and a separate pass sums
- * the partials in split order, instead of relaxed fp32 atomics; and the
+ * the partials in split order, instead of relaxed fp32 atomics (a split down
+ * GEMM does so in every mode, its partials summed by the combine pass); and the
  * 256-row down GEMM gives up its stream-K pass (the last, partial round of
  * tiles cut into K ranges whose parts are added with atomics).  The output is
  * then bit-identical from run to run for the same inputs and dims (without the

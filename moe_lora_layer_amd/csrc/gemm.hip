@@ -1005,41 +1005,56 @@ static hipError_t lds_launch(const TilePlan& plan, const GemmArgs& a, const Lora
 }
 
 
-// ------------------------------------------------------------- prefill gemm
-// bf16 tiles of 256 x 256 outputs for M-tiles of 256 rows (many rows per
-// expert, so every weight tile is reused by several M-tiles and the GEMM is
-// bound by the matrix cores).  Eight waves (two per SIMD) of 128 x 64 outputs.
-// The K walk is staged in LDS in steps of 64 (128-byte rows) with two stages:
-// the operands go from global memory straight into LDS
-// (global_load_lds_dwordx4, no register round trip, no LDS store
-// instructions), and step kt+2 is requested as soon as every wave has read
-// step kt, so one step of loads is always in flight behind the MFMAs.  The
-// LDS rows keep the 16-byte-chunk XOR swizzle of the register-staged kernel:
-// a load instruction fills 8 whole rows, each lane fetching the global chunk
-// that belongs at its LDS position.
+// ------------------------------------------------------------- DMA gemm
+// bf16 tiles of BM x 256 outputs whose operands go from global memory straight
+// into LDS (global_load_lds_dwordx4, no register round trip, no LDS store
+// instructions), K staged in steps of 64 (128-byte rows).  Eight waves (two
+// per SIMD) of BM/2 x 64 outputs.  The LDS rows keep the 16-byte-chunk XOR
+// swizzle of the register-staged kernel: a load instruction fills 8 whole
+// rows, each lane fetching the global chunk that belongs at its LDS position.
+//  * BM = 256 (prefill: many rows per expert, every weight tile reused by
+//    several M-tiles, bound by the matrix cores): two stages of 64 KiB; step
+//    kt+2 is requested as soon as every wave has read step kt, so one step of
+//    loads is always in flight behind the MFMAs.
+//  * BM = 128 (one M-tile per expert, e.g. a dense layer's 128 tokens: the
+//    weights stream through once, bound by HBM): three stages of 48 KiB, so
+//    that two steps of weight loads are in flight; 256 weight rows per tile
+//    halve the activation re-reads per weight byte against 128-row tiles.
 
-constexpr int kDmaTile = 256;                       // BM = BN
+constexpr int kDmaTile = 256;                       // weight rows (BN) of a tile
 constexpr int kDmaRowB = 128;                       // bytes of K per LDS row (64 bf16)
-constexpr int kDmaStage = 2 * kDmaTile * kDmaRowB;  // A and B rows of one K-step: 64 KiB
 constexpr int kDmaThreads = 512;
 
-// The four A and four B load instructions of one wave for the K-step at
-// element offset ko into stage `slot` (8 rows of 128 bytes each; KN, k-major
-// weights: the B tile is 64 k-rows of 512 bytes, 2 rows per instruction, and
-// the step advances the weight rows by ko * N).
-template <bool KN>
-__device__ __forceinline__ void dma_issue(unsigned char* smem, int slot, int64_t ko, int64_t N,
+template <int BM>
+struct DmaShape {
+  static_assert(BM == 128 || BM == 256, "DMA tiles have 128 or 256 activation rows");
+  static constexpr int kStages = BM == 256 ? 2 : 3;
+  static constexpr int kStage = (BM + kDmaTile) * kDmaRowB;  // A and B rows of one K-step
+  static constexpr int kARows = BM / 8;                      // activation rows loaded per wave
+  static constexpr int kAIns = kARows / 8;                   // ... in load instructions of 8 rows
+  static constexpr int kLoads = kAIns + 4;                   // loads per wave per K-step
+  static constexpr int kWaveRows = BM / 2;                   // a wave's output rows
+  static constexpr int kFM = kWaveRows / 32;                 // ... in 32-row MFMA blocks
+};
+
+// The kAIns A and four B load instructions of one wave for the K-step at
+// element offset ko into the stage at `st` (8 rows of 128 bytes each; KN,
+// k-major weights: the B tile is 64 k-rows of 512 bytes, 2 rows per
+// instruction, and the step advances the weight rows by ko * N).
+template <int BM, bool KN>
+__device__ __forceinline__ void dma_issue(unsigned char* st, int64_t ko, int64_t N,
                                           const bf16_t* const* a_src, const bf16_t* const* b_src,
                                           int wave) {
-  unsigned char* st = smem + slot * kDmaStage;
+  typedef DmaShape<BM> S;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma_piece(a_src[j] + ko, st + (32 * wave + 8 * j) * kDmaRowB);
+  for (int j = 0; j < S::kAIns; ++j)
+    dma_piece(a_src[j] + ko, st + (S::kARows * wave + 8 * j) * kDmaRowB);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (KN)
-      dma_piece(b_src[j] + ko * N, st + kDmaTile * kDmaRowB + (8 * wave + 2 * j) * (2 * kDmaTile));
+      dma_piece(b_src[j] + ko * N, st + BM * kDmaRowB + (8 * wave + 2 * j) * (2 * kDmaTile));
     else
-      dma_piece(b_src[j] + ko, st + (kDmaTile + 32 * wave + 8 * j) * kDmaRowB);
+      dma_piece(b_src[j] + ko, st + (BM + 32 * wave + 8 * j) * kDmaRowB);
   }
 }
 
@@ -1052,7 +1067,7 @@ enum { DMA_OUT_STORE = 0, DMA_OUT_ATOMIC = 1, DMA_OUT_PART = 2 };
 // (M-tile `tile`, N-tile nt), written as `out` says; with_lora adds the fused
 // LoRA expand (exactly one item of a tile carries it).  Every wave of the
 // workgroup calls it with the same arguments.
-template <bool GATHER, int EPI, bool KN>
+template <int BM, bool GATHER, int EPI, bool KN>
 __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __restrict__ X,
                                          int x_rows, const int32_t* __restrict__ gather_slots,
                                          int gather_k, const bf16_t* __restrict__ Wt, int64_t N,
@@ -1060,6 +1075,8 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
                                          int kbeg, int nk, int out, bool with_lora,
                                          const LoraEpilogue& lora, float* __restrict__ part,
                                          int kstart) {
+  typedef DmaShape<BM> S;
+  constexpr int FM = S::kFM, WR = S::kWaveRows;
   lds_barrier();  // every wave is done with what the LDS held for the previous item
   const int e = tile.x, row0 = tile.y, row_end = tile.z;
   // Output columns.  EPI_GATE_UP: the tile covers 128 columns i of the
@@ -1075,20 +1092,25 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
   const int wm = wave >> 2, wn = wave & 3;
   const int c32 = lane & 31, h = lane >> 5;
 
-  // Load instruction j of wave w fills tile rows 32w + 8j + lane/8 (A and B);
-  // the lane's LDS chunk is lane%8, so it fetches logical chunk
-  // (lane%8) ^ swz(row).  Rows past the tile's end (M) or past N read a valid
-  // clamped row: they only feed outputs that are never stored.
-  const bf16_t* a_src[4];
+  // Load instruction j of wave w fills A rows kARows w + 8j + lane/8 and B
+  // rows 32w + 8j + lane/8; the lane's LDS chunk is lane%8, so it fetches
+  // logical chunk (lane%8) ^ swz(row).  Rows past the tile's end (M) or past
+  // N read a valid clamped row: they only feed outputs that are never stored.
+  const bf16_t* a_src[S::kAIns];
   const bf16_t* b_src[4];
   const bf16_t* We = Wt + static_cast<int64_t>(e) * N * K;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rt = 32 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < S::kAIns; ++j) {
+    const int rt = S::kARows * wave + 8 * j + (lane >> 3);
     const int lch = (lane & 7) ^ swz<1>(rt);
     const int p = min(row0 + rt, row_end - 1);
     const int r = GATHER ? gather_slots[p] / gather_k : p;
     a_src[j] = X + static_cast<int64_t>(min(max(r, 0), x_rows - 1)) * K + lch * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rt = 32 * wave + 8 * j + (lane >> 3);
+    const int lch = (lane & 7) ^ swz<1>(rt);
     if (!KN) {
       int64_t wrow;
       if (is_gu(EPI)) {  // B tile row rt = 64 wn' + 32 half + c
@@ -1120,20 +1142,20 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
   int lb = 0, ub = 0;
   if (EPI != EPI_STORE && with_lora) lora_buckets(lora, e, row0, row_end, lb, ub);
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[FM][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = zero_acc();
 
-  // fragment reads: substep s (16 of the 64 K) of row r = 128 wm + 32 i + c32;
+  // fragment reads: substep s (16 of the 64 K) of row r = WR wm + 32 i + c32;
   // (r >> 1) & 7 depends on c32 only
   const int sw = swz<1>(c32);
-  const int a_off = (wm * 128 + c32) * kDmaRowB;
-  const int b_off = (kDmaTile + wn * 64 + c32) * kDmaRowB;
-  bf16x8_t fa[2][4], fb[2][2];
+  const int a_off = (wm * WR + c32) * kDmaRowB;
+  const int b_off = (BM + wn * 64 + c32) * kDmaRowB;
+  bf16x8_t fa[2][FM], fb[2][2];
   // Only the wave's 32-row blocks that hold rows of the tile are read and
-  // multiplied (NB of the 4; an expert's last tile is often partly empty);
+  // multiplied (NB of the FM; an expert's last tile is often partly empty);
   // the K loop below is instantiated per NB.
   auto rd = [&](int f, const unsigned char* st, int s, auto nbc) {
     constexpr int NB = decltype(nbc)::value;
@@ -1144,7 +1166,7 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (KN)
-        fb[f][j] = kn_frag(st + kDmaTile * kDmaRowB, 2 * kDmaTile, wn * 64 + 32 * j + (c32 & 16),
+        fb[f][j] = kn_frag(st + BM * kDmaRowB, 2 * kDmaTile, wn * 64 + 32 * j + (c32 & 16),
                            16 * s, lane);
       else
         fb[f][j] = *reinterpret_cast<const bf16x8_t*>(st + b_off + j * 32 * kDmaRowB + ch);
@@ -1171,41 +1193,60 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
     if constexpr (NR > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NR - PAIRS, 0);
   };
   // workgroup barrier that orders LDS accesses only; the DMA is waited for
-  // explicitly with vmcnt
-  auto bar = [&]() { lds_barrier(); };
+  // explicitly with vmcnt.  Two stages: the fenced barrier (its fence waits
+  // for every LDS write in flight, the DMA included, which the two-stage loop
+  // has waited for anyway).  Three stages: a bare s_barrier, so that the
+  // step still in flight stays in flight (a compiler barrier for memory
+  // accesses on both sides).
+  constexpr int NS = S::kStages, LD = S::kLoads;
+  auto bar = [&]() {
+    if constexpr (NS == 2) {
+      lds_barrier();
+    } else {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto ko = [&](int kt) {
     const int kk = kt + kstart;
     return static_cast<int64_t>(kbeg + (kk >= nk ? kk - nk : kk)) * 64;
   };
+  auto stage = [&](int q) { return smem + q * S::kStage; };
 
-  // K-step kt lives in stage kt % 2.  Both stages are requested up front;
-  // steps past the end repeat the last one (never read), which keeps the
-  // vmcnt accounting the same in every iteration.
-  dma_issue<KN>(smem, 0, ko(0), N, a_src, b_src, wave);
-  dma_issue<KN>(smem, 1, ko(min(1, nk - 1)), N, a_src, b_src, wave);
-  wait_vmcnt<8>();  // this wave's loads of step 0 are in LDS
-  bar();            // ... and every other wave's
+  // K-step kt lives in stage kt % NS.  The first NS steps are requested up
+  // front; steps past the end repeat the last one (never read), which keeps
+  // the vmcnt accounting the same in every iteration.
+#pragma unroll
+  for (int q = 0; q < NS; ++q)
+    dma_issue<BM, KN>(stage(q), ko(min(q, nk - 1)), N, a_src, b_src, wave);
+  wait_vmcnt<(NS - 1) * LD>();  // this wave's loads of step 0 are in LDS
+  bar();                        // ... and every other wave's
   auto k_loop = [&](auto nbc) {
     rd(0, smem, 0, nbc);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing scalar or LDS pending into the loop
+    int cs = 0;                          // stage of step kt
     for (int kt = 0; kt + 1 < nk; ++kt) {
-      const unsigned char* cur = smem + (kt & 1) * kDmaStage;
+      const int nx = cs + 1 == NS ? 0 : cs + 1;  // stage of step kt+1
+      unsigned char* cur = stage(cs);
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
         rd((s + 1) & 1, cur, s + 1, nbc);
         mm(s & 1, nbc);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // step kt+1 has landed and every wave has finished reading step kt
-      // (lgkmcnt(0) before the barrier): refill that stage with step kt+2
-      wait_vmcnt_lgkm0<0>();
+      // step kt+1 has landed (step kt+2 may still be in flight) and every
+      // wave has finished reading step kt (lgkmcnt(0) before the barrier):
+      // refill that stage with step kt+NS
+      wait_vmcnt_lgkm0<(NS - 2) * LD>();
       bar();
-      dma_issue<KN>(smem, kt & 1, ko(min(kt + 2, nk - 1)), N, a_src, b_src, wave);
-      rd(0, smem + ((kt + 1) & 1) * kDmaStage, 0, nbc);
+      dma_issue<BM, KN>(cur, ko(min(kt + NS, nk - 1)), N, a_src, b_src, wave);
+      rd(0, stage(nx), 0, nbc);
       mm(1, nbc);
       __builtin_amdgcn_sched_barrier(0);
+      cs = nx;
     }
-    const unsigned char* cur = smem + ((nk - 1) & 1) * kDmaStage;
+    const unsigned char* cur = stage(cs);
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       rd((s + 1) & 1, cur, s + 1, nbc);
@@ -1216,16 +1257,16 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
     __builtin_amdgcn_sched_barrier(0);
   };
   // 32-row blocks of this wave that hold tile rows (every wave runs the same
-  // number of K steps and barriers whatever its count; in a tile of at most
-  // 128 rows, an expert's last, the second wave row has none and leaves its
-  // SIMD's matrix core to the first)
-  const int wave_rows = min(128, row_end - row0 - 128 * wm);
+  // number of K steps and barriers whatever its count; in a 256-row tile of
+  // at most 128 rows, an expert's last, the second wave row has none and
+  // leaves its SIMD's matrix core to the first)
+  const int wave_rows = min(WR, row_end - row0 - WR * wm);
   switch (max(0, (wave_rows + 31) / 32)) {
     case 0: k_loop(std::integral_constant<int, 0>{}); break;
     case 1: k_loop(std::integral_constant<int, 1>{}); break;
-    case 2: k_loop(std::integral_constant<int, 2>{}); break;
-    case 3: k_loop(std::integral_constant<int, 3>{}); break;
-    default: k_loop(std::integral_constant<int, 4>{}); break;
+    case 2: k_loop(std::integral_constant<int, (FM < 2 ? FM : 2)>{}); break;
+    case 3: k_loop(std::integral_constant<int, (FM < 3 ? FM : 3)>{}); break;
+    default: k_loop(std::integral_constant<int, FM>{}); break;
   }
   wait_vmcnt<0>();  // no LDS write of this item may outlive it
 
@@ -1237,8 +1278,8 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
     col[j] = is_gu(EPI) ? n0 + 32 * wn + c32 : n0 + 64 * wn + 32 * j + c32;
     col_ok[j] = col[j] < cols;
   }
-  const int rw0 = row0 + 128 * wm;                 // this wave's rows [rw0, rw1)
-  const int rw1 = min(row_end, rw0 + 128);
+  const int rw0 = row0 + WR * wm;                  // this wave's rows [rw0, rw1)
+  const int rw1 = min(row_end, rw0 + WR);
 
   if (EPI != EPI_STORE && with_lora) {
     // operands staged in the idle K stages: up to 14, 6, 2 buckets per round
@@ -1247,14 +1288,15 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       lrow[j] = is_gu(EPI) ? j * (kDmaTile / 2) + 32 * wn + c32 : 64 * wn + 32 * j + c32;
-    staged_lora_expand<expand_form(EPI), 4, 2, KN>(acc, lora, smem, 2 * kDmaStage, kDmaThreads / kWave, e, lb, ub,
-                                  row0, row_end, kDmaTile, kDmaTile, n0, N, lrow, rw0 < rw1, rw0,
-                                  rw1, wave, lane, c32, h);
+    staged_lora_expand<expand_form(EPI), FM, 2, KN>(acc, lora, smem, NS * S::kStage,
+                                                    kDmaThreads / kWave, e, lb, ub, row0, row_end,
+                                                    BM, kDmaTile, n0, N, lrow, rw0 < rw1, rw0,
+                                                    rw1, wave, lane, c32, h);
   }
 
   if (is_gu(EPI)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         acc[i][0][r] = silu(acc[i][0][r]) * acc[i][1][r];  // the activation, in place of gate
@@ -1264,14 +1306,14 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
       }
     if constexpr (EPI == EPI_GATE_UP_FOLD) {
       const bool wr[2] = {true, false};
-      folded_down_shrink<4, 2, 1, KN>(acc, col, wr, col_ok, rw0, lora, smem, kDmaThreads / kWave, e,
-                                      row0, row_end, kDmaTile, 128, n0, I, nt, wave, lane);
+      folded_down_shrink<FM, 2, 1, KN>(acc, col, wr, col_ok, rw0, lora, smem, kDmaThreads / kWave,
+                                       e, row0, row_end, BM, 128, n0, I, nt, wave, lane);
     }
     return;
   }
   auto store = [&](auto&& put) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1321,14 +1363,14 @@ __device__ __forceinline__ int dma_dp_tiles(int tiles, int nwg) {
 // most two tiles and adds each part with atomics, the part holding K-step 0
 // carrying the LoRA expand.  Used for the down projection, whose few long
 // tiles otherwise leave a last round with most CUs idle.
-template <bool GATHER, int EPI, bool KN>
+template <int BM, bool GATHER, int EPI, bool KN>
 __global__ void __launch_bounds__(kDmaThreads)
 k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__ gather_slots,
            int gather_k, const bf16_t* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
            const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
            const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, LoraEpilogue lora,
            float* __restrict__ parts, int64_t part_stride, int sk_mode, int nwg, int order) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDmaStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[DmaShape<BM>::kStages * DmaShape<BM>::kStage];
   const int tiles = counts[0] * n_ntiles;
   const int dp = sk_mode == 0 ? tiles : dma_dp_tiles(tiles, nwg);
   const int nk_all = static_cast<int>(K / 64);
@@ -1396,15 +1438,15 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
       else if (order == ORDER_XCD_STAGGERED)
         kstart = (kOrderStagger * m_local) % nk;
     }
-    dma_item<GATHER, EPI, KN>(smem, X, x_rows, gather_slots, gather_k, Wt, N, K, C, tile, nt, kbeg,
-                              nk, out, with_lora, lora, part, kstart);
+    dma_item<BM, GATHER, EPI, KN>(smem, X, x_rows, gather_slots, gather_k, Wt, N, K, C, tile, nt,
+                                  kbeg, nk, out, with_lora, lora, part, kstart);
   }
 }
 
 // Stream-K for the non-gate_up forms with unsplit K and no deterministic
 // partials, when the tiles exceed one round: the data-parallel launch, then
 // the stream-K launch over one workgroup per CU.
-template <bool GATHER, int EPI, bool KN>
+template <int BM, bool GATHER, int EPI, bool KN>
 static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue& lora,
                              hipStream_t stream) {
   const int64_t cols = is_gu(EPI) ? a.N / 2 : a.N;
@@ -1420,7 +1462,7 @@ static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const Lora
   }
   // the tiles' upper bound must reach a round for the device to pick stream-K
   const int mode = nwg > 0 && static_cast<int64_t>(plan.max_mt) * n_ntiles >= nwg ? 1 : 0;
-  hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI, KN>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
+  hipLaunchKernelGGL((k_gemm_dma<BM, GATHER, EPI, KN>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
                      a.expert_tiles, n_ntiles, a.ksplit, lora, a.parts, a.part_stride, mode, nwg,
@@ -1428,11 +1470,22 @@ static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const Lora
   if (mode == 0) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gemm_dma<GATHER, EPI, KN>), dim3(static_cast<unsigned>(nwg)), dim3(kDmaThreads),
+  hipLaunchKernelGGL((k_gemm_dma<BM, GATHER, EPI, KN>), dim3(static_cast<unsigned>(nwg)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
                      a.expert_tiles, n_ntiles, 1, lora, a.parts, a.part_stride, 2, nwg, plan.order);
   return hipGetLastError();
+}
+
+// the DMA tiles' epilogue picked by lora, as in lds_launch
+template <int BM, bool GATHER, bool KN>
+static hipError_t dma_dispatch(const TilePlan& plan, const GemmArgs& a, const LoraEpilogue* lora,
+                               hipStream_t stream) {
+  if (lora == nullptr) return dma_launch<BM, GATHER, EPI_STORE, KN>(plan, a, LoraEpilogue{}, stream);
+  if (lora->act != nullptr && lora->dn_a != nullptr)
+    return dma_launch<BM, GATHER, EPI_GATE_UP_FOLD, KN>(plan, a, *lora, stream);
+  if (lora->act != nullptr) return dma_launch<BM, GATHER, EPI_GATE_UP, KN>(plan, a, *lora, stream);
+  return dma_launch<BM, GATHER, EPI_DOWN, KN>(plan, a, *lora, stream);
 }
 
 template <typename T, bool GATHER, bool KN>
@@ -1443,16 +1496,16 @@ static hipError_t gemm_dispatch(const TilePlan& plan, const GemmArgs& a, const L
     case 32: return lds_launch<KN, T, 32, 128, 1, 4, 2, true, GATHER>(plan, a, lora, stream);
     case 64: return lds_launch<KN, T, 64, 128, 2, 2, 2, true, GATHER>(plan, a, lora, stream);
     case 128:
+      if constexpr (sizeof(T) == 2) {
+        if (plan.dma128)  // 128 x 256 DMA tiles, three stages
+          return dma_dispatch<128, GATHER, KN>(plan, a, lora, stream);
+      }
       if (plan.stream)  // eight waves of 64 x 32
         return lds_launch<KN, T, 128, 128, 2, 4, 2, true, GATHER>(plan, a, lora, stream);
       return lds_launch<KN, T, 128, 128, 2, 2, 1, false, GATHER, false, 1, true>(plan, a, lora, stream);
     case 256:  // prefill: 256x256 tiles, 8 waves of 128x64 (bf16: operands DMA'd into LDS)
       if constexpr (sizeof(T) == 2) {
-        if (lora == nullptr) return dma_launch<GATHER, EPI_STORE, KN>(plan, a, LoraEpilogue{}, stream);
-        if (lora->act != nullptr && lora->dn_a != nullptr)
-          return dma_launch<GATHER, EPI_GATE_UP_FOLD, KN>(plan, a, *lora, stream);
-        if (lora->act != nullptr) return dma_launch<GATHER, EPI_GATE_UP, KN>(plan, a, *lora, stream);
-        return dma_launch<GATHER, EPI_DOWN, KN>(plan, a, *lora, stream);
+        return dma_dispatch<256, GATHER, KN>(plan, a, lora, stream);
       } else {
         return lds_launch<KN, T, 256, 256, 2, 4, 1, false, GATHER, false, 1, true>(plan, a, nullptr, stream);
       }
@@ -1471,7 +1524,8 @@ hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_row
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, int64_t c_rows, const int4* mtiles,
                        const int32_t* counts, const int32_t* expert_tiles, int ksplit,
-                       const LoraEpilogue* lora, float* parts, hipStream_t stream) {
+                       const LoraEpilogue* lora, float* parts, hipStream_t stream,
+                       bool sum_parts) {
   ksplit = ksplit < 1 ? 1 : ksplit;
   float* pp = ksplit > 1 ? parts : nullptr;
   const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts, expert_tiles,
@@ -1487,7 +1541,8 @@ hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_row
   else
     e = plan.kn ? gemm_dispatch_g<float, true>(gather, plan, a, nullptr, stream)
                 : gemm_dispatch_g<float, false>(gather, plan, a, nullptr, stream);
-  if (e == hipSuccess && pp != nullptr) e = launch_reduce_parts(pp, ksplit, c_rows * N, C, stream);
+  if (e == hipSuccess && pp != nullptr && sum_parts)
+    e = launch_reduce_parts(pp, ksplit, c_rows * N, C, stream);
   return e;
 }
 

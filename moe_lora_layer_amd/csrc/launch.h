@@ -52,6 +52,7 @@ struct TilePlan {
   int max_mt;    // upper bound of M-tiles, known on the host
   int max_lt;    // upper bound of LoRA tiles
   bool stream;   // weight tiles are used by one M-tile only: stream them
+  bool dma128;   // bf16, bm 128: the 128 x 256 DMA tiles (three LDS stages)
   int ksplit_gu; // K splits of the gate_up GEMM (1 = none)
   int ksplit_dn; // K splits of the down GEMM (1 = none)
   bool lora_db;  // LoRA tiles average many rows: double-buffer their row blocks
@@ -105,14 +106,16 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 // C with fp32 atomics (C must be zero beforehand).  lora != nullptr fuses the
 // LoRA expand (and for gate_up the SiLU-mul) into the epilogue; only the bf16
 // 256-row plan with ksplit == 1 has it (hipErrorInvalidValue otherwise).
-// parts != nullptr (deterministic mode, ksplit > 1): split s writes its partial
-// tile to parts + s * c_rows * N and a second launch sums them into C in split
-// order; C needs no clearing then.
+// parts != nullptr (ksplit > 1): split s writes its partial tile to
+// parts + s * c_rows * N with plain stores and, when sum_parts, a second launch
+// sums them into C in split order (C needs no clearing then); without
+// sum_parts the caller consumes the partials.
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, int64_t c_rows, const int4* mtiles,
                        const int32_t* counts, const int32_t* expert_tiles, int ksplit,
-                       const LoraEpilogue* lora, float* parts, hipStream_t stream);
+                       const LoraEpilogue* lora, float* parts, hipStream_t stream,
+                       bool sum_parts = true);
 
 // out[i] = sum over p < nparts, in order, of parts[p * n + i] (n a multiple of 4).
 hipError_t launch_reduce_parts(const float* parts, int nparts, int64_t n, float* out,
@@ -141,9 +144,10 @@ hipError_t launch_expand_down(int dtype, int rank, const TilePlan& plan, const f
                               const void* Bt, int E, int L, float* D, int64_t h,
                               const int4* ltiles, const int32_t* counts, hipStream_t stream);
 
-// out[t][n] = sum_{j<k} w[t][j] * D[pos[t*k+j]][n], in j order.
-// out[t] = sum_j w[t][j] * D[pos[t*k + j]] in j order (w == nullptr: weights 1).
+// out[t] = sum_j w[t][j] * D[pos[t*k + j]] in j order (w == nullptr: weights 1),
+// D[p] being the sum, in order, of nparts planes of [T*k][h] (the partials of
+// a split down GEMM).
 hipError_t launch_combine(int dtype, const float* D, const int32_t* pos, const float* w, int T,
-                          int k, int64_t h, void* out, hipStream_t stream);
+                          int k, int64_t h, void* out, hipStream_t stream, int nparts = 1);
 
 }  // namespace moelora

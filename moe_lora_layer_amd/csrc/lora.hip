@@ -730,10 +730,13 @@ k_expand(const float* __restrict__ Z, const T* __restrict__ Bt, int E, int L, in
 }
 
 // -------------------------------------------------------------------- combine
+// D: nparts planes of [S][h] (pstride floats apart) whose sum, in plane order,
+// is the down projection's output per slot (one plane unless its K range was
+// split over workgroups that stored their partials).
 template <typename T>
 __global__ void __launch_bounds__(256)
-k_combine(const float* __restrict__ D, const int32_t* __restrict__ pos, const float* __restrict__ w,
-          int k, int S, int64_t h, T* __restrict__ out) {
+k_combine(const float* __restrict__ D, int nparts, int64_t pstride, const int32_t* __restrict__ pos,
+          const float* __restrict__ w, int k, int S, int64_t h, T* __restrict__ out) {
   const int t = blockIdx.x;
   const int64_t c = (static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x) * 4;
   if (c >= h) return;
@@ -741,7 +744,24 @@ k_combine(const float* __restrict__ D, const int32_t* __restrict__ pos, const fl
   for (int j = 0; j < k; ++j) {
     const int p = min(max(pos[t * k + j], 0), S - 1);
     const float wj = w != nullptr ? w[t * k + j] : 1.0f;
-    const float4 d = *reinterpret_cast<const float4*>(D + static_cast<int64_t>(p) * h + c);
+    const float* src = D + static_cast<int64_t>(p) * h + c;
+    float4 d = *reinterpret_cast<const float4*>(src);
+    // planes in order, four loads in flight at a time
+    auto add = [&](const float4& v) {
+      d.x += v.x;
+      d.y += v.y;
+      d.z += v.z;
+      d.w += v.w;
+    };
+    int s = 1;
+    for (; s + 3 < nparts; s += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const float4*>(src + (s + i) * pstride);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) add(v[i]);
+    }
+    for (; s < nparts; ++s) add(*reinterpret_cast<const float4*>(src + s * pstride));
     acc.x += wj * d.x;
     acc.y += wj * d.y;
     acc.z += wj * d.z;
@@ -940,14 +960,15 @@ hipError_t launch_expand_down(int dtype, int rank, const TilePlan& plan, const f
 }
 
 hipError_t launch_combine(int dtype, const float* D, const int32_t* pos, const float* w, int T,
-                          int k, int64_t h, void* out, hipStream_t stream) {
+                          int k, int64_t h, void* out, hipStream_t stream, int nparts) {
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>((h + 1023) / 1024));
+  const int64_t pstride = static_cast<int64_t>(T) * k * h;
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL((k_combine<bf16_t>), grid, dim3(256), 0, stream, D, pos, w, k, T * k, h,
-                       static_cast<bf16_t*>(out));
+    hipLaunchKernelGGL((k_combine<bf16_t>), grid, dim3(256), 0, stream, D, nparts, pstride, pos, w,
+                       k, T * k, h, static_cast<bf16_t*>(out));
   else
-    hipLaunchKernelGGL((k_combine<float>), grid, dim3(256), 0, stream, D, pos, w, k, T * k, h,
-                       static_cast<float*>(out));
+    hipLaunchKernelGGL((k_combine<float>), grid, dim3(256), 0, stream, D, nparts, pstride, pos, w,
+                       k, T * k, h, static_cast<float*>(out));
   return hipGetLastError();
 }
 

@@ -37,9 +37,9 @@ int check_plan(const moelora_plan& o) {
   const int rows = o.gemm_rows;
   if (rows != 0 && rows != 32 && rows != 64 && rows != 128 && rows != 256)
     return MOELORA_ERR_UNSUPPORTED;
-  if (o.gemm_form < 0 || o.gemm_form > 2) return MOELORA_ERR_UNSUPPORTED;
+  if (o.gemm_form < 0 || o.gemm_form > 3) return MOELORA_ERR_UNSUPPORTED;
   if (o.gemm_form != 0 && (rows == 0 || (o.gemm_form == 1 && rows == 256) ||
-                           (o.gemm_form == 2 && rows < 128)))
+                           (o.gemm_form == 2 && rows < 128) || (o.gemm_form == 3 && rows != 128)))
     return MOELORA_ERR_UNSUPPORTED;
   if (o.lora_rows != 0 && o.lora_rows != 16 && o.lora_rows != 64) return MOELORA_ERR_UNSUPPORTED;
   if (o.ksplit_gate_up < 0 || o.ksplit_gate_up > 1024 || o.ksplit_down < 0 || o.ksplit_down > 1024)
@@ -67,6 +67,7 @@ int check_dims(const moelora_dims* d) {
       static_cast<int64_t>(d->experts) * buckets_per_expert(d) > 2 * kMaxExpertAdapters)
     return MOELORA_ERR_DIMS;
   if (d->tokens * d->top_k >= (1ll << 31)) return MOELORA_ERR_DIMS;
+  if (d->plan.gemm_form == 3 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
   return check_plan(d->plan);
 }
 
@@ -81,11 +82,21 @@ TilePlan make_plan(const moelora_dims* d) {
   TilePlan p;
   // one M-tile per expert in the common case: mean rows per expert plus 25%
   const int64_t want = (avg * 5 + 3) / 4;
+  // (bf16: 128-row tiles only up to 160 rows; above that one 256-row tile per
+  // expert streams the weights once, 1536 tokens x 16 experts top-2: 1.31 ms
+  // against 1.44 ms on 128-row DMA tiles and 1.74 ms on 128-row reuse tiles)
+  const int64_t big = d->dtype == MOELORA_BF16 ? 160 : 256;
   p.bm = o.gemm_rows != 0 ? o.gemm_rows
-                          : (want <= 32 ? 32 : (want <= 64 ? 64 : (want <= 256 ? 128 : 256)));
+                          : (want <= 32 ? 32 : (want <= 64 ? 64 : (want <= big ? 128 : 256)));
   // at most one 128-row M-tile per expert: nothing reuses a weight tile, so the
   // weights are streamed (nontemporal loads, rotated K walk)
-  p.stream = o.gemm_form != 0 ? o.gemm_form == 1 : (p.bm < 128 || (p.bm == 128 && want <= 160));
+  p.stream = o.gemm_form != 0 ? o.gemm_form == 1 || o.gemm_form == 3
+                              : (p.bm < 128 || (p.bm == 128 && want <= 160));
+  // bf16 weight-streaming 128-row M-tiles run on the DMA tiles of 256 weight
+  // rows with three stages (dense 128 x 8192 -> 57344 gate_up 212 -> 197 us,
+  // a 1024-token 16-expert layer 1.65 -> 1.42 ms)
+  p.dma128 = d->dtype == MOELORA_BF16 && p.bm == 128 &&
+             (o.gemm_form == 3 || (o.gemm_form == 0 && p.stream));
   // LoRA tiles: 64 rows when buckets average many rows (the tall-tile kernels),
   // else one 16-row MFMA block (the weight-streaming kernels)
   p.lora_db = o.lora_rows != 0 ? o.lora_rows == 64
@@ -98,13 +109,18 @@ TilePlan make_plan(const moelora_dims* d) {
   // more splits cost more in fp32 atomics than they gain), >= 8 K-steps per
   // split.
   const int64_t est_tiles = std::max<int64_t>((S + p.bm - 1) / p.bm, std::min<int64_t>(E, S));
+  // The 128 x 256 DMA tiles hold a CU's LDS (one workgroup per CU): they
+  // aim at about one round of 256 workgroups, and leave K whole from three
+  // quarters of a round up.
   auto splits = [&](int64_t N, int64_t K, int64_t forced) {
-    const int64_t wgs = std::max<int64_t>(1, est_tiles * ((N + 127) / 128));
+    const int64_t tn = p.dma128 ? 256 : 128;
+    const int64_t wgs = std::max<int64_t>(1, est_tiles * ((N + tn - 1) / tn));
     const int64_t steps = K / (d->dtype == MOELORA_BF16 ? 64 : 32);
-    if (forced == 0 && wgs >= 256) return 1;
+    if (forced == 0 && wgs >= (p.dma128 ? 192 : 256)) return 1;
+    const int64_t auto_want = p.dma128 ? (256 + wgs / 2) / wgs : (512 + wgs - 1) / wgs;
     const int64_t want =
         forced != 0 ? std::min<int64_t>(forced, steps)
-                    : std::max<int64_t>(1, std::min<int64_t>((512 + wgs - 1) / wgs, steps / 8));
+                    : std::max<int64_t>(1, std::min<int64_t>(auto_want, steps / 8));
     // equal K ranges with none empty: every split then owns real work (and
     // writes its whole partial in deterministic mode)
     const int64_t per = (steps + want - 1) / want;
@@ -133,10 +149,12 @@ TilePlan make_plan(const moelora_dims* d) {
   p.nad = d->adapters;
   p.kn = (d->flags & MOELORA_FLAG_IN_OUT) != 0;
   // workgroup order: tiles that reuse their weight tile (256 rows, 128-row
-  // reuse) run each expert's tiles together per XCD (one L2); weight-streaming
-  // tiles rotate every workgroup's K walk, except over k-major weights, whose
-  // neighbouring N-tiles read neighbouring pieces of the same k-rows
-  const bool reuse = p.bm == 256 || (p.bm == 128 && !p.stream);
+  // reuse) and the 128-row DMA tiles run each expert's tiles together per XCD
+  // (one L2 holds the expert's activation rows: a 1024-token 16-expert layer
+  // 1.28 ms against 1.48 ms rotated); the other weight-streaming tiles rotate
+  // every workgroup's K walk, except over k-major weights, whose neighbouring
+  // N-tiles read neighbouring pieces of the same k-rows
+  const bool reuse = p.bm == 256 || (p.bm == 128 && !p.stream) || p.dma128;
   p.order = o.order != 0 ? o.order
                          : (reuse ? moelora::ORDER_XCD : (p.kn ? moelora::ORDER_LAUNCH : moelora::ORDER_ROTATED));
   return p;
@@ -146,7 +164,7 @@ TilePlan make_plan(const moelora_dims* d) {
 // 256-row bf16 tiles, 64 in the others): the partial slots of the folded
 // down shrink in deterministic mode.
 int64_t gate_up_ntiles(const moelora_dims* d, const TilePlan& plan) {
-  const int64_t tn = (plan.bm == 256 && d->dtype == MOELORA_BF16) ? 128 : 64;
+  const int64_t tn = ((plan.bm == 256 && d->dtype == MOELORA_BF16) || plan.dma128) ? 128 : 64;
   return (d->intermediate + tn - 1) / tn;
 }
 
@@ -173,17 +191,18 @@ ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
   L.z2 = off + S * r * 4;  // too when the down GEMM accumulates with atomics
   L.d = off + 2 * S * r * 4;
   off += round_up(2 * S * r * 4 + S * h * 4);
-  // deterministic mode: one region for the split-K partials of whichever
-  // reduction runs (they run one after another)
+  // one region for the partials of whichever split reduction runs (they run
+  // one after another): the shrinks' (deterministic mode or tall tiles), the
+  // split gate_up GEMM's (deterministic mode) and the split down GEMM's
   L.parts = off;
-  if (plan.shrink_partials || (plan.det && plan.fold_dn)) {
+  if (plan.shrink_partials || (plan.det && plan.fold_dn) || plan.ksplit_dn > 1) {
     const int dt = d->dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
     size_t n = 0;
     n = std::max(n, static_cast<size_t>(moelora::shrink_parts(dt, d->rank, plan, d->hidden)) * S * r);
     n = std::max(n, static_cast<size_t>(moelora::shrink_parts(dt, d->rank, plan, d->intermediate)) * S * r);
     if (plan.det && plan.ksplit_gu > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_gu) * S * 2 * I);
     if (plan.det && plan.fold_dn) n = std::max(n, static_cast<size_t>(gate_up_ntiles(d, plan)) * S * r);
-    if (plan.det && plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * S * h);
+    if (plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * S * h);
     off += round_up(n * 4);
   }
   L.total = off;
@@ -210,10 +229,12 @@ moelora_dims dense_as_layer(const moelora_dense_dims* d) {
 // the dense dims as layer dims, checked (the projection is planned as the
 // layer's down GEMM, so a gate_up split count is refused).  Automatic tiles of
 // the projection: when its rows would get the 128-row weight-streaming tiles
-// and those tiles fall short of one round of the MI355X's 256 CUs, the
-// four-wave weight-reuse tiles split over K into about one round instead (q/k/v
-// projection 128 x 8192 -> 10240: 76-80 against 97-100 us per call), with at
-// least 8 K-steps per split as in the layer's own rule.
+// and those tiles fall short of one round of the MI355X's 256 CUs, bf16 takes
+// the 128 x 256 DMA tiles and fp32 the four-wave weight-reuse tiles, split
+// over K into about one round (q/k/v projection 128 x 8192 -> 10240: 61-64
+// us per call with 6 splits of the DMA tiles, 71-72 with the reuse tiles in
+// 3, 97-100 with unsplit streaming tiles), with at least 8 K-steps per split
+// as in the layer's own rule.
 int dense_check(const moelora_dense_dims* d, moelora_dims* m) {
   if (d == nullptr) return MOELORA_ERR_NULL;
   *m = dense_as_layer(d);
@@ -225,11 +246,14 @@ int dense_check(const moelora_dense_dims* d, moelora_dims* m) {
   if (p.gemm_rows == 0 && p.gemm_form == 0 && p.ksplit_down == 0 && want > 64 && want <= 256) {
     const int64_t tiles = ((d->tokens + 127) / 128) * ((d->out_features + 127) / 128);
     if (tiles < 256) {
+      const bool bf16 = d->dtype == MOELORA_BF16;
+      // the DMA tiles are 256 outputs wide
+      const int64_t wtiles = bf16 ? ((d->tokens + 127) / 128) * ((d->out_features + 255) / 256) : tiles;
       p.gemm_rows = 128;
-      p.gemm_form = 2;
-      const int64_t steps = d->in_features / (d->dtype == MOELORA_BF16 ? 64 : 32);
+      p.gemm_form = bf16 ? 3 : 2;
+      const int64_t steps = d->in_features / (bf16 ? 64 : 32);
       p.ksplit_down = static_cast<int32_t>(std::max<int64_t>(
-          1, std::min<int64_t>((256 + tiles / 2) / tiles, steps / 8)));
+          1, std::min<int64_t>((256 + wtiles / 2) / wtiles, steps / 8)));
     }
   }
   return MOELORA_OK;
@@ -239,7 +263,7 @@ int dense_check(const moelora_dense_dims* d, moelora_dims* m) {
 moelora_plan plan_out(const TilePlan& p) {
   moelora_plan o;
   o.gemm_rows = p.bm;
-  o.gemm_form = p.bm < 128 || (p.bm == 128 && p.stream) ? 1 : 2;
+  o.gemm_form = p.dma128 ? 3 : (p.bm < 128 || (p.bm == 128 && p.stream) ? 1 : 2);
   o.lora_rows = p.bml;
   o.ksplit_gate_up = p.ksplit_gu;
   o.ksplit_down = p.ksplit_dn;
@@ -272,10 +296,12 @@ DenseLayout dense_layout(const moelora_dims* m, const TilePlan& plan) {
   L.d = off + T * r * 4;
   off += round_up(T * r * 4 + T * N * 4);
   L.parts = off;
-  if (plan.shrink_partials) {
+  if (plan.shrink_partials || plan.ksplit_dn > 1) {
     const int dt = m->dtype == MOELORA_BF16 ? moelora::DT_BF16 : moelora::DT_F32;
-    size_t n = static_cast<size_t>(moelora::shrink_parts(dt, m->rank, plan, m->intermediate)) * T * r;
-    if (plan.det && plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * T * N);
+    size_t n = plan.shrink_partials
+                   ? static_cast<size_t>(moelora::shrink_parts(dt, m->rank, plan, m->intermediate)) * T * r
+                   : 0;
+    if (plan.ksplit_dn > 1) n = std::max(n, static_cast<size_t>(plan.ksplit_dn) * T * N);
     off += round_up(n * 4);
   }
   L.total = off;
@@ -551,13 +577,14 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
     if (stage_events == nullptr || stage_events[i] == nullptr) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st);
   };
-  // the prep launch also clears Z1, Z2 (and D when the down GEMM is split)
-  const int64_t nzero =
-      plan.det ? 0 : 2ll * S * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * h : 0);
-  // one partials region: the shrinks' (deterministic mode or tall tiles) and,
-  // in deterministic mode, the split-K GEMMs' (they run one after another)
+  // the prep launch also clears Z1 and Z2 (atomic shrinks)
+  const int64_t nzero = plan.det ? 0 : 2ll * S * r;
+  // one partials region: the shrinks' (deterministic mode or tall tiles), in
+  // deterministic mode the split gate_up GEMM's, and the split down GEMM's
+  // (they run one after another)
   float* sparts = plan.shrink_partials ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
   float* parts = plan.det ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
+  float* dparts = plan.ksplit_dn > 1 ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
   hipError_t e = mark(MOELORA_STAGE_PREP);
   if (e == hipSuccess)
     e = moelora::launch_prep(sorted_slots, bucket_offsets, S, E, Lad, plan, pos, mtiles, ltiles,
@@ -595,18 +622,23 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
     e = moelora::launch_reduce_parts(parts, static_cast<int>(gate_up_ntiles(dims, plan)),
                                      static_cast<int64_t>(S) * r, Z2, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_GEMM_DOWN);
+  // split K: every split stores its partial plane (no atomics, no clearing),
+  // the expand adds into plane 0 and the combine sums the planes in order
+  float* Dn = plan.ksplit_dn > 1 ? dparts : D;
   if (e == hipSuccess) {
     const moelora::LoraEpilogue epi{Z2, static_cast<const uint16_t*>(b_down), bucket_offsets,
                                     E, dims->adapters, r, Lad, h, nullptr};
     e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, S, mtiles, counts,
-                             etiles, plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, parts, st);
+                             etiles, plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, dparts, st,
+                             false);
   }
   if (e == hipSuccess) e = mark(MOELORA_STAGE_EXPAND_DOWN);
   if (e == hipSuccess && !plan.fuse_dn)
-    e = moelora::launch_expand_down(dt, r, plan, Z2, b_down, E, Lad, D, h, ltiles, counts, st);
+    e = moelora::launch_expand_down(dt, r, plan, Z2, b_down, E, Lad, Dn, h, ltiles, counts, st);
   if (e == hipSuccess) e = mark(MOELORA_STAGE_COMBINE);
   if (e == hipSuccess)
-    e = moelora::launch_combine(dt, D, pos, topk_weights, static_cast<int>(T), k, h, out, st);
+    e = moelora::launch_combine(dt, Dn, pos, topk_weights, static_cast<int>(T), k, h, out, st,
+                                plan.ksplit_dn);
   if (e == hipSuccess) e = mark(MOELORA_NUM_STAGES);
   return hip_status(e);
 }
@@ -661,15 +693,14 @@ int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const v
   float* Z = reinterpret_cast<float*>(ws + L.z);
   float* D = reinterpret_cast<float*>(ws + L.d);
   float* sparts = plan.shrink_partials ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
-  float* parts = plan.det ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
+  float* dparts = plan.ksplit_dn > 1 ? reinterpret_cast<float*>(ws + L.parts) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   // tokens bucketed by adapter (one expert, k = 1)
   hipError_t e = moelora::launch_align(nullptr, nullptr, adapter_ids, S, 1, 1, nad, Lb, nullptr,
                                        nullptr, slots, offsets, device_status, ws_key, ws_rank,
                                        ws_cnt, st);
-  const int64_t nzero =
-      plan.det ? 0 : static_cast<int64_t>(S) * r + (plan.ksplit_dn > 1 ? static_cast<int64_t>(S) * N : 0);
+  const int64_t nzero = plan.det ? 0 : static_cast<int64_t>(S) * r;
   if (e == hipSuccess)
     e = moelora::launch_prep(slots, offsets, S, 1, Lb, plan, pos, mtiles, ltiles, counts, etiles, Z,
                              nzero, st);
@@ -680,11 +711,14 @@ int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const v
     const moelora::LoraEpilogue epi{Z, static_cast<const uint16_t*>(b), offsets, 1, nad, r, Lb, N,
                                     nullptr};
     e = moelora::launch_gemm(dt, plan, x, S, slots, 1, w, N, K, D, S, mtiles, counts, etiles,
-                             plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, parts, st);
+                             plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, dparts, st, false);
   }
+  // split K: partial planes, the expand into plane 0, the ordered sum in the combine
+  float* Dn = plan.ksplit_dn > 1 ? dparts : D;
   if (e == hipSuccess && !plan.fuse_dn)
-    e = moelora::launch_expand_down(dt, r, plan, Z, b, 1, Lb, D, N, ltiles, counts, st);
-  if (e == hipSuccess) e = moelora::launch_combine(dt, D, pos, nullptr, S, 1, N, out, st);
+    e = moelora::launch_expand_down(dt, r, plan, Z, b, 1, Lb, Dn, N, ltiles, counts, st);
+  if (e == hipSuccess)
+    e = moelora::launch_combine(dt, Dn, pos, nullptr, S, 1, N, out, st, plan.ksplit_dn);
   return hip_status(e);
 }
 

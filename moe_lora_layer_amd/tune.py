@@ -41,7 +41,7 @@ LAYER_KEYS = ["tokens", "hidden", "intermediate", "experts", "top_k", "adapters"
 DENSE_KEYS = ["tokens", "in_features", "out_features", "adapters", "rank", "dtype", "flags"]
 
 # values tried per field (gemm_rows and gemm_form move together)
-GEMM_SHAPES = [(32, 1), (64, 1), (128, 1), (128, 2), (256, 2)]
+GEMM_SHAPES = [(32, 1), (64, 1), (128, 1), (128, 2), (128, 3), (256, 2)]
 SPLITS = [1, 2, 3, 4, 5, 6, 8, 12, 16]
 
 

@@ -185,7 +185,8 @@ PLAN_CASES = [
     dict(gemm_rows=48), dict(gemm_rows=-32), dict(gemm_form=3), dict(gemm_form=1),  # form needs rows
     dict(gemm_rows=256, gemm_form=1), dict(gemm_rows=64, gemm_form=2), dict(lora_rows=32),
     dict(ksplit_gate_up=-1), dict(ksplit_down=1025), dict(fuse=4), dict(fuse=-1), dict(order=6),
-    dict(order=-1),
+    dict(order=-1), dict(gemm_rows=64, gemm_form=3), dict(gemm_rows=256, gemm_form=3),
+    dict(gemm_form=4),
 ]
 
 
@@ -199,6 +200,18 @@ def test_bad_plans_are_refused_everywhere(plan):
     out = ops.Plan()
     assert lib.moelora_forward_plan(ctypes.byref(d), ctypes.byref(out)) == ERR_UNSUPPORTED
     dd = ops.make_dense_dims(64, 256, 512, 4, 16, "bf16", plan=plan)
+    assert lib.moelora_dense_workspace_size(ctypes.byref(dd), ctypes.byref(n)) == ERR_UNSUPPORTED
+
+
+def test_dma128_tiles_are_bf16_only():
+    # plan form 3 (128 x 256 DMA tiles) resolves for bf16 and is refused for fp32
+    p = ops.forward_plan(good_dims(plan=dict(gemm_rows=128, gemm_form=3)))
+    assert (p["gemm_rows"], p["gemm_form"]) == (128, 3)
+    n = ctypes.c_size_t()
+    lib = ops.library()
+    d = good_dims(dtype="f32", plan=dict(gemm_rows=128, gemm_form=3))
+    assert lib.moelora_forward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == ERR_UNSUPPORTED
+    dd = ops.make_dense_dims(64, 256, 512, 4, 16, "f32", plan=dict(gemm_rows=128, gemm_form=3))
     assert lib.moelora_dense_workspace_size(ctypes.byref(dd), ctypes.byref(n)) == ERR_UNSUPPORTED
 
 
@@ -246,13 +259,17 @@ def test_dense_plan():
 
 def test_dense_automatic_plan_fills_one_round():
     # 128 rows: the 128-row weight-streaming tiles would make 80 workgroups for
-    # 10240 outputs; the automatic plan takes weight-reuse tiles split over K
-    # into about one round of 256 instead (3 splits), and keeps the streaming
-    # tiles when they fill a round by themselves (65536 outputs: 512 tiles)
+    # 10240 outputs; the automatic plan takes the 128 x 256 DMA tiles (bf16:
+    # 40 of them) split over K into about one round of 256 instead (6 splits),
+    # fp32 the weight-reuse tiles (80, 3 splits), and keeps unsplit streaming
+    # tiles when they fill a round by themselves (65536 outputs: 512 tiles;
+    # bf16 streams them on the DMA tiles)
     p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16"))
+    assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 3, 6)
+    p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 10240, 16, 16, "f32"))
     assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 2, 3)
     p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 65536, 16, 16, "bf16"))
-    assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 1, 1)
+    assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 3, 1)
     # decode-sized rows keep their own tiles; an explicit field is respected
     assert ops.dense_forward_plan(ops.make_dense_dims(16, 8192, 10240, 16, 16, "bf16"))["gemm_rows"] == 32
     p = ops.dense_forward_plan(ops.make_dense_dims(128, 8192, 10240, 16, 16, "bf16",
@@ -261,7 +278,7 @@ def test_dense_automatic_plan_fills_one_round():
     # a narrow output over a short K: the forced split keeps >= 8 K-steps per
     # split (96 rows, K 2048 = 32 steps, N 128: 4 splits, not 256 / 1)
     p = ops.dense_forward_plan(ops.make_dense_dims(96, 2048, 128, 4, 16, "bf16"))
-    assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 2, 4)
+    assert (p["gemm_rows"], p["gemm_form"], p["ksplit_down"]) == (128, 3, 4)
 
 
 def test_plan_table_round_trip(tmp_path):

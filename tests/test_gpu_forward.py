@@ -469,16 +469,30 @@ FOLD_SHAPES = [(64, 256, 512, 8, 2, 4, 16, "bf16"), (96, 192, 320, 5, 2, 3, 32, 
 @pytest.mark.parametrize("shape", FOLD_SHAPES, ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
 def test_folded_down_shrink_z2(shape, det, in_out):
     """Plan fuse = 3: the down projection's shrink folded into the fused
-    gate_up epilogue (every fused tile family: 32-, 64-row, 128-row streaming
-    and reuse, 256-row; both weight layouts): Z2 read back from the workspace
-    against the oracle's z2 = a A_dn per slot, and the layer output against
-    the oracle."""
+    gate_up epilogue (every fused tile family the automatic plan picks: 32-,
+    64-row, 128-row streaming and reuse, 256-row; both weight layouts): Z2
+    read back from the workspace against the oracle's z2 = a A_dn per slot,
+    and the layer output against the oracle."""
+    _check_folded(shape, det, in_out, dict(fuse=3))
+
+
+@pytest.mark.parametrize("in_out", [False, True], ids=["k_contig", "in_out"])
+@pytest.mark.parametrize("det", [False, True], ids=["atomics", "deterministic"])
+@pytest.mark.parametrize("shape", FOLD_SHAPES[1:4], ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
+def test_folded_down_shrink_z2_dma128(shape, det, in_out):
+    """The same on the 128 x 256 DMA tiles (plan form 3)."""
+    _check_folded(shape, det, in_out, dict(fuse=3, gemm_rows=128, gemm_form=3))
+
+
+def _check_folded(shape, det, in_out, plan):
     from gpu_util import in_out as to_in_out
     cfg = _small(*shape, seed=sum(shape[:7]) + 11)
     inp = synth.make_inputs(cfg)
-    d = ops.dims_for(cfg, deterministic=det, in_out=in_out, plan=dict(fuse=3))
+    d = ops.dims_for(cfg, deterministic=det, in_out=in_out, plan=plan)
     assert ops.forward_fusion(d)["down_shrink"] and ops.forward_plan(d)["fuse"] == 3
     assert not ops.forward_fusion(ops.dims_for(cfg))["down_shrink"]   # never automatic
+    if "gemm_form" in plan:
+        assert ops.forward_plan(d)["gemm_form"] == plan["gemm_form"]
     _, (ids, w, ss, off), out, ws = _layer(cfg, to_in_out(inp) if in_out else inp, d)
     lay = ops.forward_workspace_layout(d)
     S, r = cfg.slots, cfg.rank
