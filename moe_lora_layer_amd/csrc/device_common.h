@@ -165,6 +165,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier after this wave's LDS accesses have completed (lgkmcnt(0)),
+// with no fence: outstanding global stores and loads are not waited for.  For
+// points where no direct-to-LDS load is in flight.
+__device__ __forceinline__ void lds_only_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Row (within the 32x32 block) of accumulator element i held by a lane of half h.
 __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 

@@ -23,7 +23,6 @@ namespace moelora {
 
 // ------------------------------------------------------------------------- prep
 constexpr int kPrepThreads = 1024;
-constexpr int kXcds = 8;  // XCDs of an MI355X
 
 // Writes tiles for items [i0, i1) whose lengths come from offsets at stride
 // `step`; `first` is the index of the first tile of item i0.
@@ -67,6 +66,8 @@ k_prep(const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ off
     const int s = sorted_slots[p];
     if (s >= 0 && s < S) pos[s] = p;
   }
+  // the work queues of the persistent GEMM launches start empty
+  if (tid >= kQueueBase && tid < kQueueBase + 2 * kXcds) counts[tid] = 0;
 
   // M-tiles: one item per expert, rows [offsets[e*L], offsets[(e+1)*L]).
   {
@@ -964,8 +965,9 @@ struct GemmArgs {
   const int32_t* counts;
   const int32_t* expert_tiles;
   int ksplit;
-  float* parts;         // deterministic split-K partials, or nullptr
+  float* parts;         // split-K partials, or nullptr
   int64_t part_stride;  // elements per partial (rows of C times N)
+  int32_t* queue;       // kXcds tile-queue counters (zero) for a persistent launch, or nullptr
 };
 
 template <bool KN, typename T, int BM, int BN, int WM, int WN, int P, bool NT, bool GATHER,
@@ -1074,10 +1076,16 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
                                          int64_t K, float* __restrict__ C, int4 tile, int nt,
                                          int kbeg, int nk, int out, bool with_lora,
                                          const LoraEpilogue& lora, float* __restrict__ part,
-                                         int kstart) {
+                                         int kstart, int32_t* qpop, int& qraw) {
   typedef DmaShape<BM> S;
   constexpr int FM = S::kFM, WR = S::kWaveRows;
-  lds_barrier();  // every wave is done with what the LDS held for the previous item
+  // every wave is done with what the LDS held for the previous item (its
+  // direct-to-LDS loads were all waited for; a persistent workgroup's next
+  // tile does not wait for the previous epilogue's global stores either)
+  if (qpop != nullptr)
+    lds_only_barrier();
+  else
+    lds_barrier();
   const int e = tile.x, row0 = tile.y, row_end = tile.z;
   // Output columns.  EPI_GATE_UP: the tile covers 128 columns i of the
   // intermediate width I = N/2; wave column group wn owns i in
@@ -1269,6 +1277,10 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
     default: k_loop(std::integral_constant<int, FM>{}); break;
   }
   wait_vmcnt<0>();  // no LDS write of this item may outlive it
+  // persistent workgroup: take the next tile now, so that the pop's round trip
+  // overlaps the epilogue (a pop at the start of the tile instead let the
+  // M-tiles sharing a weight tile drift apart)
+  if (qpop != nullptr && threadIdx.x == 0) qraw = atomicAdd(qpop, 1);
 
   // output column of fragment j held by this lane
   int64_t col[2];
@@ -1369,19 +1381,62 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
            int gather_k, const bf16_t* __restrict__ Wt, int64_t N, int64_t K, float* __restrict__ C,
            const int4* __restrict__ mtiles, const int32_t* __restrict__ counts,
            const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, LoraEpilogue lora,
-           float* __restrict__ parts, int64_t part_stride, int sk_mode, int nwg, int order) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[DmaShape<BM>::kStages * DmaShape<BM>::kStage];
+           float* __restrict__ parts, int64_t part_stride, int sk_mode, int nwg, int order,
+           int32_t* __restrict__ queue) {
+  // the K stages, then 16 bytes for the next tile of a persistent workgroup
+  // (inside the one LDS array: a second LDS object made the compiler wait
+  // for every direct-to-LDS load before each fragment read of the K loop)
+  constexpr int kStagesBytes = DmaShape<BM>::kStages * DmaShape<BM>::kStage;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStagesBytes + 16];
+  int* const s_next = reinterpret_cast<int*>(smem + kStagesBytes);
   const int tiles = counts[0] * n_ntiles;
   const int dp = sk_mode == 0 ? tiles : dma_dp_tiles(tiles, nwg);
   const int nk_all = static_cast<int>(K / 64);
-  // the items of this workgroup: one (tile, K split) in modes 0 and 1, the
-  // units [u, u1) in mode 2 (one call site of dma_item, so one inlined copy)
+  // Persistent workgroups (queue != nullptr; the gate_up forms' data-parallel
+  // tiles without stream-K, unsplit K, XCD-grouped order): one workgroup per CU takes tile after tile from the
+  // queue of its XCD (the XCD-grouped numbering: XCD y's tiles are the
+  // contiguous run [y q + min(y, rem), + q + (y < rem))), then from the other
+  // XCDs' queues once its own is empty.  No workgroup launch between tiles,
+  // and the XCDs finish together.  queue[y] counts the pops of run y; it
+  // starts at zero and may overshoot its run's length.
+  // (compiled for the gate_up forms only: the others run stream-K for their
+  // last round, and the persistent loop's code cost their K loop 1-2 %)
+  const bool pers = is_gu(EPI) && queue != nullptr && sk_mode != 2;
+  const int qq = dp / kXcds, qrem = dp % kXcds, qx = static_cast<int>(blockIdx.x) % kXcds;
+  auto qlen = [&](int y) { return qq + (y < qrem ? 1 : 0); };
+  auto pop = [&](int idx0) {  // thread 0; idx0 >= 0: a pop of run qx already made
+    if (idx0 < 0) idx0 = atomicAdd(&queue[qx], 1);
+    if (idx0 < qlen(qx)) return qx * qq + min(qx, qrem) + idx0;
+    // the own run is done: read every run's counter at once, then pop from
+    // those not yet exhausted
+    int c[kXcds];
+#pragma unroll
+    for (int y = 0; y < kXcds; ++y)
+      c[y] = __hip_atomic_load(&queue[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 1; i < kXcds; ++i) {
+      const int y = (qx + i) % kXcds;
+      if (c[y] >= qlen(y)) continue;
+      const int idx = atomicAdd(&queue[y], 1);
+      if (idx < qlen(y)) return y * qq + min(y, qrem) + idx;
+    }
+    return -1;
+  };
+  // the items of this workgroup: one (tile, K split) in modes 0 and 1 (tiles
+  // until the queues are empty when persistent), the units [u, u1) in mode 2
+  // (one call site of dma_item, so one inlined copy)
   int u = 0, u1 = 0;  // at most 255 tiles x 16384 K-steps
   int bid = 0, ks = 0;
+  int raw = -1;  // thread 0: the pop of run qx made during the last epilogue
   if (sk_mode == 2) {
     const int64_t units = static_cast<int64_t>(tiles - dp) * nk_all;
     u = static_cast<int>(units * blockIdx.x / nwg);
     u1 = static_cast<int>(units * (blockIdx.x + 1) / nwg);
+  } else if (pers) {
+    if (threadIdx.x == 0) *s_next = pop(-1);
+    __syncthreads();
+    bid = *s_next;
+    if (bid < 0) return;  // uniform
+    u1 = 1;
   } else {
     // workgroup order: XCD remap over the real workgroups, then tile index
     ks = static_cast<int>(blockIdx.x) % ksplit;
@@ -1427,7 +1482,7 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
       out = ksplit == 1 ? DMA_OUT_STORE : (parts != nullptr ? DMA_OUT_PART : DMA_OUT_ATOMIC);
       if (parts != nullptr) part = parts + ks * part_stride;
       with_lora = true;
-      u = u1;
+      if (!pers) u = u1;
     }
     // rotated or staggered K walk (data-parallel items only, as in k_gemm):
     // this workgroup starts at step kstart
@@ -1439,7 +1494,15 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
         kstart = (kOrderStagger * m_local) % nk;
     }
     dma_item<BM, GATHER, EPI, KN>(smem, X, x_rows, gather_slots, gather_k, Wt, N, K, C, tile, nt,
-                                  kbeg, nk, out, with_lora, lora, part, kstart);
+                                  kbeg, nk, out, with_lora, lora, part, kstart,
+                                  pers ? queue + qx : nullptr, raw);
+    if (pers) {
+      // every wave has read s_next (the item's barriers lie between)
+      if (threadIdx.x == 0) *s_next = pop(raw);
+      lds_only_barrier();
+      bid = *s_next;
+      if (bid < 0) u = u1;  // uniform
+    }
   }
 }
 
@@ -1462,18 +1525,33 @@ static hipError_t dma_launch(const TilePlan& plan, const GemmArgs& a, const Lora
   }
   // the tiles' upper bound must reach a round for the device to pick stream-K
   const int mode = nwg > 0 && static_cast<int64_t>(plan.max_mt) * n_ntiles >= nwg ? 1 : 0;
-  hipLaunchKernelGGL((k_gemm_dma<BM, GATHER, EPI, KN>), dim3(static_cast<unsigned>(grid)), dim3(kDmaThreads),
-                     0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
+  // persistent data-parallel launch: one workgroup per CU over the tile
+  // queues, when the tiles may exceed one round (unsplit K, XCD-grouped order)
+  int ncu = 0;
+  // (not with stream-K, which already evens out the last round)
+  const bool pers = is_gu(EPI) && a.queue != nullptr && a.ksplit == 1 && mode == 0 &&
+                    (plan.order == ORDER_XCD || plan.order == ORDER_XCD_STAGGERED);
+  if (pers) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+  }
+  const bool use_q = pers && grid > ncu;
+  hipLaunchKernelGGL((k_gemm_dma<BM, GATHER, EPI, KN>),
+                     dim3(static_cast<unsigned>(use_q ? ncu : grid)), dim3(kDmaThreads), 0, stream,
+                     static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
                      a.expert_tiles, n_ntiles, a.ksplit, lora, a.parts, a.part_stride, mode, nwg,
-                     plan.order);
+                     plan.order, use_q ? a.queue : nullptr);
   if (mode == 0) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemm_dma<BM, GATHER, EPI, KN>), dim3(static_cast<unsigned>(nwg)), dim3(kDmaThreads),
                      0, stream, static_cast<const bf16_t*>(a.X), a.x_rows, a.gather_slots, a.gather_k,
                      static_cast<const bf16_t*>(a.Wt), a.N, a.K, a.C, a.mtiles, a.counts,
-                     a.expert_tiles, n_ntiles, 1, lora, a.parts, a.part_stride, 2, nwg, plan.order);
+                     a.expert_tiles, n_ntiles, 1, lora, a.parts, a.part_stride, 2, nwg, plan.order,
+                     nullptr);
   return hipGetLastError();
 }
 
@@ -1525,11 +1603,11 @@ hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_row
                        int64_t K, float* C, int64_t c_rows, const int4* mtiles,
                        const int32_t* counts, const int32_t* expert_tiles, int ksplit,
                        const LoraEpilogue* lora, float* parts, hipStream_t stream,
-                       bool sum_parts) {
+                       bool sum_parts, int32_t* queue) {
   ksplit = ksplit < 1 ? 1 : ksplit;
   float* pp = ksplit > 1 ? parts : nullptr;
   const GemmArgs a{X, x_rows, gather_slots, gather_k, Wt, N, K, C, mtiles, counts, expert_tiles,
-                   ksplit, pp, c_rows * N};
+                   ksplit, pp, c_rows * N, queue};
   const bool gather = gather_slots != nullptr;
   // the fused epilogues: bf16, unsplit K
   if (lora != nullptr && (dtype != DT_BF16 || a.ksplit != 1))

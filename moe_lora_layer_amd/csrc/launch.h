@@ -34,6 +34,13 @@ hipError_t launch_align(const float* logits, const int32_t* ids_in, const int32_
                         int32_t* sorted_slots, int32_t* offsets, int32_t* status, int32_t* ws_key,
                         int32_t* ws_rank, int32_t* ws_cnt, hipStream_t stream);
 
+constexpr int kXcds = 8;  // XCDs of an MI355X
+// counts[] in the forward workspace: [0] M-tiles, [1] LoRA tiles, then from
+// kQueueBase the tile-queue counters of the persistent GEMM launches (kXcds
+// for gate_up, kXcds for down), cleared by the prep launch
+constexpr int kQueueBase = 4;
+constexpr int kCountsInts = kQueueBase + 2 * kXcds;
+
 // Workgroup order of the base GEMMs (moelora_plan.order): launch order, the
 // expert's tiles grouped per XCD, every workgroup's K walk rotated, or both.
 enum { ORDER_LAUNCH = 1, ORDER_XCD = 2, ORDER_ROTATED = 3, ORDER_XCD_ROTATED = 4, ORDER_XCD_STAGGERED = 5 };
@@ -109,13 +116,15 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
 // parts != nullptr (ksplit > 1): split s writes its partial tile to
 // parts + s * c_rows * N with plain stores and, when sum_parts, a second launch
 // sums them into C in split order (C needs no clearing then); without
-// sum_parts the caller consumes the partials.
+// sum_parts the caller consumes the partials.  queue != nullptr: kXcds
+// counters, zero beforehand, for the 256- and 128-row bf16 tiles' persistent
+// launch (one workgroup per CU taking tiles from per-XCD queues).
 hipError_t launch_gemm(int dtype, const TilePlan& plan, const void* X, int x_rows,
                        const int32_t* gather_slots, int gather_k, const void* Wt, int64_t N,
                        int64_t K, float* C, int64_t c_rows, const int4* mtiles,
                        const int32_t* counts, const int32_t* expert_tiles, int ksplit,
                        const LoraEpilogue* lora, float* parts, hipStream_t stream,
-                       bool sum_parts = true);
+                       bool sum_parts = true, int32_t* queue = nullptr);
 
 // out[i] = sum over p < nparts, in order, of parts[p * n + i] (n a multiple of 4).
 hipError_t launch_reduce_parts(const float* parts, int nparts, int64_t n, float* out,

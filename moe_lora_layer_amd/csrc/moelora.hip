@@ -180,7 +180,7 @@ ForwardLayout forward_layout(const moelora_dims* d, const TilePlan& plan) {
   ForwardLayout L;
   size_t off = 0;
   L.pos = off;    off += round_up(S * 4);
-  L.counts = off; off += round_up(4 * 4);
+  L.counts = off; off += round_up(moelora::kCountsInts * 4);
   L.etiles = off; off += round_up((static_cast<size_t>(d->experts) + 1) * 4);
   L.mtiles = off; off += round_up(static_cast<size_t>(plan.max_mt) * 16);
   L.ltiles = off; off += round_up(static_cast<size_t>(plan.max_lt) * 16);
@@ -288,7 +288,7 @@ DenseLayout dense_layout(const moelora_dims* m, const TilePlan& plan) {
   L.slots = off;   off += round_up(T * 4);
   L.offsets = off; off += round_up((Lb + 1) * 4);
   L.pos = off;     off += round_up(T * 4);
-  L.counts = off;  off += round_up(4 * 4);
+  L.counts = off;  off += round_up(moelora::kCountsInts * 4);
   L.etiles = off;  off += round_up(2 * 4);
   L.mtiles = off;  off += round_up(static_cast<size_t>(plan.max_mt) * 16);
   L.ltiles = off;  off += round_up(static_cast<size_t>(plan.max_lt) * 16);
@@ -608,7 +608,8 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
                                     static_cast<int64_t>(S) * r};
     e = moelora::launch_gemm(dt, plan, x, static_cast<int>(T), sorted_slots, k, w_gate_up, 2 * I,
                              h, G, S, mtiles, counts, etiles, plan.ksplit_gu,
-                             plan.fuse_gu ? &epi : nullptr, parts, st);
+                             plan.fuse_gu ? &epi : nullptr, parts, st, true,
+                             counts + moelora::kQueueBase);
   }
   if (e == hipSuccess) e = mark(MOELORA_STAGE_EXPAND_GATE_UP);
   if (e == hipSuccess && !plan.fuse_gu)
@@ -630,7 +631,7 @@ int moelora_forward_profiled(const moelora_dims* dims, const void* x, const void
                                     E, dims->adapters, r, Lad, h, nullptr};
     e = moelora::launch_gemm(dt, plan, ACT, S, nullptr, 1, w_down, h, I, D, S, mtiles, counts,
                              etiles, plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, dparts, st,
-                             false);
+                             false, counts + moelora::kQueueBase + moelora::kXcds);
   }
   if (e == hipSuccess) e = mark(MOELORA_STAGE_EXPAND_DOWN);
   if (e == hipSuccess && !plan.fuse_dn)
@@ -711,7 +712,8 @@ int moelora_dense_forward(const moelora_dense_dims* dims, const void* x, const v
     const moelora::LoraEpilogue epi{Z, static_cast<const uint16_t*>(b), offsets, 1, nad, r, Lb, N,
                                     nullptr};
     e = moelora::launch_gemm(dt, plan, x, S, slots, 1, w, N, K, D, S, mtiles, counts, etiles,
-                             plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, dparts, st, false);
+                             plan.ksplit_dn, plan.fuse_dn ? &epi : nullptr, dparts, st, false,
+                             counts + moelora::kQueueBase + moelora::kXcds);
   }
   // split K: partial planes, the expand into plane 0, the ordered sum in the combine
   float* Dn = plan.ksplit_dn > 1 ? dparts : D;
