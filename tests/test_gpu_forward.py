@@ -62,10 +62,11 @@ SMALL = [
     (700, 256, 320, 3, 2, 5, 32, "bf16"),
     (520, 192, 256, 2, 1, 9, 64, "bf16"),
     (300, 128, 256, 1, 1, 16, 16, "bf16"),
-    # one expert, narrow output: split-K with atomics in the down GEMM
+    # one expert, narrow output: the down GEMM split over K into partial
+    # planes that the combine sums
     (96, 128, 2048, 1, 1, 4, 16, "bf16"),
-    # 175 rows per expert: 128-row tiles that reuse the weight tile (four
-    # waves of 64 x 64), fused epilogues with two fragments per wave
+    # 175 rows per expert: one 256-row tile per expert (bf16 above 160 rows
+    # per expert; the 128-row reuse tiles run under forced plans)
     (350, 192, 320, 4, 2, 3, 32, "bf16"),
     # top-8 routing over 64 experts; and the largest bucket count (E x L =
     # 8192) with most experts and buckets empty
@@ -172,6 +173,29 @@ def test_forward_workload(name):
     assert covered == tiles
     ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w, tokens=toks)
     assert_close(to_f64(out)[toks], ref, cfg.dtype, f"{name} out")
+
+
+def test_persistent_gate_up_queues():
+    """More gate_up tiles than CUs (bf16, 256-row tiles, XCD-grouped order:
+    6 M-tiles x 64 N-tiles): the gate_up GEMM runs one workgroup per CU over
+    per-XCD tile queues, stealing from the other XCDs' queues at the end.
+    Against the oracle, and bit for bit against the same plan in launch order
+    (one workgroup per tile) in deterministic mode."""
+    cfg = _small(512, 64, 8192, 3, 2, 4, 16, "bf16", seed=71)
+    inp = synth.make_inputs(cfg)
+    d = ops.dims_for(cfg, deterministic=True)
+    plan = ops.forward_plan(d)
+    assert (plan["gemm_rows"], plan["order"], plan["ksplit_gate_up"]) == (256, 2, 1)
+    _, _, out, _ = _layer(cfg, inp, d)
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
+    assert_close(to_f64(out), ref, "bf16", "persistent gate_up")
+    for _ in range(2):  # the queues start empty on every call
+        _, _, again, _ = _layer(cfg, inp, d)
+        assert torch.equal(again, out)
+    d1 = ops.dims_for(cfg, deterministic=True, plan=dict(plan, order=1))
+    _, _, out1, _ = _layer(cfg, inp, d1)
+    assert torch.equal(out1, out)
 
 
 def test_forward_tile_boundaries():
