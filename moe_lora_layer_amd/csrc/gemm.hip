@@ -450,17 +450,32 @@ __device__ __forceinline__ void folded_down_shrink(const f32x16_t (&acc)[FM][FN]
 
 // Adapter buckets of expert e meeting rows [row0, row_end), as [lb, ub); a
 // base-only bucket, if any, comes last in the expert and is left out.
+// lb is the last bucket starting at or before row0 (0 if none), ub the first
+// at or after lb starting at or after row_end.  Up to 64 adapters every lane
+// of the wave loads one bucket start and two ballots give both ends in one
+// memory round trip (the offsets are nondecreasing, so the buckets starting
+// before row_end are a prefix); above that a binary search and a scan.
 __device__ __forceinline__ void lora_buckets(const LoraEpilogue& lora, int e, int row0, int row_end,
                                              int& lb, int& ub) {
   const int32_t* off = lora.offsets + static_cast<int64_t>(e) * lora.buckets;
+  const int nad = lora.adapters;
+  if (nad <= kWave) {
+    const int l = threadIdx.x & (kWave - 1);
+    const int o = l < nad ? off[l] : 0;
+    const uint64_t le = __ballot(l < nad && o <= row0);
+    const uint64_t lt = __ballot(l < nad && o < row_end);
+    lb = le == 0 ? 0 : 63 - __builtin_clzll(le);
+    ub = max(lb, __popcll(lt));
+    return;
+  }
   lb = 0;
-  int hb = lora.adapters - 1;
+  int hb = nad - 1;
   while (lb < hb) {
     const int mid = (lb + hb + 1) >> 1;
     if (off[mid] <= row0) lb = mid; else hb = mid - 1;
   }
   ub = lb;
-  while (ub < lora.adapters && off[ub] < row_end) ++ub;
+  while (ub < nad && off[ub] < row_end) ++ub;
 }
 
 // ksplit > 1: workgroup (tile, s) covers the s-th of ksplit K ranges and adds
