@@ -19,11 +19,10 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round to nearest, ties to even.  Inputs are finite here.
+// Round to nearest, ties to even: gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32), one instruction instead of three integer ones.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
@@ -118,7 +117,6 @@ template <> struct Mfma16<float> {
   __device__ __forceinline__ static frag_t zero() { return 0.0f; }
 };
 
-// SiLU(v) = v / (1 + e^-v), with the device expf.
 // SiLU(v) = v * sigma(v) = v / (1 + e^-v), from the hardware base-2
 // exponential and reciprocal (each within about one fp32 ulp, so the result
 // is good to a few fp32 ulps, far inside the bf16 rounding of an activation).

@@ -1322,15 +1322,31 @@ __device__ __forceinline__ void dma_item(unsigned char* smem, const bf16_t* __re
   }
 
   if (is_gu(EPI)) {
+    // Activation (block i, accumulator element r) of this lane lies at row
+    // rw0 + 4h + ro(i, r) of its column: a lane base address plus a row
+    // offset that is the same for every lane (a scalar product), rather than
+    // a 64-bit product per element.  A wave's 32 columns are all inside or
+    // all outside the output (I is a multiple of 64, tile columns start at
+    // multiples of 128), so a block with all of its 32 rows in the tile
+    // stores without per-element tests.
+    auto ro = [](int i, int r) { return 32 * i + acc_row(r, 0); };
+    bf16_t* const act_l = lora.act + static_cast<int64_t>(rw0 + 4 * h) * I + col[0];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; ++r)
         acc[i][0][r] = silu(acc[i][0][r]) * acc[i][1][r];  // the activation, in place of gate
-        const int p = rw0 + 32 * i + acc_row(r, h);
-        if (p < row_end && col_ok[0])
-          lora.act[static_cast<int64_t>(p) * I + col[0]] = f32_to_bf16(acc[i][0][r]);
+      if (col_ok[0] && rw0 + 32 * i + 32 <= row_end) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          act_l[static_cast<int64_t>(ro(i, r)) * I] = f32_to_bf16(acc[i][0][r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (col_ok[0] && rw0 + 4 * h + ro(i, r) < row_end)
+            act_l[static_cast<int64_t>(ro(i, r)) * I] = f32_to_bf16(acc[i][0][r]);
       }
+    }
     if constexpr (EPI == EPI_GATE_UP_FOLD) {
       const bool wr[2] = {true, false};
       folded_down_shrink<FM, 2, 1, KN>(acc, col, wr, col_ok, rw0, lora, smem, kDmaThreads / kWave,
