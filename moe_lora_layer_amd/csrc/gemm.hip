@@ -1414,11 +1414,12 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
            const int32_t* __restrict__ expert_tiles, int n_ntiles, int ksplit, LoraEpilogue lora,
            float* __restrict__ parts, int64_t part_stride, int sk_mode, int nwg, int order,
            int32_t* __restrict__ queue) {
-  // the K stages, then 16 bytes for the next tile of a persistent workgroup
-  // (inside the one LDS array: a second LDS object made the compiler wait
-  // for every direct-to-LDS load before each fragment read of the K loop)
+  // the K stages, then 32 bytes for the next tile of a persistent workgroup:
+  // its index and descriptor (inside the one LDS array: a second LDS object
+  // made the compiler wait for every direct-to-LDS load before each fragment
+  // read of the K loop)
   constexpr int kStagesBytes = DmaShape<BM>::kStages * DmaShape<BM>::kStage;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStagesBytes + 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStagesBytes + 32];
   int* const s_next = reinterpret_cast<int*>(smem + kStagesBytes);
   const int tiles = counts[0] * n_ntiles;
   const int dp = sk_mode == 0 ? tiles : dma_dp_tiles(tiles, nwg);
@@ -1452,6 +1453,25 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     }
     return -1;
   };
+  // thread 0: the next tile and its descriptor to s_next ([0] tile index or
+  // -1, [1..4] the M-tile, [5] N-tile, [6] M-tile within the expert), so that
+  // the descriptor's three dependent loads overlap the other waves' epilogue
+  // instead of following the barrier
+  auto pop_next = [&](int idx0) {
+    const int b = pop(idx0);
+    s_next[0] = b;
+    if (b >= 0) {
+      int4 t;
+      int n, m;
+      dma_tile_of(b, n_ntiles, mtiles, expert_tiles, t, n, m);
+      s_next[1] = t.x;
+      s_next[2] = t.y;
+      s_next[3] = t.z;
+      s_next[4] = t.w;
+      s_next[5] = n;
+      s_next[6] = m;
+    }
+  };
   // the items of this workgroup: one (tile, K split) in modes 0 and 1 (tiles
   // until the queues are empty when persistent), the units [u, u1) in mode 2
   // (one call site of dma_item, so one inlined copy)
@@ -1463,9 +1483,9 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
     u = static_cast<int>(units * blockIdx.x / nwg);
     u1 = static_cast<int>(units * (blockIdx.x + 1) / nwg);
   } else if (pers) {
-    if (threadIdx.x == 0) *s_next = pop(-1);
+    if (threadIdx.x == 0) pop_next(-1);
     __syncthreads();
-    bid = *s_next;
+    bid = s_next[0];
     if (bid < 0) return;  // uniform
     u1 = 1;
   } else {
@@ -1505,7 +1525,13 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
       with_lora = kbeg == 0;
       u += nk;
     } else {
-      dma_tile_of(bid, n_ntiles, mtiles, expert_tiles, tile, nt, m_local);
+      if (pers) {
+        tile = make_int4(s_next[1], s_next[2], s_next[3], s_next[4]);
+        nt = s_next[5];
+        m_local = s_next[6];
+      } else {
+        dma_tile_of(bid, n_ntiles, mtiles, expert_tiles, tile, nt, m_local);
+      }
       const int nk_per = (nk_all + ksplit - 1) / ksplit;
       kbeg = min(nk_all, ks * nk_per);
       nk = min(nk_all, kbeg + nk_per) - kbeg;
@@ -1529,9 +1555,9 @@ k_gemm_dma(const bf16_t* __restrict__ X, int x_rows, const int32_t* __restrict__
                                   pers ? queue + qx : nullptr, raw);
     if (pers) {
       // every wave has read s_next (the item's barriers lie between)
-      if (threadIdx.x == 0) *s_next = pop(raw);
+      if (threadIdx.x == 0) pop_next(raw);
       lds_only_barrier();
-      bid = *s_next;
+      bid = s_next[0];
       if (bid < 0) u = u1;  // uniform
     }
   }
