@@ -294,7 +294,8 @@ __device__ __forceinline__ void staged_lora_expand(f32x16_t (&acc)[FM][FN], cons
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4)
-            bfr[j][q4] = *reinterpret_cast<const bf16x8_t*>(bt + lrow[j] * rk * 2 + 32 * min(q4, nks - 1));
+            if (q4 < nks)  // (rk is known at run time only: no reads for unused steps)
+              bfr[j][q4] = *reinterpret_cast<const bf16x8_t*>(bt + lrow[j] * rk * 2 + 32 * q4);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
