@@ -99,6 +99,40 @@ def test_forward_small(shape):
     assert_close(to_f64(out), ref, cfg.dtype, "out")
 
 
+def _times_pow2(a, dtype, factor):
+    """a * factor for a power of two (exact: bf16 patterns are widened to fp32,
+    scaled and narrowed back without rounding)."""
+    if dtype == "f32":
+        return (a * np.float32(factor)).astype(np.float32)
+    f = (a.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# Gate values far outside SiLU's curved part: gate_up weights times 2^6 (exact)
+# put G = xW at a standard deviation near 64, so the epilogues meet SiLU's
+# linear side and its saturated side, where e^-v overflows fp32 (v < -88):
+# the 256-row direct-to-LDS tiles (first shape) and the register-staged ones
+LARGE_GATE = [(600, 128, 192, 4, 2, 3, 16, "bf16"), (96, 192, 320, 5, 2, 3, 32, "bf16"),
+              (96, 192, 320, 5, 2, 3, 32, "f32")]
+
+
+@pytest.mark.parametrize("shape", LARGE_GATE, ids=lambda s: "T%d_h%d_I%d_E%d_k%d_L%d_r%d_%s" % s)
+def test_forward_large_gate_values(shape):
+    cfg = _small(*shape, seed=7 + sum(shape[:7]))
+    say(f"forward large gate values {shape}")
+    inp = dict(synth.make_inputs(cfg))
+    inp["w_gate_up"] = _times_pow2(inp["w_gate_up"], cfg.dtype, 64)
+    # the premise: the gate values reach both SiLU regions
+    f64 = lambda a: (a if cfg.dtype == "f32" else (a.astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+    g = np.einsum("th,enh->ten", f64(inp["x"]), f64(inp["w_gate_up"])[:, :cfg.intermediate, :])
+    assert g.max() > 88.0 and g.min() < -88.0
+    _, (ids, w, ss, off), out, _ = _layer(cfg, inp)
+    ref_ids, ref_w = oracle.route(inp["logits"], cfg.top_k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref = oracle.forward(inp, oracle.dims_of(cfg), ref_ids, ref_w)
+    assert_close(to_f64(out), ref, cfg.dtype, "out")
+
+
 # bf16 shapes run again with MOELORA_FLAG_UNFUSED: the LoRA expands as
 # kernels of their own after each GEMM (one shape per GEMM tile shape)
 UNFUSED = [(64, 256, 512, 8, 2, 4, 16, "bf16"), (96, 192, 320, 5, 2, 3, 32, "bf16"),
