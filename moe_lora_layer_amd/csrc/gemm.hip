@@ -14,6 +14,7 @@
 // fragment reads (consecutive rows, same chunk) hit all banks, double
 // buffered: the next K-step's global loads are in flight while the MFMAs of
 // the current one run.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -55,16 +56,19 @@ k_prep(const int32_t* __restrict__ sorted_slots, const int32_t* __restrict__ off
        int32_t* __restrict__ expert_tiles, float4* __restrict__ zero, int64_t zero_n4) {
   __shared__ int wave_tmp[16];
   const int tid = threadIdx.x;
+  // every workgroup: its share of the inverse permutation (one pass per
+  // thread for the batches here, instead of S / 1024 dependent round trips
+  // in one workgroup)
+  for (int p = blockIdx.x * kPrepThreads + tid; p < S; p += gridDim.x * kPrepThreads) {
+    const int s = sorted_slots[p];
+    if (s >= 0 && s < S) pos[s] = p;
+  }
   if (blockIdx.x > 0) {  // the other workgroups clear the accumulator region
     const int64_t stride = static_cast<int64_t>(gridDim.x - 1) * kPrepThreads;
     for (int64_t i = (blockIdx.x - 1) * static_cast<int64_t>(kPrepThreads) + tid; i < zero_n4;
          i += stride)
       zero[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
-  }
-  for (int p = tid; p < S; p += kPrepThreads) {
-    const int s = sorted_slots[p];
-    if (s >= 0 && s < S) pos[s] = p;
   }
   // the work queues of the persistent GEMM launches start empty
   if (tid >= kQueueBase && tid < kQueueBase + 2 * kXcds) counts[tid] = 0;
@@ -108,6 +112,8 @@ hipError_t launch_prep(const int32_t* sorted_slots, const int32_t* offsets, int 
   const int64_t n4 = zero_n / 4;  // callers pass multiples of 4
   int64_t zblocks = (n4 + kPrepThreads - 1) / kPrepThreads;
   if (zblocks > 512) zblocks = 512;
+  // at least one pass of the inverse permutation per thread
+  zblocks = std::max<int64_t>(zblocks, (S + kPrepThreads - 1) / kPrepThreads - 1);
   hipLaunchKernelGGL(k_prep, dim3(static_cast<unsigned>(1 + zblocks)), dim3(kPrepThreads), 0,
                      stream, sorted_slots, offsets, S, E, L, plan.bm, plan.bml, plan.max_mt,
                      plan.max_lt, pos, mtiles, ltiles, counts, expert_tiles,
